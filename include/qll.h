@@ -1,0 +1,150 @@
+/*
+ * qll.h -- C ABI of libqll.so, the quantized linear layer y = x.W^T for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *  [CPU]   llama.cpp visual guide, lesson 31 "CPU backend", section "How the
+ *          quantized dot product works" (block_q4_0, the Q4_0 x Q8_0 dot).
+ *  [FAST]  Fucina course "Chapter 06 -- Going fast on CPUs": 6.1 "Where the
+ *          time goes" (GEMM naming, decode is bandwidth-bound, prefill is
+ *          compute-bound), 6.3 "The kernel contract: small, unchecked,
+ *          allocation-free", 6.4 "The scalar backend is the specification".
+ *  [BACK]  Fucina reference "Backends": 9.2 (the kernel contract: validate
+ *          once above, kernels below are unchecked), 9.7 "Quantized matmul
+ *          dispatch" (per-call Q8_0 activation quantization; pre-quantized
+ *          LHS entries), 9.9 "GPU offload" (an entry reports that it did not
+ *          run instead of failing silently).
+ *  [LOOM]  Loom "Plan 9 SIMD Forward", section "BitNet ternary MAD kernel".
+ *
+ * Conventions shared by every entry point
+ *  - Data pointers are DEVICE pointers owned by the caller.  The library never
+ *    allocates, frees or retains them.  Base addresses must be 16-byte aligned
+ *    (every PyTorch/hipMalloc allocation is).  Tensors are dense, row-major.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call checks
+ *    its arguments on the host in O(1), enqueues its kernel(s) on `stream` and
+ *    returns without synchronising.  On error nothing is enqueued.  Faults
+ *    during execution surface at the caller's next synchronisation.
+ *  - Return value: QLL_OK (0) or a negative QLL_ERR_* code; qll_status_string
+ *    names it.  Argument checks run before any HIP call, so an invalid call
+ *    never touches the device.
+ *  - Calls are reentrant; the library keeps no mutable global state besides
+ *    a once-per-device architecture check.  Output buffers must not overlap
+ *    inputs.
+ *  - Not checked (undefined): NaN/Inf inputs, Q4_0 codes > 15 or ternary
+ *    codes > 2 handed to the pack entries (the low bits are used), ternary
+ *    code 3 inside packed words, act_sum inconsistent with xq.
+ *
+ * Byte formats (little-endian, packed)
+ *  - block_q4_0 (18 B): u16 d (IEEE binary16 bits), u8 qs[16].  Element t < 16
+ *    is the low nibble of qs[t], element t >= 16 the high nibble of qs[t-16];
+ *    weight = d * (code - 8)  [CPU].
+ *  - block_q8_0 (34 B): u16 d (binary16), int8 qs[32]; value ~ d * qs.
+ *  - Q4_0 weights W: [n][k/32] blocks, row j = output feature j.
+ *    Q8_0 activations X: [m][k/32] blocks.
+ *  - Ternary weights: uint32 [n][k/16]; code s of a word (s = 0..15, weight
+ *    index 16*word + s) sits at bits 2s..2s+1; code = weight + 1 in {0,1,2}
+ *    [LOOM].
+ */
+#ifndef QLL_H
+#define QLL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    QLL_OK = 0,
+    QLL_ERR_NULL = -1,      /* a required pointer is NULL */
+    QLL_ERR_SHAPE = -2,     /* a size is < 1, not a multiple of the block, or too large */
+    QLL_ERR_ALIGN = -3,     /* a base address is not 16-byte aligned */
+    QLL_ERR_WORKSPACE = -4, /* ws is NULL or smaller than qll_workspace_bytes() */
+    QLL_ERR_LAUNCH = -5,    /* the HIP launch itself failed */
+    QLL_ERR_DEVICE = -6     /* no usable device, or the current device is not gfx950 */
+};
+
+/* Operations that may need a caller-owned device workspace. */
+enum { QLL_OP_SGEMM = 1, QLL_OP_Q4_0_Q8_0_GEMM = 2, QLL_OP_TERNARY_GEMM = 3 };
+
+/* Bytes of device workspace `op` needs at this shape (0 if none); SIZE_MAX if
+ * the shape is invalid. */
+size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k);
+
+/* Static string naming a status code. */
+const char *qll_status_string(int status);
+
+/* ---------------------------------------------------------------- packing */
+
+/* Encode Q4_0 weights on the device: codes uint8[n][k] (0..15, weight index
+ * t of row j at codes[j*k + t]) and scales uint16[n][k/32] (binary16 bits)
+ * -> w block_q4_0[n][k/32] in the layout above [CPU].  k % 32 == 0. */
+int qll_pack_q4_0(const uint8_t *codes, const uint16_t *d_bits, void *w, int64_t n, int64_t k, void *stream);
+
+/* Encode ternary codes uint8[n][k] (0..2) into uint32[n][k/16], LSB first
+ * [LOOM].  k % 16 == 0. */
+int qll_pack_ternary(const uint8_t *codes, uint32_t *w, int64_t n, int64_t k, void *stream);
+
+/* ------------------------------------------------- Q4_0 x Q8_0 (decode, prefill) */
+
+/* Quantize f32 activations x[m][k] to Q8_0 blocks xq[m][k/32] ([BACK] 9.7:
+ * the activation rows are quantized per call).  Per 32-block: amax = max|x|,
+ * d = amax/127 (IEEE f32 division), q = round-half-away(x/d) (IEEE f32
+ * division) clamped to +-127, d stored as binary16 rounded to nearest even;
+ * a block whose f32 d is 0 stores q = 0.  Bit-exact with the oracle.
+ * k % 32 == 0. */
+int qll_quantize_q8_0(const float *x, void *xq, int64_t m, int64_t k, void *stream);
+
+/* Decode GEMV (m = 1): y[j] = sum_b f32(dw[j,b]) * f32(dx[b]) * sumi[j,b],
+ * sumi[j,b] = sum_t (qw[j,b,t] - 8) * qx[b,t] exact in int32 [CPU]; the float
+ * sum over b is accumulated in f32 in an order of the kernel's choosing
+ * (tolerance 1e-4 * sum_b |term_b| against an f64 sum).  w: block_q4_0[n][k/32],
+ * xq: block_q8_0[k/32], y: float[n].  k % 32 == 0.  Bandwidth-bound: every
+ * weight byte is read once ([FAST] 6.1). */
+int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64_t k, void *stream);
+
+/* Prefill GEMM: Y[m][n] = X.W^T with the same per-block arithmetic as the
+ * GEMV for every (i, j).  xq: block_q8_0[m][k/32], w: block_q4_0[n][k/32],
+ * y: float[m][n].  k % 32 == 0.  ws/ws_bytes: device workspace of at least
+ * qll_workspace_bytes(QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) bytes (may be NULL/0 when
+ * that is 0).  m == 1 runs the GEMV kernel. */
+int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- f32 */
+
+/* C[m][n] = A[m][k] . B[k][n], all f32 row-major (the plain orientation of
+ * [FAST] 6.4), accumulated in f32 (tolerance 1e-5 * sum_p |a*b| against an
+ * f64 sum).  m == 1 runs a split-k GEMV whose partial sums go to ws in a
+ * fixed order (results are bit-identical from run to run).  ws: at least
+ * qll_workspace_bytes(QLL_OP_SGEMM, m, n, k) bytes. */
+int qll_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, int64_t k, void *ws, size_t ws_bytes,
+              void *stream);
+
+/* ---------------------------------------------------------------- ternary */
+
+/* Per-row int8 activations [LOOM]: act_scale[i] = 127 / max|x[i,:]| (IEEE
+ * f32), xq = round-half-away(x * act_scale) (f32 product) clamped to +-127,
+ * act_sum[i] = sum_t xq[i,t].  A row whose amax is 0 or whose scale is not
+ * finite gets xq = 0, act_scale = 0, act_sum = 0.  Bit-exact with the oracle.
+ * x: float[m][k], xq: int8[m][k], act_scale: float[m], act_sum: int32[m].
+ * Any k >= 1. */
+int qll_quantize_i8_rows(const float *x, int8_t *xq, float *act_scale, int32_t *act_sum, int64_t m, int64_t k,
+                         void *stream);
+
+/* Ternary linear [LOOM]: dot[i,j] = sum_t code[j,t] * xq[i,t] - act_sum[i]
+ * (exact int32; equal to sum_t (code - 1) * xq by the ternary identity), then
+ * y[i,j] = dot * w_scale / act_scale[i] (0 where act_scale[i] == 0).
+ * w: uint32[n][k/16], xq: int8[m][k], y: float[m][n].  k % 16 == 0.
+ * The GEMV is the m = 1 case. */
+int qll_ternary_gemv(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
+                     const int32_t *act_sum, float *y, int64_t n, int64_t k, void *stream);
+int qll_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
+                     const int32_t *act_sum, float *y, int64_t m, int64_t n, int64_t k, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLL_H */

@@ -1,0 +1,103 @@
+// Internal header of libqll.so: device helpers shared by the kernels and the
+// launcher declarations called by the C-ABI layer (abi.hip).  Kernels below
+// the ABI are unchecked: the ABI validates shapes, pointers and alignment
+// once, then launches (the kernel contract of Fucina course "Chapter 06 --
+// Going fast on CPUs", 6.3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qll {
+
+// 16-byte vector of dwords that only promises 4-byte alignment: global
+// dwordx4 loads need no more on gfx950, and the 18- and 34-byte block formats
+// only give dword alignment for pairs of blocks.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
+}
+
+// f32 -> binary16 bits, round to nearest even (v_cvt_f16_f32 in the default
+// rounding mode).
+__device__ __forceinline__ uint16_t float_to_half_bits(float f)
+{
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Low 32 bits of ({hi, lo} >> s).
+__device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t s)
+{
+    return __builtin_amdgcn_alignbit(hi, lo, s);
+}
+
+// Signed 4x8-bit dot product accumulated into c (v_dot4_i32_i8).
+__device__ __forceinline__ int32_t sdot4(uint32_t a, uint32_t b, int32_t c)
+{
+    return __builtin_amdgcn_sdot4((int32_t)a, (int32_t)b, c, false);
+}
+
+__device__ __forceinline__ u32x4 load4_a4(const uint8_t *p)
+{
+    return *reinterpret_cast<const u32x4_a4 *>(p);
+}
+
+// Q8_0 block at byte offset o of `base` (o % 4 is 0 or 2) -> binary16 d bits
+// and the 32 int8 codes as 8 dwords.  Reads only bytes of this block and, when
+// o % 4 == 2, the two bytes before it (inside the same buffer, since o >= 34).
+__device__ __forceinline__ void load_q8_0_block(const uint8_t *base, int64_t o, uint32_t &d, uint32_t q[8])
+{
+    if ((o & 3) == 0) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(base + o);
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            w[i] = p[i];
+        uint32_t tail = *reinterpret_cast<const uint16_t *>(base + o + 32);
+        d = w[0] & 0xffffu;
+#pragma unroll
+        for (int i = 0; i < 7; i++)
+            q[i] = funnel(w[i + 1], w[i], 16);
+        q[7] = funnel(tail, w[7], 16);
+    } else {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(base + o - 2);
+        uint32_t w0 = p[0];
+        d = w0 >> 16;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            q[i] = p[i + 1];
+    }
+}
+
+// ------------------------------------------------------------ launchers
+// Each returns a hipError_t of the launch; arguments are already validated.
+
+hipError_t launch_pack_q4_0(const uint8_t *codes, const uint16_t *d_bits, uint8_t *w, int64_t n, int64_t k,
+                            hipStream_t s);
+hipError_t launch_pack_ternary(const uint8_t *codes, uint32_t *w, int64_t n, int64_t k, hipStream_t s);
+hipError_t launch_quantize_q8_0(const float *x, uint8_t *xq, int64_t nblocks, hipStream_t s);
+hipError_t launch_quantize_i8_rows(const float *x, int8_t *xq, float *act_scale, int32_t *act_sum, int64_t m,
+                                   int64_t k, hipStream_t s);
+hipError_t launch_q4_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int64_t k,
+                                 hipStream_t s);
+hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
+                                 void *ws, hipStream_t s);
+size_t q4_0_q8_0_gemm_workspace(int64_t m, int64_t n, int64_t k);
+hipError_t launch_sgemv(const float *x, const float *b, float *c, int64_t n, int64_t k, float *ws, hipStream_t s);
+size_t sgemv_workspace(int64_t n, int64_t k);
+hipError_t launch_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, int64_t k, hipStream_t s);
+hipError_t launch_ternary_gemv(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
+                               const int32_t *act_sum, float *y, int64_t n, int64_t k, hipStream_t s);
+hipError_t launch_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
+                               const int32_t *act_sum, float *y, int64_t m, int64_t n, int64_t k, hipStream_t s);
+
+// Largest k the LDS-staged decode kernels accept (the activation of one row
+// is kept whole in LDS).
+constexpr int64_t kMaxKQ4Gemv = 49152;
+constexpr int64_t kMaxKTernaryGemv = 65536;
+
+} // namespace qll

@@ -1,0 +1,296 @@
+// f32 GEMM in the plain orientation, C[m][n] = A[m][k] . B[k][n] (Fucina
+// course "Chapter 06 -- Going fast on CPUs", 6.1 for the naming and 6.4 for
+// the definition).
+//
+//  * m = 1 is a GEMV bound by reading B once (64 MiB at 4096^2).  Each lane
+//    owns four adjacent columns (16-byte loads along a row of B), the four
+//    waves of a workgroup split a k-chunk between them and combine in LDS, and
+//    the k-chunks write partial sums to the caller's workspace; a second
+//    kernel adds the chunks in a fixed order, so runs are bit-identical
+//    (deterministic reductions rather than float atomics).
+//  * m > 1 is compute-bound and runs on the f32 matrix cores
+//    (v_mfma_f32_32x32x2_f32; gfx950 has no reduced-precision xf32 path, so
+//    products are full f32).  128 x 128 output tiles, k-tiles of 16 staged in
+//    double-buffered LDS (A stored k-major so a wave's 32 rows are contiguous,
+//    B row-major), four waves of 64 x 64 each.
+#include "common.h"
+
+namespace qll {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------------ GEMV
+
+constexpr int kSgemvThreads = 256;
+
+struct SgemvPlan {
+    int64_t col_groups; // workgroups along n
+    int64_t kc;         // rows of B per k-chunk
+    int64_t ks;         // number of k-chunks
+    int vec;            // columns per lane
+};
+
+static SgemvPlan sgemv_plan(int64_t n, int64_t k)
+{
+    SgemvPlan p;
+    p.vec = (n % 4 == 0) ? 4 : 1;
+    const int64_t cols_per_wg = 64 * p.vec;
+    p.col_groups = (n + cols_per_wg - 1) / cols_per_wg;
+    int64_t want = (2048 + p.col_groups - 1) / p.col_groups; // about 2048 workgroups
+    int64_t max_ks = (k + 15) / 16;                           // at least 16 rows per chunk
+    if (want > max_ks)
+        want = max_ks;
+    if (want < 1)
+        want = 1;
+    p.kc = (k + want - 1) / want;
+    p.ks = (k + p.kc - 1) / p.kc;
+    return p;
+}
+
+size_t sgemv_workspace(int64_t n, int64_t k)
+{
+    SgemvPlan p = sgemv_plan(n, k);
+    return (size_t)(p.ks * n) * sizeof(float);
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kSgemvThreads) void sgemv_partial_kernel(const float *__restrict__ x,
+                                                                      const float *__restrict__ b,
+                                                                      float *__restrict__ ws, int64_t n, int64_t k,
+                                                                      int64_t kc)
+{
+    __shared__ float s_part[3][64 * VEC];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t col = ((int64_t)blockIdx.x * 64 + lane) * VEC;
+    const int64_t chunk = blockIdx.y;
+    const int64_t p0 = chunk * kc;
+    const int64_t p1 = (p0 + kc < k) ? p0 + kc : k;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; e++)
+        acc[e] = 0.0f;
+    if (col < n) {
+        // the four waves interleave over the rows of the chunk
+        int64_t p = p0 + wave;
+        for (; p + 12 < p1; p += 16) {
+            float xv[4];
+            float bv[4][VEC];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                xv[i] = x[p + 4 * i];
+                if (VEC == 4) {
+                    float4 v = *reinterpret_cast<const float4 *>(b + (p + 4 * i) * n + col);
+                    bv[i][0] = v.x; bv[i][1] = v.y; bv[i][2] = v.z; bv[i][3] = v.w;
+                } else {
+                    bv[i][0] = b[(p + 4 * i) * n + col];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int e = 0; e < VEC; e++)
+                    acc[e] = fmaf(xv[i], bv[i][e], acc[e]);
+        }
+        for (; p < p1; p += 4) {
+            const float xv = x[p];
+            if (VEC == 4) {
+                float4 v = *reinterpret_cast<const float4 *>(b + p * n + col);
+                acc[0] = fmaf(xv, v.x, acc[0]);
+                acc[1] = fmaf(xv, v.y, acc[1]);
+                acc[2] = fmaf(xv, v.z, acc[2]);
+                acc[3] = fmaf(xv, v.w, acc[3]);
+            } else {
+                acc[0] = fmaf(xv, b[p * n + col], acc[0]);
+            }
+        }
+    }
+    if (wave > 0)
+#pragma unroll
+        for (int e = 0; e < VEC; e++)
+            s_part[wave - 1][lane * VEC + e] = acc[e];
+    __syncthreads();
+    if (wave == 0 && col < n) {
+#pragma unroll
+        for (int e = 0; e < VEC; e++) {
+            float v = acc[e] + s_part[0][lane * VEC + e];
+            v += s_part[1][lane * VEC + e];
+            v += s_part[2][lane * VEC + e];
+            ws[chunk * n + col + e] = v;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void sgemv_finish_kernel(const float *__restrict__ ws, float *__restrict__ c,
+                                                           int64_t n, int64_t ks)
+{
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= n)
+        return;
+    float v = 0.0f;
+    for (int64_t s = 0; s < ks; s++)
+        v += ws[s * n + j];
+    c[j] = v;
+}
+
+hipError_t launch_sgemv(const float *x, const float *b, float *c, int64_t n, int64_t k, float *ws, hipStream_t s)
+{
+    SgemvPlan p = sgemv_plan(n, k);
+    dim3 grid((unsigned)p.col_groups, (unsigned)p.ks);
+    if (p.vec == 4)
+        hipLaunchKernelGGL(sgemv_partial_kernel<4>, grid, dim3(kSgemvThreads), 0, s, x, b, ws, n, k, p.kc);
+    else
+        hipLaunchKernelGGL(sgemv_partial_kernel<1>, grid, dim3(kSgemvThreads), 0, s, x, b, ws, n, k, p.kc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(sgemv_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws, c, n, p.ks);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ GEMM
+
+constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int APAD = 4, BPAD = 4;
+constexpr int kSgemmThreads = 256;
+
+struct SgemmTileRegs {
+    float a[2][4]; // two float4 of A (rows r, r+64; k 4q..4q+3)
+    float b[2][4]; // two float4 of B (k rows kr, kr+8; columns 4c..4c+3)
+};
+
+template <bool VEC>
+__device__ __forceinline__ void sgemm_load_tile(const float *__restrict__ a, const float *__restrict__ b, int64_t m,
+                                                int64_t n, int64_t k, int64_t m0, int64_t n0, int64_t k0,
+                                                SgemmTileRegs &t)
+{
+    const int tid = threadIdx.x;
+    // A: 128 rows x 16 k = 512 float4, two per thread
+#pragma unroll
+    for (int it = 0; it < 2; it++) {
+        const int64_t row = m0 + (tid >> 2) + 64 * it;
+        const int64_t kk = k0 + 4 * (tid & 3);
+        if (VEC && row < m && kk + 3 < k) {
+            float4 v = *reinterpret_cast<const float4 *>(a + row * k + kk);
+            t.a[it][0] = v.x; t.a[it][1] = v.y; t.a[it][2] = v.z; t.a[it][3] = v.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                t.a[it][e] = (row < m && kk + e < k) ? a[row * k + kk + e] : 0.0f;
+        }
+    }
+    // B: 16 rows x 128 columns = 512 float4, two per thread
+#pragma unroll
+    for (int it = 0; it < 2; it++) {
+        const int64_t kr = k0 + (tid >> 5) + 8 * it;
+        const int64_t col = n0 + 4 * (tid & 31);
+        if (VEC && kr < k && col + 3 < n) {
+            float4 v = *reinterpret_cast<const float4 *>(b + kr * n + col);
+            t.b[it][0] = v.x; t.b[it][1] = v.y; t.b[it][2] = v.z; t.b[it][3] = v.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                t.b[it][e] = (kr < k && col + e < n) ? b[kr * n + col + e] : 0.0f;
+        }
+    }
+}
+
+__device__ __forceinline__ void sgemm_store_tile(const SgemmTileRegs &t, float (*As)[BM + APAD],
+                                                 float (*Bs)[BN + BPAD])
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < 2; it++) {
+        const int row = (tid >> 2) + 64 * it;
+        const int kq = 4 * (tid & 3);
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            As[kq + e][row] = t.a[it][e];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; it++) {
+        const int kr = (tid >> 5) + 8 * it;
+        const int col = 4 * (tid & 31);
+        *reinterpret_cast<float4 *>(&Bs[kr][col]) = make_float4(t.b[it][0], t.b[it][1], t.b[it][2], t.b[it][3]);
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kSgemmThreads) void sgemm_mfma_kernel(const float *__restrict__ a,
+                                                                   const float *__restrict__ b,
+                                                                   float *__restrict__ c, int64_t m, int64_t n,
+                                                                   int64_t k)
+{
+    __shared__ __attribute__((aligned(16))) float As[2][BK][BM + APAD];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK][BN + BPAD];
+
+    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64; // wave tile origin inside the block tile
+    const int li = lane & 31, lh = lane >> 5;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++)
+                acc[i][j][v] = 0.0f;
+
+    const int64_t nkt = (k + BK - 1) / BK;
+    SgemmTileRegs regs;
+    sgemm_load_tile<VEC>(a, b, m, n, k, m0, n0, 0, regs);
+    sgemm_store_tile(regs, As[0], Bs[0]);
+    __syncthreads();
+
+    for (int64_t kt = 0; kt < nkt; kt++) {
+        const int cur = (int)(kt & 1);
+        if (kt + 1 < nkt)
+            sgemm_load_tile<VEC>(a, b, m, n, k, m0, n0, (kt + 1) * BK, regs);
+#pragma unroll
+        for (int s = 0; s < BK / 2; s++) {
+            const int kk = 2 * s + lh; // lanes 0-31 take k = 2s, lanes 32-63 k = 2s+1
+            float av[2], bv[2];
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+                av[i] = As[cur][kk][wm + 32 * i + li];
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                bv[j] = Bs[cur][kk][wn + 32 * j + li];
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nkt)
+            sgemm_store_tile(regs, As[cur ^ 1], Bs[cur ^ 1]);
+        __syncthreads();
+    }
+
+    // D layout of a 32x32 MFMA tile: lane l, register v holds
+    // row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
+                const int64_t col = n0 + wn + 32 * j + li;
+                if (row < m && col < n)
+                    c[row * n + col] = acc[i][j][v];
+            }
+}
+
+hipError_t launch_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, int64_t k, hipStream_t s)
+{
+    dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
+    if (k % 4 == 0 && n % 4 == 0)
+        hipLaunchKernelGGL(sgemm_mfma_kernel<true>, grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
+    else
+        hipLaunchKernelGGL(sgemm_mfma_kernel<false>, grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
+    return hipGetLastError();
+}
+
+} // namespace qll

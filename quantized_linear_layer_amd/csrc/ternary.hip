@@ -1,0 +1,232 @@
+// BitNet ternary linear layer (Loom "Plan 9 SIMD Forward", "BitNet ternary
+// MAD kernel"): weights in {-1, 0, +1} stored as 2-bit codes c = w + 1, 16 per
+// uint32; int8 activations with act_scale = 127 / max|x| per row; the dot
+// uses the ternary identity
+//     sum_t (c_t - 1) q_t = sum_t c_t q_t - sum_t q_t,
+// with sum_t q_t (act_sum) computed once per activation row, and the output
+// is dot * w_scale / act_scale.
+//
+// Unlike the page's CPU design (a byte-per-weight code cache built once), the
+// codes are unpacked in registers on every call, so W is read at 2 bits per
+// weight: (word >> 2j) & 0x03030303 puts codes j, 4+j, 8+j, 12+j of the word
+// into the four bytes of a dword.  The activation bytes are transposed to the
+// same order once per workgroup when they are staged in LDS, and
+// v_dot4_i32_i8 multiplies the two (codes are 0..2, valid signed bytes).
+#include "common.h"
+
+namespace qll {
+
+// 16 activation bytes (dwords D0..D3, byte e of Dr = x[4r + e]) -> A0..A3 with
+// byte r of Aj = x[4r + j], the order of the code unpack.
+__device__ __forceinline__ u32x4 transpose_4x4_bytes(u32x4 d)
+{
+    u32x4 a;
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        a[j] = ((d[0] >> (8 * j)) & 0xffu) | (((d[1] >> (8 * j)) & 0xffu) << 8) |
+               (((d[2] >> (8 * j)) & 0xffu) << 16) | (((d[3] >> (8 * j)) & 0xffu) << 24);
+    return a;
+}
+
+__device__ __forceinline__ int ternary_word_dot(uint32_t word, u32x4 a, int acc)
+{
+    acc = sdot4(word & 0x03030303u, a[0], acc);
+    acc = sdot4((word >> 2) & 0x03030303u, a[1], acc);
+    acc = sdot4((word >> 4) & 0x03030303u, a[2], acc);
+    acc = sdot4((word >> 6) & 0x03030303u, a[3], acc);
+    return acc;
+}
+
+__device__ __forceinline__ float ternary_output(int dot_c, int asum, float w_scale, float s)
+{
+    if (s == 0.0f)
+        return 0.0f;
+    return (float)(dot_c - asum) * w_scale / s;
+}
+
+constexpr int kTerGemvThreads = 64;
+constexpr int kTerUnroll = 4;
+
+// m = 1.  VEC: 4 words (one dwordx4) per unit when k % 64 == 0, else 1 word.
+template <int L, int VEC>
+__global__ __launch_bounds__(kTerGemvThreads) void ternary_gemv_kernel(
+    const uint32_t *__restrict__ w, float w_scale, const int8_t *__restrict__ xq, const float *__restrict__ act_scale,
+    const int32_t *__restrict__ act_sum, float *__restrict__ y, int64_t n, int nw)
+{
+    extern __shared__ u32x4 s_x[]; // [nw] transposed activation words
+    for (int i = threadIdx.x; i < nw; i += blockDim.x)
+        s_x[i] = transpose_4x4_bytes(reinterpret_cast<const u32x4 *>(xq)[i]);
+    __syncthreads();
+
+    constexpr int R = 64 / L;
+    constexpr int WAVES = kTerGemvThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / L, r = lane % L;
+    const int nu = nw / VEC;
+    const float s = act_scale[0];
+    const int asum = act_sum[0];
+    const int64_t stride = (int64_t)gridDim.x * WAVES * R;
+    for (int64_t row0 = ((int64_t)blockIdx.x * WAVES + wave) * R; row0 < n; row0 += stride) {
+        const int64_t row = row0 + g;
+        int acc = 0;
+        if (row < n) {
+            const uint32_t *wr = w + row * nw;
+            for (int u0 = r; u0 < nu; u0 += kTerUnroll * L) {
+                uint32_t wd[kTerUnroll][VEC];
+#pragma unroll
+                for (int i = 0; i < kTerUnroll; i++) {
+                    const int u = u0 + i * L;
+                    if (u < nu) {
+                        if (VEC == 4) {
+                            u32x4 v = reinterpret_cast<const u32x4 *>(wr)[u];
+#pragma unroll
+                            for (int e = 0; e < VEC; e++)
+                                wd[i][e] = v[e];
+                        } else {
+                            wd[i][0] = wr[u];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kTerUnroll; i++) {
+                    const int u = u0 + i * L;
+                    if (u < nu) {
+#pragma unroll
+                        for (int e = 0; e < VEC; e++)
+                            acc = ternary_word_dot(wd[i][e], s_x[u * VEC + e], acc);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int off = L / 2; off > 0; off >>= 1)
+            acc += __shfl_xor(acc, off);
+        if (row < n && r == 0)
+            y[row] = ternary_output(acc, asum, w_scale, s);
+    }
+}
+
+template <int L, int VEC>
+static hipError_t launch_ter_l(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
+                               const int32_t *act_sum, float *y, int64_t n, int nw, hipStream_t st)
+{
+    constexpr int R = 64 / L;
+    const int64_t waves = (n + R - 1) / R;
+    int64_t grid = (waves + kTerGemvThreads / 64 - 1) / (kTerGemvThreads / 64);
+    if (grid > 16384)
+        grid = 16384;
+    hipLaunchKernelGGL((ternary_gemv_kernel<L, VEC>), dim3((unsigned)grid), dim3(kTerGemvThreads),
+                       (size_t)nw * 16, st, w, w_scale, xq, act_scale, act_sum, y, n, nw);
+    return hipGetLastError();
+}
+
+template <int VEC>
+static hipError_t launch_ter_vec(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
+                                 const int32_t *act_sum, float *y, int64_t n, int nw, hipStream_t st)
+{
+    const int nu = nw / VEC;
+    if (nu >= 256)
+        return launch_ter_l<64, VEC>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+    if (nu >= 128)
+        return launch_ter_l<32, VEC>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+    if (nu >= 64)
+        return launch_ter_l<16, VEC>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+    return launch_ter_l<8, VEC>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+}
+
+hipError_t launch_ternary_gemv(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
+                               const int32_t *act_sum, float *y, int64_t n, int64_t k, hipStream_t st)
+{
+    const int nw = (int)(k / 16);
+    if (nw % 4 == 0)
+        return launch_ter_vec<4>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+    return launch_ter_vec<1>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+}
+
+// ------------------------------------------------------------------ GEMM (m > 1)
+// v_mfma_i32_16x16x64_i8: one MFMA covers 64 codes = 4 words of a weight row.
+// Lane group h of an operand takes word h*Q + s at k-step s (Q = ceil(nw/4)),
+// so a lane walks its own contiguous quarter of the row; the activation
+// bytes of the same word (transposed like the unpack) are its A operand.
+// Words past the row end are zero activation, so their codes do not matter.
+// Workgroup tile: 64 activation rows x 32 weight rows; wave w owns rows
+// 16w..16w+15 and both 16-column halves.  The activation is staged in LDS
+// in chunks of kTerSC k-steps.
+
+constexpr int TBM = 64, TBN = 32, kTerSC = 8;
+constexpr int kTerGemmThreads = 256;
+
+__global__ __launch_bounds__(kTerGemmThreads) void ternary_gemm_kernel(
+    const uint32_t *__restrict__ w, float w_scale, const int8_t *__restrict__ xq, const float *__restrict__ act_scale,
+    const int32_t *__restrict__ act_sum, float *__restrict__ y, int64_t m, int64_t n, int nw)
+{
+    __shared__ u32x4 xs[4][kTerSC][TBM];
+    const int64_t m0 = (int64_t)blockIdx.y * TBM, n0 = (int64_t)blockIdx.x * TBN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lh = lane >> 4;
+    const int Q = (nw + 3) / 4;
+
+    i32x4 acc[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+    for (int s0 = 0; s0 < Q; s0 += kTerSC) {
+        __syncthreads();
+        for (int it = threadIdx.x; it < 4 * kTerSC * TBM; it += kTerGemmThreads) {
+            const int row = it % TBM, ss = (it / TBM) % kTerSC, h = it / (TBM * kTerSC);
+            const int s = s0 + ss;
+            const int wi = h * Q + s;
+            const int64_t gi = m0 + row;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (gi < m && s < Q && wi < nw)
+                v = transpose_4x4_bytes(*reinterpret_cast<const u32x4 *>(xq + gi * (int64_t)nw * 16 + (int64_t)wi * 16));
+            xs[h][ss][row] = v;
+        }
+        __syncthreads();
+        uint32_t wd[2][kTerSC];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int64_t col = n0 + 16 * j + lr;
+#pragma unroll
+            for (int ss = 0; ss < kTerSC; ss++) {
+                const int s = s0 + ss, wi = lh * Q + s;
+                wd[j][ss] = (col < n && s < Q && wi < nw) ? w[col * nw + wi] : 0u;
+            }
+        }
+#pragma unroll
+        for (int ss = 0; ss < kTerSC; ss++) {
+            const u32x4 av = xs[lh][ss][16 * wave + lr];
+            const i32x4 a = __builtin_bit_cast(i32x4, av);
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const uint32_t c = wd[j][ss];
+                const i32x4 b = {(int)(c & 0x03030303u), (int)((c >> 2) & 0x03030303u), (int)((c >> 4) & 0x03030303u),
+                                 (int)((c >> 6) & 0x03030303u)};
+                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[j], 0, 0, 0);
+            }
+        }
+    }
+    // D layout of a 16x16 tile: lane l, register v -> row 4*(l/16)+v, column l%16
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        const int64_t row = m0 + 16 * wave + 4 * lh + v;
+        if (row >= m)
+            continue;
+        const float s = act_scale[row];
+        const int asum = act_sum[row];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int64_t col = n0 + 16 * j + lr;
+            if (col < n)
+                y[row * n + col] = ternary_output(acc[j][v], asum, w_scale, s);
+        }
+    }
+}
+
+hipError_t launch_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
+                               const int32_t *act_sum, float *y, int64_t m, int64_t n, int64_t k, hipStream_t st)
+{
+    dim3 grid((unsigned)((n + TBN - 1) / TBN), (unsigned)((m + TBM - 1) / TBM));
+    hipLaunchKernelGGL(ternary_gemm_kernel, grid, dim3(kTerGemmThreads), 0, st, w, w_scale, xq, act_scale, act_sum,
+                       y, m, n, (int)(k / 16));
+    return hipGetLastError();
+}
+
+} // namespace qll

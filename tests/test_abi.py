@@ -1,0 +1,126 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/qll.h declares, and rejects bad arguments with the documented status
+before touching any device (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_linear_layer_amd as qll
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qll.h")
+
+OK, NULL, SHAPE, ALIGN, WORKSPACE = 0, -1, -2, -3, -4
+SIZE_MAX = 2 ** 64 - 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qll_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qll.load()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", qll.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s(qll_\w+)", out))
+    assert set(names) <= exported
+    assert exported <= set(names), f"undeclared exports: {exported - set(names)}"
+
+
+def test_library_is_built_for_gfx950():
+    # the offload bundle inside libqll.so names its target triple
+    out = subprocess.run(["strings", qll.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "amdgcn-amd-amdhsa--gfx950" in out
+
+
+def test_status_strings(L):
+    for rc in (0, -1, -2, -3, -4, -5, -6):
+        assert qll.qll_status_string(rc) != "unknown status"
+    assert qll.qll_status_string(-99) == "unknown status"
+
+
+def test_workspace_sizes(L):
+    assert qll.qll_workspace_bytes(qll.QLL_OP_SGEMM, 4096, 4096, 4096) == 0
+    ws = qll.qll_workspace_bytes(qll.QLL_OP_SGEMM, 1, 4096, 4096)
+    assert 0 < ws <= 4096 * 4096 * 4
+    assert ws % (4096 * 4) == 0
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 1, 4096, 4096) == 0
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 512, 4096, 33) == SIZE_MAX
+    assert qll.qll_workspace_bytes(qll.QLL_OP_TERNARY_GEMM, 64, 6912, 2560) == 0
+    assert qll.qll_workspace_bytes(qll.QLL_OP_TERNARY_GEMM, 64, 6912, 2561) == SIZE_MAX
+    assert qll.qll_workspace_bytes(99, 1, 1, 1) == SIZE_MAX
+    assert qll.qll_workspace_bytes(qll.QLL_OP_SGEMM, 0, 4, 4) == SIZE_MAX
+
+
+GOOD = ctypes.c_void_p(0x10000)
+MIS = ctypes.c_void_p(0x10004)  # not 16-byte aligned
+NUL = None
+
+
+def test_pack_errors(L):
+    assert L.qll_pack_q4_0(NUL, GOOD, GOOD, 4, 64, None) == NULL
+    assert L.qll_pack_q4_0(GOOD, GOOD, GOOD, 4, 48, None) == SHAPE
+    assert L.qll_pack_q4_0(GOOD, GOOD, GOOD, 0, 64, None) == SHAPE
+    assert L.qll_pack_q4_0(GOOD, MIS, GOOD, 4, 64, None) == ALIGN
+    assert L.qll_pack_ternary(GOOD, NUL, 4, 64, None) == NULL
+    assert L.qll_pack_ternary(GOOD, GOOD, 4, 24, None) == SHAPE
+    assert L.qll_pack_ternary(MIS, GOOD, 4, 32, None) == ALIGN
+
+
+def test_q4_errors(L):
+    assert L.qll_quantize_q8_0(NUL, GOOD, 1, 64, None) == NULL
+    assert L.qll_quantize_q8_0(GOOD, GOOD, 1, 40, None) == SHAPE
+    assert L.qll_quantize_q8_0(GOOD, GOOD, -1, 64, None) == SHAPE
+    assert L.qll_quantize_q8_0(GOOD, MIS, 1, 64, None) == ALIGN
+    assert L.qll_q4_0_q8_0_gemv(GOOD, GOOD, NUL, 8, 64, None) == NULL
+    assert L.qll_q4_0_q8_0_gemv(GOOD, GOOD, GOOD, 8, 65, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemv(GOOD, GOOD, GOOD, 8, 49152 + 32, None) == SHAPE  # beyond the LDS-staged k
+    assert L.qll_q4_0_q8_0_gemv(GOOD, GOOD, GOOD, 2 ** 31, 64, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemv(MIS, GOOD, GOOD, 8, 64, None) == ALIGN
+    assert L.qll_q4_0_q8_0_gemm(GOOD, NUL, GOOD, 4, 8, 64, NUL, 0, None) == NULL
+    assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 16, NUL, 0, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, MIS, 4, 8, 64, NUL, 0, None) == ALIGN
+
+
+def test_sgemm_errors(L):
+    assert L.qll_sgemm(NUL, GOOD, GOOD, 2, 2, 2, NUL, 0, None) == NULL
+    assert L.qll_sgemm(GOOD, GOOD, GOOD, 2, 0, 2, NUL, 0, None) == SHAPE
+    assert L.qll_sgemm(GOOD, GOOD, GOOD, 2 ** 30, 2 ** 30, 2, NUL, 0, None) == SHAPE
+    assert L.qll_sgemm(GOOD, MIS, GOOD, 2, 2, 2, NUL, 0, None) == ALIGN
+    need = qll.qll_workspace_bytes(qll.QLL_OP_SGEMM, 1, 4096, 4096)
+    assert L.qll_sgemm(GOOD, GOOD, GOOD, 1, 4096, 4096, NUL, 0, None) == WORKSPACE
+    assert L.qll_sgemm(GOOD, GOOD, GOOD, 1, 4096, 4096, GOOD, need - 1, None) == WORKSPACE
+    assert L.qll_sgemm(GOOD, GOOD, GOOD, 1, 4096, 4096, MIS, need, None) == ALIGN
+
+
+def test_ternary_errors(L):
+    f = ctypes.c_float(1.0)
+    assert L.qll_quantize_i8_rows(GOOD, GOOD, NUL, GOOD, 1, 16, None) == NULL
+    assert L.qll_quantize_i8_rows(GOOD, GOOD, GOOD, GOOD, 1, 0, None) == SHAPE
+    assert L.qll_quantize_i8_rows(GOOD, GOOD, GOOD, MIS, 1, 16, None) == ALIGN
+    assert L.qll_ternary_gemv(GOOD, f, GOOD, GOOD, NUL, GOOD, 4, 32, None) == NULL
+    assert L.qll_ternary_gemv(GOOD, f, GOOD, GOOD, GOOD, GOOD, 4, 40, None) == SHAPE
+    assert L.qll_ternary_gemv(GOOD, f, GOOD, GOOD, GOOD, GOOD, 4, 65536 + 16, None) == SHAPE
+    assert L.qll_ternary_gemv(GOOD, f, MIS, GOOD, GOOD, GOOD, 4, 32, None) == ALIGN
+    assert L.qll_ternary_gemm(GOOD, f, GOOD, GOOD, GOOD, NUL, 4, 4, 32, None) == NULL
+    assert L.qll_ternary_gemm(GOOD, f, GOOD, GOOD, GOOD, GOOD, 4, 4, 8, None) == SHAPE
+    assert L.qll_ternary_gemm(GOOD, f, GOOD, GOOD, GOOD, MIS, 4, 4, 32, None) == ALIGN
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(64, dtype=torch.float32)
+    with pytest.raises(ValueError, match="CUDA"):
+        qll._ptr(x, 4, "x")

@@ -1,0 +1,78 @@
+"""Parity of the f32 GEMM and GEMV on the GPU against the f64 oracle:
+|C - C_ref| <= 1e-5 * sum_p |a_ip * b_pj|, plus exact closed-form cases."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from gpu_util import assert_within, dev, host, sgemm
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _check(a, b, what):
+    m, k = a.shape
+    n = b.shape[1]
+    c = host(sgemm(dev(a), dev(b), m, n, k)).reshape(m, n)
+    c_ref, mag = O.sgemm(a, b)
+    assert_within(c, c_ref, mag, TOL, what)
+    return c
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (2, 3, 5), (7, 11, 13), (33, 17, 23), (48, 192, 128), (130, 257, 300),
+                                   (128, 128, 16), (129, 130, 17), (256, 64, 1000), (1, 7, 3), (1, 4096, 33),
+                                   (1, 300, 4096), (1, 1000, 1000)])
+def test_shapes(qll_gpu, m, n, k):
+    rng = np.random.default_rng(m * 7919 + n * 31 + k)
+    a = synth.uniform_f32(rng, (m, k))
+    b = synth.uniform_f32(rng, (k, n))
+    _check(a, b, f"sgemm {m}x{n}x{k}")
+
+
+def test_exact_cases(qll_gpu):
+    rng = np.random.default_rng(2)
+    a = synth.uniform_f32(rng, (70, 96))
+    c = _check(a, np.eye(96, dtype=np.float32), "identity")
+    assert np.array_equal(c, a)
+    ai = rng.integers(-2, 3, (150, 200)).astype(np.float32)
+    bi = rng.integers(-2, 3, (200, 90)).astype(np.float32)
+    c = _check(ai, bi, "small integers")
+    assert np.array_equal(c.astype(np.int64), ai.astype(np.int64) @ bi.astype(np.int64))
+    c = _check(np.ones((1, 777), np.float32), np.ones((777, 65), np.float32), "ones gemv")
+    assert np.all(c == 777.0)
+
+
+def test_gemv_config_full(qll_gpu):
+    a, b, x = synth.f32_gemm()
+    c = _check(x, b, "f32 GEMV 4096x4096")
+    c2 = host(sgemm(dev(x), dev(b), 1, 4096, 4096)).reshape(1, 4096)
+    assert np.array_equal(c.view(np.uint32), c2.view(np.uint32)), "GEMV not deterministic"
+
+
+def test_gemm_config_sampled(qll_gpu):
+    a, b, _ = synth.f32_gemm()
+    m, k = a.shape
+    n = b.shape[1]
+    c = host(sgemm(dev(a), dev(b), m, n, k)).reshape(m, n)
+    rng = np.random.default_rng(99)
+    ii = np.concatenate([[0, 0, m - 1, m - 1], rng.integers(0, m, 4000)])
+    jj = np.concatenate([[0, n - 1, 0, n - 1], rng.integers(0, n, 4000)])
+    c_ref, mag = O.sgemm_sampled(a, b, ii, jj)
+    assert_within(c[ii, jj], c_ref, mag, TOL, "f32 GEMM 4096^3 (sampled)")
+    # a whole row and a whole column too
+    c_ref, mag = O.sgemm_sampled(a, b, np.full(n, 1234), np.arange(n))
+    assert_within(c[1234], c_ref, mag, TOL, "row 1234")
+    c_ref, mag = O.sgemm_sampled(a, b, np.arange(m), np.full(m, 4001))
+    assert_within(c[:, 4001], c_ref, mag, TOL, "column 4001")
+
+
+def test_gemm_row_matches_gemv(qll_gpu):
+    rng = np.random.default_rng(5)
+    a = synth.uniform_f32(rng, (40, 512))
+    b = synth.uniform_f32(rng, (512, 300))
+    c = _check(a, b, "gemm")
+    for i in (0, 17, 39):
+        ci = host(sgemm(dev(a[i:i + 1]), dev(b), 1, 300, 512))
+        _, mag = O.sgemm(a[i:i + 1], b)
+        assert np.all(np.abs(ci - c[i]) <= 2 * TOL * mag[0])
