@@ -1,0 +1,340 @@
+"""Benchmark of the quantized linear layer hot path on one MI355X.
+
+One step is one pass of every operation of the path at its full workload
+size, on inputs already resident in HBM:
+  * Q8_0 quantization of the decode activation and Q4_0 x Q8_0 decode GEMV
+    (m = 1) on the four 8B-class linear shapes (k, n) = (4096, 14336),
+    (14336, 4096), (4096, 4096), (4096, 128256);
+  * Q8_0 quantization of the prefill activations and the Q4_0 x Q8_0 prefill
+    GEMM (m = 512) on the same four shapes and weights;
+  * the f32 GEMM 4096^3 and the f32 GEMV 4096 x 4096;
+  * the BitNet ternary layer 2560 -> 6912: int8 row quantization, GEMV (m = 1)
+    and GEMM (m = 64).
+Decode weights rotate through enough device copies (>= 1 GiB per shape) that
+no decode GEMV reads its weights from the 256 MiB Infinity Cache.
+
+Every kernel is bracketed by HIP events recorded on the stream it runs on
+(torch's current stream, which the library launches on).  The JSON line's
+`value` is the Q4_0 x Q8_0 decode GEMV bandwidth over the four shapes
+(algorithmic bytes / summed kernel time); `per_format` holds decode GB/s and
+prefill TOPS of every format with their fractions of the MI355X peaks, and
+`roofline` describes the kernel that takes the largest share of the step.
+`cpu_baseline` times the oracle (the test suite's plain C reference, never
+tuned) on the same decode GEMVs on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"f16": 2500.0, "i8": 5000.0, "f32": 157.3}
+METRIC = "decode GEMV HBM GB/s (% of peak) + prefill GEMM TOPS (% MFMA peak) per format"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's CPU sample")
+    p.add_argument("--only", default="", help="comma-separated op-name prefixes to run (profiling)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy per step (counter calibration)")
+    return p.parse_args()
+
+
+class Op:
+    def __init__(self, name, fmt, kind, fn, nbytes, flops, bound, peak_key=None):
+        self.name, self.fmt, self.kind, self.fn = name, fmt, kind, fn
+        self.nbytes, self.flops, self.bound, self.peak_key = nbytes, flops, bound, peak_key
+        self.times_ms = []
+
+    def roofline(self, ms):
+        if self.bound == "hbm":
+            achieved = self.nbytes / (ms * 1e-3) / 1e9
+            return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": achieved / PEAK_HBM_GBS}
+        achieved = self.flops / (ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[self.peak_key]
+        return {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s" if self.peak_key != "i8"
+                else "TOP/s", "frac": achieved / peak}
+
+
+def build_ops(qll, synth, torch, np, dev, only):
+    ops = []
+    keep = [s for s in only.split(",") if s]
+
+    def want(name):
+        return not keep or any(name.startswith(s) for s in keep)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    gib = 1 << 30
+    step_ref = {"i": 0}
+
+    # ---------------------------------------------------------------- Q4_0 x Q8_0
+    for s, (k, n) in enumerate(synth.SHAPES_8B):
+        need_dec = want(f"q4_gemv_{s}") or want(f"q8_quant_decode_{s}")
+        need_pre = want(f"q4_gemm_{s}") or want(f"q8_quant_prefill_{s}")
+        if not (need_dec or need_pre):
+            continue
+        codes, d_bits, x = synth.q4_decode(s)
+        w0 = torch.empty(n * (k // 32) * 18, dtype=torch.uint8, device=dev)
+        qll.qll_pack_q4_0(to_dev(codes), to_dev(d_bits.view(np.int16)), w0, n, k)
+        del codes, d_bits
+        wbytes = w0.numel()
+        if need_dec:
+            copies = [w0] + [w0.clone() for _ in range(max(1, -(-gib // wbytes)) - 1)]
+            xd = to_dev(x)
+            xqd = torch.empty((k // 32) * 34, dtype=torch.uint8, device=dev)
+            yd = torch.empty(n, dtype=torch.float32, device=dev)
+            if want(f"q8_quant_decode_{s}"):
+                ops.append(Op(f"q8_quant_decode_{s}", "q4_0", "quant",
+                              lambda xd=xd, xqd=xqd, k=k: qll.qll_quantize_q8_0(xd, xqd, 1, k),
+                              4 * k + (k // 32) * 34, 0, "hbm"))
+            if want(f"q4_gemv_{s}"):
+                ops.append(Op(f"q4_gemv_{s}", "q4_0", "decode",
+                              lambda c=copies, xqd=xqd, yd=yd, n=n, k=k: qll.qll_q4_0_q8_0_gemv(
+                                  c[step_ref["i"] % len(c)], xqd, yd, n, k),
+                              wbytes + (k // 32) * 34 + 4 * n, 2 * n * k, "hbm"))
+        if need_pre:
+            m = 512
+            xp = to_dev(synth.q4_prefill_x(s))
+            xqp = torch.empty(m * (k // 32) * 34, dtype=torch.uint8, device=dev)
+            yp = torch.empty(m * n, dtype=torch.float32, device=dev)
+            if want(f"q8_quant_prefill_{s}"):
+                ops.append(Op(f"q8_quant_prefill_{s}", "q4_0", "quant",
+                              lambda xp=xp, xqp=xqp, k=k: qll.qll_quantize_q8_0(xp, xqp, 512, k),
+                              4 * m * k + m * (k // 32) * 34, 0, "hbm"))
+            if want(f"q4_gemm_{s}"):
+                # the prefill GEMM needs quantized activations even when profiled alone
+                qll.qll_quantize_q8_0(xp, xqp, m, k)
+                ops.append(Op(f"q4_gemm_{s}", "q4_0", "prefill",
+                              lambda w0=w0, xqp=xqp, yp=yp, n=n, k=k: qll.qll_q4_0_q8_0_gemm(
+                                  w0, xqp, yp, 512, n, k),
+                              wbytes + m * (k // 32) * 34 + 4 * m * n, 2 * m * n * k, "mfma", "f16"))
+        if need_dec and want(f"q4_gemv_{s}") and not want(f"q8_quant_decode_{s}"):
+            qll.qll_quantize_q8_0(xd, xqd, 1, k)
+
+    # ---------------------------------------------------------------- f32
+    if want("sgemm") or want("sgemv"):
+        a, b, x = synth.f32_gemm()
+        M = N = K = 4096
+        bd = to_dev(b)
+        if want("sgemm"):
+            ad = to_dev(a)
+            cd = torch.empty(M * N, dtype=torch.float32, device=dev)
+            ops.append(Op("sgemm_4096", "f32", "prefill", lambda: qll.qll_sgemm(ad, bd, cd, M, N, K),
+                          4 * (M * K + K * N + M * N), 2 * M * N * K, "mfma", "f32"))
+        if want("sgemv"):
+            copies = [bd] + [bd.clone() for _ in range(max(1, -(-gib // (4 * K * N))) - 1)]
+            xd = to_dev(x)
+            yd = torch.empty(N, dtype=torch.float32, device=dev)
+            ws = torch.empty(qll.qll_workspace_bytes(qll.QLL_OP_SGEMM, 1, N, K), dtype=torch.uint8, device=dev)
+            ops.append(Op("sgemv_4096", "f32", "decode",
+                          lambda c=copies: qll.qll_sgemm(xd, c[step_ref["i"] % len(c)], yd, 1, N, K, ws=ws),
+                          4 * (K + K * N + N), 2 * N * K, "hbm"))
+        del a, b, x
+
+    # ---------------------------------------------------------------- ternary
+    if any(want(s) for s in ("i8_quant", "ternary")):
+        codes, w_scale, x = synth.ternary_layer()
+        n, k = codes.shape
+        m = x.shape[0]
+        tw0 = torch.empty(n * (k // 16), dtype=torch.int32, device=dev)
+        qll.qll_pack_ternary(to_dev(codes), tw0, n, k)
+        tcopies = [tw0] + [tw0.clone() for _ in range(max(1, -(-gib // (n * k // 4))) - 1)]
+        xd = to_dev(x)
+        q = torch.empty(m * k, dtype=torch.int8, device=dev)
+        sc = torch.empty(m, dtype=torch.float32, device=dev)
+        sm = torch.empty(m, dtype=torch.int32, device=dev)
+        xd1 = to_dev(x[:1])
+        q1 = torch.empty(k, dtype=torch.int8, device=dev)
+        sc1 = torch.empty(4, dtype=torch.float32, device=dev)
+        sm1 = torch.empty(4, dtype=torch.int32, device=dev)
+        y1 = torch.empty(n, dtype=torch.float32, device=dev)
+        ym = torch.empty(m * n, dtype=torch.float32, device=dev)
+        qll.qll_quantize_i8_rows(xd, q, sc, sm, m, k)
+        qll.qll_quantize_i8_rows(xd1, q1, sc1, sm1, 1, k)
+        if want("i8_quant_decode"):
+            ops.append(Op("i8_quant_decode", "ternary", "quant", lambda: qll.qll_quantize_i8_rows(
+                xd1, q1, sc1, sm1, 1, k), 5 * k + 8, 0, "hbm"))
+        if want("ternary_gemv"):
+            ops.append(Op("ternary_gemv", "ternary", "decode", lambda: qll.qll_ternary_gemv(
+                tcopies[step_ref["i"] % len(tcopies)], w_scale, q1, sc1, sm1, y1, n, k),
+                n * k // 4 + k + 8 + 4 * n, 2 * n * k, "hbm"))
+        if want("i8_quant_prefill"):
+            ops.append(Op("i8_quant_prefill", "ternary", "quant", lambda: qll.qll_quantize_i8_rows(
+                xd, q, sc, sm, m, k), 5 * m * k + 8 * m, 0, "hbm"))
+        if want("ternary_gemm"):
+            ops.append(Op("ternary_gemm", "ternary", "prefill", lambda: qll.qll_ternary_gemm(
+                tw0, w_scale, q, sc, sm, ym, m, n, k),
+                n * k // 4 + m * k + 8 * m + 4 * m * n, 2 * m * n * k, "mfma", "i8"))
+    return ops, step_ref
+
+
+def cpu_baseline(synth, np, seconds):
+    """The oracle's Q4_0 x Q8_0 decode GEMV on the four 8B-class shapes, on
+    the host's cores, repeated until `seconds` of wall time have passed."""
+    import oracle as O
+    data = []
+    for s, (k, n) in enumerate(synth.SHAPES_8B):
+        codes, d_bits, x = synth.q4_decode(s)
+        data.append((O.pack_q4_0(codes, d_bits), O.quantize_q8_0(x), n, k))
+        del codes, d_bits
+    nbytes = sum(w.size + xq.size + 4 * n for w, xq, n, k in data)
+    t_total, passes = 0.0, 0
+    while passes < 1 or (t_total < seconds and passes < 50):
+        t0 = time.perf_counter()
+        for w, xq, n, k in data:
+            O.q4_0_q8_0(w, xq, 1, n, k)
+        t_total += time.perf_counter() - t0
+        passes += 1
+    return {"value": nbytes * passes / t_total / 1e9, "unit": "GB/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{passes} pass(es) of the Q4_0 x Q8_0 decode GEMV oracle (int32 block sums, f64 scaling) "
+                      f"over the four 8B-class shapes, {nbytes / 1e6:.1f} MB per pass, {t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by output rows across GPUs, which this build does not run).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import quantized_linear_layer_amd as qll
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    qll.load()
+    print("bench: setting up inputs", file=sys.stderr, flush=True)
+    ops, step_ref = build_ops(qll, synth, torch, np, dev, args.only)
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        ops.append(Op("copy_1gib", "calibration", "copy", lambda: dst.copy_(src), 2 * src.numel() * 4, 0, "hbm"))
+    torch.cuda.synchronize()
+    print(f"bench: {len(ops)} ops per step; warmup {args.warmup}", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step_ref["i"] = i
+        for op in ops:
+            op.fn()
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        step_ref["i"] = args.warmup + st
+        for j, op in enumerate(ops):
+            evs[st][j][0].record(stream)
+            op.fn()
+            evs[st][j][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    for st in range(args.steps):
+        for j, op in enumerate(ops):
+            op.times_ms.append(evs[st][j][0].elapsed_time(evs[st][j][1]))
+    print(f"bench: timed {args.steps} steps, {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    kernels = []
+    for op in ops:
+        t = np.array(op.times_ms)
+        ms = float(np.mean(t))
+        rl = op.roofline(ms)
+        entry = {"op": op.name, "format": op.fmt, "kind": op.kind, "ms": ms, "ms_median": float(np.median(t)),
+                 "cv": float(np.std(t) / ms) if ms > 0 else 0.0, "bytes": op.nbytes, "flops": op.flops, **rl}
+        if op.kind == "prefill" and op.peak_key == "f16":
+            entry["frac_int8_peak"] = rl["achieved"] / PEAK_TFLOPS["i8"]
+        if op.name == "ternary_gemm":
+            entry["hbm_gbs"] = op.nbytes / (ms * 1e-3) / 1e9
+            entry["hbm_frac"] = entry["hbm_gbs"] / PEAK_HBM_GBS
+        kernels.append(entry)
+        print(f"  {op.name:22s} {ms * 1e3:10.2f} us  {rl['achieved']:10.1f} {rl['unit']:8s} "
+              f"{100 * rl['frac']:6.1f}% of {rl['bound']} peak  (cv {entry['cv']:.3f})", file=sys.stderr)
+
+    def agg(fmt, kind):
+        sel = [(op, e) for op, e in zip(ops, kernels) if op.fmt == fmt and op.kind == kind]
+        if not sel:
+            return None
+        t = sum(e["ms"] for _, e in sel) * 1e-3
+        if kind == "decode":
+            v = sum(op.nbytes for op, _ in sel) / t / 1e9
+            return {"gbs": v, "frac_hbm": v / PEAK_HBM_GBS}
+        v = sum(op.flops for op, _ in sel) / t / 1e12
+        key = sel[0][0].peak_key
+        out = {"tops": v, "mfma_dtype": key, "frac_mfma": v / PEAK_TFLOPS[key]}
+        if key == "f16":
+            out["frac_int8_peak"] = v / PEAK_TFLOPS["i8"]
+        return out
+
+    per_format = {}
+    for fmt in ("q4_0", "f32", "ternary"):
+        d = {"decode": agg(fmt, "decode"), "prefill": agg(fmt, "prefill")}
+        if any(d.values()):
+            per_format[fmt] = d
+
+    dom = max(kernels, key=lambda e: e["ms"]) if kernels else None
+    roofline = None
+    if dom is not None:
+        roofline = {"kernel": dom["op"], "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
+                    "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic_for(dom["op"])}
+
+    value = per_format.get("q4_0", {}).get("decode", {}) or {}
+    cpu = None
+    if not args.no_cpu_baseline and not args.only:
+        print("bench: timing the oracle on the host (cpu_baseline)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(synth, np, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": value.get("gbs"), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8 (Q4_0 x Q8_0 int8 block dots, f32 scaling)", "data": "synthetic",
+        "config": {"workload": "one pass of the whole path: Q4_0 x Q8_0 decode GEMV (m=1) and prefill GEMM (m=512) "
+                               "on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256); f32 GEMM 4096^3 "
+                               "and GEMV 4096x4096; BitNet ternary 2560->6912 at m=1 and m=64",
+                   "value_is": "Q4_0 x Q8_0 decode GEMV algorithmic bytes / summed kernel time over the four shapes",
+                   "parallelism": "single GPU"},
+        "per_format": per_format, "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def traffic_for(op_name):
+    """HBM bytes per launch measured with rocprofv3 counters, read from the
+    committed summary if it was taken on the current kernel sources."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    entry = rec.get("ops", {}).get(op_name)
+    if not entry:
+        return None
+    src = os.path.join(ROOT, "quantized_linear_layer_amd", "csrc", entry["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != entry["source_sha256"]:
+        return None
+    return entry["bytes_per_launch"]
+
+
+if __name__ == "__main__":
+    main()
