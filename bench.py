@@ -118,9 +118,11 @@ def build_ops(qll, synth, torch, np, dev, only):
             if want(f"q4_gemm_{s}"):
                 # the prefill GEMM needs quantized activations even when profiled alone
                 qll.qll_quantize_q8_0(xp, xqp, m, k)
+                need = qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, m, n, k)
+                wsp = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
                 ops.append(Op(f"q4_gemm_{s}", "q4_0", "prefill",
-                              lambda w0=w0, xqp=xqp, yp=yp, n=n, k=k: qll.qll_q4_0_q8_0_gemm(
-                                  w0, xqp, yp, 512, n, k),
+                              lambda w0=w0, xqp=xqp, yp=yp, n=n, k=k, wsp=wsp: qll.qll_q4_0_q8_0_gemm(
+                                  w0, xqp, yp, 512, n, k, ws=wsp),
                               wbytes + m * (k // 32) * 34 + 4 * m * n, 2 * m * n * k, "mfma", "f16"))
         if need_dec and want(f"q4_gemv_{s}") and not want(f"q8_quant_decode_{s}"):
             qll.qll_quantize_q8_0(xd, xqd, 1, k)

@@ -22,9 +22,15 @@ FLAGS = ["-std=c++17", "-O3", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-source extra flags.  q4_gemm: MFMA results go to VGPRs, so the block
+# sums of a row of subtiles can be in flight together (the default AGPR form
+# serialised them through one accumulator).
+EXTRA = {"q4_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "not a recognized feature" not in l
                     and "ignoring feature" not in l)

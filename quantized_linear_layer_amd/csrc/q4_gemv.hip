@@ -100,102 +100,237 @@ __device__ __forceinline__ float q4_block_dot(uint32_t dbits, const uint32_t qs[
 }
 
 // Decode the Q8_0 activation row into LDS (all threads of the workgroup).
-__device__ __forceinline__ ActLds stage_q8_row(const uint8_t *__restrict__ xq, int nb, void *smem)
+// Split in two so that a kernel can issue the activation loads BEFORE its
+// weight loads: loads retire in order, so waiting for activation bytes that
+// were requested after the weights would also wait for the weights.
+constexpr int kStageRegs = 2; // blocks per thread held in registers (nb <= 2 * blockDim)
+
+struct ActRaw {
+    uint32_t w[kStageRegs][9]; // raw dword window of each block, decoded later
+    uint32_t tail[kStageRegs]; // the block's last two bytes
+};
+
+// Block b starts at byte 34b: dword aligned for even b, 2 bytes past a dword
+// for odd b.  Every block loads the nine dwords from floor(34b / 4) with the
+// same code (no divergent branch, so nothing waits for these loads until
+// stage_q8_finish), plus the block's last two bytes as a u16.  An even block
+// uses that u16 in place of its ninth dword, which for the last block of the
+// row would lie past the end of the buffer (its index is clamped here).
+__device__ __forceinline__ void stage_q8_load(const uint8_t *xq, int nb, ActRaw &raw)
+{
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(xq);
+    const int64_t max_dw = (int64_t)nb * 34 / 4 - 1;
+#pragma unroll
+    for (int i = 0; i < kStageRegs; i++) {
+        // unconditional loads (threads past the row end reload the last block,
+        // which stage_q8_finish then ignores): a branch here would make the
+        // compiler wait for these loads at its join
+        int b = threadIdx.x + i * blockDim.x;
+        b = b < nb ? b : nb - 1;
+        const int64_t a = ((int64_t)b * 34 - 2 * (b & 1)) / 4;
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            raw.w[i][e] = p[a + e];
+        raw.w[i][8] = p[a + 8 <= max_dw ? a + 8 : max_dw];
+        raw.tail[i] = *reinterpret_cast<const uint16_t *>(xq + (int64_t)b * 34 + 32);
+    }
+}
+
+__device__ __forceinline__ void decode_q8_window(const uint32_t w[9], bool odd, uint32_t &d, uint32_t q[8])
+{
+    // even block: d = low half of dword 0, codes shifted by two bytes;
+    // odd block: d = high half of dword 0, codes are dwords 1..8
+    const uint32_t sh = odd ? 0u : 16u;
+    d = odd ? (w[0] >> 16) : (w[0] & 0xffffu);
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        q[i] = funnel(w[i + 1], odd ? w[i + 1] : w[i], sh);
+}
+
+__device__ __forceinline__ void stage_q8_store_block(int b, uint32_t d, const uint32_t q[8], int nb, bool store,
+                                                     void *smem)
 {
     u32x4 *s_qs = reinterpret_cast<u32x4 *>(smem);
     float *s_dx = reinterpret_cast<float *>(s_qs + 2 * nb);
     int *s_c8 = reinterpret_cast<int *>(s_dx + nb);
-    for (int b = threadIdx.x; b < nb; b += blockDim.x) {
-        uint32_t d, q[8];
-        load_q8_0_block(xq, (int64_t)b * 34, d, q);
-        int sx = 0;
+    int sx = 0;
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            sx = sdot4(q[i], 0x01010101u, sx);
+    for (int i = 0; i < 8; i++)
+        sx = sdot4(q[i], 0x01010101u, sx);
+    const float dx = half_bits_to_float(d);
+    if (store) {
         s_qs[2 * b] = u32x4{q[0], q[1], q[2], q[3]};
         s_qs[2 * b + 1] = u32x4{q[4], q[5], q[6], q[7]};
-        s_dx[b] = half_bits_to_float(d);
+        s_dx[b] = dx;
         s_c8[b] = -8 * sx;
     }
+}
+
+// Writes the blocks held in `raw`, stages any remaining blocks directly (only
+// when nb > kStageRegs * blockDim), and synchronises the workgroup.
+__device__ __forceinline__ ActLds stage_q8_finish(const uint8_t *xq, int nb, const ActRaw &raw,
+                                                  void *smem)
+{
+    // decode unconditionally (only the stores are guarded): a use inside a
+    // branch would let the compiler sink the loads past the weight loads
+#pragma unroll
+    for (int i = 0; i < kStageRegs; i++) {
+        const int b = threadIdx.x + i * blockDim.x;
+        const int bc = b < nb ? b : nb - 1;
+        uint32_t w9[9];
+#pragma unroll
+        for (int e = 0; e < 9; e++)
+            w9[e] = raw.w[i][e];
+        w9[8] = (bc & 1) ? w9[8] : raw.tail[i];
+        uint32_t d, q[8];
+        decode_q8_window(w9, (bc & 1) != 0, d, q);
+        stage_q8_store_block(bc, d, q, nb, b < nb, smem);
+    }
+    for (int b = threadIdx.x + kStageRegs * blockDim.x; b < nb; b += blockDim.x) {
+        uint32_t d, q[8];
+        load_q8_0_block(xq, (int64_t)b * 34, d, q);
+        stage_q8_store_block(b, d, q, nb, true, smem);
+    }
     __syncthreads();
+    u32x4 *s_qs = reinterpret_cast<u32x4 *>(smem);
+    float *s_dx = reinterpret_cast<float *>(s_qs + 2 * nb);
+    int *s_c8 = reinterpret_cast<int *>(s_dx + nb);
     return ActLds{s_qs, s_dx, s_c8};
 }
 
 constexpr int kGemvThreads = 256;
-constexpr int kGemvUnroll = 4;
 
-template <int L, bool PAIR>
+// One work item of a wave: a group of R = 64/L rows and a chunk of U * L
+// consecutive units of those rows (U per lane).
+template <int U>
+struct GemvRaw {
+    uint32_t w[U][9];
+};
+
+template <int L, int U, bool PAIR>
+__device__ __forceinline__ void gemv_load(const uint8_t *__restrict__ w, int64_t row, int64_t n, int64_t row_bytes,
+                                          int nu, int ubase, int r, GemvRaw<U> &raw)
+{
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        // Units outside the matrix load the first unit of row 0 instead (and
+        // are masked in gemv_compute): unconditional loads let the compiler
+        // count them, so waits for earlier loads do not drain these.
+        int u = ubase + r + i * L;
+        const bool ok = row < n && u < nu;
+        const int64_t rr = ok ? row : 0;
+        u = ok ? u : 0;
+        if (PAIR) {
+            load_q4_pair(w + rr * row_bytes + (int64_t)u * 36, raw.w[i]);
+        } else {
+            load_q4_single(w, rr * row_bytes + (int64_t)u * 18, raw.w[i]);
+        }
+    }
+}
+
+template <int L, int U, bool PAIR>
+__device__ __forceinline__ float gemv_compute(const GemvRaw<U> &raw, int64_t row, int64_t n, int64_t row_bytes,
+                                              int nu, int ubase, int r, const ActLds &act)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        const int u = ubase + r + i * L;
+        if (row < n && u < nu) {
+            Q4Unit unit;
+            if (PAIR) {
+                decode_q4_pair(raw.w[i], unit);
+                acc += q4_block_dot(unit.d[0], unit.qs[0], act, 2 * u);
+                acc += q4_block_dot(unit.d[1], unit.qs[1], act, 2 * u + 1);
+            } else {
+                const int64_t o = row * row_bytes + (int64_t)u * 18;
+                decode_q4_single(raw.w[i], (o & 3) != 0, unit);
+                acc += q4_block_dot(unit.d[0], unit.qs[0], act, u);
+            }
+        }
+    }
+    return acc;
+}
+
+// Persistent over work items: each wave walks the row groups
+// wave_id, wave_id + total_waves, ... and, within a row group, its chunks in
+// order; the next item's weight bytes are loaded while the current one is
+// computed.  The activation loads are issued first, then the first item's
+// weight loads, then the activation is decoded into LDS: loads complete in
+// order, so the staging waits only for its own bytes and HBM traffic starts
+// at once.  (xq is deliberately not __restrict__: with it, the compiler may
+// move the activation loads past the barrier that keeps them ahead.)
+template <int L, int U, bool PAIR>
 __global__ __launch_bounds__(kGemvThreads) void q4_0_q8_0_gemv_kernel(const uint8_t *__restrict__ w,
-                                                                      const uint8_t *__restrict__ xq,
+                                                                      const uint8_t *xq,
                                                                       float *__restrict__ y, int64_t n, int nb)
 {
     extern __shared__ u32x4 smem[];
-    const ActLds act = stage_q8_row(xq, nb, smem);
-
     constexpr int R = 64 / L; // rows per wave
     constexpr int WAVES = kGemvThreads / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / L, r = lane % L;
     const int nu = PAIR ? nb / 2 : nb;
+    const int chunk_units = U * L;
+    const int chunks = (nu + chunk_units - 1) / chunk_units;
     const int64_t row_bytes = (int64_t)nb * 18;
-    const int64_t stride = (int64_t)gridDim.x * WAVES * R;
+    const int64_t n_groups = (n + R - 1) / R;
+    const int64_t stride = (int64_t)gridDim.x * WAVES;
 
-    for (int64_t row0 = ((int64_t)blockIdx.x * WAVES + wave) * R; row0 < n; row0 += stride) {
-        const int64_t row = row0 + g;
-        float acc = 0.0f;
-        if (row < n) {
-            const uint8_t *wr = w + row * row_bytes;
-            for (int u0 = r; u0 < nu; u0 += kGemvUnroll * L) {
-                Q4Unit unit[kGemvUnroll];
-#pragma unroll
-                for (int i = 0; i < kGemvUnroll; i++) {
-                    const int u = u0 + i * L;
-                    if (u < nu) {
-                        if (PAIR) {
-                            uint32_t raw[9];
-                            load_q4_pair(wr + (int64_t)u * 36, raw);
-                            decode_q4_pair(raw, unit[i]);
-                        } else {
-                            uint32_t raw[5];
-                            const int64_t o = row * row_bytes + (int64_t)u * 18;
-                            load_q4_single(w, o, raw);
-                            decode_q4_single(raw, (o & 3) != 0, unit[i]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < kGemvUnroll; i++) {
-                    const int u = u0 + i * L;
-                    if (u < nu) {
-                        if (PAIR) {
-                            acc += q4_block_dot(unit[i].d[0], unit[i].qs[0], act, 2 * u);
-                            acc += q4_block_dot(unit[i].d[1], unit[i].qs[1], act, 2 * u + 1);
-                        } else {
-                            acc += q4_block_dot(unit[i].d[0], unit[i].qs[0], act, u);
-                        }
-                    }
-                }
-            }
+    ActRaw araw;
+    stage_q8_load(xq, nb, araw);
+    asm volatile("" ::: "memory"); // keep these loads ahead of the weight loads
+
+    int64_t grp = (int64_t)blockIdx.x * WAVES + wave;
+    int c = 0;
+    GemvRaw<U> cur;
+    // unconditional (a wave without work loads masked dummies): see gemv_load
+    gemv_load<L, U, PAIR>(w, grp * R + g, n, row_bytes, nu, 0, r, cur);
+
+    const ActLds act = stage_q8_finish(xq, nb, araw, smem);
+
+    float acc = 0.0f;
+    while (grp < n_groups) {
+        int64_t grp2 = grp;
+        int c2 = c + 1;
+        if (c2 == chunks) {
+            c2 = 0;
+            grp2 += stride;
         }
+        GemvRaw<U> nxt;
+        if (grp2 < n_groups)
+            gemv_load<L, U, PAIR>(w, grp2 * R + g, n, row_bytes, nu, c2 * chunk_units, r, nxt);
+        const int64_t row = grp * R + g;
+        acc += gemv_compute<L, U, PAIR>(cur, row, n, row_bytes, nu, c * chunk_units, r, act);
+        if (c == chunks - 1) {
 #pragma unroll
-        for (int off = L / 2; off > 0; off >>= 1)
-            acc += __shfl_xor(acc, off);
-        if (row < n && r == 0)
-            y[row] = acc;
+            for (int off = L / 2; off > 0; off >>= 1)
+                acc += __shfl_xor(acc, off);
+            if (row < n && r == 0)
+                y[row] = acc;
+            acc = 0.0f;
+        }
+        cur = nxt;
+        grp = grp2;
+        c = c2;
     }
 }
 
 size_t q4_gemv_lds_bytes(int nb) { return (size_t)nb * 40; }
 
-template <int L, bool PAIR>
+// One work item per wave: the dispatcher starts new workgroups as others
+// finish, which measured faster on the 296 MB vocabulary projection than
+// looping resident waves over items (47 vs 53 us), and equal on one-pass
+// shapes.  The kernel still loops if the grid limit were ever reached.
+template <int L, int U, bool PAIR>
 static hipError_t launch_l(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int nb, hipStream_t s)
 {
     constexpr int R = 64 / L;
-    const int64_t waves = (n + R - 1) / R;
-    int64_t grid = (waves + kGemvThreads / 64 - 1) / (kGemvThreads / 64);
-    if (grid > 8192)
-        grid = 8192;
-    hipLaunchKernelGGL((q4_0_q8_0_gemv_kernel<L, PAIR>), dim3((unsigned)grid), dim3(kGemvThreads),
+    const int64_t groups = (n + R - 1) / R;
+    int64_t grid = (groups + kGemvThreads / 64 - 1) / (kGemvThreads / 64);
+    if (grid > 0x7fffffff)
+        grid = 0x7fffffff;
+    hipLaunchKernelGGL((q4_0_q8_0_gemv_kernel<L, U, PAIR>), dim3((unsigned)grid), dim3(kGemvThreads),
                        q4_gemv_lds_bytes(nb), s, w, xq, y, n, nb);
     return hipGetLastError();
 }
@@ -204,14 +339,26 @@ template <bool PAIR>
 static hipError_t launch_pair(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int nb, hipStream_t s)
 {
     const int nu = PAIR ? nb / 2 : nb;
-    // about four units per lane per row; 8..64 lanes per row
-    if (nu >= 256)
-        return launch_l<64, PAIR>(w, xq, y, n, nb, s);
-    if (nu >= 128)
-        return launch_l<32, PAIR>(w, xq, y, n, nb, s);
-    if (nu >= 64)
-        return launch_l<16, PAIR>(w, xq, y, n, nb, s);
-    return launch_l<8, PAIR>(w, xq, y, n, nb, s);
+    // Lanes per row (8..64).  A matrix that fits in one pass of the resident
+    // waves gets about two units per lane (more, lighter waves: a shorter
+    // compute tail after the last bytes land); a larger one about four (less
+    // per-row overhead in the persistent loop).
+    if (n <= 16384) {
+        if (nu > 64)
+            return launch_l<64, 4, PAIR>(w, xq, y, n, nb, s);
+        if (nu > 32)
+            return launch_l<32, 2, PAIR>(w, xq, y, n, nb, s);
+        if (nu > 16)
+            return launch_l<16, 2, PAIR>(w, xq, y, n, nb, s);
+        return launch_l<8, 2, PAIR>(w, xq, y, n, nb, s);
+    }
+    if (nu > 128)
+        return launch_l<64, 4, PAIR>(w, xq, y, n, nb, s);
+    if (nu > 64)
+        return launch_l<32, 4, PAIR>(w, xq, y, n, nb, s);
+    if (nu > 32)
+        return launch_l<16, 4, PAIR>(w, xq, y, n, nb, s);
+    return launch_l<8, 4, PAIR>(w, xq, y, n, nb, s);
 }
 
 hipError_t launch_q4_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int64_t k,

@@ -22,10 +22,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // ------------------------------------------------------------------ GEMV
 
 constexpr int kSgemvThreads = 256;
+constexpr int kSgemvUnroll = 8; // rows of B in flight per lane
 
 struct SgemvPlan {
-    int64_t col_groups; // workgroups along n
-    int64_t kc;         // rows of B per k-chunk
+    int64_t col_groups; // workgroups along n (64 lanes x vec columns each)
+    int64_t kc;         // rows of B per k-chunk (a multiple of 4)
     int64_t ks;         // number of k-chunks
     int vec;            // columns per lane
 };
@@ -36,13 +37,14 @@ static SgemvPlan sgemv_plan(int64_t n, int64_t k)
     p.vec = (n % 4 == 0) ? 4 : 1;
     const int64_t cols_per_wg = 64 * p.vec;
     p.col_groups = (n + cols_per_wg - 1) / cols_per_wg;
-    int64_t want = (2048 + p.col_groups - 1) / p.col_groups; // about 2048 workgroups
-    int64_t max_ks = (k + 15) / 16;                           // at least 16 rows per chunk
+    int64_t want = (512 + p.col_groups - 1) / p.col_groups; // about 512 workgroups
+    const int64_t max_ks = (k + 31) / 32;                    // at least 32 rows per chunk
     if (want > max_ks)
         want = max_ks;
     if (want < 1)
         want = 1;
     p.kc = (k + want - 1) / want;
+    p.kc = (p.kc + 3) / 4 * 4;
     p.ks = (k + p.kc - 1) / p.kc;
     return p;
 }
@@ -53,6 +55,9 @@ size_t sgemv_workspace(int64_t n, int64_t k)
     return (size_t)(p.ks * n) * sizeof(float);
 }
 
+// Workgroup (column group, k-chunk): wave w takes rows p0 + w, p0 + w + 4, ...
+// of the chunk, kSgemvUnroll at a time; the four waves combine in LDS in a
+// fixed order and write the chunk's partial sums to ws[chunk][n].
 template <int VEC>
 __global__ __launch_bounds__(kSgemvThreads) void sgemv_partial_kernel(const float *__restrict__ x,
                                                                       const float *__restrict__ b,
@@ -70,38 +75,32 @@ __global__ __launch_bounds__(kSgemvThreads) void sgemv_partial_kernel(const floa
     for (int e = 0; e < VEC; e++)
         acc[e] = 0.0f;
     if (col < n) {
-        // the four waves interleave over the rows of the chunk
-        int64_t p = p0 + wave;
-        for (; p + 12 < p1; p += 16) {
-            float xv[4];
-            float bv[4][VEC];
+        for (int64_t p = p0 + wave; p < p1; p += 4 * kSgemvUnroll) {
+            float xv[kSgemvUnroll];
+            float bv[kSgemvUnroll][VEC];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                xv[i] = x[p + 4 * i];
-                if (VEC == 4) {
-                    float4 v = *reinterpret_cast<const float4 *>(b + (p + 4 * i) * n + col);
-                    bv[i][0] = v.x; bv[i][1] = v.y; bv[i][2] = v.z; bv[i][3] = v.w;
+            for (int i = 0; i < kSgemvUnroll; i++) {
+                const int64_t pi = p + 4 * i;
+                if (pi < p1) {
+                    xv[i] = x[pi];
+                    if (VEC == 4) {
+                        float4 v = *reinterpret_cast<const float4 *>(b + pi * n + col);
+                        bv[i][0] = v.x; bv[i][1] = v.y; bv[i][2] = v.z; bv[i][3] = v.w;
+                    } else {
+                        bv[i][0] = b[pi * n + col];
+                    }
                 } else {
-                    bv[i][0] = b[(p + 4 * i) * n + col];
+                    xv[i] = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < VEC; e++)
+                        bv[i][e] = 0.0f;
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+            for (int i = 0; i < kSgemvUnroll; i++)
 #pragma unroll
                 for (int e = 0; e < VEC; e++)
                     acc[e] = fmaf(xv[i], bv[i][e], acc[e]);
-        }
-        for (; p < p1; p += 4) {
-            const float xv = x[p];
-            if (VEC == 4) {
-                float4 v = *reinterpret_cast<const float4 *>(b + p * n + col);
-                acc[0] = fmaf(xv, v.x, acc[0]);
-                acc[1] = fmaf(xv, v.y, acc[1]);
-                acc[2] = fmaf(xv, v.z, acc[2]);
-                acc[3] = fmaf(xv, v.w, acc[3]);
-            } else {
-                acc[0] = fmaf(xv, b[p * n + col], acc[0]);
-            }
         }
     }
     if (wave > 0)
@@ -120,16 +119,32 @@ __global__ __launch_bounds__(kSgemvThreads) void sgemv_partial_kernel(const floa
     }
 }
 
+// c[j] = sum over chunks of ws[s][j]: wave w adds chunks w, w+4, ... in order
+// (independent loads, unrolled), then the four waves combine in LDS.
 __global__ __launch_bounds__(256) void sgemv_finish_kernel(const float *__restrict__ ws, float *__restrict__ c,
                                                            int64_t n, int64_t ks)
 {
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= n)
-        return;
+    __shared__ float s_part[3][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t j = (int64_t)blockIdx.x * 64 + lane;
     float v = 0.0f;
-    for (int64_t s = 0; s < ks; s++)
-        v += ws[s * n + j];
-    c[j] = v;
+    if (j < n) {
+        int64_t s = wave;
+        for (; s + 12 < ks; s += 16) {
+            float t0 = ws[s * n + j], t1 = ws[(s + 4) * n + j], t2 = ws[(s + 8) * n + j], t3 = ws[(s + 12) * n + j];
+            v += t0;
+            v += t1;
+            v += t2;
+            v += t3;
+        }
+        for (; s < ks; s += 4)
+            v += ws[s * n + j];
+    }
+    if (wave > 0)
+        s_part[wave - 1][lane] = v;
+    __syncthreads();
+    if (wave == 0 && j < n)
+        c[j] = ((v + s_part[0][lane]) + s_part[1][lane]) + s_part[2][lane];
 }
 
 hipError_t launch_sgemv(const float *x, const float *b, float *c, int64_t n, int64_t k, float *ws, hipStream_t s)
@@ -143,7 +158,7 @@ hipError_t launch_sgemv(const float *x, const float *b, float *c, int64_t n, int
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(sgemv_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws, c, n, p.ks);
+    hipLaunchKernelGGL(sgemv_finish_kernel, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, ws, c, n, p.ks);
     return hipGetLastError();
 }
 

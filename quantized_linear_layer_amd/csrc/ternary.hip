@@ -144,61 +144,103 @@ hipError_t launch_ternary_gemv(const uint32_t *w, float w_scale, const int8_t *x
 }
 
 // ------------------------------------------------------------------ GEMM (m > 1)
-// v_mfma_i32_16x16x64_i8: one MFMA covers 64 codes = 4 words of a weight row.
-// Lane group h of an operand takes word h*Q + s at k-step s (Q = ceil(nw/4)),
-// so a lane walks its own contiguous quarter of the row; the activation
-// bytes of the same word (transposed like the unpack) are its A operand.
-// Words past the row end are zero activation, so their codes do not matter.
+// v_mfma_i32_16x16x64_i8: one MFMA covers 64 codes = 4 weight words.  The
+// k range is walked in chunks of kTerKC codes (32 words).  Within a chunk,
+// lane group h of an operand (lanes 16h..16h+15) takes words 8h..8h+7 in
+// successive k-steps, so a lane's weight words are contiguous (two 16-byte
+// loads per chunk) and the activation bytes of the same words, transposed
+// like the code unpack, are its A operand.  Words past the end of the row
+// meet zero activation, so the codes there do not matter.
 // Workgroup tile: 64 activation rows x 32 weight rows; wave w owns rows
-// 16w..16w+15 and both 16-column halves.  The activation is staged in LDS
-// in chunks of kTerSC k-steps.
+// 16w..16w+15 and both 16-column halves.  The activation chunk (64 rows x
+// 512 bytes) is loaded with consecutive lanes on consecutive 16-byte pieces
+// of a row and double buffered in LDS; rows are padded by 16 bytes so the 16
+// rows read by one MFMA operand fall in distinct banks.
 
-constexpr int TBM = 64, TBN = 32, kTerSC = 8;
+constexpr int TBM = 64, TBN = 32, kTerKC = 512, kTerWPC = kTerKC / 16; // words per chunk
 constexpr int kTerGemmThreads = 256;
+constexpr int kTerPieces = TBM * kTerWPC / kTerGemmThreads;             // 16-byte pieces per thread
 
+struct TerStage {
+    u32x4 x[kTerPieces];
+    uint32_t w[2][8];
+};
+
+template <bool VEC>
+__device__ __forceinline__ void ternary_gemm_load(const uint32_t *__restrict__ w, const int8_t *__restrict__ xq,
+                                                  int64_t m, int64_t n, int nw, int64_t m0, int64_t n0, int chunk,
+                                                  TerStage &st)
+{
+    const int lane = threadIdx.x & 63;
+    const int lr = lane & 15, lh = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < kTerPieces; i++) {
+        const int piece = threadIdx.x + i * kTerGemmThreads;
+        const int row = piece / kTerWPC, word = chunk * kTerWPC + piece % kTerWPC;
+        const int64_t gi = m0 + row;
+        st.x[i] = (gi < m && word < nw)
+                      ? *reinterpret_cast<const u32x4 *>(xq + gi * (int64_t)nw * 16 + (int64_t)word * 16)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int64_t col = n0 + 16 * j + lr;
+        const int word0 = chunk * kTerWPC + 8 * lh;
+        const uint32_t *wr = w + col * nw;
+        if (VEC && col < n && word0 + 8 <= nw) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(wr + word0);
+            const u32x4 b = *reinterpret_cast<const u32x4 *>(wr + word0 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                st.w[j][e] = a[e];
+                st.w[j][4 + e] = b[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                st.w[j][e] = (col < n && word0 + e < nw) ? wr[word0 + e] : 0u;
+        }
+    }
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kTerGemmThreads) void ternary_gemm_kernel(
     const uint32_t *__restrict__ w, float w_scale, const int8_t *__restrict__ xq, const float *__restrict__ act_scale,
     const int32_t *__restrict__ act_sum, float *__restrict__ y, int64_t m, int64_t n, int nw)
 {
-    __shared__ u32x4 xs[4][kTerSC][TBM];
+    __shared__ u32x4 xs[2][TBM][kTerWPC + 1];
     const int64_t m0 = (int64_t)blockIdx.y * TBM, n0 = (int64_t)blockIdx.x * TBN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lh = lane >> 4;
-    const int Q = (nw + 3) / 4;
+    const int nchunks = (nw + kTerWPC - 1) / kTerWPC;
 
     i32x4 acc[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
-    for (int s0 = 0; s0 < Q; s0 += kTerSC) {
-        __syncthreads();
-        for (int it = threadIdx.x; it < 4 * kTerSC * TBM; it += kTerGemmThreads) {
-            const int row = it % TBM, ss = (it / TBM) % kTerSC, h = it / (TBM * kTerSC);
-            const int s = s0 + ss;
-            const int wi = h * Q + s;
-            const int64_t gi = m0 + row;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (gi < m && s < Q && wi < nw)
-                v = transpose_4x4_bytes(*reinterpret_cast<const u32x4 *>(xq + gi * (int64_t)nw * 16 + (int64_t)wi * 16));
-            xs[h][ss][row] = v;
+    TerStage st;
+    ternary_gemm_load<VEC>(w, xq, m, n, nw, m0, n0, 0, st);
+    for (int c = 0; c < nchunks; c++) {
+        const int buf = c & 1;
+#pragma unroll
+        for (int i = 0; i < kTerPieces; i++) {
+            const int piece = threadIdx.x + i * kTerGemmThreads;
+            xs[buf][piece / kTerWPC][piece % kTerWPC] = transpose_4x4_bytes(st.x[i]);
         }
+        uint32_t wcur[2][8];
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                wcur[j][e] = st.w[j][e];
         __syncthreads();
-        uint32_t wd[2][kTerSC];
+        if (c + 1 < nchunks)
+            ternary_gemm_load<VEC>(w, xq, m, n, nw, m0, n0, c + 1, st);
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t col = n0 + 16 * j + lr;
-#pragma unroll
-            for (int ss = 0; ss < kTerSC; ss++) {
-                const int s = s0 + ss, wi = lh * Q + s;
-                wd[j][ss] = (col < n && s < Q && wi < nw) ? w[col * nw + wi] : 0u;
-            }
-        }
-#pragma unroll
-        for (int ss = 0; ss < kTerSC; ss++) {
-            const u32x4 av = xs[lh][ss][16 * wave + lr];
-            const i32x4 a = __builtin_bit_cast(i32x4, av);
+        for (int s = 0; s < 8; s++) {
+            const i32x4 a = __builtin_bit_cast(i32x4, xs[buf][16 * wave + lr][8 * lh + s]);
 #pragma unroll
             for (int j = 0; j < 2; j++) {
-                const uint32_t c = wd[j][ss];
-                const i32x4 b = {(int)(c & 0x03030303u), (int)((c >> 2) & 0x03030303u), (int)((c >> 4) & 0x03030303u),
-                                 (int)((c >> 6) & 0x03030303u)};
+                const uint32_t cw = wcur[j][s];
+                const i32x4 b = {(int)(cw & 0x03030303u), (int)((cw >> 2) & 0x03030303u),
+                                 (int)((cw >> 4) & 0x03030303u), (int)((cw >> 6) & 0x03030303u)};
                 acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[j], 0, 0, 0);
             }
         }
@@ -224,8 +266,13 @@ hipError_t launch_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *x
                                const int32_t *act_sum, float *y, int64_t m, int64_t n, int64_t k, hipStream_t st)
 {
     dim3 grid((unsigned)((n + TBN - 1) / TBN), (unsigned)((m + TBM - 1) / TBM));
-    hipLaunchKernelGGL(ternary_gemm_kernel, grid, dim3(kTerGemmThreads), 0, st, w, w_scale, xq, act_scale, act_sum,
-                       y, m, n, (int)(k / 16));
+    const int nw = (int)(k / 16);
+    if (nw % 4 == 0)
+        hipLaunchKernelGGL(ternary_gemm_kernel<true>, grid, dim3(kTerGemmThreads), 0, st, w, w_scale, xq, act_scale,
+                           act_sum, y, m, n, nw);
+    else
+        hipLaunchKernelGGL(ternary_gemm_kernel<false>, grid, dim3(kTerGemmThreads), 0, st, w, w_scale, xq,
+                           act_scale, act_sum, y, m, n, nw);
     return hipGetLastError();
 }
 

@@ -61,7 +61,7 @@ def test_gemv_small_layer(qll_gpu):
 
 
 @pytest.mark.parametrize("n", [1, 3, 7, 8, 15, 16, 17, 31, 64, 128, 257])
-@pytest.mark.parametrize("k", [32, 64, 96, 512, 4096])
+@pytest.mark.parametrize("k", [32, 64, 96, 256, 512, 1024, 4096, 8192, 16384])
 def test_gemv_adversarial_shapes(qll_gpu, n, k):
     codes, d_bits, x = rand_case(n * 31 + k, 1, n, k)
     _gemv_check(codes, d_bits, x, f"GEMV n={n} k={k}")
