@@ -195,7 +195,7 @@ def cpu_baseline(synth, np, seconds):
         del codes, d_bits
     nbytes = sum(w.size + xq.size + 4 * n for w, xq, n, k in data)
     t_total, passes = 0.0, 0
-    while passes < 1 or (t_total < seconds and passes < 50):
+    while passes < 1 or (t_total < seconds and passes < 5000):
         t0 = time.perf_counter()
         for w, xq, n, k in data:
             O.q4_0_q8_0(w, xq, 1, n, k)
