@@ -87,72 +87,123 @@ struct Q4GemmLds {
     float dw[QKB][QBN + 8];
 };
 
-struct Q4GemmRaw {
-    uint32_t xd, xq[8]; // one Q8_0 block
-    uint32_t wd, wq[4]; // one Q4_0 block
+// Where one thread's staging loads come from.  Thread t stages row t/2,
+// block t%2 of every stage, for both X and W; a stage advances two blocks, so
+// the parity of the flat block index, which fixes the 2-byte offset of a
+// block inside its dword window, stays the same over the whole k loop.
+struct Q4GemmSrc {
+    int64_t xa, wa; // dword index of the stage-0 windows (X: 34-byte, W: 18-byte blocks)
+    int xpar, wpar; // parity of the flat block index
+    int b0;         // block index of stage 0
+    bool xrow, wrow; // the row lies inside the matrix
 };
 
-// Thread t stages row t/2, block t%2 of the stage, for both X and W.
-// Blocks at or past b_end (the end of this split's k range) load as zero.
-__device__ __forceinline__ void q4gemm_load(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq, int64_t m,
-                                            int64_t n, int nb, int b_end, int64_t m0, int64_t n0, int b0,
-                                            Q4GemmRaw &r)
+__device__ __forceinline__ Q4GemmSrc q4gemm_src(int64_t m, int64_t n, int nb, int64_t m0, int64_t n0, int b_begin)
 {
     const int row = threadIdx.x >> 1, kb = threadIdx.x & 1;
-    const int b = b0 + kb;
-    const int64_t xi = m0 + row, wj = n0 + row;
-    if (xi < m && b < b_end) {
-        load_q8_0_block(xq, (xi * nb + b) * 34, r.xd, r.xq);
-    } else {
-        r.xd = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-            r.xq[i] = 0;
+    Q4GemmSrc c;
+    c.b0 = b_begin + kb;
+    c.xrow = m0 + row < m;
+    c.wrow = n0 + row < n;
+    const int64_t g = (c.xrow ? m0 + row : 0) * nb + c.b0; // Q8_0 block at byte 34g
+    const int64_t h = (c.wrow ? n0 + row : 0) * nb + c.b0; // Q4_0 block at byte 18h
+    c.xpar = (int)(g & 1);
+    c.wpar = (int)(h & 1);
+    c.xa = (17 * g - c.xpar) / 2; // floor(34g / 4)
+    c.wa = (9 * h - c.wpar) / 2;  // floor(18h / 4)
+    return c;
+}
+
+// Raw bytes of one stage for one thread, loaded without being looked at:
+// decoding happens in q4gemm_store, so the loads stay in flight through a
+// whole stage of compute.
+struct Q4GemmRaw {
+    uint32_t xw[9], xtail; // Q8_0: nine dwords from the window start, bytes 32..33 of the window
+    uint32_t ww[5], wtail; // Q4_0: five dwords from the window start, bytes 16..17 of the window
+    int valid_x, valid_w;
+};
+
+// Stage st.  A block at or past b_end (the end of this split's k range), or
+// in a row past the matrix edge, loads from dword 0 instead and is zeroed
+// when decoded.  Every address stays inside its buffer: an odd-parity block
+// starts 2 bytes into its window and needs the ninth (fifth) dword, which
+// ends exactly at the block's end; an even-parity block takes its last two
+// bytes from the 16-bit tail load and re-reads dword 7 (3) in place of the
+// ninth (fifth).  All loads are unconditional, so none forces an early wait.
+__device__ __forceinline__ void q4gemm_load(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
+                                            const Q4GemmSrc &c, int st, int b_end, Q4GemmRaw &r)
+{
+    const bool in_k = c.b0 + 2 * st < b_end;
+    r.valid_x = c.xrow && in_k;
+    r.valid_w = c.wrow && in_k;
+    {
+        const int64_t a = r.valid_x ? c.xa + 17 * (int64_t)st : 0;
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(xq) + a;
+        const u32x4 v0 = *reinterpret_cast<const u32x4_a4 *>(p);
+        const u32x4 v1 = *reinterpret_cast<const u32x4_a4 *>(p + 4);
+        r.xw[0] = v0[0]; r.xw[1] = v0[1]; r.xw[2] = v0[2]; r.xw[3] = v0[3];
+        r.xw[4] = v1[0]; r.xw[5] = v1[1]; r.xw[6] = v1[2]; r.xw[7] = v1[3];
+        r.xw[8] = p[7 + (r.valid_x ? c.xpar : 0)];
+        r.xtail = *reinterpret_cast<const uint16_t *>(p + 8);
     }
-    if (wj < n && b < b_end) {
-        const int64_t o = (wj * nb + b) * 18;
-        const uint8_t *p = w + (o & ~(int64_t)3);
-        if ((o & 3) == 0) {
-            u32x4 a = load4_a4(p);
-            uint32_t tail = *reinterpret_cast<const uint16_t *>(w + o + 16);
-            r.wd = a[0] & 0xffffu;
-            r.wq[0] = funnel(a[1], a[0], 16);
-            r.wq[1] = funnel(a[2], a[1], 16);
-            r.wq[2] = funnel(a[3], a[2], 16);
-            r.wq[3] = funnel(tail, a[3], 16);
-        } else {
-            u32x4 a = load4_a4(p);
-            uint32_t tail = *reinterpret_cast<const uint32_t *>(p + 16);
-            r.wd = a[0] >> 16;
-            r.wq[0] = a[1];
-            r.wq[1] = a[2];
-            r.wq[2] = a[3];
-            r.wq[3] = tail;
-        }
-    } else {
-        r.wd = 0;
-        // code 8 everywhere: weight 0 (and d = 0 too)
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            r.wq[i] = 0x88888888u;
+    {
+        const int64_t a = r.valid_w ? c.wa + 9 * (int64_t)st : 0;
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(w) + a;
+        const u32x4 v0 = *reinterpret_cast<const u32x4_a4 *>(p);
+        r.ww[0] = v0[0]; r.ww[1] = v0[1]; r.ww[2] = v0[2]; r.ww[3] = v0[3];
+        r.ww[4] = p[3 + (r.valid_w ? c.wpar : 0)];
+        r.wtail = *reinterpret_cast<const uint16_t *>(p + 4);
     }
 }
 
-__device__ __forceinline__ void q4gemm_store(const Q4GemmRaw &r, Q4GemmLds &s)
+__device__ __forceinline__ void q4gemm_store(const Q4GemmRaw &r, const Q4GemmSrc &c, Q4GemmLds &s)
 {
     const int row = threadIdx.x >> 1, kb = threadIdx.x & 1;
+    const bool xodd = r.valid_x && c.xpar;
+    const bool wodd = r.valid_w && c.wpar;
+    uint32_t xd, xq[8], wd, wq[4];
+    {
+        const uint32_t sh = xodd ? 0u : 16u;
+        xd = xodd ? (r.xw[0] >> 16) : (r.xw[0] & 0xffffu);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t hi = (i == 7 && !xodd) ? r.xtail : r.xw[i + 1];
+            xq[i] = funnel(hi, xodd ? r.xw[i + 1] : r.xw[i], sh);
+        }
+        if (!r.valid_x) {
+            xd = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                xq[i] = 0;
+        }
+    }
+    {
+        const uint32_t sh = wodd ? 0u : 16u;
+        wd = wodd ? (r.ww[0] >> 16) : (r.ww[0] & 0xffffu);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t hi = (i == 3 && !wodd) ? r.wtail : r.ww[i + 1];
+            wq[i] = funnel(hi, wodd ? r.ww[i + 1] : r.ww[i], sh);
+        }
+        if (!r.valid_w) {
+            wd = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                wq[i] = 0x88888888u; // code 8: weight 0
+        }
+    }
 #pragma unroll
     for (int h = 0; h < 4; h++) {
         uint32_t lo[2], hi[2];
-        q8_dword_to_f16(r.xq[h], lo);
-        q8_dword_to_f16(r.xq[4 + h], hi);
+        q8_dword_to_f16(xq[h], lo);
+        q8_dword_to_f16(xq[4 + h], hi);
         s.xs[kb][row][q4gemm_slot(kb, row, h)] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        q4_nibbles_to_f16(r.wq[h] & 0x0f0f0f0fu, lo);
-        q4_nibbles_to_f16((r.wq[h] >> 4) & 0x0f0f0f0fu, hi);
+        q4_nibbles_to_f16(wq[h] & 0x0f0f0f0fu, lo);
+        q4_nibbles_to_f16((wq[h] >> 4) & 0x0f0f0f0fu, hi);
         s.ws[kb][row][q4gemm_slot(kb, row, h)] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
-    s.dx[kb][row] = half_bits_to_float(r.xd);
-    s.dw[kb][row] = half_bits_to_float(r.wd);
+    s.dx[kb][row] = half_bits_to_float(xd);
+    s.dw[kb][row] = half_bits_to_float(wd);
 }
 
 // One stage: for each of its blocks, the 16 block sums of the wave's 64 x 64
@@ -234,28 +285,25 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
 
     // Pipeline: stage st+1's LDS buffer is filled from registers loaded two
     // stages earlier, so each global load has two stages of compute to land.
+    // Stages go in pairs; with an odd count the last pair's second stage is
+    // past b_end, decodes to zeros and adds nothing (0 * 0).  No exit in the
+    // middle of the pair keeps the two register sets in fixed registers.
     const int nstages = (b_end - b_begin + QKB - 1) / QKB;
+    const Q4GemmSrc src = q4gemm_src(m, n, nb, m0, n0, b_begin);
     Q4GemmRaw ra, rb;
-    q4gemm_load(w, xq, m, n, nb, b_end, m0, n0, b_begin, ra);
-    if (nstages > 1)
-        q4gemm_load(w, xq, m, n, nb, b_end, m0, n0, b_begin + QKB, rb);
-    q4gemm_store(ra, lds[0]);
+    q4gemm_load(w, xq, src, 0, b_end, ra);
+    q4gemm_load(w, xq, src, 1, b_end, rb);
+    q4gemm_store(ra, src, lds[0]);
     __syncthreads();
 
     for (int st = 0; st < nstages; st += 2) {
-        if (st + 2 < nstages)
-            q4gemm_load(w, xq, m, n, nb, b_end, m0, n0, b_begin + (st + 2) * QKB, ra);
+        q4gemm_load(w, xq, src, st + 2, b_end, ra);
         q4gemm_compute(lds[0], wm, wn, lr, lh, acc);
-        if (st + 1 < nstages)
-            q4gemm_store(rb, lds[1]);
+        q4gemm_store(rb, src, lds[1]);
         __syncthreads();
-        if (st + 1 >= nstages)
-            break;
-        if (st + 3 < nstages)
-            q4gemm_load(w, xq, m, n, nb, b_end, m0, n0, b_begin + (st + 3) * QKB, rb);
+        q4gemm_load(w, xq, src, st + 3, b_end, rb);
         q4gemm_compute(lds[1], wm, wn, lr, lh, acc);
-        if (st + 2 < nstages)
-            q4gemm_store(ra, lds[0]);
+        q4gemm_store(ra, src, lds[0]);
         __syncthreads();
     }
 
