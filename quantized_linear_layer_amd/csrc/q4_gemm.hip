@@ -6,7 +6,7 @@
 // Prefill reuses each weight m times and is compute-bound (Fucina course
 // "Chapter 06", 6.1), so the block sums run on the matrix cores.
 //
-// Matrix-core route: v_mfma_f32_16x16x32_f16 with K = 32 = one block.  Both
+// Matrix-core route: v_mfma_f32_32x32x16_f16, two steps per block.  Both
 // operands are small integers (q_w - 8 in [-8, 7], q_x in [-127, 127]), exact
 // in f16; every product and the 32-term sum (|P| <= 32512 < 2^24) are exact in
 // the f32 accumulator, so P is the exact integer block sum.  The MFMA starts
@@ -15,8 +15,8 @@
 // That epilogue, not the MFMA, bounds this kernel (ceiling near half the f16
 // matrix peak); an int8 MFMA would need a third op per output (i32 -> f32).
 //
-// Tiles: 128 x 128 outputs per workgroup (4 waves of 64 x 64, each 4 x 4 MFMA
-// tiles of 16 x 16), two blocks (64 of k) per stage.  Each stage is decoded
+// Tiles: 128 x 128 outputs per workgroup (4 waves of 64 x 64, each 2 x 2 MFMA
+// tiles of 32 x 32), two blocks (64 of k) per stage.  Each stage is decoded
 // once into LDS as f16 operands in MFMA lane order plus f32 scales, double
 // buffered, with the next stage's raw bytes prefetched in registers.
 #include "common.h"
@@ -26,6 +26,7 @@ namespace qll {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int QBM = 128, QBN = 128, QKB = 2;
 constexpr int kQ4GemmThreads = 256;
@@ -206,38 +207,59 @@ __device__ __forceinline__ void q4gemm_store(const Q4GemmRaw &r, const Q4GemmSrc
     s.dw[kb][row] = half_bits_to_float(wd);
 }
 
-// One stage: for each of its blocks, the 16 block sums of the wave's 64 x 64
-// tile on the matrix core (four at a time, one row of subtiles), each scaled
-// by d_x * d_w on the vector ALU into the f32 accumulators.
-__device__ __forceinline__ void q4gemm_compute(const Q4GemmLds &s, int wm, int wn, int lr, int lh, f32x4 acc[4][4])
+// One stage: for each of its blocks, the block sums of the wave's 64 x 64
+// tile on the matrix core -- 2 x 2 tiles of 32 x 32, each two K = 16 steps --
+// then each scaled by d_x * d_w on the vector ALU into the f32 accumulators.
+// MFMA operand lanes: lane l holds row (column) l % 32 of its tile and LDS
+// chunk 2s + l / 32 of the block in step s; A and B use the same chunks, so
+// the two steps together cover the block's 32 elements once.
+__device__ __forceinline__ void q4gemm_compute(const Q4GemmLds &s, int wm, int wn, int lane, f32x16 acc[2][2])
 {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const int lr = lane & 31, lh = lane >> 5;
+    const f32x16 zero = {};
 #pragma unroll 1
     for (int kb = 0; kb < QKB; kb++) {
-        f16x8 a[4], bm[4];
+        f16x8 a[2][2], bm[2][2];
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            a[i] = __builtin_bit_cast(f16x8, s.xs[kb][wm + 16 * i + lr][q4gemm_slot(kb, wm + 16 * i + lr, lh)]);
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            bm[j] = __builtin_bit_cast(f16x8, s.ws[kb][wn + 16 * j + lr][q4gemm_slot(kb, wn + 16 * j + lr, lh)]);
-        float dwv[4];
+            for (int st = 0; st < 2; st++) {
+                const int ra = wm + 32 * i + lr, rb = wn + 32 * i + lr;
+                a[i][st] = __builtin_bit_cast(f16x8, s.xs[kb][ra][q4gemm_slot(kb, ra, 2 * st + lh)]);
+                bm[i][st] = __builtin_bit_cast(f16x8, s.ws[kb][rb][q4gemm_slot(kb, rb, 2 * st + lh)]);
+            }
+        float dwv[2];
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            dwv[j] = s.dw[kb][wn + 16 * j + lr];
+        for (int j = 0; j < 2; j++)
+            dwv[j] = s.dw[kb][wn + 32 * j + lr];
+        // all four tiles' block sums first, so the matrix core runs ahead of
+        // the epilogue instead of waiting for it
+        f32x16 p[2][2];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            f32x4 p[4];
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bm[j], zero, 0, 0, 0);
-            // D layout of a 16x16 tile: lane l, register v -> row 4*(l/16)+v, column l%16
-            const f32x4 dxv = *reinterpret_cast<const f32x4 *>(&s.dx[kb][wm + 16 * i + 4 * lh]);
+            for (int j = 0; j < 2; j++) {
+                p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][0], bm[j][0], zero, 0, 0, 0);
+                p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][1], bm[j][1], p[i][j], 0, 0, 0);
+            }
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+        for (int i = 0; i < 2; i++) {
+            // D layout of a 32 x 32 tile: lane l, register v -> row
+            // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
+            float dxv[16];
 #pragma unroll
-                for (int v = 0; v < 4; v++)
-                    acc[i][j][v] = fmaf(dxv[v] * dwv[j], p[j][v], acc[i][j][v]);
+            for (int q = 0; q < 4; q++) {
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(&s.dx[kb][wm + 32 * i + 8 * q + 4 * lh]);
+                dxv[4 * q] = t[0];
+                dxv[4 * q + 1] = t[1];
+                dxv[4 * q + 2] = t[2];
+                dxv[4 * q + 3] = t[3];
+            }
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++)
+                    acc[i][j][v] = fmaf(dxv[v] * dwv[j], p[i][j][v], acc[i][j][v]);
         }
     }
 }
@@ -274,14 +296,13 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
     y += (int64_t)blockIdx.y * m * n;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-    const int lr = lane & 15, lh = lane >> 4;
 
-    f32x4 acc[4][4];
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; j++)
+            acc[i][j] = f32x16{};
 
     // Pipeline: stage st+1's LDS buffer is filled from registers loaded two
     // stages earlier, so each global load has two stages of compute to land.
@@ -298,23 +319,23 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
 
     for (int st = 0; st < nstages; st += 2) {
         q4gemm_load(w, xq, src, st + 2, b_end, ra);
-        q4gemm_compute(lds[0], wm, wn, lr, lh, acc);
+        q4gemm_compute(lds[0], wm, wn, lane, acc);
         q4gemm_store(rb, src, lds[1]);
         __syncthreads();
         q4gemm_load(w, xq, src, st + 3, b_end, rb);
-        q4gemm_compute(lds[1], wm, wn, lr, lh, acc);
+        q4gemm_compute(lds[1], wm, wn, lane, acc);
         q4gemm_store(ra, src, lds[0]);
         __syncthreads();
     }
 
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int64_t row = m0 + wm + 16 * i + 4 * lh + v;
-                const int64_t col = n0 + wn + 16 * j + lr;
+            for (int v = 0; v < 16; v++) {
+                const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int64_t col = n0 + wn + 32 * j + (lane & 31);
                 if (row < m && col < n)
                     y[row * n + col] = acc[i][j][v];
             }
