@@ -6,260 +6,304 @@
 // Prefill reuses each weight m times and is compute-bound (Fucina course
 // "Chapter 06", 6.1), so the block sums run on the matrix cores.
 //
-// Matrix-core route: v_mfma_f32_32x32x16_f16, two steps per block.  Both
-// operands are small integers (q_w - 8 in [-8, 7], q_x in [-127, 127]), exact
-// in f16; every product and the 32-term sum (|P| <= 32512 < 2^24) are exact in
-// the f32 accumulator, so P is the exact integer block sum.  The MFMA starts
-// from a zero accumulator for each block, and the per-block scale is applied
-// on the vector ALU: acc += (d_x * d_w) * P (two ops per output per block).
-// That epilogue, not the MFMA, bounds this kernel (ceiling near half the f16
-// matrix peak); an int8 MFMA would need a third op per output (i32 -> f32).
+// Matrix-core route: v_mfma_f32_32x32x16_f16, two K = 16 steps per block, on
+// operands that are exact small integers in f16, so every product and every
+// partial sum is an exact integer in the f32 accumulator and P is the exact
+// block sum.  The per-block scale S = d_x * d_w is the outer product of two
+// f16 vectors, and the product of two halves is exact in f32, so the matrix
+// core forms it too (v_mfma_f32_32x32x8_f16 with K = 1 used); the vector ALU
+// is left with one fma per output per block, acc += S * P, which is what
+// bounds the kernel.
 //
-// Tiles: 128 x 128 outputs per workgroup (4 waves of 64 x 64, each 2 x 2 MFMA
-// tiles of 32 x 32), two blocks (64 of k) per stage.  Each stage is decoded
-// once into LDS as f16 operands in MFMA lane order plus f32 scales, double
-// buffered, with the next stage's raw bytes prefetched in registers.
+// Operands.  A weight dword of a Q4_0 block holds codes t..t+3 in its low
+// nibbles and t+16..t+19 in its high nibbles.  One v_and_or turns two of its
+// nibbles into the halves 1024 + c (low nibble) or 1024 + 16 c (high nibble,
+// left in place), so a weight fragment costs five ALU ops and no table.  The
+// biases are removed exactly through the MFMA accumulator input instead of
+// per element: the activations are prepared once per call (q4gemm_prep_kernel)
+// as halves in the same element order -- q_x for low-nibble positions,
+// q_x / 16 for high-nibble ones (exact) -- together with
+//     C0[i,b] = -(1032 * sum_{t<16} q_x[i,b,t] + 72 * sum_{t>=16} q_x[i,b,t])
+// which is the bias term sum_t A_t * (B_t - true B_t).  Starting the block's
+// MFMA from C0 yields P exactly: every value on the way is an integer below
+// 2^23 in magnitude.
+//
+// Tiles: 128 x 128 outputs per workgroup, 4 waves of 64 x 64 (2 x 2 MFMA
+// tiles of 32 x 32), two blocks per stage, three LDS buffers.  Prepared
+// activations, d_x and C0 go straight from memory to LDS (global_load_lds);
+// weight blocks are 18 bytes and only 2-byte aligned, so each thread loads one
+// block's raw dword window into registers two stages ahead and stores its 16
+// code bytes and d_w to LDS one stage ahead.  Weights stay as nibbles in LDS
+// (a quarter of the bytes of f16) and are widened when the fragments are read.
 #include "common.h"
 
 namespace qll {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define QLL_LDS __attribute__((address_space(3)))
 
-constexpr int QBM = 128, QBN = 128, QKB = 2;
+constexpr int QBM = 128, QBN = 128, QKB = 2, QNBUF = 3;
 constexpr int kQ4GemmThreads = 256;
 
-// Element order inside the 32 halves of one (row, block) in LDS: lane group h
-// (lanes 16h..16h+15 of an MFMA operand) holds elements 4h..4h+3 then
-// 16+4h..16+4h+3 -- the low and high nibbles of qs dword h of a Q4_0 block,
-// and qs dwords h and 4+h of a Q8_0 block.  A and B use the same order, so
-// the MFMA's k-sum runs over the block's 32 elements exactly once.
+// Prepared activations: per (row, block) 32 halves = 4 chunks of 16 bytes.
+// Chunk c holds the elements paired with weight dword c, in the order the
+// weight fragment produces them: codes 4c, 4c+2, 4c+1, 4c+3 (low nibbles),
+// then 16+4c, 18+4c, 17+4c, 19+4c (high nibbles, activations divided by 16).
+// Rows are padded to a multiple of QBM and blocks to the end of the last
+// split's range, plus two stages, with zeros (zero activations and d_x = 0
+// contribute nothing), so the main loop never tests a row or block edge on
+// the activation side.
+struct Q4GemmPrep {
+    u32x4 *x;     // [mp][nbp][4]
+    uint32_t *dx; // [nbp][mp], binary16 bits of d_x in the low half
+    float *c0;    // [nbp][mp]
+    int64_t mp, nbp;
+};
 
-__device__ __forceinline__ uint32_t f16x2_add(uint32_t h, float c)
+// One thread per (row, block) of the padded prepared arrays.
+__global__ __launch_bounds__(256) void q4gemm_prep_kernel(const uint8_t *__restrict__ xq, Q4GemmPrep p, int64_t m,
+                                                          int64_t nb)
 {
-    f16x2 v = __builtin_bit_cast(f16x2, h);
-    f16x2 cc = {(_Float16)c, (_Float16)c};
-    return __builtin_bit_cast(uint32_t, v + cc);
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= p.mp * p.nbp)
+        return;
+    const int64_t row = id / p.nbp, b = id % p.nbp;
+    u32x4 *dst = p.x + id * 4;
+    if (row >= m || b >= nb) {
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+            dst[c] = u32x4{0u, 0u, 0u, 0u};
+        p.dx[b * p.mp + row] = 0u;
+        p.c0[b * p.mp + row] = 0.f;
+        return;
+    }
+    // a Q8_0 block is 34 bytes at 34 (row * nb + b): 2-byte aligned
+    const uint16_t *blk = reinterpret_cast<const uint16_t *>(xq + (row * nb + b) * 34);
+    int q[32];
+#pragma unroll
+    for (int t = 0; t < 16; t++) {
+        const uint32_t v = blk[1 + t];
+        q[2 * t] = (int8_t)(v & 0xffu);
+        q[2 * t + 1] = (int8_t)(v >> 8);
+    }
+    int lo = 0, hi = 0;
+#pragma unroll
+    for (int t = 0; t < 16; t++) {
+        lo += q[t];
+        hi += q[16 + t];
+    }
+    constexpr int order[4] = {0, 2, 1, 3};
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            const int t0 = 4 * c + order[2 * e], t1 = 4 * c + order[2 * e + 1];
+            h[e] = (uint32_t)float_to_half_bits((float)q[t0]) | ((uint32_t)float_to_half_bits((float)q[t1]) << 16);
+            h[2 + e] = (uint32_t)float_to_half_bits((float)q[16 + t0] * 0.0625f) |
+                       ((uint32_t)float_to_half_bits((float)q[16 + t1] * 0.0625f) << 16);
+        }
+        dst[c] = u32x4{h[0], h[1], h[2], h[3]};
+    }
+    p.dx[b * p.mp + row] = blk[0];
+    p.c0[b * p.mp + row] = -(1032.0f * (float)lo + 72.0f * (float)hi);
 }
 
-// 4 unsigned bytes u (each < 256) -> 4 halves 1024 + u, two per dword.
-__device__ __forceinline__ void bytes_to_f16_biased(uint32_t u, uint32_t &h01, uint32_t &h23)
-{
-    h01 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
-    h23 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-}
-
-// qs dword of a Q8_0 block (4 signed codes) -> 4 exact halves.
-__device__ __forceinline__ void q8_dword_to_f16(uint32_t d, uint32_t out[2])
-{
-    uint32_t h01, h23;
-    bytes_to_f16_biased(d ^ 0x80808080u, h01, h23); // code + 128
-    out[0] = f16x2_add(h01, -1152.0f);
-    out[1] = f16x2_add(h23, -1152.0f);
-}
-
-// 4 nibble codes (one per byte, 0..15) -> 4 exact halves code - 8.
-__device__ __forceinline__ void q4_nibbles_to_f16(uint32_t c, uint32_t out[2])
-{
-    uint32_t h01, h23;
-    bytes_to_f16_biased(c, h01, h23);
-    out[0] = f16x2_add(h01, -1032.0f);
-    out[1] = f16x2_add(h23, -1032.0f);
-}
-
-// LDS slot of 16-byte chunk h of (block kb, row).  Rows are 64 bytes, so
-// without a swizzle the 8 (or 16) consecutive rows that one phase of an
-// MFMA-operand ds_read_b128 serves sit on the same banks.  XORing h with
+// LDS slot of chunk c of (block kb, row).  Rows are 64 bytes, so without a
+// swizzle the 8 (or 16) consecutive rows that one phase of an operand
+// ds_read_b128 serves sit on the same banks.  XORing c with
 // ((row >> 1) ^ (row >> 3)) & 3 makes any 8 consecutive rows (32 banks of
-// 4 bytes) and any 16 consecutive rows (64 banks) distinct; XORing with 3 for
-// the second block separates the two blocks of a row written by adjacent
-// lanes during staging.
-__device__ __forceinline__ int q4gemm_slot(int kb, int row, int h)
+// 4 bytes) and any 16 consecutive rows (64 banks) distinct.
+__device__ __forceinline__ int q4gemm_slot(int kb, int row, int c)
 {
-    return h ^ (((row >> 1) ^ (row >> 3)) & 3) ^ (kb ? 3 : 0);
+    return c ^ (((row >> 1) ^ (row >> 3)) & 3) ^ (kb ? 3 : 0);
 }
+
+constexpr int kWqPitch = QBN + 32; // padding: the two lane halves of a fragment read hit different banks
 
 struct Q4GemmLds {
-    u32x4 xs[QKB][QBM][4]; // 32 halves per (block, row): 4 x 16 bytes, slots swizzled
-    u32x4 ws[QKB][QBN][4];
-    float dx[QKB][QBM + 8]; // padded: the two blocks' rows land on different banks
-    float dw[QKB][QBN + 8];
+    u32x4 xs[QKB][QBM][4];         // prepared activations, slots swizzled
+    uint32_t wq[QKB][4][kWqPitch]; // weight code dwords, [block][dword][row]
+    uint32_t dx[QKB][QBM];         // binary16 bits of d_x (low half)
+    float c0[QKB][QBM];
+    uint32_t dw[QKB][QBN]; // binary16 bits of d_w (low half), 0 past nb
 };
 
-// Where one thread's staging loads come from.  Thread t stages row t/2,
-// block t%2 of every stage, for both X and W; a stage advances two blocks, so
-// the parity of the flat block index, which fixes the 2-byte offset of a
-// block inside its dword window, stays the same over the whole k loop.
-struct Q4GemmSrc {
-    int64_t xa, wa; // dword index of the stage-0 windows (X: 34-byte, W: 18-byte blocks)
-    int xpar, wpar; // parity of the flat block index
-    int b0;         // block index of stage 0
-    bool xrow, wrow; // the row lies inside the matrix
+// Activation side of stage st, straight into LDS (global_load_lds): the
+// 16 KB of prepared halves (four 16-byte loads per thread; each wave
+// instruction fills 1 KB of LDS, lane l at byte 16 l, so lane l fetches the
+// chunk that belongs in that slot), then d_x and C0 (one 4-byte load each;
+// thread t -> block t / 128, row t % 128).  Six loads per thread, counted by
+// vmcnt like any other.
+constexpr int kQ4GemmDmaPerStage = 6;
+
+struct Q4GemmXSrc {
+    uint32_t xo[4]; // byte offset of this lane's chunk for each of the four 1 KB loads, from (m0, block b)
+    uint32_t so;    // byte offset of this thread's d_x / C0 entry, from (block b, m0)
 };
 
-__device__ __forceinline__ Q4GemmSrc q4gemm_src(int64_t m, int64_t n, int nb, int64_t m0, int64_t n0, int b_begin)
+__device__ __forceinline__ Q4GemmXSrc q4gemm_xsrc(const Q4GemmPrep &p)
 {
-    const int row = threadIdx.x >> 1, kb = threadIdx.x & 1;
-    Q4GemmSrc c;
-    c.b0 = b_begin + kb;
-    c.xrow = m0 + row < m;
-    c.wrow = n0 + row < n;
-    const int64_t g = (c.xrow ? m0 + row : 0) * nb + c.b0; // Q8_0 block at byte 34g
-    const int64_t h = (c.wrow ? n0 + row : 0) * nb + c.b0; // Q4_0 block at byte 18h
-    c.xpar = (int)(g & 1);
-    c.wpar = (int)(h & 1);
-    c.xa = (17 * g - c.xpar) / 2; // floor(34g / 4)
-    c.wa = (9 * h - c.wpar) / 2;  // floor(18h / 4)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    Q4GemmXSrc c;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int region = wave * 4 + j; // 1 KB = 16 rows of one block
+        const int kb = region >> 3;
+        const int row = (region & 7) * 16 + (lane >> 2);
+        c.xo[j] = (uint32_t)((row * p.nbp + kb) * 64 + q4gemm_slot(kb, row, lane & 3) * 16);
+    }
+    c.so = (uint32_t)(((threadIdx.x >> 7) * p.mp + (threadIdx.x & (QBM - 1))) * 4);
     return c;
 }
 
-// Raw bytes of one stage for one thread, loaded without being looked at:
-// decoding happens in q4gemm_store, so the loads stay in flight through a
-// whole stage of compute.
-struct Q4GemmRaw {
-    uint32_t xw[9], xtail; // Q8_0: nine dwords from the window start, bytes 32..33 of the window
-    uint32_t ww[5], wtail; // Q4_0: five dwords from the window start, bytes 16..17 of the window
-    int valid_x, valid_w;
-};
-
-// Stage st.  A block at or past b_end (the end of this split's k range), or
-// in a row past the matrix edge, loads from dword 0 instead and is zeroed
-// when decoded.  Every address stays inside its buffer: an odd-parity block
-// starts 2 bytes into its window and needs the ninth (fifth) dword, which
-// ends exactly at the block's end; an even-parity block takes its last two
-// bytes from the 16-bit tail load and re-reads dword 7 (3) in place of the
-// ninth (fifth).  All loads are unconditional, so none forces an early wait.
-__device__ __forceinline__ void q4gemm_load(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
-                                            const Q4GemmSrc &c, int st, int b_end, Q4GemmRaw &r)
+__device__ __forceinline__ void q4gemm_load_x(const Q4GemmPrep &p, const Q4GemmXSrc &c, int64_t m0, int b,
+                                              Q4GemmLds &s)
 {
-    const bool in_k = c.b0 + 2 * st < b_end;
-    r.valid_x = c.xrow && in_k;
-    r.valid_w = c.wrow && in_k;
-    {
-        const int64_t a = r.valid_x ? c.xa + 17 * (int64_t)st : 0;
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(xq) + a;
-        const u32x4 v0 = *reinterpret_cast<const u32x4_a4 *>(p);
-        const u32x4 v1 = *reinterpret_cast<const u32x4_a4 *>(p + 4);
-        r.xw[0] = v0[0]; r.xw[1] = v0[1]; r.xw[2] = v0[2]; r.xw[3] = v0[3];
-        r.xw[4] = v1[0]; r.xw[5] = v1[1]; r.xw[6] = v1[2]; r.xw[7] = v1[3];
-        r.xw[8] = p[7 + (r.valid_x ? c.xpar : 0)];
-        r.xtail = *reinterpret_cast<const uint16_t *>(p + 8);
+    const int wave = threadIdx.x >> 6;
+    const uint8_t *xb = reinterpret_cast<const uint8_t *>(p.x) + (m0 * p.nbp + b) * 64;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int region = wave * 4 + j;
+        __builtin_amdgcn_global_load_lds(xb + c.xo[j], (QLL_LDS void *)&s.xs[region >> 3][(region & 7) * 16][0], 16,
+                                         0, 0);
     }
-    {
-        const int64_t a = r.valid_w ? c.wa + 9 * (int64_t)st : 0;
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(w) + a;
-        const u32x4 v0 = *reinterpret_cast<const u32x4_a4 *>(p);
-        r.ww[0] = v0[0]; r.ww[1] = v0[1]; r.ww[2] = v0[2]; r.ww[3] = v0[3];
-        r.ww[4] = p[3 + (r.valid_w ? c.wpar : 0)];
-        r.wtail = *reinterpret_cast<const uint16_t *>(p + 4);
-    }
+    const int64_t so = (int64_t)b * p.mp + m0;
+    const int kb = threadIdx.x >> 7, rbase = threadIdx.x & (QBM - 1) & ~63;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(p.dx + so) + c.so,
+                                     (QLL_LDS void *)&s.dx[kb][rbase], 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(p.c0 + so) + c.so,
+                                     (QLL_LDS void *)&s.c0[kb][rbase], 4, 0, 0);
 }
 
-__device__ __forceinline__ void q4gemm_store(const Q4GemmRaw &r, const Q4GemmSrc &c, Q4GemmLds &s)
+// Weight side.  Weight blocks are 18 bytes and only 2-byte aligned, so they
+// go through registers: thread t stages weight row t % 128 (n - 1 past the
+// edge), block t / 128 of every stage.  A stage advances two blocks, so the
+// parity of the flat block index, which fixes the 2-byte offset of a block
+// inside its dword window, stays the same over the whole k loop.
+struct Q4GemmWSrc {
+    const uint32_t *p0; // stage-0 window (dword aligned)
+    int par;            // parity of the flat block index
+    int b0;             // block index of stage 0
+};
+
+// Raw bytes of one weight block, loaded without being looked at.
+struct Q4GemmWRaw {
+    uint32_t ww[5], wtail; // five dwords from the window start, bytes 16..17 of the window
+    int valid;
+};
+
+// Stage st.  A block at or past nb (stages past the k range) loads from
+// dword 0 instead and gets d_w = 0.  Every address stays inside the weight
+// buffer: an odd-parity block starts 2 bytes into its window and needs the
+// fifth dword, which ends exactly at the block's end; an even-parity block
+// takes its last two bytes from the 16-bit tail load and re-reads dword 3 in
+// place of the fifth.
+__device__ __forceinline__ void q4gemm_load_w(const uint8_t *__restrict__ w, const Q4GemmWSrc &c, int st, int nb,
+                                              Q4GemmWRaw &r)
 {
-    const int row = threadIdx.x >> 1, kb = threadIdx.x & 1;
-    const bool xodd = r.valid_x && c.xpar;
-    const bool wodd = r.valid_w && c.wpar;
-    uint32_t xd, xq[8], wd, wq[4];
-    {
-        const uint32_t sh = xodd ? 0u : 16u;
-        xd = xodd ? (r.xw[0] >> 16) : (r.xw[0] & 0xffffu);
+    r.valid = c.b0 + 2 * st < nb;
+    const uint32_t *p = r.valid ? c.p0 + 9 * st : reinterpret_cast<const uint32_t *>(w);
+    const u32x4 v0 = *reinterpret_cast<const u32x4_a4 *>(p);
+    r.ww[0] = v0[0];
+    r.ww[1] = v0[1];
+    r.ww[2] = v0[2];
+    r.ww[3] = v0[3];
+    r.ww[4] = p[3 + (r.valid ? c.par : 0)];
+    r.wtail = *reinterpret_cast<const uint16_t *>(p + 4);
+}
+
+__device__ __forceinline__ void q4gemm_store_w(const Q4GemmWRaw &r, const Q4GemmWSrc &c, Q4GemmLds &s)
+{
+    const int row = threadIdx.x & (QBN - 1), kb = threadIdx.x >> 7;
+    const bool odd = r.valid && c.par;
+    const uint32_t sh = odd ? 0u : 16u;
+    const uint32_t d = odd ? (r.ww[0] >> 16) : (r.ww[0] & 0xffffu);
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const uint32_t hi = (i == 7 && !xodd) ? r.xtail : r.xw[i + 1];
-            xq[i] = funnel(hi, xodd ? r.xw[i + 1] : r.xw[i], sh);
-        }
-        if (!r.valid_x) {
-            xd = 0;
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-                xq[i] = 0;
-        }
+    for (int i = 0; i < 4; i++) {
+        const uint32_t hi = (i == 3 && !odd) ? r.wtail : r.ww[i + 1];
+        s.wq[kb][i][row] = funnel(hi, odd ? r.ww[i + 1] : r.ww[i], sh);
     }
-    {
-        const uint32_t sh = wodd ? 0u : 16u;
-        wd = wodd ? (r.ww[0] >> 16) : (r.ww[0] & 0xffffu);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t hi = (i == 3 && !wodd) ? r.wtail : r.ww[i + 1];
-            wq[i] = funnel(hi, wodd ? r.ww[i + 1] : r.ww[i], sh);
-        }
-        if (!r.valid_w) {
-            wd = 0;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                wq[i] = 0x88888888u; // code 8: weight 0
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-        uint32_t lo[2], hi[2];
-        q8_dword_to_f16(xq[h], lo);
-        q8_dword_to_f16(xq[4 + h], hi);
-        s.xs[kb][row][q4gemm_slot(kb, row, h)] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        q4_nibbles_to_f16(wq[h] & 0x0f0f0f0fu, lo);
-        q4_nibbles_to_f16((wq[h] >> 4) & 0x0f0f0f0fu, hi);
-        s.ws[kb][row][q4gemm_slot(kb, row, h)] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
-    s.dx[kb][row] = half_bits_to_float(xd);
-    s.dw[kb][row] = half_bits_to_float(wd);
+    s.dw[kb][row] = r.valid ? d : 0u;
+}
+
+// Weight fragment: dword w of a block (bytes b0..b3) -> eight biased halves,
+// 1024 + c for the low nibbles of b0, b2, b1, b3 and 1024 + 16 c for their
+// high nibbles in the same order.
+// `bias` is 0x64006400 held in a register: with both constants as literals
+// the and/or pair cannot be one instruction (no literal operands in VOP3 on
+// this architecture), with one of them in a register it is one v_and_or_b32.
+__device__ __forceinline__ f16x8 q4gemm_wfrag(uint32_t w, uint32_t bias)
+{
+    const uint32_t w8 = w >> 8;
+    u32x4 h;
+    h[0] = (w & 0x000f000fu) | bias;
+    h[1] = (w8 & 0x000f000fu) | bias;
+    h[2] = (w & 0x00f000f0u) | bias;
+    h[3] = (w8 & 0x00f000f0u) | bias;
+    return __builtin_bit_cast(f16x8, h);
 }
 
 // One stage: for each of its blocks, the block sums of the wave's 64 x 64
-// tile on the matrix core -- 2 x 2 tiles of 32 x 32, each two K = 16 steps --
-// then each scaled by d_x * d_w on the vector ALU into the f32 accumulators.
-// MFMA operand lanes: lane l holds row (column) l % 32 of its tile and LDS
-// chunk 2s + l / 32 of the block in step s; A and B use the same chunks, so
-// the two steps together cover the block's 32 elements once.
-__device__ __forceinline__ void q4gemm_compute(const Q4GemmLds &s, int wm, int wn, int lane, f32x16 acc[2][2])
+// tile on the matrix core -- 2 x 2 tiles of 32 x 32, each two K = 16 steps
+// started from C0 -- and the scale tiles S = d_x d_w^T (one K = 8 step whose
+// only nonzero term is k = 0: lanes 0..31 hold k = 0..3, lanes 32..63 hold
+// zeros), then acc += S * P.  MFMA operand lanes: lane l holds row (column)
+// l % 32 of its tile and chunk 2s + l / 32 of the block in step s; A and B
+// use the same chunks, so the two steps together cover the block's 32
+// elements once.
+__device__ __forceinline__ void q4gemm_compute(const Q4GemmLds &s, int wm, int wn, int lane, uint32_t bias,
+                                               f32x16 acc[2][2])
 {
     const int lr = lane & 31, lh = lane >> 5;
-    const f32x16 zero = {};
-#pragma unroll 1
+    const uint32_t keep = lh ? 0u : ~0u; // scale operands: k = 0 only
+#pragma unroll 1 // unrolled, the two blocks' address math is hoisted and spills
     for (int kb = 0; kb < QKB; kb++) {
         f16x8 a[2][2], bm[2][2];
+        f16x4 sa[2], sb[2];
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++) {
 #pragma unroll
             for (int st = 0; st < 2; st++) {
-                const int ra = wm + 32 * i + lr, rb = wn + 32 * i + lr;
+                const int ra = wm + 32 * i + lr;
                 a[i][st] = __builtin_bit_cast(f16x8, s.xs[kb][ra][q4gemm_slot(kb, ra, 2 * st + lh)]);
-                bm[i][st] = __builtin_bit_cast(f16x8, s.ws[kb][rb][q4gemm_slot(kb, rb, 2 * st + lh)]);
+                bm[i][st] = q4gemm_wfrag(s.wq[kb][2 * st + lh][wn + 32 * i + lr], bias);
             }
-        float dwv[2];
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-            dwv[j] = s.dw[kb][wn + 32 * j + lr];
-        // all four tiles' block sums first, so the matrix core runs ahead of
-        // the epilogue instead of waiting for it
-        f32x16 p[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][0], bm[j][0], zero, 0, 0, 0);
-                p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][1], bm[j][1], p[i][j], 0, 0, 0);
-            }
+            const uint32_t dxb = s.dx[kb][wm + 32 * i + lr] & keep;
+            const uint32_t dwb = s.dw[kb][wn + 32 * i + lr] & keep;
+            sa[i] = __builtin_bit_cast(f16x4, u32x2{dxb, 0u});
+            sb[i] = __builtin_bit_cast(f16x4, u32x2{dwb, 0u});
+        }
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             // D layout of a 32 x 32 tile: lane l, register v -> row
             // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
-            float dxv[16];
+            f32x16 c0;
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const f32x4 t = *reinterpret_cast<const f32x4 *>(&s.dx[kb][wm + 32 * i + 8 * q + 4 * lh]);
-                dxv[4 * q] = t[0];
-                dxv[4 * q + 1] = t[1];
-                dxv[4 * q + 2] = t[2];
-                dxv[4 * q + 3] = t[3];
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(&s.c0[kb][wm + 32 * i + 8 * q + 4 * lh]);
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    c0[4 * q + e] = t[e];
+            }
+            f32x16 p[2], sc[2];
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                p[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][0], bm[j][0], c0, 0, 0, 0);
+                p[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][1], bm[j][1], p[j], 0, 0, 0);
+                sc[j] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], f32x16{}, 0, 0, 0);
             }
 #pragma unroll
             for (int j = 0; j < 2; j++)
 #pragma unroll
                 for (int v = 0; v < 16; v++)
-                    acc[i][j][v] = fmaf(dxv[v] * dwv[j], p[i][j][v], acc[i][j][v]);
+                    acc[i][j][v] = fmaf(sc[j][v], p[j][v], acc[i][j][v]);
+            // one row tile's C0 and tiles live at a time
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -279,20 +323,32 @@ __device__ __forceinline__ void q4gemm_tile(int64_t mt_count, int64_t nt_count, 
     m_tile = logical % mt_count;
 }
 
-__global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const uint8_t *__restrict__ w,
-                                                                           const uint8_t *__restrict__ xq,
-                                                                           float *__restrict__ y, int64_t m,
-                                                                           int64_t n, int nb, int splits)
+// Wait until at most N vector-memory loads of this wave are outstanding and
+// all its LDS operations are done, then meet the workgroup.  Neither the
+// wait nor the barrier is a fence, so compiler barriers keep memory
+// operations from moving across them.
+template <int N>
+__device__ __forceinline__ void q4gemm_sync()
 {
-    __shared__ Q4GemmLds lds[2];
+    static_assert(N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4)); // vmcnt(N) expcnt(7) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const uint8_t *__restrict__ w, Q4GemmPrep prep,
+                                                                           float *__restrict__ y, int64_t m,
+                                                                           int64_t n, int nb, int per_split)
+{
+    __shared__ Q4GemmLds lds[QNBUF];
     int64_t m_tile, n_tile;
-    q4gemm_tile((m + QBM - 1) / QBM, (n + QBN - 1) / QBN, m_tile, n_tile);
+    q4gemm_tile(prep.mp / QBM, (n + QBN - 1) / QBN, m_tile, n_tile);
     const int64_t m0 = m_tile * QBM, n0 = n_tile * QBN;
-    // split-k: blockIdx.y takes blocks [b_begin, b_end) and writes its partial
-    // tile to y + blockIdx.y * m * n (the workspace when splits > 1)
-    const int per = (nb + splits - 1) / splits;
-    const int b_begin = blockIdx.y * per;
-    const int b_end = (b_begin + per < nb) ? b_begin + per : nb;
+    // split-k: blockIdx.y takes blocks [b_begin, b_begin + per_split) and
+    // writes its partial tile to y + blockIdx.y * m * n (the workspace when
+    // there are splits); blocks past nb have d_x = 0 in the prepared arrays
+    const int b_begin = blockIdx.y * per_split;
     y += (int64_t)blockIdx.y * m * n;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
@@ -304,29 +360,46 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
         for (int j = 0; j < 2; j++)
             acc[i][j] = f32x16{};
 
-    // Pipeline: stage st+1's LDS buffer is filled from registers loaded two
-    // stages earlier, so each global load has two stages of compute to land.
-    // Stages go in pairs; with an odd count the last pair's second stage is
-    // past b_end, decodes to zeros and adds nothing (0 * 0).  No exit in the
-    // middle of the pair keeps the two register sets in fixed registers.
-    const int nstages = (b_end - b_begin + QKB - 1) / QKB;
-    const Q4GemmSrc src = q4gemm_src(m, n, nb, m0, n0, b_begin);
-    Q4GemmRaw ra, rb;
-    q4gemm_load(w, xq, src, 0, b_end, ra);
-    q4gemm_load(w, xq, src, 1, b_end, rb);
-    q4gemm_store(ra, src, lds[0]);
-    __syncthreads();
-
-    for (int st = 0; st < nstages; st += 2) {
-        q4gemm_load(w, xq, src, st + 2, b_end, ra);
-        q4gemm_compute(lds[0], wm, wn, lane, acc);
-        q4gemm_store(rb, src, lds[1]);
-        __syncthreads();
-        q4gemm_load(w, xq, src, st + 3, b_end, rb);
-        q4gemm_compute(lds[1], wm, wn, lane, acc);
-        q4gemm_store(ra, src, lds[0]);
-        __syncthreads();
+    const Q4GemmXSrc xsrc = q4gemm_xsrc(prep);
+    Q4GemmWSrc wsrc;
+    {
+        const int row = threadIdx.x & (QBN - 1);
+        const int64_t wrow = (n0 + row < n) ? n0 + row : n - 1; // rows past n: any valid row, output dropped
+        wsrc.b0 = b_begin + (threadIdx.x >> 7);
+        const int64_t h = wrow * nb + wsrc.b0; // Q4_0 block at byte 18 h
+        wsrc.par = (int)(h & 1);
+        wsrc.p0 = reinterpret_cast<const uint32_t *>(w) + (9 * h - wsrc.par) / 2; // floor(18 h / 4)
     }
+    const int nstages = per_split / QKB;
+    uint32_t bias; // 0x64006400, opaque to the compiler (see q4gemm_wfrag)
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));
+
+    // Pipeline, stage st computed from buffer st % 3.  During stage st the
+    // weight registers of stage st+1 are loaded (before the compute) and
+    // stored to buffer (st+1) % 3 (after it); the activation loads of stage
+    // st+2 go out last, straight into buffer (st+2) % 3, and have all of
+    // stage st+1 to land.  Register loads are consumed before the next
+    // LDS-bound loads are issued, so the compiler's own waits never hold
+    // those back; the end-of-stage wait leaves exactly them in flight.  Stages
+    // past the range load padding and are never computed.
+    Q4GemmWRaw r;
+    q4gemm_load_w(w, wsrc, 0, nb, r);
+    q4gemm_load_x(prep, xsrc, m0, b_begin, lds[0]);
+    q4gemm_load_x(prep, xsrc, m0, b_begin + QKB, lds[1]);
+    q4gemm_store_w(r, wsrc, lds[0]);
+    q4gemm_sync<kQ4GemmDmaPerStage>();
+    int cur = 0; // buffer of stage st
+    for (int st = 0; st < nstages; st++) {
+        const int nx1 = cur == 2 ? 0 : cur + 1, nx2 = cur == 0 ? 2 : cur - 1;
+        q4gemm_load_w(w, wsrc, st + 1, nb, r);
+        q4gemm_compute(lds[cur], wm, wn, lane, bias, acc);
+        q4gemm_store_w(r, wsrc, lds[nx1]);
+        q4gemm_load_x(prep, xsrc, m0, b_begin + (st + 2) * QKB, lds[nx2]);
+        q4gemm_sync<kQ4GemmDmaPerStage>();
+        cur = nx1;
+    }
+    // no load may still be writing this workgroup's LDS when it ends
+    __builtin_amdgcn_s_waitcnt(0x7 << 4); // vmcnt(0) expcnt(7) lgkmcnt(0)
 
 #pragma unroll
     for (int i = 0; i < 2; i++)
@@ -355,39 +428,77 @@ __global__ __launch_bounds__(256) void q4gemm_sum_splits_kernel(const float *__r
 }
 
 // Split k when the output tiles alone leave workgroup slots empty (two
-// workgroups fit per CU); each split keeps at least 16 blocks.
-static int q4gemm_splits(int64_t m, int64_t n, int64_t k)
+// workgroups fit per CU); each split keeps at least 16 blocks and a multiple
+// of 2 QKB of them.  The workspace holds the split partials (if any), then
+// the prepared activations, d_x and C0.
+struct Q4GemmPlan {
+    int splits, per_split;
+    int64_t mp, nbp;
+    size_t x_off, dx_off, c0_off, total;
+};
+
+static Q4GemmPlan q4gemm_plan(int64_t m, int64_t n, int64_t k)
 {
-    const int64_t tiles = ((n + QBN - 1) / QBN) * ((m + QBM - 1) / QBM);
+    Q4GemmPlan p;
+    const int64_t nb = k / 32;
+    p.mp = (m + QBM - 1) / QBM * QBM;
+    const int64_t tiles = ((n + QBN - 1) / QBN) * (p.mp / QBM);
     int64_t s = 512 / tiles;
-    const int64_t max_s = (k / 32) / 16;
-    if (s > max_s)
-        s = max_s;
+    if (s > nb / 16)
+        s = nb / 16;
     if (s > 8)
         s = 8;
-    return s < 2 ? 1 : (int)s;
+    if (s < 2)
+        s = 1;
+    const int64_t q = 2 * QKB;
+    int64_t per = (nb + s - 1) / s;
+    per = (per + q - 1) / q * q;
+    s = (nb + per - 1) / per;
+    p.splits = (int)s;
+    p.per_split = (int)per;
+    p.nbp = per * s + 2 * QKB; // >= nb: the last split's range, plus the two stages the pipeline reads past it
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t parts = s > 1 ? up((size_t)s * (size_t)(m * n) * sizeof(float)) : 0;
+    p.x_off = parts;
+    p.dx_off = p.x_off + up((size_t)(p.mp * p.nbp) * 64);
+    p.c0_off = p.dx_off + up((size_t)(p.mp * p.nbp) * sizeof(float));
+    p.total = p.c0_off + up((size_t)(p.mp * p.nbp) * sizeof(float));
+    return p;
 }
 
 size_t q4_0_q8_0_gemm_workspace(int64_t m, int64_t n, int64_t k)
 {
-    const int s = q4gemm_splits(m, n, k);
-    return s > 1 ? (size_t)s * (size_t)(m * n) * sizeof(float) : 0;
+    return q4gemm_plan(m, n, k).total;
 }
 
 hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                  void *ws, hipStream_t s)
 {
-    const int64_t tiles = ((n + QBN - 1) / QBN) * ((m + QBM - 1) / QBM);
-    const int splits = q4gemm_splits(m, n, k);
-    float *out = splits > 1 ? static_cast<float *>(ws) : y;
-    hipLaunchKernelGGL(q4_0_q8_0_gemm_kernel, dim3((unsigned)tiles, (unsigned)splits), dim3(kQ4GemmThreads), 0, s,
-                       w, xq, out, m, n, (int)(k / 32), splits);
+    const Q4GemmPlan plan = q4gemm_plan(m, n, k);
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    Q4GemmPrep prep;
+    prep.x = reinterpret_cast<u32x4 *>(base + plan.x_off);
+    prep.dx = reinterpret_cast<uint32_t *>(base + plan.dx_off);
+    prep.c0 = reinterpret_cast<float *>(base + plan.c0_off);
+    prep.mp = plan.mp;
+    prep.nbp = plan.nbp;
+    const int64_t nb = k / 32;
+    const int64_t prep_threads = plan.mp * plan.nbp;
+    hipLaunchKernelGGL(q4gemm_prep_kernel, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s, xq, prep, m,
+                       nb);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1)
+    if (e != hipSuccess)
+        return e;
+    const int64_t tiles = ((n + QBN - 1) / QBN) * (plan.mp / QBM);
+    float *out = plan.splits > 1 ? reinterpret_cast<float *>(base) : y;
+    hipLaunchKernelGGL(q4_0_q8_0_gemm_kernel, dim3((unsigned)tiles, (unsigned)plan.splits), dim3(kQ4GemmThreads), 0,
+                       s, w, prep, out, m, n, (int)nb, plan.per_split);
+    e = hipGetLastError();
+    if (e != hipSuccess || plan.splits == 1)
         return e;
     const int64_t count = m * n;
     hipLaunchKernelGGL(q4gemm_sum_splits_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, out, y,
-                       count, splits);
+                       count, plan.splits);
     return hipGetLastError();
 }
 
