@@ -265,6 +265,7 @@ __device__ __forceinline__ void q4gemm_compute(const Q4GemmLds &s, int wm, int w
     for (int kb = 0; kb < QKB; kb++) {
         f16x8 a[2][2], bm[2][2];
         f16x4 sa[2], sb[2];
+        f32x16 c0[2];
 #pragma unroll
         for (int i = 0; i < 2; i++) {
 #pragma unroll
@@ -277,34 +278,47 @@ __device__ __forceinline__ void q4gemm_compute(const Q4GemmLds &s, int wm, int w
             const uint32_t dwb = s.dw[kb][wn + 32 * i + lr] & keep;
             sa[i] = __builtin_bit_cast(f16x4, u32x2{dxb, 0u});
             sb[i] = __builtin_bit_cast(f16x4, u32x2{dwb, 0u});
-        }
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
             // D layout of a 32 x 32 tile: lane l, register v -> row
             // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
-            f32x16 c0;
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const f32x4 t = *reinterpret_cast<const f32x4 *>(&s.c0[kb][wm + 32 * i + 8 * q + 4 * lh]);
 #pragma unroll
                 for (int e = 0; e < 4; e++)
-                    c0[4 * q + e] = t[e];
+                    c0[i][4 * q + e] = t[e];
             }
-            f32x16 p[2], sc[2];
+        }
+        // Software pipeline over the four tiles: the matrix core works on
+        // tile t while the vector ALU applies tile t-1's scales.  Per tile,
+        // in issue order: the first K step and the scale product, half of
+        // the previous tile's fmas, the second K step (by then the first has
+        // finished), the other half.
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 p[2], sc[2];
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                p[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][0], bm[j][0], c0, 0, 0, 0);
-                p[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][1], bm[j][1], p[j], 0, 0, 0);
-                sc[j] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], f32x16{}, 0, 0, 0);
+        for (int t = 0; t <= 4; t++) {
+            if (t < 4) {
+                const int i = t >> 1, j = t & 1;
+                p[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][0], bm[j][0], c0[i], 0, 0, 0);
+                sc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], f32x16{}, 0, 0, 0);
+                p[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][1], bm[j][1], p[t & 1], 0, 0, 0);
             }
-#pragma unroll
-            for (int j = 0; j < 2; j++)
+            if (t > 0) {
+                const int u = t - 1, i = u >> 1, j = u & 1;
 #pragma unroll
                 for (int v = 0; v < 16; v++)
-                    acc[i][j][v] = fmaf(sc[j][v], p[j][v], acc[i][j][v]);
-            // one row tile's C0 and tiles live at a time
-            __builtin_amdgcn_sched_barrier(0);
+                    acc[i][j][v] = fmaf(sc[u & 1][v], p[u & 1][v], acc[i][j][v]);
+            }
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0); // tile 0
+#pragma unroll
+        for (int t = 1; t < 4; t++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
     }
 }
 
