@@ -64,53 +64,82 @@ struct Q4GemmPrep {
     int64_t mp, nbp;
 };
 
-// One thread per (row, block) of the padded prepared arrays.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two halves of a dword, h -> h * mul + add (exact for the values used here).
+__device__ __forceinline__ uint32_t f16x2_fma(uint32_t h, float mul, float add)
+{
+    const f16x2 v = __builtin_bit_cast(f16x2, h);
+    const f16x2 mm = {(_Float16)mul, (_Float16)mul}, aa = {(_Float16)add, (_Float16)add};
+    return __builtin_bit_cast(uint32_t, v * mm + aa);
+}
+
+// One thread per (row, block) of the padded prepared arrays; a workgroup
+// takes 16 rows x 16 blocks (mp and nbp are multiples of 16), so that both
+// the activation chunks (16 blocks of a row are 1 KB) and, through LDS, d_x
+// and C0 (16 rows of a block are 64 bytes) are written in contiguous runs.
+// The Q8_0 block
+// (34 bytes at 34 g, g = row * nb + b) is read as the dword window from
+// 34 g - 2 (g & 1): eight dwords plus, for an odd g, a ninth that ends at the
+// block's end, for an even g the block's last two bytes as a 16-bit load.
+// Codes become halves exactly by the usual exponent trick: the byte q + 128
+// placed under the high byte 0x64 is the half 1024 + q + 128.
 __global__ __launch_bounds__(256) void q4gemm_prep_kernel(const uint8_t *__restrict__ xq, Q4GemmPrep p, int64_t m,
                                                           int64_t nb)
 {
-    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (id >= p.mp * p.nbp)
-        return;
-    const int64_t row = id / p.nbp, b = id % p.nbp;
-    u32x4 *dst = p.x + id * 4;
+    __shared__ uint32_t sdx[16][17];
+    __shared__ float sc0[16][17];
+    const int64_t bt = p.nbp / 16;
+    const int64_t row0 = (int64_t)(blockIdx.x / bt) * 16, b0 = (int64_t)(blockIdx.x % bt) * 16;
+    const int tr = threadIdx.x >> 4, tb = threadIdx.x & 15;
+    const int64_t row = row0 + tr, b = b0 + tb;
+    u32x4 *dst = p.x + (row * p.nbp + b) * 4;
+    uint32_t dxo = 0u;
+    float c0o = 0.f;
     if (row >= m || b >= nb) {
 #pragma unroll
         for (int c = 0; c < 4; c++)
             dst[c] = u32x4{0u, 0u, 0u, 0u};
-        p.dx[b * p.mp + row] = 0u;
-        p.c0[b * p.mp + row] = 0.f;
-        return;
-    }
-    // a Q8_0 block is 34 bytes at 34 (row * nb + b): 2-byte aligned
-    const uint16_t *blk = reinterpret_cast<const uint16_t *>(xq + (row * nb + b) * 34);
-    int q[32];
+    } else {
+    const int64_t g = row * nb + b;
+    const bool odd = g & 1;
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(xq + 34 * g - (odd ? 2 : 0));
+    const u32x4 v0 = *reinterpret_cast<const u32x4_a4 *>(w);
+    const u32x4 v1 = *reinterpret_cast<const u32x4_a4 *>(w + 4);
+    const uint32_t last = odd ? w[8] : (uint32_t)*reinterpret_cast<const uint16_t *>(w + 8);
+    const uint32_t win[9] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3], last};
+    uint32_t q[8]; // code dwords: codes 4i..4i+3
 #pragma unroll
-    for (int t = 0; t < 16; t++) {
-        const uint32_t v = blk[1 + t];
-        q[2 * t] = (int8_t)(v & 0xffu);
-        q[2 * t + 1] = (int8_t)(v >> 8);
-    }
+    for (int i = 0; i < 8; i++)
+        q[i] = odd ? win[i + 1] : funnel(win[i + 1], win[i], 16);
+    const uint32_t d = odd ? (win[0] >> 16) : (win[0] & 0xffffu);
     int lo = 0, hi = 0;
 #pragma unroll
-    for (int t = 0; t < 16; t++) {
-        lo += q[t];
-        hi += q[16 + t];
+    for (int i = 0; i < 4; i++) {
+        lo = sdot4(q[i], 0x01010101u, lo);
+        hi = sdot4(q[4 + i], 0x01010101u, hi);
     }
-    constexpr int order[4] = {0, 2, 1, 3};
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-        uint32_t h[4];
-#pragma unroll
-        for (int e = 0; e < 2; e++) {
-            const int t0 = 4 * c + order[2 * e], t1 = 4 * c + order[2 * e + 1];
-            h[e] = (uint32_t)float_to_half_bits((float)q[t0]) | ((uint32_t)float_to_half_bits((float)q[t1]) << 16);
-            h[2 + e] = (uint32_t)float_to_half_bits((float)q[16 + t0] * 0.0625f) |
-                       ((uint32_t)float_to_half_bits((float)q[16 + t1] * 0.0625f) << 16);
-        }
-        dst[c] = u32x4{h[0], h[1], h[2], h[3]};
+        // codes 4c, 4c+2 | 4c+1, 4c+3 of dword q[c] (low-nibble partners) and
+        // of q[4+c] (high-nibble partners, divided by 16)
+        const uint32_t ul = q[c] ^ 0x80808080u, uh = q[4 + c] ^ 0x80808080u;
+        const uint32_t l02 = __builtin_amdgcn_perm(0x64646464u, ul, 0x04020400u);
+        const uint32_t l13 = __builtin_amdgcn_perm(0x64646464u, ul, 0x04030401u);
+        const uint32_t h02 = __builtin_amdgcn_perm(0x64646464u, uh, 0x04020400u);
+        const uint32_t h13 = __builtin_amdgcn_perm(0x64646464u, uh, 0x04030401u);
+        dst[c] = u32x4{f16x2_fma(l02, 1.0f, -1152.0f), f16x2_fma(l13, 1.0f, -1152.0f),
+                       f16x2_fma(h02, 0.0625f, -72.0f), f16x2_fma(h13, 0.0625f, -72.0f)};
     }
-    p.dx[b * p.mp + row] = blk[0];
-    p.c0[b * p.mp + row] = -(1032.0f * (float)lo + 72.0f * (float)hi);
+    dxo = d;
+    c0o = -(1032.0f * (float)lo + 72.0f * (float)hi);
+    }
+    sdx[tb][tr] = dxo;
+    sc0[tb][tr] = c0o;
+    __syncthreads();
+    const int wb = threadIdx.x >> 4, wr = threadIdx.x & 15; // write: block wb, row wr
+    p.dx[(b0 + wb) * p.mp + row0 + wr] = sdx[wb][wr];
+    p.c0[(b0 + wb) * p.mp + row0 + wr] = sc0[wb][wr];
 }
 
 // LDS slot of chunk c of (block kb, row).  Rows are 64 bytes, so without a
@@ -470,7 +499,9 @@ static Q4GemmPlan q4gemm_plan(int64_t m, int64_t n, int64_t k)
     s = (nb + per - 1) / per;
     p.splits = (int)s;
     p.per_split = (int)per;
-    p.nbp = per * s + 2 * QKB; // >= nb: the last split's range, plus the two stages the pipeline reads past it
+    // >= nb: the last split's range plus the two stages the pipeline reads
+    // past it, rounded up to the prepass's 16-block tiles
+    p.nbp = (per * s + 2 * QKB + 15) / 16 * 16;
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     const size_t parts = s > 1 ? up((size_t)s * (size_t)(m * n) * sizeof(float)) : 0;
     p.x_off = parts;
@@ -497,9 +528,8 @@ hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, 
     prep.mp = plan.mp;
     prep.nbp = plan.nbp;
     const int64_t nb = k / 32;
-    const int64_t prep_threads = plan.mp * plan.nbp;
-    hipLaunchKernelGGL(q4gemm_prep_kernel, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s, xq, prep, m,
-                       nb);
+    hipLaunchKernelGGL(q4gemm_prep_kernel, dim3((unsigned)((plan.mp / 16) * (plan.nbp / 16))), dim3(256), 0, s, xq,
+                       prep, m, nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
