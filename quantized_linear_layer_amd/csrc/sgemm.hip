@@ -4,9 +4,10 @@
 //
 //  * m = 1 is a GEMV bound by reading B once (64 MiB at 4096^2).  Each lane
 //    owns four adjacent columns (16-byte loads along a row of B), the four
-//    waves of a workgroup split a k-chunk between them and combine in LDS, and
-//    the k-chunks write partial sums to the caller's workspace; a second
-//    kernel adds the chunks in a fixed order, so runs are bit-identical
+//    waves of a workgroup split a 64-row k-chunk between them (16 rows each,
+//    all loads issued before any arithmetic) and combine in LDS, and the
+//    k-chunks write partial sums to the caller's workspace; a second kernel
+//    adds the chunks in a fixed order, so runs are bit-identical
 //    (deterministic reductions rather than float atomics).
 //  * m > 1 is compute-bound and runs on the f32 matrix cores
 //    (v_mfma_f32_32x32x2_f32; gfx950 has no reduced-precision xf32 path, so
@@ -22,11 +23,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // ------------------------------------------------------------------ GEMV
 
 constexpr int kSgemvThreads = 256;
-constexpr int kSgemvUnroll = 8; // rows of B in flight per lane
+constexpr int kSgemvRows = 16; // rows of B per wave per chunk, all loads in flight at once
 
 struct SgemvPlan {
     int64_t col_groups; // workgroups along n (64 lanes x vec columns each)
-    int64_t kc;         // rows of B per k-chunk (a multiple of 4)
+    int64_t kc;         // rows of B per k-chunk: 4 waves x kSgemvRows
     int64_t ks;         // number of k-chunks
     int vec;            // columns per lane
 };
@@ -37,14 +38,7 @@ static SgemvPlan sgemv_plan(int64_t n, int64_t k)
     p.vec = (n % 4 == 0) ? 4 : 1;
     const int64_t cols_per_wg = 64 * p.vec;
     p.col_groups = (n + cols_per_wg - 1) / cols_per_wg;
-    int64_t want = (512 + p.col_groups - 1) / p.col_groups; // about 512 workgroups
-    const int64_t max_ks = (k + 31) / 32;                    // at least 32 rows per chunk
-    if (want > max_ks)
-        want = max_ks;
-    if (want < 1)
-        want = 1;
-    p.kc = (k + want - 1) / want;
-    p.kc = (p.kc + 3) / 4 * 4;
+    p.kc = 4 * kSgemvRows;
     p.ks = (k + p.kc - 1) / p.kc;
     return p;
 }
@@ -55,9 +49,11 @@ size_t sgemv_workspace(int64_t n, int64_t k)
     return (size_t)(p.ks * n) * sizeof(float);
 }
 
-// Workgroup (column group, k-chunk): wave w takes rows p0 + w, p0 + w + 4, ...
-// of the chunk, kSgemvUnroll at a time; the four waves combine in LDS in a
-// fixed order and write the chunk's partial sums to ws[chunk][n].
+// Workgroup (column group, k-chunk of 64 rows): wave w takes rows
+// p0 + w, p0 + w + 4, ... of the chunk, issuing all of its 16 loads before
+// the first fma (one memory round trip per wave); the four waves combine in
+// LDS in a fixed order and write the chunk's partial sums to ws[chunk][n].
+// A chunk cut short by the end of k masks its missing rows' products.
 template <int VEC>
 __global__ __launch_bounds__(kSgemvThreads) void sgemv_partial_kernel(const float *__restrict__ x,
                                                                       const float *__restrict__ b,
@@ -75,32 +71,38 @@ __global__ __launch_bounds__(kSgemvThreads) void sgemv_partial_kernel(const floa
     for (int e = 0; e < VEC; e++)
         acc[e] = 0.0f;
     if (col < n) {
-        for (int64_t p = p0 + wave; p < p1; p += 4 * kSgemvUnroll) {
-            float xv[kSgemvUnroll];
-            float bv[kSgemvUnroll][VEC];
+        float xv[kSgemvRows];
+        float bv[kSgemvRows][VEC];
+        const bool full = p1 - p0 == kc;
 #pragma unroll
-            for (int i = 0; i < kSgemvUnroll; i++) {
-                const int64_t pi = p + 4 * i;
-                if (pi < p1) {
-                    xv[i] = x[pi];
-                    if (VEC == 4) {
-                        float4 v = *reinterpret_cast<const float4 *>(b + pi * n + col);
-                        bv[i][0] = v.x; bv[i][1] = v.y; bv[i][2] = v.z; bv[i][3] = v.w;
-                    } else {
-                        bv[i][0] = b[pi * n + col];
-                    }
-                } else {
-                    xv[i] = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < VEC; e++)
-                        bv[i][e] = 0.0f;
-                }
+        for (int i = 0; i < kSgemvRows; i++) {
+            int64_t pi = p0 + wave + 4 * i;
+            if (!full)
+                pi = pi < p1 ? pi : p1 - 1; // a valid row; its product is masked below
+            xv[i] = x[pi];
+            if (VEC == 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(b + pi * n + col);
+                bv[i][0] = v.x;
+                bv[i][1] = v.y;
+                bv[i][2] = v.z;
+                bv[i][3] = v.w;
+            } else {
+                bv[i][0] = b[pi * n + col];
             }
+        }
+        if (full) {
 #pragma unroll
-            for (int i = 0; i < kSgemvUnroll; i++)
+            for (int i = 0; i < kSgemvRows; i++)
 #pragma unroll
                 for (int e = 0; e < VEC; e++)
                     acc[e] = fmaf(xv[i], bv[i][e], acc[e]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kSgemvRows; i++)
+                if (p0 + wave + 4 * i < p1)
+#pragma unroll
+                    for (int e = 0; e < VEC; e++)
+                        acc[e] = fmaf(xv[i], bv[i][e], acc[e]);
         }
     }
     if (wave > 0)
