@@ -45,28 +45,68 @@ __device__ __forceinline__ float ternary_output(int dot_c, int asum, float w_sca
 }
 
 constexpr int kTerGemvThreads = 64;
-constexpr int kTerUnroll = 4;
+constexpr int kTerUnroll = 8;
 
 // m = 1.  VEC: 4 words (one dwordx4) per unit when k % 64 == 0, else 1 word.
+// Each lane issues the weight loads of its first row group before the
+// activation staging, so the two memory round trips overlap.
 template <int L, int VEC>
 __global__ __launch_bounds__(kTerGemvThreads) void ternary_gemv_kernel(
     const uint32_t *__restrict__ w, float w_scale, const int8_t *__restrict__ xq, const float *__restrict__ act_scale,
     const int32_t *__restrict__ act_sum, float *__restrict__ y, int64_t n, int nw)
 {
     extern __shared__ u32x4 s_x[]; // [nw] transposed activation words
-    for (int i = threadIdx.x; i < nw; i += blockDim.x)
-        s_x[i] = transpose_4x4_bytes(reinterpret_cast<const u32x4 *>(xq)[i]);
-    __syncthreads();
-
     constexpr int R = 64 / L;
     constexpr int WAVES = kTerGemvThreads / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / L, r = lane % L;
     const int nu = nw / VEC;
+    const int64_t stride = (int64_t)gridDim.x * WAVES * R;
+    int64_t row0 = ((int64_t)blockIdx.x * WAVES + wave) * R;
+
+    // first kTerUnroll units of this lane's first row, in flight during the staging
+    uint32_t pre[kTerUnroll][VEC];
+    {
+        const int64_t row = row0 + g;
+        const uint32_t *wr = w + (row < n ? row : 0) * nw;
+#pragma unroll
+        for (int i = 0; i < kTerUnroll; i++) {
+            const int u = r + i * L;
+            const int uc = u < nu ? u : 0;
+            if (VEC == 4) {
+                const u32x4 v = reinterpret_cast<const u32x4 *>(wr)[uc];
+#pragma unroll
+                for (int e = 0; e < VEC; e++)
+                    pre[i][e] = v[e];
+            } else {
+                pre[i][0] = wr[uc];
+            }
+        }
+    }
+    // activation staging: all of a lane's loads first, then the transposes
+    {
+        constexpr int kStage = 8; // words per lane per round (k up to 8192 in one round)
+        for (int i0 = threadIdx.x; i0 < nw; i0 += kStage * kTerGemvThreads) {
+            u32x4 t[kStage];
+#pragma unroll
+            for (int j = 0; j < kStage; j++) {
+                const int i = i0 + j * kTerGemvThreads;
+                t[j] = reinterpret_cast<const u32x4 *>(xq)[i < nw ? i : 0];
+            }
+#pragma unroll
+            for (int j = 0; j < kStage; j++) {
+                const int i = i0 + j * kTerGemvThreads;
+                if (i < nw)
+                    s_x[i] = transpose_4x4_bytes(t[j]);
+            }
+        }
+    }
+    __syncthreads();
+
     const float s = act_scale[0];
     const int asum = act_sum[0];
-    const int64_t stride = (int64_t)gridDim.x * WAVES * R;
-    for (int64_t row0 = ((int64_t)blockIdx.x * WAVES + wave) * R; row0 < n; row0 += stride) {
+    bool first = true;
+    for (; row0 < n; row0 += stride) {
         const int64_t row = row0 + g;
         int acc = 0;
         if (row < n) {
@@ -76,7 +116,11 @@ __global__ __launch_bounds__(kTerGemvThreads) void ternary_gemv_kernel(
 #pragma unroll
                 for (int i = 0; i < kTerUnroll; i++) {
                     const int u = u0 + i * L;
-                    if (u < nu) {
+                    if (first && u0 == r) {
+#pragma unroll
+                        for (int e = 0; e < VEC; e++)
+                            wd[i][e] = pre[i][e];
+                    } else if (u < nu) {
                         if (VEC == 4) {
                             u32x4 v = reinterpret_cast<const u32x4 *>(wr)[u];
 #pragma unroll
@@ -98,6 +142,7 @@ __global__ __launch_bounds__(kTerGemvThreads) void ternary_gemv_kernel(
                 }
             }
         }
+        first = false;
 #pragma unroll
         for (int off = L / 2; off > 0; off >>= 1)
             acc += __shfl_xor(acc, off);
