@@ -107,8 +107,11 @@ int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64
 /* Prefill GEMM: Y[m][n] = X.W^T with the same per-block arithmetic as the
  * GEMV for every (i, j).  xq: block_q8_0[m][k/32], w: block_q4_0[n][k/32],
  * y: float[m][n].  k % 32 == 0.  ws/ws_bytes: device workspace of at least
- * qll_workspace_bytes(QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) bytes (may be NULL/0 when
- * that is 0).  m == 1 runs the GEMV kernel. */
+ * qll_workspace_bytes(QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) bytes (nonzero for
+ * m > 1): the call first writes the activations there in the matrix-core
+ * operand form (exact f16 codes, scale bits, bias terms), then split-k partial
+ * sums when it splits k; contents on return are unspecified.  m == 1 runs the
+ * GEMV kernel and needs no workspace. */
 int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                        size_t ws_bytes, void *stream);
 
