@@ -17,15 +17,17 @@
 namespace qll {
 
 // 16 activation bytes (dwords D0..D3, byte e of Dr = x[4r + e]) -> A0..A3 with
-// byte r of Aj = x[4r + j], the order of the code unpack.
+// byte r of Aj = x[4r + j], the order of the code unpack: a 4x4 byte transpose
+// in two rounds of byte permutes (interleave pairs of dwords, then pairs of
+// halves).
 __device__ __forceinline__ u32x4 transpose_4x4_bytes(u32x4 d)
 {
-    u32x4 a;
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-        a[j] = ((d[0] >> (8 * j)) & 0xffu) | (((d[1] >> (8 * j)) & 0xffu) << 8) |
-               (((d[2] >> (8 * j)) & 0xffu) << 16) | (((d[3] >> (8 * j)) & 0xffu) << 24);
-    return a;
+    const uint32_t p0 = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u); // D0.b0 D1.b0 D0.b1 D1.b1
+    const uint32_t p1 = __builtin_amdgcn_perm(d[1], d[0], 0x07030602u); // D0.b2 D1.b2 D0.b3 D1.b3
+    const uint32_t p2 = __builtin_amdgcn_perm(d[3], d[2], 0x05010400u);
+    const uint32_t p3 = __builtin_amdgcn_perm(d[3], d[2], 0x07030602u);
+    return u32x4{__builtin_amdgcn_perm(p2, p0, 0x05040100u), __builtin_amdgcn_perm(p2, p0, 0x07060302u),
+                 __builtin_amdgcn_perm(p3, p1, 0x05040100u), __builtin_amdgcn_perm(p3, p1, 0x07060302u)};
 }
 
 __device__ __forceinline__ int ternary_word_dot(uint32_t word, u32x4 a, int acc)
