@@ -150,8 +150,11 @@ def _gemm_check(codes, d_bits, x, what):
     return y, y_ref, w, xq
 
 
+# (128, 256, 3232): 101 blocks split six ways -- the last split holds one real
+# block and 19 of padding; (257, 131, 608): odd block count, three row tiles
+# with a one-row tail, weight buffer length 2 mod 4 (131 x 19 blocks)
 @pytest.mark.parametrize("m,n,k", [(2, 1, 32), (3, 7, 96), (17, 64, 512), (130, 129, 320), (128, 128, 4096),
-                                   (200, 300, 64), (64, 33, 14336)])
+                                   (200, 300, 64), (64, 33, 14336), (128, 256, 3232), (257, 131, 608)])
 def test_gemm_shapes(qll_gpu, m, n, k):
     codes, d_bits, x = rand_case(m * 1000 + n + k, m, n, k)
     _gemm_check(codes, d_bits, x, f"GEMM m={m} n={n} k={k}")
