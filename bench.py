@@ -13,12 +13,22 @@ size, on inputs already resident in HBM:
 Decode weights rotate through enough device copies (>= 1 GiB per shape) that
 no decode GEMV reads its weights from the 256 MiB Infinity Cache.
 
-Every kernel is bracketed by HIP events recorded on the stream it runs on
-(torch's current stream, which the library launches on).  The JSON line's
-`value` is the Q4_0 x Q8_0 decode GEMV bandwidth over the four shapes
-(algorithmic bytes / summed kernel time); `per_format` holds decode GB/s and
-prefill TOPS of every format with their fractions of the MI355X peaks, and
-`roofline` describes the kernel that takes the largest share of the step.
+Timing uses HIP events recorded on the stream the library launches on
+(torch's current stream).  `ms_per_step` is the wall time of the timed steps,
+each op bracketed by its own event pair (`ms_in_step` per kernel).  An event
+pair around one lone launch also holds the event and dispatch latency (about
+2-3 us, which is a third of a small decode GEMV), so each op's average launch
+duration (`ms` per kernel) is taken as well from runs of R back-to-back
+launches between one event pair, R chosen per op for about a millisecond per
+run, the decode ops still rotating through their weight copies.  The R
+launches are captured once into a HIP graph and replayed, so that the host's
+per-call overhead (Python argument checks, the launch itself: longer than a
+small kernel) cannot leave the GPU idle between them.  The JSON
+line's `value` is the Q4_0 x Q8_0 decode GEMV bandwidth over the four shapes
+(algorithmic bytes / summed average launch duration); `per_format` holds
+decode GB/s and prefill TOPS of every format with their fractions of the
+MI355X peaks, and `roofline` describes the kernel that takes the largest share
+of the step.
 `cpu_baseline` times the oracle (the test suite's plain C reference, never
 tuned) on the same decode GEMVs on the host's cores.
 
@@ -55,7 +65,9 @@ class Op:
     def __init__(self, name, fmt, kind, fn, nbytes, flops, bound, peak_key=None):
         self.name, self.fmt, self.kind, self.fn = name, fmt, kind, fn
         self.nbytes, self.flops, self.bound, self.peak_key = nbytes, flops, bound, peak_key
-        self.times_ms = []
+        self.times_ms = []  # event pair around the op's single launch in each step
+        self.batch_ms = []  # per launch, from runs of back-to-back launches
+        self.reps = 1
 
     def roofline(self, ms):
         if self.bound == "hbm":
@@ -255,20 +267,48 @@ def main():
             op.times_ms.append(evs[st][j][0].elapsed_time(evs[st][j][1]))
     print(f"bench: timed {args.steps} steps, {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # Back-to-back launches: R launches of the op (decode ops on R successive
+    # weight copies) captured once into a HIP graph, so that the host's
+    # per-call Python and launch overhead stays out of the GPU timeline, and
+    # the graph replayed `steps` times, one event pair per replay.
+    launch = args.warmup + args.steps
+    for op in ops:
+        op.reps = int(min(64, max(1, round(1.0 / max(float(np.median(op.times_ms)), 1e-3)))))
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(op.reps):
+                step_ref["i"] = launch
+                launch += 1
+                op.fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        for e0, e1 in pairs:
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        op.batch_ms = [e0.elapsed_time(e1) / op.reps for e0, e1 in pairs]
+        del graph
+    print("bench: timed back-to-back launches (graph replays)", file=sys.stderr, flush=True)
+
     kernels = []
     for op in ops:
-        t = np.array(op.times_ms)
+        t = np.array(op.batch_ms)
         ms = float(np.mean(t))
         rl = op.roofline(ms)
         entry = {"op": op.name, "format": op.fmt, "kind": op.kind, "ms": ms, "ms_median": float(np.median(t)),
-                 "cv": float(np.std(t) / ms) if ms > 0 else 0.0, "bytes": op.nbytes, "flops": op.flops, **rl}
+                 "cv": float(np.std(t) / ms) if ms > 0 else 0.0, "reps": op.reps,
+                 "ms_in_step": float(np.mean(op.times_ms)), "bytes": op.nbytes, "flops": op.flops, **rl}
         if op.kind == "prefill" and op.peak_key == "f16":
             entry["frac_int8_peak"] = rl["achieved"] / PEAK_TFLOPS["i8"]
         if op.name == "ternary_gemm":
             entry["hbm_gbs"] = op.nbytes / (ms * 1e-3) / 1e9
             entry["hbm_frac"] = entry["hbm_gbs"] / PEAK_HBM_GBS
         kernels.append(entry)
-        print(f"  {op.name:22s} {ms * 1e3:10.2f} us  {rl['achieved']:10.1f} {rl['unit']:8s} "
+        print(f"  {op.name:22s} {ms * 1e3:10.2f} us (in step {entry['ms_in_step'] * 1e3:8.2f})  "
+              f"{rl['achieved']:10.1f} {rl['unit']:8s} "
               f"{100 * rl['frac']:6.1f}% of {rl['bound']} peak  (cv {entry['cv']:.3f})", file=sys.stderr)
 
     def agg(fmt, kind):
@@ -311,7 +351,8 @@ def main():
         "config": {"workload": "one pass of the whole path: Q4_0 x Q8_0 decode GEMV (m=1) and prefill GEMM (m=512) "
                                "on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256); f32 GEMM 4096^3 "
                                "and GEMV 4096x4096; BitNet ternary 2560->6912 at m=1 and m=64",
-                   "value_is": "Q4_0 x Q8_0 decode GEMV algorithmic bytes / summed kernel time over the four shapes",
+                   "value_is": "Q4_0 x Q8_0 decode GEMV algorithmic bytes / summed average launch duration (back-to-back "
+                               "launches on rotating weight copies) over the four shapes",
                    "parallelism": "single GPU"},
         "per_format": per_format, "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
     }
