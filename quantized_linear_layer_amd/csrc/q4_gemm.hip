@@ -157,9 +157,9 @@ constexpr int kWqPitch = QBN + 32; // padding: the two lane halves of a fragment
 struct Q4GemmLds {
     u32x4 xs[QKB][QBM][4];         // prepared activations, slots swizzled
     uint32_t wq[QKB][4][kWqPitch]; // weight code dwords, [block][dword][row]
-    uint32_t dx[QKB][QBM];         // binary16 bits of d_x (low half)
-    float c0[QKB][QBM];
-    uint32_t dw[QKB][QBN]; // binary16 bits of d_w (low half), 0 past nb
+    uint32_t dx[QKB][QBM + 4];     // binary16 bits of d_x (low half); the pad is zero
+    alignas(16) float c0[QKB][QBM];
+    u32x2 dw[QKB][QBN]; // {binary16 bits of d_w (low half), 0}, d_w = 0 past nb
 };
 
 // Activation side of stage st, straight into LDS (global_load_lds): the
@@ -257,7 +257,7 @@ __device__ __forceinline__ void q4gemm_store_w(const Q4GemmWRaw &r, const Q4Gemm
         const uint32_t hi = (i == 3 && !odd) ? r.wtail : r.ww[i + 1];
         s.wq[kb][i][row] = funnel(hi, odd ? r.ww[i + 1] : r.ww[i], sh);
     }
-    s.dw[kb][row] = r.valid ? d : 0u;
+    s.dw[kb][row] = u32x2{r.valid ? d : 0u, 0u};
 }
 
 // Weight fragment: dword w of a block (bytes b0..b3) -> eight biased halves,
@@ -277,21 +277,59 @@ __device__ __forceinline__ f16x8 q4gemm_wfrag(uint32_t w, uint32_t bias)
     return __builtin_bit_cast(f16x8, h);
 }
 
-// One stage: for each of its blocks, the block sums of the wave's 64 x 64
-// tile on the matrix core -- 2 x 2 tiles of 32 x 32, each two K = 16 steps
-// started from C0 -- and the scale tiles S = d_x d_w^T (one K = 8 step whose
-// only nonzero term is k = 0: lanes 0..31 hold k = 0..3, lanes 32..63 hold
-// zeros), then acc += S * P.  MFMA operand lanes: lane l holds row (column)
-// l % 32 of its tile and chunk 2s + l / 32 of the block in step s; A and B
-// use the same chunks, so the two steps together cover the block's 32
-// elements once.
-__device__ __forceinline__ void q4gemm_compute(const Q4GemmLds &s, int wm, int wn, int lane, uint32_t bias,
-                                               f32x16 acc[2][2])
+// Byte offsets, from the start of a stage buffer, of everything one lane
+// reads in a stage; the reads add only immediates (block, tile, step) to
+// them.  Activation slots: q4gemm_slot depends on the row only through bits
+// 1..4, which the tile offsets (multiples of 32 rows) leave alone.
+struct Q4GemmLaneOff {
+    uint32_t x[QKB][2]; // activation chunk of step st, tile row 0
+    uint32_t w;         // weight dword of step 0, tile column 0
+    uint32_t dx, dw, c0;
+};
+
+__device__ __forceinline__ Q4GemmLaneOff q4gemm_lane_offsets(int wm, int wn, int lane)
 {
     const int lr = lane & 31, lh = lane >> 5;
-    const uint32_t keep = lh ? 0u : ~0u; // scale operands: k = 0 only
-#pragma unroll 1 // unrolled, the two blocks' address math is hoisted and spills
+    Q4GemmLaneOff o;
+#pragma unroll
+    for (int kb = 0; kb < QKB; kb++)
+#pragma unroll
+        for (int st = 0; st < 2; st++)
+            o.x[kb][st] = (uint32_t)(offsetof(Q4GemmLds, xs) + (kb * QBM + wm + lr) * 64 +
+                                     q4gemm_slot(kb, wm + lr, 2 * st + lh) * 16);
+    o.w = (uint32_t)(offsetof(Q4GemmLds, wq) + (lh * kWqPitch + wn + lr) * 4);
+    o.dx = (uint32_t)(offsetof(Q4GemmLds, dx) + (wm + lr) * 4);
+    o.dw = (uint32_t)(offsetof(Q4GemmLds, dw) + (wn + lr) * 8);
+    o.c0 = (uint32_t)(offsetof(Q4GemmLds, c0) + (wm + 4 * lh) * 4);
+    return o;
+}
+
+template <typename T>
+__device__ __forceinline__ T q4gemm_lds(const QLL_LDS char *base, uint32_t off)
+{
+    return *reinterpret_cast<const QLL_LDS T *>(base + off);
+}
+
+// One stage: for each of its blocks, the block sums of the wave's 64 x 64
+// tile on the matrix core -- 2 x 2 tiles of 32 x 32, each two K = 16 steps
+// started from C0 -- and the scale tiles, then acc += S * P.  MFMA operand
+// lanes: lane l holds row (column) l % 32 of its tile and chunk 2s + l / 32
+// of the block in step s; A and B use the same chunks, so the two steps
+// together cover the block's 32 elements once.
+//
+// Scale tiles, one K = 8 step: lane l holds k = 4 (l / 32) .. +3.  A row
+// lane carries the halves {d_x[r], 0, d_x[r+1], 0}, a column lane
+// {d_w[c], 0, 0, 0}, so the products are zero except at k = 0 and k = 4,
+// both d_x[r] d_w[c]: S = 2 d_x d_w exactly (a product of two halves is
+// exact in f32, and so is its double).  The factor 2 leaves the kernel as an
+// exact halving of the outputs.  (Row 128's neighbour is the zero pad.)
+__device__ __forceinline__ void q4gemm_compute(const QLL_LDS char *base, const Q4GemmLaneOff &o, uint32_t bias,
+                                               f32x16 acc[2][2])
+{
+#pragma unroll
     for (int kb = 0; kb < QKB; kb++) {
+        // keeps the two blocks' reads apart (hoisted together they spill)
+        __builtin_amdgcn_sched_barrier(0);
         f16x8 a[2][2], bm[2][2];
         f16x4 sa[2], sb[2];
         f32x16 c0[2];
@@ -299,19 +337,19 @@ __device__ __forceinline__ void q4gemm_compute(const Q4GemmLds &s, int wm, int w
         for (int i = 0; i < 2; i++) {
 #pragma unroll
             for (int st = 0; st < 2; st++) {
-                const int ra = wm + 32 * i + lr;
-                a[i][st] = __builtin_bit_cast(f16x8, s.xs[kb][ra][q4gemm_slot(kb, ra, 2 * st + lh)]);
-                bm[i][st] = q4gemm_wfrag(s.wq[kb][2 * st + lh][wn + 32 * i + lr], bias);
+                a[i][st] = __builtin_bit_cast(f16x8, q4gemm_lds<u32x4>(base, o.x[kb][st] + 2048 * i));
+                bm[i][st] = q4gemm_wfrag(
+                    q4gemm_lds<uint32_t>(base, o.w + (kb * 4 + 2 * st) * kWqPitch * 4 + 128 * i), bias);
             }
-            const uint32_t dxb = s.dx[kb][wm + 32 * i + lr] & keep;
-            const uint32_t dwb = s.dw[kb][wn + 32 * i + lr] & keep;
-            sa[i] = __builtin_bit_cast(f16x4, u32x2{dxb, 0u});
-            sb[i] = __builtin_bit_cast(f16x4, u32x2{dwb, 0u});
+            const uint32_t dxo = o.dx + kb * (QBM + 4) * 4 + 128 * i;
+            sa[i] = __builtin_bit_cast(f16x4, u32x2{q4gemm_lds<uint32_t>(base, dxo),
+                                                    q4gemm_lds<uint32_t>(base, dxo + 4)});
+            sb[i] = __builtin_bit_cast(f16x4, q4gemm_lds<u32x2>(base, o.dw + kb * QBN * 8 + 256 * i));
             // D layout of a 32 x 32 tile: lane l, register v -> row
             // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const f32x4 t = *reinterpret_cast<const f32x4 *>(&s.c0[kb][wm + 32 * i + 8 * q + 4 * lh]);
+                const f32x4 t = q4gemm_lds<f32x4>(base, o.c0 + kb * QBM * 4 + 128 * i + 32 * q);
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     c0[i][4 * q + e] = t[e];
@@ -414,6 +452,10 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
         wsrc.p0 = reinterpret_cast<const uint32_t *>(w) + (9 * h - wsrc.par) / 2; // floor(18 h / 4)
     }
     const int nstages = per_split / QKB;
+    const Q4GemmLaneOff lo = q4gemm_lane_offsets(wm, wn, lane);
+    // zero pads after each block's d_x row (read as a row's neighbour)
+    if (threadIdx.x < QNBUF * QKB * 4)
+        lds[threadIdx.x / (QKB * 4)].dx[(threadIdx.x / 4) % QKB][QBM + threadIdx.x % 4] = 0u;
     uint32_t bias; // 0x64006400, opaque to the compiler (see q4gemm_wfrag)
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));
 
@@ -435,7 +477,7 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
     for (int st = 0; st < nstages; st++) {
         const int nx1 = cur == 2 ? 0 : cur + 1, nx2 = cur == 0 ? 2 : cur - 1;
         q4gemm_load_w(w, wsrc, st + 1, nb, r);
-        q4gemm_compute(lds[cur], wm, wn, lane, bias, acc);
+        q4gemm_compute((const QLL_LDS char *)&lds[cur], lo, bias, acc);
         q4gemm_store_w(r, wsrc, lds[nx1]);
         q4gemm_load_x(prep, xsrc, m0, b_begin + (st + 2) * QKB, lds[nx2]);
         q4gemm_sync<kQ4GemmDmaPerStage>();
@@ -453,7 +495,7 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
                 const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                 const int64_t col = n0 + wn + 32 * j + (lane & 31);
                 if (row < m && col < n)
-                    y[row * n + col] = acc[i][j][v];
+                    y[row * n + col] = 0.5f * acc[i][j][v]; // the scale tiles are 2 d_x d_w
             }
 }
 
