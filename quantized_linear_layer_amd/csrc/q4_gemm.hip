@@ -177,7 +177,7 @@ struct Q4GemmXSrc {
 
 __device__ __forceinline__ Q4GemmXSrc q4gemm_xsrc(const Q4GemmPrep &p)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     Q4GemmXSrc c;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -193,7 +193,7 @@ __device__ __forceinline__ Q4GemmXSrc q4gemm_xsrc(const Q4GemmPrep &p)
 __device__ __forceinline__ void q4gemm_load_x(const Q4GemmPrep &p, const Q4GemmXSrc &c, int64_t m0, int b,
                                               Q4GemmLds &s)
 {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // uniform: LDS targets in scalar registers
     const uint8_t *xb = reinterpret_cast<const uint8_t *>(p.x) + (m0 * p.nbp + b) * 64;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -202,7 +202,7 @@ __device__ __forceinline__ void q4gemm_load_x(const Q4GemmPrep &p, const Q4GemmX
                                          0, 0);
     }
     const int64_t so = (int64_t)b * p.mp + m0;
-    const int kb = threadIdx.x >> 7, rbase = threadIdx.x & (QBM - 1) & ~63;
+    const int kb = wave >> 1, rbase = (wave & 1) * 64;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(p.dx + so) + c.so,
                                      (QLL_LDS void *)&s.dx[kb][rbase], 4, 0, 0);
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(p.c0 + so) + c.so,
@@ -218,6 +218,8 @@ struct Q4GemmWSrc {
     const uint32_t *p0; // stage-0 window (dword aligned)
     int par;            // parity of the flat block index
     int b0;             // block index of stage 0
+    uint32_t qsel;      // v_perm selector: code dword i from window dwords i, i + 1
+    uint32_t dsel;      // v_perm selector: d_w from window dword 0
 };
 
 // Raw bytes of one weight block, loaded without being looked at.
@@ -246,17 +248,19 @@ __device__ __forceinline__ void q4gemm_load_w(const uint8_t *__restrict__ w, con
     r.wtail = *reinterpret_cast<const uint16_t *>(p + 4);
 }
 
+// Code dword i is bytes 2 + 4 i .. 5 + 4 i of the window (even parity) or
+// bytes 4 + 4 i .. 7 + 4 i (odd), one v_perm of window dwords i and i + 1
+// with the thread's selector; the last one's upper dword is the tail load
+// (even) or the fifth dword (odd).  A block past nb keeps the selectors of
+// its parity: its codes are don't-cares (d_w = 0, activations zero).
 __device__ __forceinline__ void q4gemm_store_w(const Q4GemmWRaw &r, const Q4GemmWSrc &c, Q4GemmLds &s)
 {
     const int row = threadIdx.x & (QBN - 1), kb = threadIdx.x >> 7;
-    const bool odd = r.valid && c.par;
-    const uint32_t sh = odd ? 0u : 16u;
-    const uint32_t d = odd ? (r.ww[0] >> 16) : (r.ww[0] & 0xffffu);
+    const uint32_t last = c.par ? r.ww[4] : r.wtail;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint32_t hi = (i == 3 && !odd) ? r.wtail : r.ww[i + 1];
-        s.wq[kb][i][row] = funnel(hi, odd ? r.ww[i + 1] : r.ww[i], sh);
-    }
+    for (int i = 0; i < 4; i++)
+        s.wq[kb][i][row] = __builtin_amdgcn_perm(i == 3 ? last : r.ww[i + 1], r.ww[i], c.qsel);
+    const uint32_t d = __builtin_amdgcn_perm(0u, r.ww[0], c.dsel);
     s.dw[kb][row] = u32x2{r.valid ? d : 0u, 0u};
 }
 
@@ -301,6 +305,14 @@ __device__ __forceinline__ Q4GemmLaneOff q4gemm_lane_offsets(int wm, int wn, int
     o.dx = (uint32_t)(offsetof(Q4GemmLds, dx) + (wm + lr) * 4);
     o.dw = (uint32_t)(offsetof(Q4GemmLds, dw) + (wn + lr) * 8);
     o.c0 = (uint32_t)(offsetof(Q4GemmLds, c0) + (wm + 4 * lh) * 4);
+    // opaque to the compiler: it would otherwise split off the constant
+    // parts again and re-add them per read (read2 pairs take 8-bit offsets)
+#pragma unroll
+    for (int kb = 0; kb < QKB; kb++)
+#pragma unroll
+        for (int st = 0; st < 2; st++)
+            asm volatile("" : "+v"(o.x[kb][st]));
+    asm volatile("" : "+v"(o.w), "+v"(o.dx), "+v"(o.dw), "+v"(o.c0));
     return o;
 }
 
@@ -450,6 +462,8 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
         const int64_t h = wrow * nb + wsrc.b0; // Q4_0 block at byte 18 h
         wsrc.par = (int)(h & 1);
         wsrc.p0 = reinterpret_cast<const uint32_t *>(w) + (9 * h - wsrc.par) / 2; // floor(18 h / 4)
+        wsrc.qsel = wsrc.par ? 0x07060504u : 0x05040302u;
+        wsrc.dsel = wsrc.par ? 0x0c0c0302u : 0x0c0c0100u; // 0x0c: zero byte
     }
     const int nstages = per_split / QKB;
     const Q4GemmLaneOff lo = q4gemm_lane_offsets(wm, wn, lane);
