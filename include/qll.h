@@ -106,7 +106,9 @@ int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64
 
 /* Prefill GEMM: Y[m][n] = X.W^T with the same per-block arithmetic as the
  * GEMV for every (i, j).  xq: block_q8_0[m][k/32], w: block_q4_0[n][k/32],
- * y: float[m][n].  k % 32 == 0.  ws/ws_bytes: device workspace of at least
+ * y: float[m][n].  k % 32 == 0, and k < 2^24 when m > 1 (else QLL_ERR_SHAPE:
+ * the kernel addresses a 128-row panel with 32-bit offsets).  ws/ws_bytes:
+ * device workspace of at least
  * qll_workspace_bytes(QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) bytes (nonzero for
  * m > 1): the call first writes the activations there in the matrix-core
  * operand form (exact f16 codes, scale bits, bias terms), then split-k partial

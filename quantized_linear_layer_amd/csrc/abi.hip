@@ -18,6 +18,7 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;    // every dimension below 2^31
 constexpr int64_t kMaxElems = (int64_t)1 << 40;  // and every tensor below 2^40 elements
+constexpr int64_t kMaxGemmK = (int64_t)1 << 24;  // Q4_0 GEMM (m > 1): per-lane 32-bit load offsets
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -88,7 +89,7 @@ size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k)
             return SIZE_MAX;
         return m == 1 ? sgemv_workspace(n, k) : 0;
     case QLL_OP_Q4_0_Q8_0_GEMM:
-        if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
+        if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0 || (m > 1 && k >= kMaxGemmK))
             return SIZE_MAX;
         return m == 1 ? 0 : q4_0_q8_0_gemm_workspace(m, n, k);
     case QLL_OP_TERNARY_GEMM:
@@ -162,6 +163,8 @@ int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64
         return QLL_ERR_SHAPE;
     if (m == 1)
         return qll_q4_0_q8_0_gemv(w, xq, y, n, k, stream);
+    if (k >= kMaxGemmK)
+        return QLL_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(xq) || !aligned16(y))
         return QLL_ERR_ALIGN;
     const size_t need = q4_0_q8_0_gemm_workspace(m, n, k);

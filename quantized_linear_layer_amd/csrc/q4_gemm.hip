@@ -29,12 +29,12 @@
 // 2^23 in magnitude.
 //
 // Tiles: 128 x 128 outputs per workgroup, 4 waves of 64 x 64 (2 x 2 MFMA
-// tiles of 32 x 32), two blocks per stage, three LDS buffers.  Prepared
-// activations, d_x and C0 go straight from memory to LDS (global_load_lds);
-// weight blocks are 18 bytes and only 2-byte aligned, so each thread loads one
-// block's raw dword window into registers two stages ahead and stores its 16
-// code bytes and d_w to LDS one stage ahead.  Weights stay as nibbles in LDS
-// (a quarter of the bytes of f16) and are widened when the fragments are read.
+// tiles of 32 x 32), two blocks per stage, three LDS buffers.  Everything a
+// stage reads -- prepared activations, d_x, C0, the weight blocks' code bytes
+// and d_w -- goes straight from memory to LDS (global_load_lds, which takes
+// the 2-byte aligned addresses of 18-byte weight blocks), two stages ahead.
+// Weights stay as nibbles in LDS (a quarter of the bytes of f16) and are
+// widened when the fragments are read.
 #include "common.h"
 
 namespace qll {
@@ -58,9 +58,9 @@ constexpr int kQ4GemmThreads = 256;
 // contribute nothing), so the main loop never tests a row or block edge on
 // the activation side.
 struct Q4GemmPrep {
-    u32x4 *x;     // [mp][nbp][4]
-    uint32_t *dx; // [nbp][mp], binary16 bits of d_x in the low half
-    float *c0;    // [nbp][mp]
+    u32x4 *x;  // [mp][nbp][4]
+    u32x2 *dx; // [nbp][mp]: {binary16 bits of d_x in the low half, 0}
+    float *c0; // [nbp][mp]
     int64_t mp, nbp;
 };
 
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void q4gemm_prep_kernel(const uint8_t *__restr
     sc0[tb][tr] = c0o;
     __syncthreads();
     const int wb = threadIdx.x >> 4, wr = threadIdx.x & 15; // write: block wb, row wr
-    p.dx[(b0 + wb) * p.mp + row0 + wr] = sdx[wb][wr];
+    p.dx[(b0 + wb) * p.mp + row0 + wr] = u32x2{sdx[wb][wr], 0u};
     p.c0[(b0 + wb) * p.mp + row0 + wr] = sc0[wb][wr];
 }
 
@@ -152,33 +152,41 @@ __device__ __forceinline__ int q4gemm_slot(int kb, int row, int c)
     return c ^ (((row >> 1) ^ (row >> 3)) & 3) ^ (kb ? 3 : 0);
 }
 
-constexpr int kWqPitch = QBN + 32; // padding: the two lane halves of a fragment read hit different banks
-
 struct Q4GemmLds {
-    u32x4 xs[QKB][QBM][4];         // prepared activations, slots swizzled
-    uint32_t wq[QKB][4][kWqPitch]; // weight code dwords, [block][dword][row]
-    uint32_t dx[QKB][QBM + 4];     // binary16 bits of d_x (low half); the pad is zero
-    alignas(16) float c0[QKB][QBM];
-    u32x2 dw[QKB][QBN]; // {binary16 bits of d_w (low half), 0}, d_w = 0 past nb
+    u32x4 xs[QKB][QBM][4]; // prepared activations, slots swizzled
+    u32x4 wq[QKB][QBN];    // weight code dwords 0..3 of (block, row)
+    u32x2 dx[QKB][QBM];    // {binary16 bits of d_x, 0}
+    float c0[QKB][QBM];
+    uint32_t dw[QKB][QBN]; // binary16 bits of d_w, zero-extended
 };
 
-// Activation side of stage st, straight into LDS (global_load_lds): the
-// 16 KB of prepared halves (four 16-byte loads per thread; each wave
-// instruction fills 1 KB of LDS, lane l at byte 16 l, so lane l fetches the
-// chunk that belongs in that slot), then d_x and C0 (one 4-byte load each;
-// thread t -> block t / 128, row t % 128).  Six loads per thread, counted by
-// vmcnt like any other.
-constexpr int kQ4GemmDmaPerStage = 6;
+// Every byte a stage needs goes straight from memory to LDS
+// (global_load_lds), seven wave-wide loads per wave and stage:
+//   * the 16 KB of prepared activations, four 1 KB loads per wave (lane l
+//     of a load writes LDS byte 16 l, so it fetches the chunk that belongs
+//     in that slot);
+//   * waves 0 and 1: the {d_x, 0} pairs of block kb = wave (1 KB, two rows
+//     per lane); waves 2 and 3: C0 of block kb = wave - 2 (512 B, lanes
+//     0..31);
+//   * weight rows (wave & 1) * 64 + lane of block kb = wave >> 1: the 16
+//     code bytes (block + 2) and d_w (block + 0, a 16-bit load, which the
+//     hardware writes to LDS as a zero-extended dword).  Weight blocks are
+//     18 bytes, so these addresses are only 2-byte aligned, which the
+//     global -> LDS path takes.
+// No stage data passes through registers, so the compiler has no loads of
+// its own to wait for; the end-of-stage wait (q4gemm_sync) counts these.
+constexpr int kQ4GemmDmaPerStage = 7;
 
-struct Q4GemmXSrc {
-    uint32_t xo[4]; // byte offset of this lane's chunk for each of the four 1 KB loads, from (m0, block b)
-    uint32_t so;    // byte offset of this thread's d_x / C0 entry, from (block b, m0)
+struct Q4GemmSrc {
+    uint32_t xo[4]; // byte offset of this lane's activation chunk for each 1 KB load, from (m0, block b)
+    uint32_t so;    // byte offset of this lane's d_x pair / C0 entries, from (block b, m0)
+    uint32_t wo;    // byte offset of this lane's weight block, from (row n0, block b)
 };
 
-__device__ __forceinline__ Q4GemmXSrc q4gemm_xsrc(const Q4GemmPrep &p)
+__device__ __forceinline__ Q4GemmSrc q4gemm_src(const Q4GemmPrep &p, int64_t n0, int64_t n, int nb)
 {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    Q4GemmXSrc c;
+    Q4GemmSrc c;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int region = wave * 4 + j; // 1 KB = 16 rows of one block
@@ -186,82 +194,55 @@ __device__ __forceinline__ Q4GemmXSrc q4gemm_xsrc(const Q4GemmPrep &p)
         const int row = (region & 7) * 16 + (lane >> 2);
         c.xo[j] = (uint32_t)((row * p.nbp + kb) * 64 + q4gemm_slot(kb, row, lane & 3) * 16);
     }
-    c.so = (uint32_t)(((threadIdx.x >> 7) * p.mp + (threadIdx.x & (QBM - 1))) * 4);
+    c.so = (uint32_t)(16 * lane);
+    const int row = (wave & 1) * 64 + lane;
+    const int64_t wrow = (n0 + row < n) ? row : n - 1 - n0; // rows past n: any valid row, output dropped
+    c.wo = (uint32_t)(18 * wrow * nb);
     return c;
 }
 
-__device__ __forceinline__ void q4gemm_load_x(const Q4GemmPrep &p, const Q4GemmXSrc &c, int64_t m0, int b,
-                                              Q4GemmLds &s)
+// One wave-wide global -> LDS load: lane l reads `size` bytes at base + off
+// (base uniform, in scalar registers) and the wave writes them to LDS at
+// lds + 4 l (sizes 1 to 4, zero-extended) or lds + 16 l (size 16).  Inline
+// assembly keeps these loads out of the compiler's wait bookkeeping.
+__device__ __forceinline__ void q4gemm_dma16(const void *base, uint32_t off, const QLL_LDS void *lds)
 {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // uniform: LDS targets in scalar registers
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+                 "s"((uint32_t)(uintptr_t)lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void q4gemm_dma2(const void *base, uint32_t off, const QLL_LDS void *lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(off), "s"(base),
+                 "s"((uint32_t)(uintptr_t)lds)
+                 : "memory", "m0");
+}
+
+// The loads of stage st (blocks b = b_begin + QKB st + 0, 1).  Weight blocks
+// at or past nb load block nb - 1 of the row instead: their activations
+// and d_x are zero in the prepared arrays, so they add nothing.
+__device__ __forceinline__ void q4gemm_load_stage(const uint8_t *__restrict__ w, const Q4GemmPrep &p,
+                                                  const Q4GemmSrc &c, int64_t m0, int64_t n0, int nb, int b,
+                                                  Q4GemmLds &s)
+{
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t *xb = reinterpret_cast<const uint8_t *>(p.x) + (m0 * p.nbp + b) * 64;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int region = wave * 4 + j;
-        __builtin_amdgcn_global_load_lds(xb + c.xo[j], (QLL_LDS void *)&s.xs[region >> 3][(region & 7) * 16][0], 16,
-                                         0, 0);
+        q4gemm_dma16(xb, c.xo[j], (const QLL_LDS void *)&s.xs[region >> 3][(region & 7) * 16][0]);
     }
-    const int64_t so = (int64_t)b * p.mp + m0;
+    if (wave < 2) {
+        q4gemm_dma16(p.dx + ((int64_t)(b + wave) * p.mp + m0), c.so, (const QLL_LDS void *)&s.dx[wave][0]);
+    } else if (lane < 32) {
+        q4gemm_dma16(p.c0 + ((int64_t)(b + wave - 2) * p.mp + m0), c.so, (const QLL_LDS void *)&s.c0[wave - 2][0]);
+    }
     const int kb = wave >> 1, rbase = (wave & 1) * 64;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(p.dx + so) + c.so,
-                                     (QLL_LDS void *)&s.dx[kb][rbase], 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(p.c0 + so) + c.so,
-                                     (QLL_LDS void *)&s.c0[kb][rbase], 4, 0, 0);
-}
-
-// Weight side.  Weight blocks are 18 bytes and only 2-byte aligned, so they
-// go through registers: thread t stages weight row t % 128 (n - 1 past the
-// edge), block t / 128 of every stage.  A stage advances two blocks, so the
-// parity of the flat block index, which fixes the 2-byte offset of a block
-// inside its dword window, stays the same over the whole k loop.
-struct Q4GemmWSrc {
-    const uint32_t *p0; // stage-0 window (dword aligned)
-    int par;            // parity of the flat block index
-    int b0;             // block index of stage 0
-    uint32_t qsel;      // v_perm selector: code dword i from window dwords i, i + 1
-    uint32_t dsel;      // v_perm selector: d_w from window dword 0
-};
-
-// Raw bytes of one weight block, loaded without being looked at.
-struct Q4GemmWRaw {
-    uint32_t ww[5], wtail; // five dwords from the window start, bytes 16..17 of the window
-    int valid;
-};
-
-// Stage st.  A block at or past nb (stages past the k range) loads from
-// dword 0 instead and gets d_w = 0.  Every address stays inside the weight
-// buffer: an odd-parity block starts 2 bytes into its window and needs the
-// fifth dword, which ends exactly at the block's end; an even-parity block
-// takes its last two bytes from the 16-bit tail load and re-reads dword 3 in
-// place of the fifth.
-__device__ __forceinline__ void q4gemm_load_w(const uint8_t *__restrict__ w, const Q4GemmWSrc &c, int st, int nb,
-                                              Q4GemmWRaw &r)
-{
-    r.valid = c.b0 + 2 * st < nb;
-    const uint32_t *p = r.valid ? c.p0 + 9 * st : reinterpret_cast<const uint32_t *>(w);
-    const u32x4 v0 = *reinterpret_cast<const u32x4_a4 *>(p);
-    r.ww[0] = v0[0];
-    r.ww[1] = v0[1];
-    r.ww[2] = v0[2];
-    r.ww[3] = v0[3];
-    r.ww[4] = p[3 + (r.valid ? c.par : 0)];
-    r.wtail = *reinterpret_cast<const uint16_t *>(p + 4);
-}
-
-// Code dword i is bytes 2 + 4 i .. 5 + 4 i of the window (even parity) or
-// bytes 4 + 4 i .. 7 + 4 i (odd), one v_perm of window dwords i and i + 1
-// with the thread's selector; the last one's upper dword is the tail load
-// (even) or the fifth dword (odd).  A block past nb keeps the selectors of
-// its parity: its codes are don't-cares (d_w = 0, activations zero).
-__device__ __forceinline__ void q4gemm_store_w(const Q4GemmWRaw &r, const Q4GemmWSrc &c, Q4GemmLds &s)
-{
-    const int row = threadIdx.x & (QBN - 1), kb = threadIdx.x >> 7;
-    const uint32_t last = c.par ? r.ww[4] : r.wtail;
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-        s.wq[kb][i][row] = __builtin_amdgcn_perm(i == 3 ? last : r.ww[i + 1], r.ww[i], c.qsel);
-    const uint32_t d = __builtin_amdgcn_perm(0u, r.ww[0], c.dsel);
-    s.dw[kb][row] = u32x2{r.valid ? d : 0u, 0u};
+    const int bw = (b + kb < nb) ? b + kb : nb - 1;
+    const uint8_t *wb = w + 18 * (n0 * nb + bw);
+    q4gemm_dma16(wb + 2, c.wo, (const QLL_LDS void *)&s.wq[kb][rbase]);
+    q4gemm_dma2(wb, c.wo, (const QLL_LDS void *)&s.dw[kb][rbase]);
 }
 
 // Weight fragment: dword w of a block (bytes b0..b3) -> eight biased halves,
@@ -287,7 +268,7 @@ __device__ __forceinline__ f16x8 q4gemm_wfrag(uint32_t w, uint32_t bias)
 // 1..4, which the tile offsets (multiples of 32 rows) leave alone.
 struct Q4GemmLaneOff {
     uint32_t x[QKB][2]; // activation chunk of step st, tile row 0
-    uint32_t w;         // weight dword of step 0, tile column 0
+    uint32_t w;         // weight dwords of both steps, tile column 0
     uint32_t dx, dw, c0;
 };
 
@@ -300,10 +281,10 @@ __device__ __forceinline__ Q4GemmLaneOff q4gemm_lane_offsets(int wm, int wn, int
 #pragma unroll
         for (int st = 0; st < 2; st++)
             o.x[kb][st] = (uint32_t)(offsetof(Q4GemmLds, xs) + (kb * QBM + wm + lr) * 64 +
-                                     q4gemm_slot(kb, wm + lr, 2 * st + lh) * 16);
-    o.w = (uint32_t)(offsetof(Q4GemmLds, wq) + (lh * kWqPitch + wn + lr) * 4);
-    o.dx = (uint32_t)(offsetof(Q4GemmLds, dx) + (wm + lr) * 4);
-    o.dw = (uint32_t)(offsetof(Q4GemmLds, dw) + (wn + lr) * 8);
+                                     q4gemm_slot(kb, wm + lr, 2 * lh + st) * 16);
+    o.w = (uint32_t)(offsetof(Q4GemmLds, wq) + (wn + lr) * 16 + lh * 8);
+    o.dx = (uint32_t)(offsetof(Q4GemmLds, dx) + (wm + lr) * 8);
+    o.dw = (uint32_t)(offsetof(Q4GemmLds, dw) + (wn + lr) * 4);
     o.c0 = (uint32_t)(offsetof(Q4GemmLds, c0) + (wm + 4 * lh) * 4);
     // opaque to the compiler: it would otherwise split off the constant
     // parts again and re-add them per read (read2 pairs take 8-bit offsets)
@@ -325,16 +306,17 @@ __device__ __forceinline__ T q4gemm_lds(const QLL_LDS char *base, uint32_t off)
 // One stage: for each of its blocks, the block sums of the wave's 64 x 64
 // tile on the matrix core -- 2 x 2 tiles of 32 x 32, each two K = 16 steps
 // started from C0 -- and the scale tiles, then acc += S * P.  MFMA operand
-// lanes: lane l holds row (column) l % 32 of its tile and chunk 2s + l / 32
-// of the block in step s; A and B use the same chunks, so the two steps
-// together cover the block's 32 elements once.
+// lanes: lane l holds row (column) l % 32 of its tile and chunk
+// 2 (l / 32) + s of the block in step s (one 8-byte read of a weight row
+// gives a lane both of its dwords); A and B use the same chunks, so the two
+// steps together cover the block's 32 elements once.
 //
 // Scale tiles, one K = 8 step: lane l holds k = 4 (l / 32) .. +3.  A row
-// lane carries the halves {d_x[r], 0, d_x[r+1], 0}, a column lane
+// lane carries the halves {d_x[r], 0, 0, 0}, a column lane
 // {d_w[c], 0, 0, 0}, so the products are zero except at k = 0 and k = 4,
 // both d_x[r] d_w[c]: S = 2 d_x d_w exactly (a product of two halves is
 // exact in f32, and so is its double).  The factor 2 leaves the kernel as an
-// exact halving of the outputs.  (Row 128's neighbour is the zero pad.)
+// exact halving of the outputs.
 __device__ __forceinline__ void q4gemm_compute(const QLL_LDS char *base, const Q4GemmLaneOff &o, uint32_t bias,
                                                f32x16 acc[2][2])
 {
@@ -347,16 +329,14 @@ __device__ __forceinline__ void q4gemm_compute(const QLL_LDS char *base, const Q
         f32x16 c0[2];
 #pragma unroll
         for (int i = 0; i < 2; i++) {
+            const u32x2 wv = q4gemm_lds<u32x2>(base, o.w + kb * QBN * 16 + 512 * i);
 #pragma unroll
             for (int st = 0; st < 2; st++) {
                 a[i][st] = __builtin_bit_cast(f16x8, q4gemm_lds<u32x4>(base, o.x[kb][st] + 2048 * i));
-                bm[i][st] = q4gemm_wfrag(
-                    q4gemm_lds<uint32_t>(base, o.w + (kb * 4 + 2 * st) * kWqPitch * 4 + 128 * i), bias);
+                bm[i][st] = q4gemm_wfrag(wv[st], bias);
             }
-            const uint32_t dxo = o.dx + kb * (QBM + 4) * 4 + 128 * i;
-            sa[i] = __builtin_bit_cast(f16x4, u32x2{q4gemm_lds<uint32_t>(base, dxo),
-                                                    q4gemm_lds<uint32_t>(base, dxo + 4)});
-            sb[i] = __builtin_bit_cast(f16x4, q4gemm_lds<u32x2>(base, o.dw + kb * QBN * 8 + 256 * i));
+            sa[i] = __builtin_bit_cast(f16x4, q4gemm_lds<u32x2>(base, o.dx + kb * QBM * 8 + 256 * i));
+            sb[i] = __builtin_bit_cast(f16x4, u32x2{q4gemm_lds<uint32_t>(base, o.dw + kb * QBN * 4 + 128 * i), 0u});
             // D layout of a 32 x 32 tile: lane l, register v -> row
             // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
 #pragma unroll
@@ -453,49 +433,28 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
         for (int j = 0; j < 2; j++)
             acc[i][j] = f32x16{};
 
-    const Q4GemmXSrc xsrc = q4gemm_xsrc(prep);
-    Q4GemmWSrc wsrc;
-    {
-        const int row = threadIdx.x & (QBN - 1);
-        const int64_t wrow = (n0 + row < n) ? n0 + row : n - 1; // rows past n: any valid row, output dropped
-        wsrc.b0 = b_begin + (threadIdx.x >> 7);
-        const int64_t h = wrow * nb + wsrc.b0; // Q4_0 block at byte 18 h
-        wsrc.par = (int)(h & 1);
-        wsrc.p0 = reinterpret_cast<const uint32_t *>(w) + (9 * h - wsrc.par) / 2; // floor(18 h / 4)
-        wsrc.qsel = wsrc.par ? 0x07060504u : 0x05040302u;
-        wsrc.dsel = wsrc.par ? 0x0c0c0302u : 0x0c0c0100u; // 0x0c: zero byte
-    }
+    const Q4GemmSrc src = q4gemm_src(prep, n0, n, nb);
     const int nstages = per_split / QKB;
     const Q4GemmLaneOff lo = q4gemm_lane_offsets(wm, wn, lane);
-    // zero pads after each block's d_x row (read as a row's neighbour)
-    if (threadIdx.x < QNBUF * QKB * 4)
-        lds[threadIdx.x / (QKB * 4)].dx[(threadIdx.x / 4) % QKB][QBM + threadIdx.x % 4] = 0u;
     uint32_t bias; // 0x64006400, opaque to the compiler (see q4gemm_wfrag)
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));
 
-    // Pipeline, stage st computed from buffer st % 3.  During stage st the
-    // weight registers of stage st+1 are loaded (before the compute) and
-    // stored to buffer (st+1) % 3 (after it); the activation loads of stage
-    // st+2 go out last, straight into buffer (st+2) % 3, and have all of
-    // stage st+1 to land.  Register loads are consumed before the next
-    // LDS-bound loads are issued, so the compiler's own waits never hold
-    // those back; the end-of-stage wait leaves exactly them in flight.  Stages
-    // past the range load padding and are never computed.
-    Q4GemmWRaw r;
-    q4gemm_load_w(w, wsrc, 0, nb, r);
-    q4gemm_load_x(prep, xsrc, m0, b_begin, lds[0]);
-    q4gemm_load_x(prep, xsrc, m0, b_begin + QKB, lds[1]);
-    q4gemm_store_w(r, wsrc, lds[0]);
+    // Pipeline, stage st computed from buffer st % 3.  The loads of stage
+    // st+2 go out at the start of stage st, into the buffer of stage st-1,
+    // which every wave finished reading before the barrier that ended stage
+    // st-1; the end-of-stage wait leaves exactly them in flight, so each
+    // stage's loads have two stages of compute to land.  Stages past the
+    // range load padding and are never computed.
+    q4gemm_load_stage(w, prep, src, m0, n0, nb, b_begin, lds[0]);
+    q4gemm_load_stage(w, prep, src, m0, n0, nb, b_begin + QKB, lds[1]);
     q4gemm_sync<kQ4GemmDmaPerStage>();
     int cur = 0; // buffer of stage st
     for (int st = 0; st < nstages; st++) {
-        const int nx1 = cur == 2 ? 0 : cur + 1, nx2 = cur == 0 ? 2 : cur - 1;
-        q4gemm_load_w(w, wsrc, st + 1, nb, r);
+        const int nx2 = cur == 0 ? 2 : cur - 1;
+        q4gemm_load_stage(w, prep, src, m0, n0, nb, b_begin + (st + 2) * QKB, lds[nx2]);
         q4gemm_compute((const QLL_LDS char *)&lds[cur], lo, bias, acc);
-        q4gemm_store_w(r, wsrc, lds[nx1]);
-        q4gemm_load_x(prep, xsrc, m0, b_begin + (st + 2) * QKB, lds[nx2]);
         q4gemm_sync<kQ4GemmDmaPerStage>();
-        cur = nx1;
+        cur = cur == 2 ? 0 : cur + 1;
     }
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(0x7 << 4); // vmcnt(0) expcnt(7) lgkmcnt(0)
@@ -562,7 +521,7 @@ static Q4GemmPlan q4gemm_plan(int64_t m, int64_t n, int64_t k)
     const size_t parts = s > 1 ? up((size_t)s * (size_t)(m * n) * sizeof(float)) : 0;
     p.x_off = parts;
     p.dx_off = p.x_off + up((size_t)(p.mp * p.nbp) * 64);
-    p.c0_off = p.dx_off + up((size_t)(p.mp * p.nbp) * sizeof(float));
+    p.c0_off = p.dx_off + up((size_t)(p.mp * p.nbp) * 8);
     p.total = p.c0_off + up((size_t)(p.mp * p.nbp) * sizeof(float));
     return p;
 }
@@ -579,7 +538,7 @@ hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, 
     uint8_t *base = static_cast<uint8_t *>(ws);
     Q4GemmPrep prep;
     prep.x = reinterpret_cast<u32x4 *>(base + plan.x_off);
-    prep.dx = reinterpret_cast<uint32_t *>(base + plan.dx_off);
+    prep.dx = reinterpret_cast<u32x2 *>(base + plan.dx_off);
     prep.c0 = reinterpret_cast<float *>(base + plan.c0_off);
     prep.mp = plan.mp;
     prep.nbp = plan.nbp;

@@ -58,6 +58,8 @@ def test_workspace_sizes(L):
     assert ws % (4096 * 4) == 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 1, 4096, 4096) == 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 512, 4096, 33) == SIZE_MAX
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 2, 64, 2 ** 24) == SIZE_MAX  # GEMM k limit
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 1, 64, 2 ** 24) == 0        # the GEMV has none
     assert qll.qll_workspace_bytes(qll.QLL_OP_TERNARY_GEMM, 64, 6912, 2560) == 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_TERNARY_GEMM, 64, 6912, 2561) == SIZE_MAX
     assert qll.qll_workspace_bytes(99, 1, 1, 1) == SIZE_MAX
@@ -92,6 +94,7 @@ def test_q4_errors(L):
     assert L.qll_q4_0_q8_0_gemm(GOOD, NUL, GOOD, 4, 8, 64, NUL, 0, None) == NULL
     assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 16, NUL, 0, None) == SHAPE
     assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, MIS, 4, 8, 64, NUL, 0, None) == ALIGN
+    assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 2 ** 24, GOOD, 2 ** 40, None) == SHAPE
 
 
 def test_sgemm_errors(L):
