@@ -106,16 +106,28 @@ int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64
 
 /* Prefill GEMM: Y[m][n] = X.W^T with the same per-block arithmetic as the
  * GEMV for every (i, j).  xq: block_q8_0[m][k/32], w: block_q4_0[n][k/32],
- * y: float[m][n].  k % 32 == 0, and k < 2^24 when m > 1 (else QLL_ERR_SHAPE:
+ * y: float[m][n].  k % 32 == 0, and k < 2^24 when m > 8 (else QLL_ERR_SHAPE:
  * the kernel addresses a 128-row panel with 32-bit offsets).  ws/ws_bytes:
  * device workspace of at least
  * qll_workspace_bytes(QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) bytes (nonzero for
- * m > 1): the call first writes the activations there in the matrix-core
+ * m > 8): the call first writes the activations there in the matrix-core
  * operand form (exact f16 codes, scale bits, bias terms), then split-k partial
  * sums when it splits k; contents on return are unspecified.  m == 1 runs the
- * GEMV kernel and needs no workspace. */
+ * GEMV kernel; 2 <= m <= 8 (the small-m decode band that [BACK] 9.9 gates
+ * apart from the general GEMM, one row-dot per weight row in 9.9.2) runs a
+ * GEMV-shaped kernel that loads every weight once for all m rows; neither
+ * needs a workspace. */
 int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                        size_t ws_bytes, void *stream);
+
+/* Quantize-fused decode: Y[m][n] = Q8_0(X).W^T for 1 <= m <= 8, where the f32
+ * activation rows x: float[m][k] are quantized to Q8_0 inside the launch with
+ * exactly the arithmetic of qll_quantize_q8_0 ([BACK] 9.7 quantizes the
+ * activation per call), then dotted as in qll_q4_0_q8_0_gemm: the result is
+ * that of qll_quantize_q8_0 followed by qll_q4_0_q8_0_gemm, in one launch and
+ * without the intermediate buffer.  w: block_q4_0[n][k/32], y: float[m][n],
+ * k % 32 == 0; QLL_ERR_SHAPE for m outside [1, 8].  No workspace. */
+int qll_q4_0_q8_0_gemv_f32(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k, void *stream);
 
 /* ---------------------------------------------------------------- f32 */
 

@@ -46,6 +46,7 @@ def load(path=LIB_PATH):
         "qll_quantize_q8_0": [P, P, I, I, P],
         "qll_q4_0_q8_0_gemv": [P, P, P, I, I, P],
         "qll_q4_0_q8_0_gemm": [P, P, P, I, I, I, P, S, P],
+        "qll_q4_0_q8_0_gemv_f32": [P, P, P, I, I, I, P],
         "qll_sgemm": [P, P, P, I, I, I, P, S, P],
         "qll_quantize_i8_rows": [P, P, P, P, I, I, P],
         "qll_ternary_gemv": [P, F, P, P, P, P, I, I, P],
@@ -134,6 +135,12 @@ def qll_q4_0_q8_0_gemm(w, xq, y, m, n, k, ws=None, stream=None):
     _call("qll_q4_0_q8_0_gemm", _ptr(w, n * (k // 32) * Q4_0_BLOCK_BYTES, "w"),
           _ptr(xq, m * (k // 32) * Q8_0_BLOCK_BYTES, "xq"), _ptr(y, m * n * 4, "y"), m, n, k, wsp, wsb,
           _stream(stream))
+
+
+def qll_q4_0_q8_0_gemv_f32(w, x, y, m, n, k, stream=None):
+    """Quantize-fused decode, 1 <= m <= 8: y[m][n] = Q8_0(x).W^T in one launch."""
+    _call("qll_q4_0_q8_0_gemv_f32", _ptr(w, n * (k // 32) * Q4_0_BLOCK_BYTES, "w"), _ptr(x, m * k * 4, "x"),
+          _ptr(y, m * n * 4, "y"), m, n, k, _stream(stream))
 
 
 # ----------------------------------------------------------------- f32

@@ -89,9 +89,9 @@ size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k)
             return SIZE_MAX;
         return m == 1 ? sgemv_workspace(n, k) : 0;
     case QLL_OP_Q4_0_Q8_0_GEMM:
-        if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0 || (m > 1 && k >= kMaxGemmK))
+        if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0 || (m > kMaxMSmall && k >= kMaxGemmK))
             return SIZE_MAX;
-        return m == 1 ? 0 : q4_0_q8_0_gemm_workspace(m, n, k);
+        return m <= kMaxMSmall ? 0 : q4_0_q8_0_gemm_workspace(m, n, k);
     case QLL_OP_TERNARY_GEMM:
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 16 != 0)
             return SIZE_MAX;
@@ -154,6 +154,20 @@ int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64
                                           k, as_stream(stream)));
 }
 
+int qll_q4_0_q8_0_gemv_f32(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k, void *stream)
+{
+    if (!w || !x || !y)
+        return QLL_ERR_NULL;
+    if (m < 1 || m > kMaxMSmall || !dims_ok(n, k) || k % 32 != 0)
+        return QLL_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(x) || !aligned16(y))
+        return QLL_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    return launched(
+        launch_q4_0_q8_0_gemv_f32(static_cast<const uint8_t *>(w), x, y, m, n, k, as_stream(stream)));
+}
+
 int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                        size_t ws_bytes, void *stream)
 {
@@ -163,10 +177,16 @@ int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64
         return QLL_ERR_SHAPE;
     if (m == 1)
         return qll_q4_0_q8_0_gemv(w, xq, y, n, k, stream);
-    if (k >= kMaxGemmK)
-        return QLL_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(xq) || !aligned16(y))
         return QLL_ERR_ALIGN;
+    if (m <= kMaxMSmall) {
+        if (int rc = check_device())
+            return rc;
+        return launched(launch_q4_0_q8_0_gemv_m(static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(xq), y,
+                                                m, n, k, as_stream(stream)));
+    }
+    if (k >= kMaxGemmK)
+        return QLL_ERR_SHAPE;
     const size_t need = q4_0_q8_0_gemm_workspace(m, n, k);
     if (need > 0 && (!ws || ws_bytes < need))
         return QLL_ERR_WORKSPACE;

@@ -46,6 +46,17 @@ __device__ __forceinline__ u32x4 load4_a4(const uint8_t *p)
     return *reinterpret_cast<const u32x4_a4 *>(p);
 }
 
+// Q8_0 code of x for the block scale d (IEEE f32 division, ties away from
+// zero, clamped to +-127; d = 0 gives 0).
+__device__ __forceinline__ int quant_code(float x, float d)
+{
+    if (d == 0.0f)
+        return 0;
+    float r = roundf(x / d);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
 // Q8_0 block at byte offset o of `base` (o % 4 is 0 or 2) -> binary16 d bits
 // and the 32 int8 codes as 8 dwords.  Reads only bytes of this block and, when
 // o % 4 == 2, the two bytes before it (inside the same buffer, since o >= 34).
@@ -86,6 +97,13 @@ hipError_t launch_q4_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, 
                                  hipStream_t s);
 hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                  void *ws, hipStream_t s);
+// Small-m decode (1 <= m <= kMaxMSmall): Q8_0 activations, or f32 activations
+// quantized to Q8_0 inside the launch.
+constexpr int64_t kMaxMSmall = 8;
+hipError_t launch_q4_0_q8_0_gemv_m(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
+                                   hipStream_t s);
+hipError_t launch_q4_0_q8_0_gemv_f32(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
+                                     hipStream_t s);
 size_t q4_0_q8_0_gemm_workspace(int64_t m, int64_t n, int64_t k);
 hipError_t launch_sgemv(const float *x, const float *b, float *c, int64_t n, int64_t k, float *ws, hipStream_t s);
 size_t sgemv_workspace(int64_t n, int64_t k);

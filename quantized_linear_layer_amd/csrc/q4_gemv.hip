@@ -370,4 +370,264 @@ hipError_t launch_q4_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, 
     return launch_pair<false>(w, xq, y, n, nb, s);
 }
 
+// ------------------------------------------------------------------ small m
+// Y[i][j] for 1 <= m <= 8 activation rows (speculative or batched decode):
+// every weight unit is loaded once, as in the m = 1 kernel, and dotted with
+// all M rows.  Per row and block the arithmetic is the same exact int32 sum
+// and f32 scaling.  The activations are staged into LDS one k-chunk at a
+// time (a chunk is the U * L units a row's lanes cover in one pass), so LDS
+// holds M x 128 blocks at most whatever k is; the next chunk's activation
+// bytes and weight units are loaded into registers while the current chunk
+// is computed.  The activations come either as Q8_0 blocks or as f32 rows,
+// quantized here exactly as quantize_q8_0_kernel does (amax, d = amax / 127
+// in f32, codes rounded half away from zero, d stored as binary16), so the
+// f32 entry is the Q8_0 quantization and the GEMV in one launch.
+constexpr int kGmL = 16, kGmU = 4;             // lanes per weight row, units per lane per chunk
+constexpr int kGmR = 64 / kGmL;                // weight rows per wave
+constexpr int kGmThreads = 256;
+
+template <int M, bool PAIR>
+struct GmLds {
+    static constexpr int CB = kGmL * kGmU * (PAIR ? 2 : 1); // blocks per chunk
+    u32x4 qs[M][CB][2]; // codes 0..15, 16..31
+    float dx[M][CB];
+    int c8[M][CB];      // -8 * sum of the block's codes
+};
+
+// Raw activation bytes of one chunk, loaded without being looked at.
+template <int M, bool PAIR, bool F32>
+struct GmRaw {
+    static constexpr int CB = GmLds<M, PAIR>::CB;
+    // Q8_0: one block per task (row-major over M x CB), its nine-dword window
+    // and last two bytes; f32: eight lanes per block, four floats each
+    static constexpr int T = F32 ? M * CB * 8 / kGmThreads : (M * CB + kGmThreads - 1) / kGmThreads;
+    uint32_t v[T][F32 ? 4 : 10];
+};
+
+template <int M, bool PAIR, bool F32>
+__device__ __forceinline__ void gm_act_load(const void *xin, int64_t m, int nb, int chunk, GmRaw<M, PAIR, F32> &raw)
+{
+    constexpr int CB = GmLds<M, PAIR>::CB;
+#pragma unroll
+    for (int t = 0; t < GmRaw<M, PAIR, F32>::T; t++) {
+        const int task = threadIdx.x + t * kGmThreads;
+        if (F32) {
+            const int blk = task >> 3, sub = task & 7;
+            const int r = blk / CB, b = chunk * CB + blk % CB;
+            const bool ok = r < m && b < nb;
+            const float *x = static_cast<const float *>(xin);
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(x + (ok ? ((int64_t)r * nb + b) * 32 + 4 * sub : 0));
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                raw.v[t][e] = v[e];
+        } else {
+            const int r = task / CB, b = chunk * CB + task % CB;
+            const bool ok = task < M * CB && r < m && b < nb;
+            const int64_t g = ok ? (int64_t)r * nb + b : 0; // flat block index
+            const uint8_t *xq = static_cast<const uint8_t *>(xin);
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(xq);
+            const int64_t a = (g * 34 - 2 * (g & 1)) / 4;         // window start (dword)
+            const int64_t max_dw = (m * (int64_t)nb * 34) / 4 - 1; // last whole dword of the buffer
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                raw.v[t][e] = p[a + e];
+            raw.v[t][8] = p[a + 8 <= max_dw ? a + 8 : max_dw];
+            raw.v[t][9] = *reinterpret_cast<const uint16_t *>(xq + g * 34 + 32);
+        }
+    }
+}
+
+template <int M, bool PAIR, bool F32>
+__device__ __forceinline__ void gm_act_store(const GmRaw<M, PAIR, F32> &raw, int64_t m, int nb, int chunk,
+                                             GmLds<M, PAIR> &s)
+{
+    constexpr int CB = GmLds<M, PAIR>::CB;
+#pragma unroll
+    for (int t = 0; t < GmRaw<M, PAIR, F32>::T; t++) {
+        const int task = threadIdx.x + t * kGmThreads;
+        if (F32) {
+            const int blk = task >> 3, sub = task & 7;
+            const int r = blk / CB, bl = blk % CB;
+            const bool ok = r < m && chunk * CB + bl < nb;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                v[e] = ok ? __builtin_bit_cast(float, raw.v[t][e]) : 0.0f;
+            float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+            a = fmaxf(a, __shfl_xor(a, 1));
+            a = fmaxf(a, __shfl_xor(a, 2));
+            a = fmaxf(a, __shfl_xor(a, 4));
+            const float d = a / 127.0f;
+            uint32_t q = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                q |= ((uint32_t)quant_code(v[e], d) & 0xffu) << (8 * e);
+            int sx = sdot4(q, 0x01010101u, 0);
+            sx += __shfl_xor(sx, 1);
+            sx += __shfl_xor(sx, 2);
+            sx += __shfl_xor(sx, 4);
+            reinterpret_cast<uint32_t *>(&s.qs[r][bl][0])[sub] = q; // codes 4 sub .. 4 sub + 3
+            if (sub == 0) {
+                s.dx[r][bl] = half_bits_to_float(float_to_half_bits(d));
+                s.c8[r][bl] = -8 * sx;
+            }
+        } else {
+            if (task >= M * CB)
+                continue;
+            const int r = task / CB, bl = task % CB, b = chunk * CB + bl;
+            const bool ok = r < m && b < nb;
+            const int64_t g = ok ? (int64_t)r * nb + b : 0;
+            uint32_t w9[9];
+#pragma unroll
+            for (int e = 0; e < 9; e++)
+                w9[e] = raw.v[t][e];
+            if (!(g & 1))
+                w9[8] = raw.v[t][9];
+            uint32_t d, q[8];
+            decode_q8_window(w9, (g & 1) != 0, d, q);
+            int sx = 0;
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                sx = sdot4(q[e], 0x01010101u, sx);
+            s.qs[r][bl][0] = ok ? u32x4{q[0], q[1], q[2], q[3]} : u32x4{0u, 0u, 0u, 0u};
+            s.qs[r][bl][1] = ok ? u32x4{q[4], q[5], q[6], q[7]} : u32x4{0u, 0u, 0u, 0u};
+            s.dx[r][bl] = ok ? half_bits_to_float(d) : 0.0f;
+            s.c8[r][bl] = ok ? -8 * sx : 0;
+        }
+    }
+}
+
+// The units of one chunk held by this lane, dotted with the M staged rows.
+template <int M, bool PAIR>
+__device__ __forceinline__ void gm_compute(const GemvRaw<kGmU> &raw, int64_t row, int64_t n, int64_t row_bytes,
+                                           int nu, int ubase, int r, const GmLds<M, PAIR> &s, float acc[M])
+{
+#pragma unroll
+    for (int i = 0; i < kGmU; i++) {
+        const int u = ubase + r + i * kGmL;
+        if (row < n && u < nu) {
+            Q4Unit unit;
+            int nblk;
+            if (PAIR) {
+                decode_q4_pair(raw.w[i], unit);
+                nblk = 2;
+            } else {
+                decode_q4_single(raw.w[i], ((row * row_bytes + (int64_t)u * 18) & 3) != 0, unit);
+                nblk = 1;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                if (h >= nblk)
+                    break;
+                const int bl = (PAIR ? 2 * (r + i * kGmL) : r + i * kGmL) + h; // block within the chunk
+                const float dw = half_bits_to_float(unit.d[h]);
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    lo[e] = unit.qs[h][e] & 0x0f0f0f0fu;
+                    hi[e] = (unit.qs[h][e] >> 4) & 0x0f0f0f0fu;
+                }
+#pragma unroll
+                for (int a = 0; a < M; a++) {
+                    const u32x4 xlo = s.qs[a][bl][0], xhi = s.qs[a][bl][1];
+                    int sum = s.c8[a][bl];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        sum = sdot4(lo[e], xlo[e], sum);
+                        sum = sdot4(hi[e], xhi[e], sum);
+                    }
+                    acc[a] += dw * s.dx[a][bl] * (float)sum;
+                }
+            }
+        }
+    }
+}
+
+template <int M, bool PAIR, bool F32>
+__global__ __launch_bounds__(kGmThreads) void q4_0_gemv_m_kernel(const uint8_t *__restrict__ w, const void *xin,
+                                                                  float *__restrict__ y, int64_t m, int64_t n, int nb)
+{
+    __shared__ GmLds<M, PAIR> s;
+    constexpr int CB = GmLds<M, PAIR>::CB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / kGmL, r = lane % kGmL;
+    const int nu = PAIR ? nb / 2 : nb;
+    const int chunks = (nb + CB - 1) / CB;
+    const int64_t row_bytes = (int64_t)nb * 18;
+    const int64_t row = ((int64_t)blockIdx.x * (kGmThreads / 64) + wave) * kGmR + g; // may be >= n: masked
+
+    float acc[M];
+#pragma unroll
+    for (int a = 0; a < M; a++)
+        acc[a] = 0.0f;
+    // Activation loads of a chunk go out before its weight loads: loads
+    // retire in order, so the staging waits only for its own bytes.
+    GmRaw<M, PAIR, F32> act;
+    gm_act_load<M, PAIR, F32>(xin, m, nb, 0, act);
+    GemvRaw<kGmU> cur, nxt;
+    gemv_load<kGmL, kGmU, PAIR>(w, row, n, row_bytes, nu, 0, r, cur);
+    for (int c = 0; c < chunks; c++) {
+        if (c > 0)
+            __syncthreads(); // every wave is done with the previous chunk
+        gm_act_store<M, PAIR, F32>(act, m, nb, c, s);
+        __syncthreads();
+        if (c + 1 < chunks) {
+            gm_act_load<M, PAIR, F32>(xin, m, nb, c + 1, act);
+            gemv_load<kGmL, kGmU, PAIR>(w, row, n, row_bytes, nu, (c + 1) * kGmU * kGmL, r, nxt);
+        }
+        gm_compute<M, PAIR>(cur, row, n, row_bytes, nu, c * kGmU * kGmL, r, s, acc);
+        cur = nxt;
+    }
+#pragma unroll
+    for (int a = 0; a < M; a++) {
+        float v = acc[a];
+#pragma unroll
+        for (int off = kGmL / 2; off > 0; off >>= 1)
+            v += __shfl_xor(v, off);
+        if (r == 0 && row < n && a < m)
+            y[(int64_t)a * n + row] = v;
+    }
+}
+
+template <bool F32>
+static hipError_t launch_gm(const uint8_t *w, const void *xin, float *y, int64_t m, int64_t n, int64_t k,
+                            hipStream_t s)
+{
+    const int nb = (int)(k / 32);
+    const int64_t groups = (n + kGmR - 1) / kGmR;
+    const int64_t grid = (groups + kGmThreads / 64 - 1) / (kGmThreads / 64);
+    if (grid > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    const dim3 gd((unsigned)grid), bd(kGmThreads);
+#define QLL_GM(MM)                                                                                                    \
+    do {                                                                                                              \
+        if (nb % 2 == 0)                                                                                              \
+            hipLaunchKernelGGL((q4_0_gemv_m_kernel<MM, true, F32>), gd, bd, 0, s, w, xin, y, m, n, nb);               \
+        else                                                                                                          \
+            hipLaunchKernelGGL((q4_0_gemv_m_kernel<MM, false, F32>), gd, bd, 0, s, w, xin, y, m, n, nb);              \
+    } while (0)
+    if (m <= 1)
+        QLL_GM(1);
+    else if (m <= 2)
+        QLL_GM(2);
+    else if (m <= 4)
+        QLL_GM(4);
+    else
+        QLL_GM(8);
+#undef QLL_GM
+    return hipGetLastError();
+}
+
+hipError_t launch_q4_0_q8_0_gemv_m(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
+                                   hipStream_t s)
+{
+    return launch_gm<false>(w, xq, y, m, n, k, s);
+}
+
+hipError_t launch_q4_0_q8_0_gemv_f32(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
+                                     hipStream_t s)
+{
+    return launch_gm<true>(w, x, y, m, n, k, s);
+}
+
 } // namespace qll

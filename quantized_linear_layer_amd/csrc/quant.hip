@@ -75,15 +75,6 @@ hipError_t launch_pack_ternary(const uint8_t *codes, uint32_t *w, int64_t n, int
 
 // ------------------------------------------------------------------ Q8_0
 
-__device__ __forceinline__ int quant_code(float x, float d)
-{
-    if (d == 0.0f)
-        return 0;
-    float r = roundf(x / d); // IEEE division, ties away from zero
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
-}
-
 // Flat over all m*k/32 blocks (rows of x are whole blocks).  Eight lanes own a
 // block, four floats each; a workgroup of 256 lanes owns 32 blocks, assembles
 // their 1088 bytes in LDS and writes them with dword stores.

@@ -58,8 +58,11 @@ def test_workspace_sizes(L):
     assert ws % (4096 * 4) == 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 1, 4096, 4096) == 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 512, 4096, 33) == SIZE_MAX
-    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 2, 64, 2 ** 24) == SIZE_MAX  # GEMM k limit
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 9, 64, 2 ** 24) == SIZE_MAX  # GEMM k limit
     assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 1, 64, 2 ** 24) == 0        # the GEMV has none
+    for m in range(2, 9):                                                                  # small-m decode
+        assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, m, 4096, 14336) == 0
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 9, 4096, 14336) > 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_TERNARY_GEMM, 64, 6912, 2560) == 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_TERNARY_GEMM, 64, 6912, 2561) == SIZE_MAX
     assert qll.qll_workspace_bytes(99, 1, 1, 1) == SIZE_MAX
@@ -94,7 +97,12 @@ def test_q4_errors(L):
     assert L.qll_q4_0_q8_0_gemm(GOOD, NUL, GOOD, 4, 8, 64, NUL, 0, None) == NULL
     assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 16, NUL, 0, None) == SHAPE
     assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, MIS, 4, 8, 64, NUL, 0, None) == ALIGN
-    assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 2 ** 24, GOOD, 2 ** 40, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, GOOD, 16, 8, 2 ** 24, GOOD, 2 ** 40, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, NUL, GOOD, 1, 8, 64, None) == NULL
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 0, 8, 64, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 9, 8, 64, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 2, 8, 48, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, MIS, GOOD, 2, 8, 64, None) == ALIGN
 
 
 def test_sgemm_errors(L):
