@@ -6,7 +6,10 @@ size, on inputs already resident in HBM:
     (m = 1) on the four 8B-class linear shapes (k, n) = (4096, 14336),
     (14336, 4096), (4096, 4096), (4096, 128256);
   * Q8_0 quantization of the prefill activations and the Q4_0 x Q8_0 prefill
-    GEMM (m = 512) on the same four shapes and weights;
+    GEMM (m = 512) on the same four shapes and weights, once on the block_q4_0
+    bytes as they are and once on the same weights repacked at load time into
+    the matrix core's 6-bit operand form (the repack itself is load-time work
+    and is not part of a step);
   * the f32 GEMM 4096^3 and the f32 GEMV 4096 x 4096;
   * the BitNet ternary layer 2560 -> 6912: int8 row quantization, GEMV (m = 1)
     and GEMM (m = 64).
@@ -44,7 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"f16": 2500.0, "i8": 5000.0, "f32": 157.3}
+PEAK_TFLOPS = {"f16": 2500.0, "i8": 5000.0, "f32": 157.3, "bf6": 10100.0}
 METRIC = "decode GEMV HBM GB/s (% of peak) + prefill GEMM TOPS (% MFMA peak) per format"
 
 
@@ -96,7 +99,7 @@ def build_ops(qll, synth, torch, np, dev, only):
     # ---------------------------------------------------------------- Q4_0 x Q8_0
     for s, (k, n) in enumerate(synth.SHAPES_8B):
         need_dec = want(f"q4_gemv_{s}") or want(f"q8_quant_decode_{s}")
-        need_pre = want(f"q4_gemm_{s}") or want(f"q8_quant_prefill_{s}")
+        need_pre = want(f"q4_gemm_{s}") or want(f"q8_quant_prefill_{s}") or want(f"q4r_gemm_{s}")
         if not (need_dec or need_pre):
             continue
         codes, d_bits, x = synth.q4_decode(s)
@@ -136,6 +139,17 @@ def build_ops(qll, synth, torch, np, dev, only):
                               lambda w0=w0, xqp=xqp, yp=yp, n=n, k=k, wsp=wsp: qll.qll_q4_0_q8_0_gemm(
                                   w0, xqp, yp, 512, n, k, ws=wsp),
                               wbytes + m * (k // 32) * 34 + 4 * m * n, 2 * m * n * k, "mfma", "f16"))
+            if want(f"q4r_gemm_{s}"):
+                qll.qll_quantize_q8_0(xp, xqp, m, k)
+                wp = torch.empty(qll.qll_q4_0_repacked_bytes(n, k), dtype=torch.uint8, device=dev)
+                qll.qll_q4_0_repack(w0, wp, n, k)
+                need = qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_REPACKED_GEMM, m, n, k)
+                wsr = torch.empty(need, dtype=torch.uint8, device=dev)
+                yr = torch.empty(m * n, dtype=torch.float32, device=dev)
+                ops.append(Op(f"q4r_gemm_{s}", "q4_0_repacked", "prefill",
+                              lambda wp=wp, xqp=xqp, yr=yr, n=n, k=k, wsr=wsr: qll.qll_q4_0_repacked_q8_0_gemm(
+                                  wp, xqp, yr, 512, n, k, ws=wsr),
+                              wp.numel() + m * (k // 32) * 34 + 4 * m * n, 2 * m * n * k, "mfma", "bf6"))
         if need_dec and want(f"q4_gemv_{s}") and not want(f"q8_quant_decode_{s}"):
             qll.qll_quantize_q8_0(xd, xqd, 1, k)
 
@@ -301,8 +315,10 @@ def main():
         entry = {"op": op.name, "format": op.fmt, "kind": op.kind, "ms": ms, "ms_median": float(np.median(t)),
                  "cv": float(np.std(t) / ms) if ms > 0 else 0.0, "reps": op.reps,
                  "ms_in_step": float(np.mean(op.times_ms)), "bytes": op.nbytes, "flops": op.flops, **rl}
-        if op.kind == "prefill" and op.peak_key == "f16":
+        if op.kind == "prefill" and op.peak_key in ("f16", "bf6"):
             entry["frac_int8_peak"] = rl["achieved"] / PEAK_TFLOPS["i8"]
+        if op.kind == "prefill" and op.peak_key == "bf6":
+            entry["frac_f16_peak"] = rl["achieved"] / PEAK_TFLOPS["f16"]
         if op.name == "ternary_gemm":
             entry["hbm_gbs"] = op.nbytes / (ms * 1e-3) / 1e9
             entry["hbm_frac"] = entry["hbm_gbs"] / PEAK_HBM_GBS
@@ -322,12 +338,14 @@ def main():
         v = sum(op.flops for op, _ in sel) / t / 1e12
         key = sel[0][0].peak_key
         out = {"tops": v, "mfma_dtype": key, "frac_mfma": v / PEAK_TFLOPS[key]}
-        if key == "f16":
+        if key in ("f16", "bf6"):
             out["frac_int8_peak"] = v / PEAK_TFLOPS["i8"]
+        if key == "bf6":
+            out["frac_f16_peak"] = v / PEAK_TFLOPS["f16"]
         return out
 
     per_format = {}
-    for fmt in ("q4_0", "f32", "ternary"):
+    for fmt in ("q4_0", "q4_0_repacked", "f32", "ternary"):
         d = {"decode": agg(fmt, "decode"), "prefill": agg(fmt, "prefill")}
         if any(d.values()):
             per_format[fmt] = d
@@ -349,7 +367,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "i8 (Q4_0 x Q8_0 int8 block dots, f32 scaling)", "data": "synthetic",
         "config": {"workload": "one pass of the whole path: Q4_0 x Q8_0 decode GEMV (m=1) and prefill GEMM (m=512) "
-                               "on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256); f32 GEMM 4096^3 "
+                               "on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256), the prefill also on "
+                               "load-time repacked weights; f32 GEMM 4096^3 "
                                "and GEMV 4096x4096; BitNet ternary 2560->6912 at m=1 and m=64",
                    "value_is": "Q4_0 x Q8_0 decode GEMV algorithmic bytes / summed average launch duration (back-to-back "
                                "launches on rotating weight copies) over the four shapes",

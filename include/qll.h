@@ -66,7 +66,7 @@ enum {
 };
 
 /* Operations that may need a caller-owned device workspace. */
-enum { QLL_OP_SGEMM = 1, QLL_OP_Q4_0_Q8_0_GEMM = 2, QLL_OP_TERNARY_GEMM = 3 };
+enum { QLL_OP_SGEMM = 1, QLL_OP_Q4_0_Q8_0_GEMM = 2, QLL_OP_TERNARY_GEMM = 3, QLL_OP_Q4_0_REPACKED_GEMM = 4 };
 
 /* Bytes of device workspace `op` needs at this shape (0 if none); SIZE_MAX if
  * the shape is invalid. */
@@ -128,6 +128,37 @@ int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64
  * without the intermediate buffer.  w: block_q4_0[n][k/32], y: float[m][n],
  * k % 32 == 0; QLL_ERR_SHAPE for m outside [1, 8].  No workspace. */
 int qll_q4_0_q8_0_gemv_f32(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k, void *stream);
+
+/* ------------------------------------- Q4_0 repacked for the matrix core (prefill) */
+
+/* Bytes of the repacked form of Q4_0 weights W[n][k/32] (SIZE_MAX if the
+ * shape is invalid): ceil(n/128) * (k/32) * 3328. */
+size_t qll_q4_0_repacked_bytes(int64_t n, int64_t k);
+
+/* Load-time repack of Q4_0 weights into the matrix-core operand form (the
+ * packed right-hand side of [BACK] 9.7: rewritten once, reused by every
+ * call).  w: block_q4_0[n][k/32]; wp: qll_q4_0_repacked_bytes(n, k) bytes,
+ * written in full.  Layout, for 128-row tiles t (rows past n are zero) and
+ * blocks b, chunk c = t*(k/32) + b: first the codes, 3072 B per chunk at
+ * 3072*c -- the six dwords of row r (r < 128) hold the 6-bit e3m2 codes of
+ * w = code - 8 for the block's elements 0..31 (element e at bits 6e), dwords
+ * 0..3 at 16*r and dwords 4..5 at 2048 + 8*r; then the scales, the binary16
+ * d of row r at byte 2*(128*c + r) of that second region.  Lossless: every
+ * w in [-8, 7] is exact in e3m2.  k % 32 == 0. */
+int qll_q4_0_repack(const void *w, void *wp, int64_t n, int64_t k, void *stream);
+
+/* Prefill GEMM on repacked weights: Y[m][n] = X.W^T with exactly the
+ * per-block arithmetic of qll_q4_0_q8_0_gemm (exact int32 block sums [CPU],
+ * f32 scaling; tolerance 1e-4 * sum_b |term_b| against an f64 sum), computed
+ * on the matrix core's 6-bit block-scaled path.  wp: the output of
+ * qll_q4_0_repack for (n, k); xq: block_q8_0[m][k/32]; y: float[m][n];
+ * k % 32 == 0, m >= 1.  ws/ws_bytes: at least
+ * qll_workspace_bytes(QLL_OP_Q4_0_REPACKED_GEMM, m, n, k) bytes: the call
+ * writes the activations there in operand form (6-bit codes of h and l with
+ * q = 16h + l, and d), then split-k partial sums when it splits k; contents on
+ * return are unspecified. */
+int qll_q4_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
+                                size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------- f32 */
 

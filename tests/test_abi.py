@@ -103,6 +103,29 @@ def test_q4_errors(L):
     assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 9, 8, 64, None) == SHAPE
     assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 2, 8, 48, None) == SHAPE
     assert L.qll_q4_0_q8_0_gemv_f32(GOOD, MIS, GOOD, 2, 8, 64, None) == ALIGN
+    # repacked weights: the repack and the GEMM on them
+    assert L.qll_q4_0_repack(NUL, GOOD, 8, 64, None) == NULL
+    assert L.qll_q4_0_repack(GOOD, GOOD, 8, 48, None) == SHAPE
+    assert L.qll_q4_0_repack(GOOD, GOOD, 0, 64, None) == SHAPE
+    assert L.qll_q4_0_repack(GOOD, MIS, 8, 64, None) == ALIGN
+    assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 64, NUL, 0, None) == NULL
+    assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 80, GOOD, 2 ** 40, None) == SHAPE
+    assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, MIS, 4, 8, 64, GOOD, 2 ** 40, None) == ALIGN
+    assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 64, MIS, 2 ** 40, None) == ALIGN
+    assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 64, GOOD, 16, None) == WORKSPACE
+
+
+def test_repacked_sizes(L):
+    L.qll_q4_0_repacked_bytes.restype = ctypes.c_size_t
+    assert qll.qll_q4_0_repacked_bytes(1, 32) == 3328
+    assert qll.qll_q4_0_repacked_bytes(129, 64) == 2 * 2 * 3328
+    assert qll.qll_q4_0_repacked_bytes(128256, 4096) == 1002 * 128 * 3328
+    assert qll.qll_q4_0_repacked_bytes(8, 48) == SIZE_MAX
+    need = qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_REPACKED_GEMM, 512, 4096, 4096)
+    # at least the prepared activations: 6144 + 256 bytes per 128 rows and block
+    assert need >= 4 * 128 * 6400
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_REPACKED_GEMM, 1, 1, 32) > 0
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_REPACKED_GEMM, 4, 8, 48) == SIZE_MAX
 
 
 def test_sgemm_errors(L):
