@@ -6,12 +6,13 @@ the HIP library.  Every function here only marshals numpy arrays; the
 arithmetic is in oracle.c, where each routine cites the passage it follows:
 
 * llama.cpp visual guide lesson 31 "CPU backend", "How the quantized dot
-  product works" -- the Q4_0 x Q8_0 block dot;
+  product works" -- the Q4_0 x Q8_0 block dot and the block_q8_0 layout;
 * Fucina course "Chapter 06 -- Going fast on CPUs", 6.4 -- the f32 GEMM
   referee, here accumulated in f64;
 * Loom "Plan 9 SIMD Forward", "BitNet ternary MAD kernel" -- packed ternary
   weights, the ternary identity, per-row int8 activations;
-* Fucina reference "Backends", 9.7 -- per-call Q8_0 activation quantization.
+* Fucina reference "Backends", 9.7 -- per-call Q8_0 activation quantization
+  and Q8_0-quantized weights (the Q8_0 x Q8_0 block dot).
 
 Every function is pinned by tests/test_oracle_*.py to something other than
 itself (numpy brute force, closed forms, identities, exhaustive fp16).
@@ -52,6 +53,10 @@ def load(path):
         "orc_q4_0_q8_0": [_P, _P, _I, _I, _I, _P, _P],
         "orc_q4_0_q8_0_sampled": [_P, _P, _I, _I, _I, _P, _P, _I, _P, _P],
         "orc_q4_0_q8_0_block_sums": [_P, _P, _I, _I, _I, _P],
+        "orc_pack_q8_0": [_P, _P, _P, _I, _I],
+        "orc_q8_0_q8_0": [_P, _P, _I, _I, _I, _P, _P],
+        "orc_q8_0_q8_0_sampled": [_P, _P, _I, _I, _I, _P, _P, _I, _P, _P],
+        "orc_q8_0_q8_0_block_sums": [_P, _P, _I, _I, _I, _P],
         "orc_sgemm": [_P, _P, _I, _I, _I, _P, _P],
         "orc_sgemm_sampled": [_P, _P, _I, _I, _I, _P, _P, _I, _P, _P],
         "orc_pack_ternary": [_P, _P, _I, _I],
@@ -171,6 +176,48 @@ def q4_0_q8_0_block_sums(w, xq, m, n, k, L=None):
     xq = _c(xq, np.uint8)
     s = np.empty((m, n, k // 32), np.int32)
     _check((L or lib()).orc_q4_0_q8_0_block_sums(_ptr(w), _ptr(xq), m, n, k, _ptr(s)), "block_sums")
+    return s
+
+
+# --------------------------------------------------------------------------- Q8_0 weights
+
+def pack_q8_0(q, d_bits, L=None):
+    """q int8[n][k], d_bits uint16[n][k/32] -> uint8[n][k/32*34] Q8_0 blocks."""
+    q = _c(q, np.int8)
+    d_bits = _c(d_bits, np.uint16)
+    n, k = q.shape
+    w = np.empty((n, k // 32 * 34), np.uint8)
+    _check((L or lib()).orc_pack_q8_0(_ptr(q), _ptr(d_bits), _ptr(w), n, k), "pack_q8_0")
+    return w
+
+
+def q8_0_q8_0(w, xq, m, n, k, L=None):
+    """Y = X.W^T with Q8_0 weights and activations: f64 outputs and mag = sum_b |term_b|."""
+    w = _c(w, np.uint8)
+    xq = _c(xq, np.uint8)
+    y = np.empty((m, n), np.float64)
+    mag = np.empty((m, n), np.float64)
+    _check((L or lib()).orc_q8_0_q8_0(_ptr(w), _ptr(xq), m, n, k, _ptr(y), _ptr(mag)), "q8_0_q8_0")
+    return y, mag
+
+
+def q8_0_q8_0_sampled(w, xq, m, n, k, ii, jj, L=None):
+    w = _c(w, np.uint8)
+    xq = _c(xq, np.uint8)
+    ii = _c(ii, np.int64)
+    jj = _c(jj, np.int64)
+    y = np.empty(ii.size, np.float64)
+    mag = np.empty(ii.size, np.float64)
+    _check((L or lib()).orc_q8_0_q8_0_sampled(_ptr(w), _ptr(xq), m, n, k, _ptr(ii), _ptr(jj), ii.size,
+                                              _ptr(y), _ptr(mag)), "q8_0_q8_0_sampled")
+    return y, mag
+
+
+def q8_0_q8_0_block_sums(w, xq, m, n, k, L=None):
+    w = _c(w, np.uint8)
+    xq = _c(xq, np.uint8)
+    s = np.empty((m, n, k // 32), np.int32)
+    _check((L or lib()).orc_q8_0_q8_0_block_sums(_ptr(w), _ptr(xq), m, n, k, _ptr(s)), "q8 block_sums")
     return s
 
 

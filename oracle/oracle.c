@@ -30,7 +30,9 @@
  *          dot = sum(code*act) - sum(act), per-row int8 activations with
  *          activation_scale = 127 / max|x|, output dot * absmean / act_scale.
  *  [BACK]  Fucina reference "Backends", 9.7 "Quantized matmul dispatch":
- *          the f32 activation rows are quantized to Q8_0 blocks per call.
+ *          the f32 activation rows are quantized to Q8_0 blocks per call;
+ *          weights may themselves be quantized to Q8_0 (the Q8_0 x Q8_0
+ *          block dot).
  *
  * Readings where the pages are silent (the same list is kept with the
  * design notes): element t < 16 of a Q4_0 block is the low nibble of qs[t],
@@ -303,6 +305,100 @@ int orc_q4_0_q8_0_block_sums(const uint8_t *w, const uint8_t *xq, int64_t m, int
         for (int64_t j = 0; j < n; j++)
             for (int64_t b = 0; b < nb; b++)
                 sumi[(i * n + j) * nb + b] = q4_0_q8_0_block_sum(w + (j * nb + b) * 18, xq + (i * nb + b) * 34);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q8_0 weights x Q8_0 activations: the weights quantized to Q8_0 blocks    */
+/* (the quantized right-hand side of [BACK] 9.7, quantizeMatmulRhsQ8_0; the  */
+/* activations quantized per call as above).  Per block b                    */
+/*   sumi_b = sum_t qw_t * qx_t                   (int32, exact)             */
+/*   term_b = f64(dw_b) * f64(dx_b) * sumi_b      (exact in f64)             */
+/* y = sum_b term_b in b order (f64), mag = sum_b |term_b|.                  */
+/* ------------------------------------------------------------------------ */
+
+/* q int8[n][k] and d_bits uint16[n][k/32] -> w[n][k/32] block_q8_0. */
+int orc_pack_q8_0(const int8_t *q, const uint16_t *d_bits, uint8_t *w, int64_t n, int64_t k)
+{
+    if (k % 32 != 0 || n < 0 || k < 0)
+        return ORC_ERR_ARG;
+    int64_t nb = k / 32;
+    for (int64_t j = 0; j < n; j++)
+        for (int64_t b = 0; b < nb; b++) {
+            uint8_t *out = w + (j * nb + b) * 34;
+            store_u16le(out, d_bits[j * nb + b]);
+            for (int t = 0; t < 32; t++)
+                out[2 + t] = (uint8_t)q[j * k + b * 32 + t];
+        }
+    return ORC_OK;
+}
+
+static int32_t q8_0_q8_0_block_sum(const uint8_t *wblk, const uint8_t *xblk)
+{
+    int32_t s = 0;
+    for (int t = 0; t < 32; t++) {
+        int qw = (int8_t)wblk[2 + t];
+        int qx = (int8_t)xblk[2 + t];
+        s += qw * qx;
+    }
+    return s;
+}
+
+static void q8_0_q8_0_one(const uint8_t *wrow, const uint8_t *xrow, int64_t nb, double *y, double *mag)
+{
+    double sum = 0.0, sum_abs = 0.0;
+    for (int64_t b = 0; b < nb; b++) {
+        const uint8_t *wblk = wrow + b * 34;
+        const uint8_t *xblk = xrow + b * 34;
+        int32_t sumi = q8_0_q8_0_block_sum(wblk, xblk);
+        double sc = orc_half_to_double(load_u16le(wblk)) * orc_half_to_double(load_u16le(xblk));
+        double term = sc * (double)sumi;
+        sum += term;
+        sum_abs += fabs(term);
+    }
+    *y = sum;
+    *mag = sum_abs;
+}
+
+/* Y[m][n] = X.W^T with X = xq[m][k/32] and W = w[n][k/32], both Q8_0. */
+int orc_q8_0_q8_0(const uint8_t *w, const uint8_t *xq, int64_t m, int64_t n, int64_t k, double *y, double *mag)
+{
+    if (k % 32 != 0 || m < 0 || n < 0 || k < 0)
+        return ORC_ERR_ARG;
+    int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; j++)
+        for (int64_t i = 0; i < m; i++)
+            q8_0_q8_0_one(w + j * nb * 34, xq + i * nb * 34, nb, &y[i * n + j], &mag[i * n + j]);
+    return ORC_OK;
+}
+
+/* The same definition evaluated only at the listed (ii[s], jj[s]) outputs. */
+int orc_q8_0_q8_0_sampled(const uint8_t *w, const uint8_t *xq, int64_t m, int64_t n, int64_t k,
+                          const int64_t *ii, const int64_t *jj, int64_t count, double *y, double *mag)
+{
+    if (k % 32 != 0 || m < 0 || n < 0 || k < 0)
+        return ORC_ERR_ARG;
+    for (int64_t s = 0; s < count; s++)
+        if (ii[s] < 0 || ii[s] >= m || jj[s] < 0 || jj[s] >= n)
+            return ORC_ERR_ARG;
+    int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < count; s++)
+        q8_0_q8_0_one(w + jj[s] * nb * 34, xq + ii[s] * nb * 34, nb, &y[s], &mag[s]);
+    return ORC_OK;
+}
+
+/* The integer block sums themselves: sumi[i][j][b] for every output. */
+int orc_q8_0_q8_0_block_sums(const uint8_t *w, const uint8_t *xq, int64_t m, int64_t n, int64_t k, int32_t *sumi)
+{
+    if (k % 32 != 0 || m < 0 || n < 0 || k < 0)
+        return ORC_ERR_ARG;
+    int64_t nb = k / 32;
+    for (int64_t i = 0; i < m; i++)
+        for (int64_t j = 0; j < n; j++)
+            for (int64_t b = 0; b < nb; b++)
+                sumi[(i * n + j) * nb + b] = q8_0_q8_0_block_sum(w + (j * nb + b) * 34, xq + (i * nb + b) * 34);
     return ORC_OK;
 }
 

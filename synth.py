@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the quantized linear layer.
 
 This module holds none of the method's arithmetic: it only draws raw values
-(4-bit codes, fp16 scales, ternary codes, f32 activations) from numpy's PCG64
+(4- and 8-bit codes, fp16 scales, ternary codes, f32 activations) from numpy's PCG64
 generator in a fixed order.  Encoding them into Q4_0 blocks or packed ternary
 words, and quantizing activations, is done separately by the HIP library
 (on the device) and by the oracle (on the host), so both sides start from the
@@ -10,7 +10,8 @@ same raw draws and nothing else.
 The shapes and value distributions follow the workloads of the pages: one
 Q4_0 layer of 512x512, an f32 GEMM of 4096^3 with its m = 1 GEMV, a BitNet
 ternary 2560 -> 6912 layer at m = 1 and m = 64, and the Q4_0 decode (m = 1)
-and prefill (m = 512) linears of an 8B-class transformer.
+and prefill (m = 512) linears of an 8B-class transformer, the same shapes
+with Q8_0 weights.
 """
 import numpy as np
 
@@ -22,6 +23,7 @@ SEED_F32 = 1002
 SEED_TERNARY = 1003
 SEED_Q4_DECODE = 1004   # + shape index
 SEED_Q4_PREFILL_X = 2004  # + shape index
+SEED_Q8W_DECODE = 3004    # + shape index: Q8_0 weights of the same shapes
 
 
 def q4_0_weights(rng, n, k):
@@ -30,6 +32,16 @@ def q4_0_weights(rng, n, k):
     [n][k/32]."""
     assert k % 32 == 0
     codes = rng.integers(0, 16, size=(n, k // 32, 32), dtype=np.uint8).reshape(n, k)
+    d = rng.uniform(0.001, 0.01, size=(n, k // 32)).astype(np.float32).astype(np.float16)
+    return codes, d.view(np.uint16)
+
+
+def q8_0_weights(rng, n, k):
+    """Raw Q8_0 weight draws: codes int8[n][k] uniform in [-127, 127] (the
+    range the Q8_0 quantizer produces) and fp16 scales ~ U(0.001, 0.01) as
+    uint16 bits [n][k/32]."""
+    assert k % 32 == 0
+    codes = rng.integers(-127, 128, size=(n, k // 32, 32), dtype=np.int16).astype(np.int8).reshape(n, k)
     d = rng.uniform(0.001, 0.01, size=(n, k // 32)).astype(np.float32).astype(np.float16)
     return codes, d.view(np.uint16)
 
@@ -94,3 +106,15 @@ def q4_prefill_x(shape_index, m=512, k=None):
     k = k or SHAPES_8B[shape_index][0]
     rng = np.random.default_rng(SEED_Q4_PREFILL_X + shape_index)
     return normal_f32(rng, (m, k))
+
+
+def q8w_decode(shape_index, k=None, n=None):
+    """8B-class layer number `shape_index` with Q8_0 weights: W draws then x
+    (m = 1); the prefill activations are those of q4_prefill_x."""
+    k0, n0 = SHAPES_8B[shape_index]
+    k = k or k0
+    n = n or n0
+    rng = np.random.default_rng(SEED_Q8W_DECODE + shape_index)
+    codes, d_bits = q8_0_weights(rng, n, k)
+    x = normal_f32(rng, (1, k))
+    return codes, d_bits, x

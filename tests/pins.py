@@ -260,6 +260,74 @@ def check_q4_0_q8_0_zero_cases(L):
     assert np.all(y == 0) and np.all(mag == 0)
 
 
+# --------------------------------------------------------------------------- Q8_0 x Q8_0
+
+
+def check_q8_0_pack(L):
+    rng = np.random.default_rng(41)
+    for n, k in ((1, 32), (5, 96), (3, 320)):
+        q, d = rand_q8(rng, n, k)
+        q[0, 0] = -128  # the full int8 range is a valid weight code
+        w = O.pack_q8_0(q, d, L=L)
+        assert np.array_equal(w, np_pack_q8_0(q, d))
+        q2, d2 = O.unpack_q8_0(w, n, k, L=L)
+        assert np.array_equal(q2, q) and np.array_equal(d2, d)
+
+
+def check_q8_0_q8_0_brute_force(L):
+    rng = np.random.default_rng(42)
+    for m, n, k in ((1, 1, 32), (1, 40, 256), (3, 17, 96), (4, 9, 160)):
+        qw, dw = rand_q8(rng, n, k)
+        qw[rng.random((n, k)) < 0.02] = -128
+        q, dx = rand_q8(rng, m, k)
+        w = np_pack_q8_0(qw, dw)
+        xq = np_pack_q8_0(q, dx)
+        y, mag = O.q8_0_q8_0(w, xq, m, n, k, L=L)
+        wf = np.repeat(np_half(dw), 32, axis=1) * qw.astype(np.float64)
+        xf = np.repeat(np_half(dx), 32, axis=1) * q.astype(np.float64)
+        assert np.all(np.abs(y - xf @ wf.T) <= 1e-12 * mag + 1e-300)
+        prod = xf[:, None, :] * wf[None, :, :]
+        tb = prod.reshape(m, n, k // 32, 32).sum(axis=3)
+        assert np.allclose(mag, np.abs(tb).sum(axis=2), rtol=1e-12, atol=0)
+        s = O.q8_0_q8_0_block_sums(w, xq, m, n, k, L=L)
+        want = np.einsum("ibt,jbt->ijb", q.reshape(m, -1, 32).astype(np.int64),
+                         qw.reshape(n, -1, 32).astype(np.int64))
+        assert np.array_equal(s.astype(np.int64), want)
+        ii = rng.integers(0, m, 9)
+        jj = rng.integers(0, n, 9)
+        ys, ms = O.q8_0_q8_0_sampled(w, xq, m, n, k, ii, jj, L=L)
+        assert np.array_equal(ys, y[ii, jj]) and np.array_equal(ms, mag[ii, jj])
+
+
+def check_q8_0_q8_0_unit_scales(L):
+    # dw = dx = 1: the output is exactly the integer dot product, including the
+    # extreme codes -128 and 127 on the weight side
+    rng = np.random.default_rng(43)
+    m, n, k = 3, 7, 256
+    qw = rng.integers(-128, 128, (n, k)).astype(np.int8)
+    qw[0, :32] = -128
+    qw[1, :32] = 127
+    q = rng.integers(-127, 128, (m, k)).astype(np.int8)
+    one = np.uint16(0x3c00)
+    y, _ = O.q8_0_q8_0(np_pack_q8_0(qw, np.full((n, k // 32), one)), np_pack_q8_0(q, np.full((m, k // 32), one)),
+                       m, n, k, L=L)
+    assert np.array_equal(y, (q.astype(np.int64) @ qw.astype(np.int64).T).astype(np.float64))
+
+
+def check_q8_0_q8_0_one_hot(L):
+    # x_p = 127 alone: y_j = dw[j, p//32] * qw[j, p] * 127
+    rng = np.random.default_rng(44)
+    n, k = 6, 128
+    qw, dw = rand_q8(rng, n, k)
+    w = np_pack_q8_0(qw, dw)
+    for p in (0, 1, 31, 32, 77, 127):
+        x = np.zeros((1, k), np.float32)
+        x[0, p] = 127.0
+        y, _ = O.q8_0_q8_0(w, O.quantize_q8_0(x, L=L), 1, n, k, L=L)
+        want = np_half(dw[:, p // 32]) * qw[:, p].astype(np.float64) * 127.0
+        assert np.array_equal(y[0], want), p
+
+
 # --------------------------------------------------------------------------- f32 GEMM
 
 

@@ -49,6 +49,14 @@ MUTATIONS = {
                            "double s = orc_half_to_double(load_u16le(wb)) * orc_half_to_double(load_u16le(wb));"),
     "dot_mag_signed": ("m += fabs(term);", "m += term;"),
     "dot_x_block_index": ("const uint8_t *xb = xrow + b * 34;", "const uint8_t *xb = xrow + (nb - 1 - b) * 34;"),
+    # Q8_0 x Q8_0 dot
+    "q8w_weight_unsigned": ("int qw = (int8_t)wblk[2 + t];", "int qw = wblk[2 + t];"),
+    "q8w_weight_block_stride": ("const uint8_t *wblk = wrow + b * 34;", "const uint8_t *wblk = wrow + b * 32;"),
+    "q8w_scale_dx_twice": ("double sc = orc_half_to_double(load_u16le(wblk)) * orc_half_to_double(load_u16le(xblk));",
+                           "double sc = orc_half_to_double(load_u16le(xblk)) * orc_half_to_double(load_u16le(xblk));"),
+    "q8w_mag_signed": ("sum_abs += fabs(term);", "sum_abs += term;"),
+    "q8w_pack_d_big_endian": ("store_u16le(out, d_bits[j * nb + b]);",
+                              "out[0] = (uint8_t)(d_bits[j * nb + b] >> 8); out[1] = (uint8_t)d_bits[j * nb + b];"),
     # f32 GEMM
     "sgemm_b_column": ("double prod = (double)a[i * k + p] * (double)b[p * n + j];",
                        "double prod = (double)a[i * k + p] * (double)b[p * n + (n - 1 - j)];"),
