@@ -10,6 +10,8 @@ size, on inputs already resident in HBM:
     bytes as they are and once on the same weights repacked at load time into
     the matrix core's 6-bit operand form (the repack itself is load-time work
     and is not part of a step);
+  * the same four shapes with Q8_0 weights: decode GEMV on the Q8_0 blocks
+    and prefill GEMM (m = 512) on the weights repacked at load time;
   * the f32 GEMM 4096^3 and the f32 GEMV 4096 x 4096;
   * the BitNet ternary layer 2560 -> 6912: int8 row quantization, GEMV (m = 1)
     and GEMM (m = 64).
@@ -152,6 +154,41 @@ def build_ops(qll, synth, torch, np, dev, only):
                               wp.numel() + m * (k // 32) * 34 + 4 * m * n, 2 * m * n * k, "mfma", "bf6"))
         if need_dec and want(f"q4_gemv_{s}") and not want(f"q8_quant_decode_{s}"):
             qll.qll_quantize_q8_0(xd, xqd, 1, k)
+
+    # ---------------------------------------------------------------- Q8_0 weights
+    import oracle as O  # host-side packing of the raw weight draws into Q8_0 blocks (set-up only)
+    for s, (k, n) in enumerate(synth.SHAPES_8B):
+        need_dec, need_pre = want(f"q8w_gemv_{s}"), want(f"q8r_gemm_{s}")
+        if not (need_dec or need_pre):
+            continue
+        codes, d_bits, x = synth.q8w_decode(s)
+        w0 = to_dev(O.pack_q8_0(codes, d_bits).reshape(-1))
+        del codes, d_bits
+        wbytes = w0.numel()
+        if need_dec:
+            copies = [w0] + [w0.clone() for _ in range(max(1, -(-gib // wbytes)) - 1)]
+            xqd = torch.empty((k // 32) * 34, dtype=torch.uint8, device=dev)
+            qll.qll_quantize_q8_0(to_dev(x), xqd, 1, k)
+            yd = torch.empty(n, dtype=torch.float32, device=dev)
+            ops.append(Op(f"q8w_gemv_{s}", "q8_0", "decode",
+                          lambda c=copies, xqd=xqd, yd=yd, n=n, k=k: qll.qll_q8_0_q8_0_gemv(
+                              c[step_ref["i"] % len(c)], xqd, yd, n, k),
+                          wbytes + (k // 32) * 34 + 4 * n, 2 * n * k, "hbm"))
+        if need_pre:
+            m = 512
+            xqp = torch.empty(m * (k // 32) * 34, dtype=torch.uint8, device=dev)
+            qll.qll_quantize_q8_0(to_dev(synth.q4_prefill_x(s)), xqp, m, k)
+            wp = torch.empty(qll.qll_q8_0_repacked_bytes(n, k), dtype=torch.uint8, device=dev)
+            qll.qll_q8_0_repack(w0, wp, n, k)
+            wsr = torch.empty(qll.qll_workspace_bytes(qll.QLL_OP_Q8_0_REPACKED_GEMM, m, n, k), dtype=torch.uint8,
+                              device=dev)
+            yr = torch.empty(m * n, dtype=torch.float32, device=dev)
+            ops.append(Op(f"q8r_gemm_{s}", "q8_0", "prefill",
+                          lambda wp=wp, xqp=xqp, yr=yr, n=n, k=k, wsr=wsr: qll.qll_q8_0_repacked_q8_0_gemm(
+                              wp, xqp, yr, 512, n, k, ws=wsr),
+                          wp.numel() + m * (k // 32) * 34 + 4 * m * n, 2 * m * n * k, "mfma", "bf6"))
+            if not need_dec:
+                del w0
 
     # ---------------------------------------------------------------- f32
     if want("sgemm") or want("sgemv"):
@@ -345,7 +382,7 @@ def main():
         return out
 
     per_format = {}
-    for fmt in ("q4_0", "q4_0_repacked", "f32", "ternary"):
+    for fmt in ("q4_0", "q4_0_repacked", "q8_0", "f32", "ternary"):
         d = {"decode": agg(fmt, "decode"), "prefill": agg(fmt, "prefill")}
         if any(d.values()):
             per_format[fmt] = d
@@ -368,7 +405,8 @@ def main():
         "vs_baseline": None, "dtype": "i8 (Q4_0 x Q8_0 int8 block dots, f32 scaling)", "data": "synthetic",
         "config": {"workload": "one pass of the whole path: Q4_0 x Q8_0 decode GEMV (m=1) and prefill GEMM (m=512) "
                                "on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256), the prefill also on "
-                               "load-time repacked weights; f32 GEMM 4096^3 "
+                               "load-time repacked weights; the same shapes with Q8_0 weights (decode GEMV, prefill GEMM on repacked "
+                               "weights); f32 GEMM 4096^3 "
                                "and GEMV 4096x4096; BitNet ternary 2560->6912 at m=1 and m=64",
                    "value_is": "Q4_0 x Q8_0 decode GEMV algorithmic bytes / summed average launch duration (back-to-back "
                                "launches on rotating weight copies) over the four shapes",

@@ -66,7 +66,13 @@ enum {
 };
 
 /* Operations that may need a caller-owned device workspace. */
-enum { QLL_OP_SGEMM = 1, QLL_OP_Q4_0_Q8_0_GEMM = 2, QLL_OP_TERNARY_GEMM = 3, QLL_OP_Q4_0_REPACKED_GEMM = 4 };
+enum {
+    QLL_OP_SGEMM = 1,
+    QLL_OP_Q4_0_Q8_0_GEMM = 2,
+    QLL_OP_TERNARY_GEMM = 3,
+    QLL_OP_Q4_0_REPACKED_GEMM = 4,
+    QLL_OP_Q8_0_REPACKED_GEMM = 5
+};
 
 /* Bytes of device workspace `op` needs at this shape (0 if none); SIZE_MAX if
  * the shape is invalid. */
@@ -158,6 +164,45 @@ int qll_q4_0_repack(const void *w, void *wp, int64_t n, int64_t k, void *stream)
  * q = 16h + l, and d), then split-k partial sums when it splits k; contents on
  * return are unspecified. */
 int qll_q4_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
+                                size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------ Q8_0 weights x Q8_0 activations */
+
+/* Weights quantized to Q8_0 blocks too ([BACK] 9.7: a Q8_0-quantized
+ * right-hand side against the per-call Q8_0 activation).  Per output and
+ * block: sumi = sum_t qw[t] * qx[t] exact in int32, term = f32(dw) * f32(dx)
+ * * sumi, summed in f32 (tolerance 1e-4 * sum_b |term_b| against an f64
+ * sum).  Weight codes may take the whole int8 range. */
+
+/* Decode GEMV (m = 1): w: block_q8_0[n][k/32], xq: block_q8_0[k/32],
+ * y: float[n].  k % 32 == 0 and k <= 49152 (the activation row is staged in
+ * LDS).  Bandwidth-bound: every weight byte is read once. */
+int qll_q8_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64_t k, void *stream);
+
+/* Bytes of the repacked form of Q8_0 weights W[n][k/32] (SIZE_MAX if the
+ * shape is invalid): ceil(n/128) * (k/32) * 6400. */
+size_t qll_q8_0_repacked_bytes(int64_t n, int64_t k);
+
+/* Load-time repack of Q8_0 weights into the matrix-core operand form
+ * ([BACK] 9.7's packed RHS): every code is split exactly as q = 16h + l with
+ * l in [-8, 7] and h in [-8, 8] (both e3m2 values).  Layout, for 128-row
+ * tiles t (rows past n are zero) and blocks b, chunk c = t*(k/32) + b: the
+ * codes first, 6144 B per chunk at 6144*c -- the six dwords of e3m2 codes of
+ * h for row r at 16*r (dwords 0..3) and 2048 + 8*r (dwords 4..5), the same
+ * for l at 3072 + 16*r and 5120 + 8*r, element e at bits 6e -- then the
+ * binary16 d of row r at byte 2*(128*c + r) of the scale region.  Lossless.
+ * w: block_q8_0[n][k/32]; wp: qll_q8_0_repacked_bytes(n, k) bytes, written
+ * in full.  k % 32 == 0. */
+int qll_q8_0_repack(const void *w, void *wp, int64_t n, int64_t k, void *stream);
+
+/* Prefill GEMM on repacked Q8_0 weights: Y[m][n] = X.W^T with the per-block
+ * arithmetic above, the exact block sum taken by two 6-bit block-scaled MFMAs
+ * (16 h_w and l_w against 16 h_x + l_x).  wp: the output of qll_q8_0_repack;
+ * xq: block_q8_0[m][k/32]; y: float[m][n]; k % 32 == 0, m >= 1.  ws/ws_bytes:
+ * at least qll_workspace_bytes(QLL_OP_Q8_0_REPACKED_GEMM, m, n, k) bytes
+ * (prepared activations, then split-k partials); contents on return are
+ * unspecified. */
+int qll_q8_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                                 size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------- f32 */

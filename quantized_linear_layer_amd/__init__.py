@@ -19,6 +19,7 @@ QLL_OP_SGEMM = 1
 QLL_OP_Q4_0_Q8_0_GEMM = 2
 QLL_OP_TERNARY_GEMM = 3
 QLL_OP_Q4_0_REPACKED_GEMM = 4
+QLL_OP_Q8_0_REPACKED_GEMM = 5
 
 Q4_0_BLOCK_BYTES = 18
 Q8_0_BLOCK_BYTES = 34
@@ -50,6 +51,9 @@ def load(path=LIB_PATH):
         "qll_q4_0_q8_0_gemv_f32": [P, P, P, I, I, I, P],
         "qll_q4_0_repack": [P, P, I, I, P],
         "qll_q4_0_repacked_q8_0_gemm": [P, P, P, I, I, I, P, S, P],
+        "qll_q8_0_q8_0_gemv": [P, P, P, I, I, P],
+        "qll_q8_0_repack": [P, P, I, I, P],
+        "qll_q8_0_repacked_q8_0_gemm": [P, P, P, I, I, I, P, S, P],
         "qll_sgemm": [P, P, P, I, I, I, P, S, P],
         "qll_quantize_i8_rows": [P, P, P, P, I, I, P],
         "qll_ternary_gemv": [P, F, P, P, P, P, I, I, P],
@@ -63,6 +67,8 @@ def load(path=LIB_PATH):
     L.qll_workspace_bytes.restype = ctypes.c_size_t
     L.qll_q4_0_repacked_bytes.argtypes = [I, I]
     L.qll_q4_0_repacked_bytes.restype = ctypes.c_size_t
+    L.qll_q8_0_repacked_bytes.argtypes = [I, I]
+    L.qll_q8_0_repacked_bytes.restype = ctypes.c_size_t
     L.qll_status_string.argtypes = [ctypes.c_int]
     L.qll_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -167,6 +173,36 @@ def qll_q4_0_repacked_q8_0_gemm(wp, xq, y, m, n, k, ws=None, stream=None):
         wsp, wsb = _ws(ws, need)
     wp_need = qll_q4_0_repacked_bytes(n, k)
     _call("qll_q4_0_repacked_q8_0_gemm", _ptr(wp, wp_need if wp_need != 2 ** 64 - 1 else 0, "wp"),
+          _ptr(xq, m * (k // 32) * Q8_0_BLOCK_BYTES, "xq"), _ptr(y, m * n * 4, "y"), m, n, k, wsp, wsb,
+          _stream(stream))
+
+
+# ----------------------------------------------------------------- Q8_0 weights
+
+def qll_q8_0_q8_0_gemv(w, xq, y, n, k, stream=None):
+    _call("qll_q8_0_q8_0_gemv", _ptr(w, n * (k // 32) * Q8_0_BLOCK_BYTES, "w"),
+          _ptr(xq, (k // 32) * Q8_0_BLOCK_BYTES, "xq"), _ptr(y, n * 4, "y"), n, k, _stream(stream))
+
+
+def qll_q8_0_repacked_bytes(n, k):
+    return int(load().qll_q8_0_repacked_bytes(int(n), int(k)))
+
+
+def qll_q8_0_repack(w, wp, n, k, stream=None):
+    """Load-time repack of Q8_0 weight blocks into the matrix-core operand form."""
+    need = qll_q8_0_repacked_bytes(n, k)
+    _call("qll_q8_0_repack", _ptr(w, n * (k // 32) * Q8_0_BLOCK_BYTES, "w"),
+          _ptr(wp, need if need != 2 ** 64 - 1 else 0, "wp"), n, k, _stream(stream))
+
+
+def qll_q8_0_repacked_q8_0_gemm(wp, xq, y, m, n, k, ws=None, stream=None):
+    need = qll_workspace_bytes(QLL_OP_Q8_0_REPACKED_GEMM, m, n, k)
+    if need == 2 ** 64 - 1:
+        wsp, wsb = None, 0
+    else:
+        wsp, wsb = _ws(ws, need)
+    wp_need = qll_q8_0_repacked_bytes(n, k)
+    _call("qll_q8_0_repacked_q8_0_gemm", _ptr(wp, wp_need if wp_need != 2 ** 64 - 1 else 0, "wp"),
           _ptr(xq, m * (k // 32) * Q8_0_BLOCK_BYTES, "xq"), _ptr(y, m * n * 4, "y"), m, n, k, wsp, wsb,
           _stream(stream))
 

@@ -97,6 +97,7 @@ size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k)
             return SIZE_MAX;
         return 0;
     case QLL_OP_Q4_0_REPACKED_GEMM:
+    case QLL_OP_Q8_0_REPACKED_GEMM:
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
             return SIZE_MAX;
         return q4_0_packed_gemm_workspace(m, n, k);
@@ -237,6 +238,58 @@ int qll_q4_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_
     if (int rc = check_device())
         return rc;
     return launched(launch_q4_0_packed_gemm(static_cast<const uint8_t *>(wp), static_cast<const uint8_t *>(xq), y, m,
+                                            n, k, ws, as_stream(stream)));
+}
+
+int qll_q8_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64_t k, void *stream)
+{
+    if (!w || !xq || !y)
+        return QLL_ERR_NULL;
+    if (!dims_ok(n, k) || k % 32 != 0 || k > kMaxKQ4Gemv)
+        return QLL_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(xq) || !aligned16(y))
+        return QLL_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    return launched(launch_q8_0_q8_0_gemv(static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(xq), y, n,
+                                          k, as_stream(stream)));
+}
+
+size_t qll_q8_0_repacked_bytes(int64_t n, int64_t k)
+{
+    if (!dims_ok(n, k) || k % 32 != 0)
+        return SIZE_MAX;
+    return q8_0_repacked_bytes(n, k);
+}
+
+int qll_q8_0_repack(const void *w, void *wp, int64_t n, int64_t k, void *stream)
+{
+    if (!w || !wp)
+        return QLL_ERR_NULL;
+    if (!dims_ok(n, k) || k % 32 != 0)
+        return QLL_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(wp))
+        return QLL_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    return launched(launch_q8_0_repack(static_cast<const uint8_t *>(w), static_cast<uint8_t *>(wp), n, k,
+                                       as_stream(stream)));
+}
+
+int qll_q8_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
+                                size_t ws_bytes, void *stream)
+{
+    if (!wp || !xq || !y || !ws)
+        return QLL_ERR_NULL;
+    if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
+        return QLL_ERR_SHAPE;
+    if (!aligned16(wp) || !aligned16(xq) || !aligned16(y) || !aligned16(ws))
+        return QLL_ERR_ALIGN;
+    if (ws_bytes < q4_0_packed_gemm_workspace(m, n, k))
+        return QLL_ERR_WORKSPACE;
+    if (int rc = check_device())
+        return rc;
+    return launched(launch_q8_0_packed_gemm(static_cast<const uint8_t *>(wp), static_cast<const uint8_t *>(xq), y, m,
                                             n, k, ws, as_stream(stream)));
 }
 

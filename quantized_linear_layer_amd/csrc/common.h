@@ -105,11 +105,17 @@ hipError_t launch_q4_0_q8_0_gemv_m(const uint8_t *w, const uint8_t *xq, float *y
 hipError_t launch_q4_0_q8_0_gemv_f32(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
                                      hipStream_t s);
 size_t q4_0_q8_0_gemm_workspace(int64_t m, int64_t n, int64_t k);
+// Decode GEMV with Q8_0 weights.
+hipError_t launch_q8_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int64_t k, hipStream_t s);
 // Load-time repack of Q4_0 weights and the GEMM on them (6-bit matrix-core path).
 size_t q4_0_repacked_bytes(int64_t n, int64_t k);
 hipError_t launch_q4_0_repack(const uint8_t *w, uint8_t *wp, int64_t n, int64_t k, hipStream_t s);
 size_t q4_0_packed_gemm_workspace(int64_t m, int64_t n, int64_t k);
 hipError_t launch_q4_0_packed_gemm(const uint8_t *wp, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
+                                   void *ws, hipStream_t s);
+size_t q8_0_repacked_bytes(int64_t n, int64_t k);
+hipError_t launch_q8_0_repack(const uint8_t *w, uint8_t *wp, int64_t n, int64_t k, hipStream_t s);
+hipError_t launch_q8_0_packed_gemm(const uint8_t *wp, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                    void *ws, hipStream_t s);
 hipError_t launch_sgemv(const float *x, const float *b, float *c, int64_t n, int64_t k, float *ws, hipStream_t s);
 size_t sgemv_workspace(int64_t n, int64_t k);

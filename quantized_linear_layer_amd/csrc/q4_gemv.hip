@@ -370,6 +370,206 @@ hipError_t launch_q4_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, 
     return launch_pair<false>(w, xq, y, n, nb, s);
 }
 
+// ------------------------------------------------------------------ Q8_0 weights
+// Decode GEMV with the weights quantized to Q8_0 blocks as well (Fucina
+// reference "Backends", 9.7: a Q8_0-quantized right-hand side against the
+// per-call Q8_0 activation): for each row j and block b
+//     sumi = sum_t q_w * q_x            exact int32 (no offset: codes are signed)
+//     y_j += f32(d_w) * f32(d_x) * sumi f32
+// Same structure as the Q4_0 kernel above: the activation staged once per
+// workgroup in LDS, L lanes per row, a lane's unit a PAIR of 34-byte blocks
+// (68 bytes = 17 dwords, dword aligned when the row's block count is even:
+// four dwordx4 loads and one dword load, every byte used) or, for an odd
+// block count, one block through a 9-dword window.
+
+template <int U>
+struct Q8wRaw {
+    uint32_t w[U][17];
+};
+
+__device__ __forceinline__ void load_q8w_pair(const uint8_t *p, uint32_t w[17])
+{
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        const u32x4 v = load4_a4(p + 16 * c);
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            w[4 * c + e] = v[e];
+    }
+    w[16] = *reinterpret_cast<const uint32_t *>(p + 64);
+}
+
+// One Q8_0 block at byte offset o (o % 4 is 0 or 2) of `base`: the nine
+// dwords from o - (o & 3), except that for o % 4 == 0 the ninth is replaced by
+// the block's last two bytes (the dword would reach past the block, and past
+// the buffer for its last block).
+__device__ __forceinline__ void load_q8w_single(const uint8_t *base, int64_t o, uint32_t w[17])
+{
+    const uint8_t *p = base + (o & ~(int64_t)3);
+    const u32x4 a = load4_a4(p), b = load4_a4(p + 16);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        w[e] = a[e];
+        w[4 + e] = b[e];
+    }
+    w[8] = (o & 3) ? *reinterpret_cast<const uint32_t *>(p + 32)
+                   : (uint32_t)*reinterpret_cast<const uint16_t *>(base + o + 32);
+}
+
+__device__ __forceinline__ float q8w_block_dot(uint32_t dbits, const uint32_t qs[8], const ActLds &a, int b)
+{
+    const u32x4 xlo = a.qs[2 * b], xhi = a.qs[2 * b + 1];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        s = sdot4(qs[i], xlo[i], s);
+        s = sdot4(qs[4 + i], xhi[i], s);
+    }
+    return half_bits_to_float(dbits) * a.dx[b] * (float)s;
+}
+
+template <int L, int U, bool PAIR>
+__device__ __forceinline__ void q8w_load(const uint8_t *__restrict__ w, int64_t row, int64_t n, int64_t row_bytes,
+                                         int nu, int ubase, int r, Q8wRaw<U> &raw)
+{
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        // out-of-range units load the first unit of row 0 (masked later), so
+        // the loads stay unconditional
+        int u = ubase + r + i * L;
+        const bool ok = row < n && u < nu;
+        const int64_t rr = ok ? row : 0;
+        u = ok ? u : 0;
+        if (PAIR)
+            load_q8w_pair(w + rr * row_bytes + (int64_t)u * 68, raw.w[i]);
+        else
+            load_q8w_single(w, rr * row_bytes + (int64_t)u * 34, raw.w[i]);
+    }
+}
+
+template <int L, int U, bool PAIR>
+__device__ __forceinline__ float q8w_compute(const Q8wRaw<U> &raw, int64_t row, int64_t n, int64_t row_bytes, int nu,
+                                             int ubase, int r, const ActLds &act)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        const int u = ubase + r + i * L;
+        if (row < n && u < nu) {
+            const uint32_t *w = raw.w[i];
+            uint32_t q[8];
+            if (PAIR) {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    q[e] = funnel(w[e + 1], w[e], 16); // block A: bytes 2..33
+                acc += q8w_block_dot(w[0] & 0xffffu, q, act, 2 * u);
+                acc += q8w_block_dot(w[8] >> 16, w + 9, act, 2 * u + 1); // block B: d at 34, codes from 36
+            } else {
+                const bool odd = ((row * row_bytes + (int64_t)u * 34) & 3) != 0;
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    q[e] = odd ? w[e + 1] : funnel(w[e + 1], w[e], 16);
+                acc += q8w_block_dot(odd ? (w[0] >> 16) : (w[0] & 0xffffu), q, act, u);
+            }
+        }
+    }
+    return acc;
+}
+
+// Persistent over work items exactly as q4_0_q8_0_gemv_kernel (same staging,
+// same ordering of the activation and weight loads).
+template <int L, int U, bool PAIR>
+__global__ __launch_bounds__(kGemvThreads) void q8_0_q8_0_gemv_kernel(const uint8_t *__restrict__ w,
+                                                                      const uint8_t *xq, float *__restrict__ y,
+                                                                      int64_t n, int nb)
+{
+    extern __shared__ u32x4 smem[];
+    constexpr int R = 64 / L;
+    constexpr int WAVES = kGemvThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / L, r = lane % L;
+    const int nu = PAIR ? nb / 2 : nb;
+    const int chunk_units = U * L;
+    const int chunks = (nu + chunk_units - 1) / chunk_units;
+    const int64_t row_bytes = (int64_t)nb * 34;
+    const int64_t n_groups = (n + R - 1) / R;
+    const int64_t stride = (int64_t)gridDim.x * WAVES;
+
+    ActRaw araw;
+    stage_q8_load(xq, nb, araw);
+    asm volatile("" ::: "memory");
+
+    int64_t grp = (int64_t)blockIdx.x * WAVES + wave;
+    int c = 0;
+    Q8wRaw<U> cur;
+    q8w_load<L, U, PAIR>(w, grp * R + g, n, row_bytes, nu, 0, r, cur);
+
+    const ActLds act = stage_q8_finish(xq, nb, araw, smem);
+
+    float acc = 0.0f;
+    while (grp < n_groups) {
+        int64_t grp2 = grp;
+        int c2 = c + 1;
+        if (c2 == chunks) {
+            c2 = 0;
+            grp2 += stride;
+        }
+        Q8wRaw<U> nxt;
+        if (grp2 < n_groups)
+            q8w_load<L, U, PAIR>(w, grp2 * R + g, n, row_bytes, nu, c2 * chunk_units, r, nxt);
+        const int64_t row = grp * R + g;
+        acc += q8w_compute<L, U, PAIR>(cur, row, n, row_bytes, nu, c * chunk_units, r, act);
+        if (c == chunks - 1) {
+#pragma unroll
+            for (int off = L / 2; off > 0; off >>= 1)
+                acc += __shfl_xor(acc, off);
+            if (row < n && r == 0)
+                y[row] = acc;
+            acc = 0.0f;
+        }
+        cur = nxt;
+        grp = grp2;
+        c = c2;
+    }
+}
+
+template <int L, int U, bool PAIR>
+static hipError_t launch_q8w_l(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int nb, hipStream_t s)
+{
+    constexpr int R = 64 / L;
+    const int64_t groups = (n + R - 1) / R;
+    int64_t grid = (groups + kGemvThreads / 64 - 1) / (kGemvThreads / 64);
+    if (grid > 0x7fffffff)
+        grid = 0x7fffffff;
+    hipLaunchKernelGGL((q8_0_q8_0_gemv_kernel<L, U, PAIR>), dim3((unsigned)grid), dim3(kGemvThreads),
+                       q4_gemv_lds_bytes(nb), s, w, xq, y, n, nb);
+    return hipGetLastError();
+}
+
+// Lanes per row: enough for one pass over the row at two units per lane
+// (a 68-byte unit is about twice a Q4_0 pair, so two units per lane carry the
+// bytes that four Q4_0 units do), 64 lanes for longer rows.
+template <bool PAIR>
+static hipError_t launch_q8w_pair(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int nb, hipStream_t s)
+{
+    const int nu = PAIR ? nb / 2 : nb;
+    if (nu > 64)
+        return launch_q8w_l<64, 2, PAIR>(w, xq, y, n, nb, s);
+    if (nu > 32)
+        return launch_q8w_l<32, 2, PAIR>(w, xq, y, n, nb, s);
+    if (nu > 16)
+        return launch_q8w_l<16, 2, PAIR>(w, xq, y, n, nb, s);
+    return launch_q8w_l<8, 2, PAIR>(w, xq, y, n, nb, s);
+}
+
+hipError_t launch_q8_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int64_t k, hipStream_t s)
+{
+    const int nb = (int)(k / 32);
+    if (nb % 2 == 0)
+        return launch_q8w_pair<true>(w, xq, y, n, nb, s);
+    return launch_q8w_pair<false>(w, xq, y, n, nb, s);
+}
+
 // ------------------------------------------------------------------ small m
 // Y[i][j] for 1 <= m <= 8 activation rows (speculative or batched decode):
 // every weight unit is loaded once, as in the m = 1 kernel, and dotted with

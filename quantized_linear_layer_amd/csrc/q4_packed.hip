@@ -197,9 +197,19 @@ __global__ __launch_bounds__(256) void q4p_prep_kernel(const uint8_t *__restrict
 
 // ------------------------------------------------------------------ GEMM
 
+// Weight formats of the packed GEMM: Q4_0 (one six-dword code group per row
+// and block: w = q - 8) or Q8_0 (two: w = 16 h + l, the split the
+// activations get).
+template <bool Q8W>
+struct PFmt {
+    static constexpr int kWChunk = Q8W ? 2 * kPWChunk : kPWChunk; // weight code bytes per chunk
+    static constexpr int kDma = Q8W ? 7 : 5;                      // global -> LDS loads per wave and stage
+};
+
+template <bool Q8W>
 struct Q4pLds {
     uint8_t xs[PKB][kPXChunk]; // h planes then l planes of each block
-    uint8_t wq[PKB][kPWChunk];
+    uint8_t wq[PKB][PFmt<Q8W>::kWChunk];
     uint16_t dx[PKB][PBM];
     uint16_t dw[PKB][PBN];
 };
@@ -214,9 +224,8 @@ __device__ __forceinline__ void q4p_dma16(const void *base, uint32_t off, const 
                  : "memory", "m0");
 }
 
-constexpr int kPDmaPerStage = 5;
-
-// The loads of the stage holding blocks b and b + 1, five per wave:
+// The loads of the stage holding blocks b and b + 1.  Q4_0 weights, five
+// per wave:
 //   * activations: the two blocks' chunks are adjacent (12 KB), three 1 KB
 //     loads per wave;
 //   * weight codes: the two chunks (6 KB) as six 1 KB loads, two each for
@@ -224,9 +233,15 @@ constexpr int kPDmaPerStage = 5;
 //     loads block nb - 1 (its activations are zero, so it adds nothing);
 //   * wave 2, lanes 0..31: the d_x of both blocks (512 adjacent bytes);
 //     wave 3, lanes 0..31: d_w of both blocks (clamped as above).
+// Q8_0 weights, seven per wave: activations as above, the weight codes
+// (12 KB) as three 1 KB loads per wave, and d_x (waves 0, 1) and d_w
+// (waves 2, 3) one block per wave on lanes 0..15.
+template <bool Q8W>
 __device__ __forceinline__ void q4p_load_stage(const uint8_t *__restrict__ wcodes, const uint16_t *__restrict__ dws,
-                                               const Q4pPrep &p, int64_t mt, int64_t nt, int nb, int b, Q4pLds &s)
+                                               const Q4pPrep &p, int64_t mt, int64_t nt, int nb, int b,
+                                               Q4pLds<Q8W> &s)
 {
+    constexpr int WC = PFmt<Q8W>::kWChunk;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lo = 16u * (uint32_t)lane;
     const uint8_t *xb = p.x + (mt * p.nbp + b) * kPXChunk;
@@ -237,24 +252,43 @@ __device__ __forceinline__ void q4p_load_stage(const uint8_t *__restrict__ wcode
         const int region = 3 * wave + j;
         q4p_dma16(xb + region * 1024, lo, xs + region * 1024);
     }
-    const uint8_t *wt = wcodes + nt * nb * (int64_t)kPWChunk;
-    const int nw = wave < 2 ? 2 : 1;
+    const uint8_t *wt = wcodes + nt * nb * (int64_t)WC;
+    const uint8_t *dwt = reinterpret_cast<const uint8_t *>(dws) + nt * nb * (int64_t)kPSChunk;
+    if (Q8W) {
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        if (j < nw) {
-            const int region = wave < 2 ? 2 * wave + j : 2 + wave;
-            const int kb = region / 3, part = region % 3;
+        for (int j = 0; j < 3; j++) {
+            const int region = 3 * wave + j;
+            const int kb = region / 6, part = region % 6;
             const int bb = b + kb < nb ? b + kb : nb - 1;
-            q4p_dma16(wt + (int64_t)bb * kPWChunk + part * 1024, lo, wq + kb * kPWChunk + part * 1024);
+            q4p_dma16(wt + (int64_t)bb * WC + part * 1024, lo, wq + kb * WC + part * 1024);
         }
-    }
-    if (wave == 2 && lane < 32) {
-        q4p_dma16(reinterpret_cast<const uint8_t *>(p.dx) + (mt * p.nbp + b) * kPSChunk, lo,
-                  (const QLL_LDS void *)&s.dx[0][0]);
-    } else if (wave == 3 && lane < 32) {
-        const int bb = b + (lane >> 4) < nb ? b + (lane >> 4) : nb - 1;
-        q4p_dma16(reinterpret_cast<const uint8_t *>(dws) + nt * nb * (int64_t)kPSChunk,
-                  (uint32_t)bb * kPSChunk + 16u * (uint32_t)(lane & 15), (const QLL_LDS void *)&s.dw[0][0]);
+        if (lane < 16) {
+            if (wave < 2) {
+                q4p_dma16(reinterpret_cast<const uint8_t *>(p.dx) + (mt * p.nbp + b + wave) * kPSChunk, lo,
+                          (const QLL_LDS void *)&s.dx[wave][0]);
+            } else {
+                const int bb = b + wave - 2 < nb ? b + wave - 2 : nb - 1;
+                q4p_dma16(dwt + (int64_t)bb * kPSChunk, lo, (const QLL_LDS void *)&s.dw[wave - 2][0]);
+            }
+        }
+    } else {
+        const int nw = wave < 2 ? 2 : 1;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            if (j < nw) {
+                const int region = wave < 2 ? 2 * wave + j : 2 + wave;
+                const int kb = region / 3, part = region % 3;
+                const int bb = b + kb < nb ? b + kb : nb - 1;
+                q4p_dma16(wt + (int64_t)bb * WC + part * 1024, lo, wq + kb * WC + part * 1024);
+            }
+        }
+        if (wave == 2 && lane < 32) {
+            q4p_dma16(reinterpret_cast<const uint8_t *>(p.dx) + (mt * p.nbp + b) * kPSChunk, lo,
+                      (const QLL_LDS void *)&s.dx[0][0]);
+        } else if (wave == 3 && lane < 32) {
+            const int bb = b + (lane >> 4) < nb ? b + (lane >> 4) : nb - 1;
+            q4p_dma16(dwt, (uint32_t)bb * kPSChunk + 16u * (uint32_t)(lane & 15), (const QLL_LDS void *)&s.dw[0][0]);
+        }
     }
 }
 
@@ -272,16 +306,18 @@ struct Q4pLaneOff {
     uint32_t dx, dw;
 };
 
+template <bool Q8W>
 __device__ __forceinline__ Q4pLaneOff q4p_lane_offsets(int wm, int wn, int lane)
 {
+    typedef Q4pLds<Q8W> Lds;
     const int lr = lane & 31, lh = lane >> 5;
     Q4pLaneOff o;
-    o.x0 = (uint32_t)(offsetof(Q4pLds, xs) + lh * 3072 + 16 * (wm + lr));
-    o.x1 = (uint32_t)(offsetof(Q4pLds, xs) + lh * 3072 + 2048 + 8 * (wm + lr));
-    o.w0 = (uint32_t)(offsetof(Q4pLds, wq) + 16 * (wn + lr));
-    o.w1 = (uint32_t)(offsetof(Q4pLds, wq) + 2048 + 8 * (wn + lr));
-    o.dx = (uint32_t)(offsetof(Q4pLds, dx) + 2 * (wm + lr));
-    o.dw = (uint32_t)(offsetof(Q4pLds, dw) + 2 * (wn + lr));
+    o.x0 = (uint32_t)(offsetof(Lds, xs) + lh * 3072 + 16 * (wm + lr));
+    o.x1 = (uint32_t)(offsetof(Lds, xs) + lh * 3072 + 2048 + 8 * (wm + lr));
+    o.w0 = (uint32_t)(offsetof(Lds, wq) + 16 * (wn + lr));
+    o.w1 = (uint32_t)(offsetof(Lds, wq) + 2048 + 8 * (wn + lr));
+    o.dx = (uint32_t)(offsetof(Lds, dx) + 2 * (wm + lr));
+    o.dw = (uint32_t)(offsetof(Lds, dw) + 2 * (wn + lr));
     asm volatile("" : "+v"(o.x0), "+v"(o.x1), "+v"(o.w0), "+v"(o.w1), "+v"(o.dx), "+v"(o.dw));
     return o;
 }
@@ -292,22 +328,29 @@ __device__ __forceinline__ Q4pLaneOff q4p_lane_offsets(int wm, int wn, int lane)
 // scale 1) of its row, and the same 32 weight codes (B) in both halves.
 // The scale tile takes {d_x, 0, 0, 0} and {d_w, 0, 0, 0} in both lane
 // halves, so S = 2 d_x d_w exactly; the outputs are halved at the end.
+template <bool Q8W>
 __device__ __forceinline__ void q4p_compute(const QLL_LDS char *base, const Q4pLaneOff &o, uint32_t scale_a,
                                             f32x16 acc[2][2])
 {
+    constexpr int WC = PFmt<Q8W>::kWChunk;
 #pragma unroll
     for (int kb = 0; kb < PKB; kb++) {
         __builtin_amdgcn_sched_barrier(0);
-        i32x8 a[2], bm[2];
+        i32x8 a[2], bm[2], bl[2];
         f16x4 sa[2], sb[2];
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             const u32x4 x0 = q4p_lds<u32x4>(base, o.x0 + kb * kPXChunk + 512 * i);
             const u32x2 x1 = q4p_lds<u32x2>(base, o.x1 + kb * kPXChunk + 256 * i);
             a[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], 0, 0};
-            const u32x4 w0 = q4p_lds<u32x4>(base, o.w0 + kb * kPWChunk + 512 * i);
-            const u32x2 w1 = q4p_lds<u32x2>(base, o.w1 + kb * kPWChunk + 256 * i);
+            const u32x4 w0 = q4p_lds<u32x4>(base, o.w0 + kb * WC + 512 * i);
+            const u32x2 w1 = q4p_lds<u32x2>(base, o.w1 + kb * WC + 256 * i);
             bm[i] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], 0, 0};
+            if (Q8W) { // the l half of the weight codes, 3072 bytes further
+                const u32x4 v0 = q4p_lds<u32x4>(base, o.w0 + kb * WC + 3072 + 512 * i);
+                const u32x2 v1 = q4p_lds<u32x2>(base, o.w1 + kb * WC + 3072 + 256 * i);
+                bl[i] = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3], (int)v1[0], (int)v1[1], 0, 0};
+            }
             const uint32_t dxb = q4p_lds<uint16_t>(base, o.dx + kb * 2 * PBM + 64 * i);
             const uint32_t dwb = q4p_lds<uint16_t>(base, o.dw + kb * 2 * PBN + 64 * i);
             sa[i] = __builtin_bit_cast(f16x4, u32x2{dxb, 0u});
@@ -321,8 +364,15 @@ __device__ __forceinline__ void q4p_compute(const QLL_LDS char *base, const Q4pL
         for (int t = 0; t <= 4; t++) {
             if (t < 4) {
                 const int i = t >> 1, j = t & 1;
-                p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bm[j], f32x16{}, 3, 3, 0, scale_a, 0,
-                                                                          kE8M0One);
+                if (Q8W) { // sum 16 h_w (16 h_x + l_x) + l_w (16 h_x + l_x)
+                    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bm[j], f32x16{}, 3, 3, 0, scale_a,
+                                                                              0, kE8M0Sixteen);
+                    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bl[j], p[t & 1], 3, 3, 0, scale_a,
+                                                                              0, kE8M0One);
+                } else {
+                    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bm[j], f32x16{}, 3, 3, 0, scale_a,
+                                                                              0, kE8M0One);
+                }
                 sc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], f32x16{}, 0, 0, 0);
             }
             if (t > 0) {
@@ -332,10 +382,11 @@ __device__ __forceinline__ void q4p_compute(const QLL_LDS char *base, const Q4pL
                     acc[i][j][v] = fmaf(sc[u & 1][v], p[u & 1][v], acc[i][j][v]);
             }
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // tile 0
+        constexpr int NM = Q8W ? 3 : 2; // MFMAs per tile
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0); // tile 0
 #pragma unroll
         for (int t = 1; t < 4; t++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
@@ -368,12 +419,14 @@ __device__ __forceinline__ void q4p_sync()
     asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(kPThreads) void q4_0_packed_gemm_kernel(const uint8_t *__restrict__ wcodes,
-                                                                     const uint16_t *__restrict__ dws, Q4pPrep prep,
-                                                                     float *__restrict__ y, int64_t m, int64_t n,
-                                                                     int nb, int per_split)
+template <bool Q8W>
+__global__ __launch_bounds__(kPThreads) void packed_gemm_kernel(const uint8_t *__restrict__ wcodes,
+                                                                const uint16_t *__restrict__ dws, Q4pPrep prep,
+                                                                float *__restrict__ y, int64_t m, int64_t n, int nb,
+                                                                int per_split)
 {
-    __shared__ Q4pLds lds[PNBUF];
+    constexpr int DMA = PFmt<Q8W>::kDma;
+    __shared__ Q4pLds<Q8W> lds[PNBUF];
     int64_t m_tile, n_tile;
     q4p_tile(prep.mp / PBM, (n + PBN - 1) / PBN, m_tile, n_tile);
     const int64_t m0 = m_tile * PBM, n0 = n_tile * PBN;
@@ -390,22 +443,22 @@ __global__ __launch_bounds__(kPThreads) void q4_0_packed_gemm_kernel(const uint8
             acc[i][j] = f32x16{};
 
     const int nstages = per_split / PKB;
-    const Q4pLaneOff lo = q4p_lane_offsets(wm, wn, lane);
+    const Q4pLaneOff lo = q4p_lane_offsets<Q8W>(wm, wn, lane);
     const uint32_t scale_a = lane < 32 ? kE8M0Sixteen : kE8M0One;
 
     // Stage st is computed from buffer st % 3; the loads of stage st + 2 go
     // out at its start into the buffer that stage st - 1 used (every wave
     // left it at the barrier that ended stage st - 1).  Stages past the range
     // load padding and are never computed.
-    q4p_load_stage(wcodes, dws, prep, m_tile, n_tile, nb, b_begin, lds[0]);
-    q4p_load_stage(wcodes, dws, prep, m_tile, n_tile, nb, b_begin + PKB, lds[1]);
-    q4p_sync<kPDmaPerStage>();
+    q4p_load_stage<Q8W>(wcodes, dws, prep, m_tile, n_tile, nb, b_begin, lds[0]);
+    q4p_load_stage<Q8W>(wcodes, dws, prep, m_tile, n_tile, nb, b_begin + PKB, lds[1]);
+    q4p_sync<DMA>();
     int cur = 0;
     for (int st = 0; st < nstages; st++) {
         const int nx2 = cur == 0 ? 2 : cur - 1;
-        q4p_load_stage(wcodes, dws, prep, m_tile, n_tile, nb, b_begin + (st + 2) * PKB, lds[nx2]);
-        q4p_compute((const QLL_LDS char *)&lds[cur], lo, scale_a, acc);
-        q4p_sync<kPDmaPerStage>();
+        q4p_load_stage<Q8W>(wcodes, dws, prep, m_tile, n_tile, nb, b_begin + (st + 2) * PKB, lds[nx2]);
+        q4p_compute<Q8W>((const QLL_LDS char *)&lds[cur], lo, scale_a, acc);
+        q4p_sync<DMA>();
         cur = cur == 2 ? 0 : cur + 1;
     }
     // no load may still be writing this workgroup's LDS when it ends
@@ -482,8 +535,9 @@ size_t q4_0_packed_gemm_workspace(int64_t m, int64_t n, int64_t k)
     return q4p_plan(m, n, k).total;
 }
 
-hipError_t launch_q4_0_packed_gemm(const uint8_t *wp, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
-                                   void *ws, hipStream_t s)
+template <bool Q8W>
+static hipError_t launch_packed_gemm(const uint8_t *wp, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
+                                     void *ws, hipStream_t s)
 {
     const Q4pPlan plan = q4p_plan(m, n, k);
     uint8_t *base = static_cast<uint8_t *>(ws);
@@ -500,10 +554,10 @@ hipError_t launch_q4_0_packed_gemm(const uint8_t *wp, const uint8_t *xq, float *
     if (e != hipSuccess)
         return e;
     const int64_t nt = (n + PBN - 1) / PBN;
-    const uint16_t *dws = reinterpret_cast<const uint16_t *>(wp + (size_t)nt * nb * kPWChunk);
+    const uint16_t *dws = reinterpret_cast<const uint16_t *>(wp + (size_t)nt * nb * PFmt<Q8W>::kWChunk);
     const int64_t tiles = nt * (plan.mp / PBM);
     float *out = plan.splits > 1 ? reinterpret_cast<float *>(base) : y;
-    hipLaunchKernelGGL(q4_0_packed_gemm_kernel, dim3((unsigned)tiles, (unsigned)plan.splits), dim3(kPThreads), 0, s,
+    hipLaunchKernelGGL(packed_gemm_kernel<Q8W>, dim3((unsigned)tiles, (unsigned)plan.splits), dim3(kPThreads), 0, s,
                        wp, dws, prep, out, m, n, nb, plan.per_split);
     e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
@@ -512,6 +566,46 @@ hipError_t launch_q4_0_packed_gemm(const uint8_t *wp, const uint8_t *xq, float *
     hipLaunchKernelGGL(q4p_sum_splits_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, out, y, count,
                        plan.splits);
     return hipGetLastError();
+}
+
+hipError_t launch_q4_0_packed_gemm(const uint8_t *wp, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
+                                   void *ws, hipStream_t s)
+{
+    return launch_packed_gemm<false>(wp, xq, y, m, n, k, ws, s);
+}
+
+// ------------------------------------------------------------------ Q8_0 weights
+
+// Q8_0 weights W[n][k/32] repacked exactly as the prepass prepares activation
+// rows: the same chunks over 128-row tiles (h and l code groups of each
+// row, 6144 bytes per chunk), then d_w, 128 binary16 per chunk.
+size_t q8_0_repacked_bytes(int64_t n, int64_t k)
+{
+    const int64_t nt = (n + PBN - 1) / PBN;
+    return (size_t)nt * (size_t)(k / 32) * (2 * kPWChunk + kPSChunk);
+}
+
+hipError_t launch_q8_0_repack(const uint8_t *w, uint8_t *wp, int64_t n, int64_t k, hipStream_t s)
+{
+    const int nb = (int)(k / 32);
+    const int64_t nt = (n + PBN - 1) / PBN;
+    Q4pPrep p;
+    p.x = wp;
+    p.dx = reinterpret_cast<uint16_t *>(wp + (size_t)nt * nb * (2 * kPWChunk));
+    p.mp = nt * PBN;
+    p.nbp = nb;
+    const int64_t total = p.mp * nb;
+    const int64_t grid = (total + 255) / 256;
+    if (grid > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(q4p_prep_kernel, dim3((unsigned)grid), dim3(256), 0, s, w, p, n, nb, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_q8_0_packed_gemm(const uint8_t *wp, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
+                                   void *ws, hipStream_t s)
+{
+    return launch_packed_gemm<true>(wp, xq, y, m, n, k, ws, s);
 }
 
 } // namespace qll

@@ -115,6 +115,25 @@ def test_q4_errors(L):
     assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 64, GOOD, 16, None) == WORKSPACE
 
 
+def test_q8w_errors(L):
+    assert L.qll_q8_0_q8_0_gemv(GOOD, NUL, GOOD, 8, 64, None) == NULL
+    assert L.qll_q8_0_q8_0_gemv(GOOD, GOOD, GOOD, 8, 65, None) == SHAPE
+    assert L.qll_q8_0_q8_0_gemv(GOOD, GOOD, GOOD, 8, 49152 + 32, None) == SHAPE
+    assert L.qll_q8_0_q8_0_gemv(MIS, GOOD, GOOD, 8, 64, None) == ALIGN
+    assert L.qll_q8_0_repack(GOOD, NUL, 8, 64, None) == NULL
+    assert L.qll_q8_0_repack(GOOD, GOOD, 8, 40, None) == SHAPE
+    assert L.qll_q8_0_repack(MIS, GOOD, 8, 64, None) == ALIGN
+    assert L.qll_q8_0_repacked_q8_0_gemm(GOOD, GOOD, NUL, 4, 8, 64, GOOD, 2 ** 40, None) == NULL
+    assert L.qll_q8_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 0, 8, 64, GOOD, 2 ** 40, None) == SHAPE
+    assert L.qll_q8_0_repacked_q8_0_gemm(GOOD, MIS, GOOD, 4, 8, 64, GOOD, 2 ** 40, None) == ALIGN
+    assert L.qll_q8_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 64, GOOD, 1, None) == WORKSPACE
+    assert qll.qll_q8_0_repacked_bytes(1, 32) == 6400
+    assert qll.qll_q8_0_repacked_bytes(130, 64) == 2 * 2 * 6400
+    assert qll.qll_q8_0_repacked_bytes(8, 40) == SIZE_MAX
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q8_0_REPACKED_GEMM, 512, 4096, 4096) == \
+        qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_REPACKED_GEMM, 512, 4096, 4096)
+
+
 def test_repacked_sizes(L):
     L.qll_q4_0_repacked_bytes.restype = ctypes.c_size_t
     assert qll.qll_q4_0_repacked_bytes(1, 32) == 3328
