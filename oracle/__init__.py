@@ -8,7 +8,8 @@ arithmetic is in oracle.c, where each routine cites the passage it follows:
 * llama.cpp visual guide lesson 31 "CPU backend", "How the quantized dot
   product works" -- the Q4_0 x Q8_0 block dot and the block_q8_0 layout;
 * Fucina course "Chapter 06 -- Going fast on CPUs", 6.4 -- the f32 GEMM
-  referee, here accumulated in f64;
+  referee, here accumulated in f64; 6.6 and "reduced precision" -- the
+  transposed-B (NT) orientation with f32, bf16 or f16 weights widened exactly;
 * Loom "Plan 9 SIMD Forward", "BitNet ternary MAD kernel" -- packed ternary
   weights, the ternary identity, per-row int8 activations;
 * Fucina reference "Backends", 9.7 -- per-call Q8_0 activation quantization
@@ -59,6 +60,8 @@ def load(path):
         "orc_q8_0_q8_0_block_sums": [_P, _P, _I, _I, _I, _P],
         "orc_sgemm": [_P, _P, _I, _I, _I, _P, _P],
         "orc_sgemm_sampled": [_P, _P, _I, _I, _I, _P, _P, _I, _P, _P],
+        "orc_gemm_nt": [_P, _P, ctypes.c_int, _I, _I, _I, _P, _P],
+        "orc_gemm_nt_sampled": [_P, _P, ctypes.c_int, _I, _I, _I, _P, _P, _I, _P, _P],
         "orc_pack_ternary": [_P, _P, _I, _I],
         "orc_unpack_ternary": [_P, _P, _I, _I],
         "orc_quantize_i8_rows": [_P, _P, _P, _P, _I, _I],
@@ -246,6 +249,41 @@ def sgemm_sampled(a, b, ii, jj, L=None):
     mag = np.empty(ii.size, np.float64)
     _check((L or lib()).orc_sgemm_sampled(_ptr(a), _ptr(b), m, n, k, _ptr(ii), _ptr(jj), ii.size,
                                           _ptr(c), _ptr(mag)), "sgemm_sampled")
+    return c, mag
+
+
+# --------------------------------------------------------------------------- NT (W stored [n][k])
+
+W_DTYPES = {"f32": (0, np.float32), "bf16": (1, np.uint16), "f16": (2, np.uint16)}
+
+
+def gemm_nt(a, w, wdtype, L=None):
+    """C = A.W^T with W [n][k] of dtype 'f32' (float32), 'bf16' or 'f16' (uint16
+    bit patterns); f64 C and mag = sum_p |a*w|."""
+    code, npdt = W_DTYPES[wdtype]
+    a = _c(a, np.float32)
+    w = _c(w, npdt)
+    m, k = a.shape
+    n, k2 = w.shape
+    assert k == k2
+    c = np.empty((m, n), np.float64)
+    mag = np.empty((m, n), np.float64)
+    _check((L or lib()).orc_gemm_nt(_ptr(a), _ptr(w), code, m, n, k, _ptr(c), _ptr(mag)), "gemm_nt")
+    return c, mag
+
+
+def gemm_nt_sampled(a, w, wdtype, ii, jj, L=None):
+    code, npdt = W_DTYPES[wdtype]
+    a = _c(a, np.float32)
+    w = _c(w, npdt)
+    m, k = a.shape
+    n = w.shape[0]
+    ii = _c(ii, np.int64)
+    jj = _c(jj, np.int64)
+    c = np.empty(ii.size, np.float64)
+    mag = np.empty(ii.size, np.float64)
+    _check((L or lib()).orc_gemm_nt_sampled(_ptr(a), _ptr(w), code, m, n, k, _ptr(ii), _ptr(jj), ii.size,
+                                            _ptr(c), _ptr(mag)), "gemm_nt_sampled")
     return c, mag
 
 

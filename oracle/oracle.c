@@ -446,6 +446,69 @@ int orc_sgemm_sampled(const float *a, const float *b, int64_t m, int64_t n, int6
 }
 
 /* ------------------------------------------------------------------------ */
+/* Transposed-B orientation, the linear layer's own [FAST] 6.6: W stored     */
+/* [n][k], C[i][j] = sum_p A[i][p] * W[j][p] -- one two-stream dot per       */
+/* output.  W is f32, bf16 or f16; bf16 and f16 weights are widened exactly   */
+/* ([FAST] "reduced precision": bf16 is the top 16 bits of an f32, widened    */
+/* by a 16-bit shift; f16 is widened once per load).  Accumulated in f64 in   */
+/* p order; mag = sum_p |A[i][p] * W[j][p]|.                                 */
+/* ------------------------------------------------------------------------ */
+
+enum { ORC_W_F32 = 0, ORC_W_BF16 = 1, ORC_W_F16 = 2 };
+
+static double widen_weight(const void *w, int wtype, int64_t idx)
+{
+    if (wtype == ORC_W_F32)
+        return (double)((const float *)w)[idx];
+    const uint16_t h = ((const uint16_t *)w)[idx];
+    if (wtype == ORC_W_BF16) {
+        uint32_t bits = (uint32_t)h << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return orc_half_to_double(h);
+}
+
+static void gemm_nt_one(const float *a, const void *w, int wtype, int64_t k, int64_t i, int64_t j, double *c,
+                        double *mag)
+{
+    double sum = 0.0, sum_abs = 0.0;
+    for (int64_t p = 0; p < k; p++) {
+        double prod = (double)a[i * k + p] * widen_weight(w, wtype, j * k + p);
+        sum += prod;
+        sum_abs += fabs(prod);
+    }
+    *c = sum;
+    *mag = sum_abs;
+}
+
+int orc_gemm_nt(const float *a, const void *w, int wtype, int64_t m, int64_t n, int64_t k, double *c, double *mag)
+{
+    if (m < 0 || n < 0 || k < 0 || wtype < ORC_W_F32 || wtype > ORC_W_F16)
+        return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; j++)
+        for (int64_t i = 0; i < m; i++)
+            gemm_nt_one(a, w, wtype, k, i, j, &c[i * n + j], &mag[i * n + j]);
+    return ORC_OK;
+}
+
+int orc_gemm_nt_sampled(const float *a, const void *w, int wtype, int64_t m, int64_t n, int64_t k,
+                        const int64_t *ii, const int64_t *jj, int64_t count, double *c, double *mag)
+{
+    if (m < 0 || n < 0 || k < 0 || wtype < ORC_W_F32 || wtype > ORC_W_F16)
+        return ORC_ERR_ARG;
+    for (int64_t s = 0; s < count; s++)
+        if (ii[s] < 0 || ii[s] >= m || jj[s] < 0 || jj[s] >= n)
+            return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < count; s++)
+        gemm_nt_one(a, w, wtype, k, ii[s], jj[s], &c[s], &mag[s]);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* BitNet ternary [LOOM].                                                    */
 /* ------------------------------------------------------------------------ */
 

@@ -359,6 +359,86 @@ def check_sgemm_exact(L):
     assert np.all(c == 37.0)
 
 
+# --------------------------------------------------------------------------- NT GEMM
+
+
+def np_bf16_widen(bits):
+    # bf16 is the upper half of an IEEE f32 (NaN patterns stay NaN)
+    with np.errstate(invalid="ignore"):
+        return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def np_f16_widen(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def _rand_w(rng, n, k, wdtype):
+    w32 = rng.uniform(-1, 1, (n, k)).astype(np.float32)
+    if wdtype == "f32":
+        return w32, w32.astype(np.float64)
+    if wdtype == "bf16":
+        bits = (w32.view(np.uint32) >> 16).astype(np.uint16)  # truncation: any bf16 pattern will do
+        return bits, np_bf16_widen(bits)
+    bits = w32.astype(np.float16).view(np.uint16)
+    return bits, np_f16_widen(bits)
+
+
+def check_gemm_nt_numpy(L):
+    rng = np.random.default_rng(51)
+    for wdtype in ("f32", "bf16", "f16"):
+        for m, n, k in ((1, 1, 1), (1, 37, 300), (7, 11, 13), (33, 17, 96)):
+            a = rng.uniform(-1, 1, (m, k)).astype(np.float32)
+            w, w64 = _rand_w(rng, n, k, wdtype)
+            c, mag = O.gemm_nt(a, w, wdtype, L=L)
+            a64 = a.astype(np.float64)
+            assert np.all(np.abs(c - a64 @ w64.T) <= 1e-12 * mag), wdtype
+            assert np.allclose(mag, np.abs(a64) @ np.abs(w64).T, rtol=1e-12, atol=0)
+            ii = rng.integers(0, m, 5)
+            jj = rng.integers(0, n, 5)
+            cs, ms = O.gemm_nt_sampled(a, w, wdtype, ii, jj, L=L)
+            assert np.array_equal(cs, c[ii, jj]) and np.array_equal(ms, mag[ii, jj])
+
+
+def check_gemm_nt_exact(L):
+    # identity weights give A back; small integers give exact integer products;
+    # NT with W equals NN with W^T (the plain orientation's oracle)
+    rng = np.random.default_rng(52)
+    a = rng.uniform(-1, 1, (5, 24)).astype(np.float32)
+    eye = np.eye(24, dtype=np.float32)
+    for wdtype, w in (("f32", eye), ("bf16", (eye.view(np.uint32) >> 16).astype(np.uint16)),
+                      ("f16", eye.astype(np.float16).view(np.uint16))):
+        c, _ = O.gemm_nt(a, w, wdtype, L=L)
+        assert np.array_equal(c, a.astype(np.float64)), wdtype
+    ai = rng.integers(-3, 4, (6, 40)).astype(np.float32)
+    wi = rng.integers(-3, 4, (9, 40)).astype(np.float32)
+    want = (ai.astype(np.int64) @ wi.astype(np.int64).T).astype(np.float64)
+    for wdtype, w in (("f32", wi), ("bf16", (wi.view(np.uint32) >> 16).astype(np.uint16)),
+                      ("f16", wi.astype(np.float16).view(np.uint16))):
+        c, _ = O.gemm_nt(ai, w, wdtype, L=L)
+        assert np.array_equal(c, want), wdtype
+    # the same products in the same p order as the plain orientation with B = W^T
+    a2 = rng.uniform(-1, 1, (5, 30)).astype(np.float32)
+    b = rng.uniform(-1, 1, (30, 12)).astype(np.float32)
+    c_nt, m_nt = O.gemm_nt(a2, np.ascontiguousarray(b.T), "f32", L=L)
+    c_nn, m_nn = O.sgemm(a2, b, L=L)
+    assert np.array_equal(c_nt, c_nn) and np.array_equal(m_nt, m_nn)
+
+
+def check_gemm_nt_bf16_f16_widening(L):
+    # every bf16 and f16 bit pattern that is finite, one weight at a time:
+    # x = [1, 0, ...] picks w[j][0], so C[0][j] must be the exact widening
+    for wdtype, widen in (("bf16", np_bf16_widen), ("f16", np_f16_widen)):
+        bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        vals = widen(bits)
+        keep = np.isfinite(vals)
+        wcol = bits[keep]
+        w = np.zeros((wcol.size, 2), np.uint16)
+        w[:, 0] = wcol
+        a = np.array([[1.0, 0.0]], np.float32)
+        c, _ = O.gemm_nt(a, w, wdtype, L=L)
+        assert np.array_equal(c[0], vals[keep]), wdtype
+
+
 # --------------------------------------------------------------------------- ternary
 
 

@@ -17,5 +17,5 @@ def test_every_oracle_entry_is_pinned():
     for name in ("half_to_double", "float_to_half", "pack_q4_0", "unpack_q4_0", "quantize_q8_0",
                  "unpack_q8_0", "q4_0_q8_0(", "q4_0_q8_0_sampled", "q4_0_q8_0_block_sums", "sgemm(",
                  "sgemm_sampled", "pack_ternary", "unpack_ternary", "quantize_i8_rows", "ternary(",
-                 "ternary_sampled", "pack_q8_0", "q8_0_q8_0(", "q8_0_q8_0_sampled", "q8_0_q8_0_block_sums"):
+                 "ternary_sampled", "pack_q8_0", "q8_0_q8_0(", "q8_0_q8_0_sampled", "q8_0_q8_0_block_sums", "gemm_nt(", "gemm_nt_sampled"):
         assert "O." + name in src, name
