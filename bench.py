@@ -12,7 +12,9 @@ size, on inputs already resident in HBM:
     and is not part of a step);
   * the same four shapes with Q8_0 weights: decode GEMV on the Q8_0 blocks
     and prefill GEMM (m = 512) on the weights repacked at load time;
-  * the f32 GEMM 4096^3 and the f32 GEMV 4096 x 4096;
+  * the f32 GEMM 4096^3 and the f32 GEMV 4096 x 4096, and the same two in
+    the transposed-B orientation (W = B^T stored [n][k]) with f32, bf16 and
+    f16 weights (the GEMM with f32 and bf16 ones is in the step too);
   * the BitNet ternary layer 2560 -> 6912: int8 row quantization, GEMV (m = 1)
     and GEMM (m = 64).
 Decode weights rotate through enough device copies (>= 1 GiB per shape) that
@@ -210,6 +212,33 @@ def build_ops(qll, synth, torch, np, dev, only):
                           4 * (K + K * N + N), 2 * N * K, "hbm"))
         del a, b, x
 
+    # ---------------------------------------------------------------- transposed B (W [n][k]), f32/bf16/f16
+    if want("nt_"):
+        a, b, x = synth.f32_gemm()
+        M = N = K = 4096
+        wt = to_dev(np.ascontiguousarray(b.T))
+        del b
+        ad = to_dev(a) if want("nt_gemm") else None
+        xd = to_dev(x)
+        dts = (("f32", qll.QLL_DTYPE_F32, torch.float32), ("bf16", qll.QLL_DTYPE_BF16, torch.bfloat16),
+               ("f16", qll.QLL_DTYPE_F16, torch.float16))
+        for name, code, tdt in dts:
+            w = wt if tdt == torch.float32 else wt.to(tdt)
+            esz = w.element_size()
+            if want(f"nt_gemv_{name}"):
+                copies = [w] + [w.clone() for _ in range(max(1, -(-gib // (esz * N * K))) - 1)]
+                yd = torch.empty(N, dtype=torch.float32, device=dev)
+                ops.append(Op(f"nt_gemv_{name}_4096", f"{name}_nt", "decode",
+                              lambda c=copies, yd=yd, code=code: qll.qll_gemm_nt(
+                                  xd, c[step_ref["i"] % len(c)], code, yd, 1, N, K),
+                              esz * N * K + 4 * K + 4 * N, 2 * N * K, "hbm"))
+            if want(f"nt_gemm_{name}"):
+                cd = torch.empty(M * N, dtype=torch.float32, device=dev)
+                ops.append(Op(f"nt_gemm_{name}_4096", f"{name}_nt", "prefill",
+                              lambda w=w, cd=cd, code=code: qll.qll_gemm_nt(ad, w, code, cd, M, N, K),
+                              4 * M * K + esz * N * K + 4 * M * N, 2 * M * N * K, "mfma", "f32"))
+        del wt
+
     # ---------------------------------------------------------------- ternary
     if any(want(s) for s in ("i8_quant", "ternary")):
         codes, w_scale, x = synth.ternary_layer()
@@ -382,7 +411,7 @@ def main():
         return out
 
     per_format = {}
-    for fmt in ("q4_0", "q4_0_repacked", "q8_0", "f32", "ternary"):
+    for fmt in ("q4_0", "q4_0_repacked", "q8_0", "f32", "f32_nt", "bf16_nt", "f16_nt", "ternary"):
         d = {"decode": agg(fmt, "decode"), "prefill": agg(fmt, "prefill")}
         if any(d.values()):
             per_format[fmt] = d
@@ -406,7 +435,7 @@ def main():
         "config": {"workload": "one pass of the whole path: Q4_0 x Q8_0 decode GEMV (m=1) and prefill GEMM (m=512) "
                                "on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256), the prefill also on "
                                "load-time repacked weights; the same shapes with Q8_0 weights (decode GEMV, prefill GEMM on repacked "
-                               "weights); f32 GEMM 4096^3 "
+                               "weights); f32 GEMM 4096^3 (also transposed-B with f32/bf16/f16 weights) "
                                "and GEMV 4096x4096; BitNet ternary 2560->6912 at m=1 and m=64",
                    "value_is": "Q4_0 x Q8_0 decode GEMV algorithmic bytes / summed average launch duration (back-to-back "
                                "launches on rotating weight copies) over the four shapes",

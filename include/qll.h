@@ -78,6 +78,9 @@ enum {
  * the shape is invalid. */
 size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k);
 
+/* Element types of the weights of qll_gemm_nt. */
+enum { QLL_DTYPE_F32 = 0, QLL_DTYPE_BF16 = 1, QLL_DTYPE_F16 = 2 };
+
 /* Static string naming a status code. */
 const char *qll_status_string(int status);
 
@@ -214,6 +217,19 @@ int qll_q8_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_
  * qll_workspace_bytes(QLL_OP_SGEMM, m, n, k) bytes. */
 int qll_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, int64_t k, void *ws, size_t ws_bytes,
               void *stream);
+
+/* Transposed-B GEMM, the linear layer's own orientation ([FAST] 6.6: W stored
+ * [n][k], each output a two-stream dot): Y[m][n] = X[m][k] . W^T, x f32
+ * row-major, w of element type w_dtype (QLL_DTYPE_F32, _BF16 or _F16)
+ * row-major [n][k], y f32 [m][n].  bf16 and f16 weights are widened to f32
+ * exactly as they are read ([FAST] on reduced precision: bf16 is the top half
+ * of an f32; f16 is converted once per load) and never stored as f32; the
+ * activations are never rounded; accumulation in f32 (tolerance
+ * 1e-5 * sum_p |x * w| against an f64 sum).  m == 1 runs a row-dot GEMV
+ * (bandwidth-bound: W is read once), m > 1 the f32 matrix-core GEMM.  Any
+ * k >= 1 (rows whose byte length is not a multiple of 16 take a scalar
+ * path).  No workspace.  QLL_ERR_SHAPE for an unknown w_dtype. */
+int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m, int64_t n, int64_t k, void *stream);
 
 /* ---------------------------------------------------------------- ternary */
 

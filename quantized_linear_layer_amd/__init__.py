@@ -20,6 +20,7 @@ QLL_OP_Q4_0_Q8_0_GEMM = 2
 QLL_OP_TERNARY_GEMM = 3
 QLL_OP_Q4_0_REPACKED_GEMM = 4
 QLL_OP_Q8_0_REPACKED_GEMM = 5
+QLL_DTYPE_F32, QLL_DTYPE_BF16, QLL_DTYPE_F16 = 0, 1, 2
 
 Q4_0_BLOCK_BYTES = 18
 Q8_0_BLOCK_BYTES = 34
@@ -55,6 +56,7 @@ def load(path=LIB_PATH):
         "qll_q8_0_repack": [P, P, I, I, P],
         "qll_q8_0_repacked_q8_0_gemm": [P, P, P, I, I, I, P, S, P],
         "qll_sgemm": [P, P, P, I, I, I, P, S, P],
+        "qll_gemm_nt": [P, P, ctypes.c_int, P, I, I, I, P],
         "qll_quantize_i8_rows": [P, P, P, P, I, I, P],
         "qll_ternary_gemv": [P, F, P, P, P, P, I, I, P],
         "qll_ternary_gemm": [P, F, P, P, P, P, I, I, I, P],
@@ -214,6 +216,13 @@ def qll_sgemm(a, b, c, m, n, k, ws=None, stream=None):
     wsp, wsb = _ws(ws, need) if need != 2 ** 64 - 1 else (None, 0)
     _call("qll_sgemm", _ptr(a, m * k * 4, "a"), _ptr(b, k * n * 4, "b"), _ptr(c, m * n * 4, "c"), m, n, k, wsp, wsb,
           _stream(stream))
+
+
+def qll_gemm_nt(x, w, w_dtype, y, m, n, k, stream=None):
+    """Y = X.W^T with W [n][k] of element type w_dtype (QLL_DTYPE_F32/BF16/F16)."""
+    esize = 4 if w_dtype == QLL_DTYPE_F32 else 2
+    _call("qll_gemm_nt", _ptr(x, m * k * 4, "x"), _ptr(w, n * k * esize, "w"), int(w_dtype), _ptr(y, m * n * 4, "y"),
+          m, n, k, _stream(stream))
 
 
 # ----------------------------------------------------------------- ternary

@@ -293,6 +293,26 @@ int qll_q8_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_
                                             n, k, ws, as_stream(stream)));
 }
 
+int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m, int64_t n, int64_t k, void *stream)
+{
+    if (!x || !w || !y)
+        return QLL_ERR_NULL;
+    if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || w_dtype < QLL_DTYPE_F32 || w_dtype > QLL_DTYPE_F16)
+        return QLL_ERR_SHAPE;
+    if (m > 1 && ((n + 127) / 128 > 0x7fffffff || (m + 127) / 128 > 65535))
+        return QLL_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y))
+        return QLL_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    static_assert((int)QLL_DTYPE_F32 == (int)QLL_W_F32 && (int)QLL_DTYPE_BF16 == (int)QLL_W_BF16 &&
+                      (int)QLL_DTYPE_F16 == (int)QLL_W_F16,
+                  "dtype codes");
+    if (m == 1)
+        return launched(launch_gemv_nt(x, w, w_dtype, y, n, k, as_stream(stream)));
+    return launched(launch_sgemm_nt(x, w, w_dtype, y, m, n, k, as_stream(stream)));
+}
+
 int qll_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, int64_t k, void *ws, size_t ws_bytes,
               void *stream)
 {

@@ -107,6 +107,12 @@ hipError_t launch_q4_0_q8_0_gemv_f32(const uint8_t *w, const float *x, float *y,
 size_t q4_0_q8_0_gemm_workspace(int64_t m, int64_t n, int64_t k);
 // Decode GEMV with Q8_0 weights.
 hipError_t launch_q8_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int64_t k, hipStream_t s);
+// Transposed-B (W stored [n][k]) f32 GEMV and GEMM with f32, bf16 or f16
+// weights (the values of the ABI's QLL_DTYPE_*).
+enum { QLL_W_F32 = 0, QLL_W_BF16 = 1, QLL_W_F16 = 2 };
+hipError_t launch_gemv_nt(const float *x, const void *w, int wfmt, float *y, int64_t n, int64_t k, hipStream_t s);
+hipError_t launch_sgemm_nt(const float *a, const void *w, int wfmt, float *c, int64_t m, int64_t n, int64_t k,
+                           hipStream_t s);
 // Load-time repack of Q4_0 weights and the GEMM on them (6-bit matrix-core path).
 size_t q4_0_repacked_bytes(int64_t n, int64_t k);
 hipError_t launch_q4_0_repack(const uint8_t *w, uint8_t *wp, int64_t n, int64_t k, hipStream_t s);

@@ -14,6 +14,11 @@
 //    products are full f32).  128 x 128 output tiles, k-tiles of 16 staged in
 //    double-buffered LDS (A stored k-major so a wave's 32 rows are contiguous,
 //    B row-major), four waves of 64 x 64 each.
+//  * The same GEMM in the transposed-B orientation (W stored [n][k], the
+//    linear layer's own, 6.6 of the same chapter): the W tile is read row-wise
+//    like A and stored k-major like A; bf16 and f16 weights are widened to f32
+//    exactly as they are loaded (the chapter's reduced-precision policy: f32
+//    accumulation, no f32 copy of the weights in memory).
 #include "common.h"
 
 namespace qll {
@@ -175,8 +180,22 @@ struct SgemmTileRegs {
     float b[2][4]; // two float4 of B (k rows kr, kr+8; columns 4c..4c+3)
 };
 
-template <bool VEC>
-__device__ __forceinline__ void sgemm_load_tile(const float *__restrict__ a, const float *__restrict__ b, int64_t m,
+// B operand kinds: the plain orientation B[k][n] f32, or the transposed one
+// (W stored [n][k], C = A.W^T) with f32, bf16 or f16 weights widened exactly
+// to f32 as they are loaded.
+constexpr int kBNN = -1;
+
+template <int BT>
+__device__ __forceinline__ float sgemm_w_elem(const void *w, int64_t idx)
+{
+    if (BT == QLL_W_F32)
+        return static_cast<const float *>(w)[idx];
+    const uint32_t h = static_cast<const uint16_t *>(w)[idx];
+    return BT == QLL_W_BF16 ? __builtin_bit_cast(float, h << 16) : half_bits_to_float(h);
+}
+
+template <bool VEC, int BT>
+__device__ __forceinline__ void sgemm_load_tile(const float *__restrict__ a, const void *__restrict__ bv, int64_t m,
                                                 int64_t n, int64_t k, int64_t m0, int64_t n0, int64_t k0,
                                                 SgemmTileRegs &t)
 {
@@ -195,22 +214,50 @@ __device__ __forceinline__ void sgemm_load_tile(const float *__restrict__ a, con
                 t.a[it][e] = (row < m && kk + e < k) ? a[row * k + kk + e] : 0.0f;
         }
     }
-    // B: 16 rows x 128 columns = 512 float4, two per thread
+    if (BT == kBNN) {
+        // B: 16 rows x 128 columns = 512 float4, two per thread
+        const float *b = static_cast<const float *>(bv);
 #pragma unroll
-    for (int it = 0; it < 2; it++) {
-        const int64_t kr = k0 + (tid >> 5) + 8 * it;
-        const int64_t col = n0 + 4 * (tid & 31);
-        if (VEC && kr < k && col + 3 < n) {
-            float4 v = *reinterpret_cast<const float4 *>(b + kr * n + col);
-            t.b[it][0] = v.x; t.b[it][1] = v.y; t.b[it][2] = v.z; t.b[it][3] = v.w;
-        } else {
+        for (int it = 0; it < 2; it++) {
+            const int64_t kr = k0 + (tid >> 5) + 8 * it;
+            const int64_t col = n0 + 4 * (tid & 31);
+            if (VEC && kr < k && col + 3 < n) {
+                float4 v = *reinterpret_cast<const float4 *>(b + kr * n + col);
+                t.b[it][0] = v.x; t.b[it][1] = v.y; t.b[it][2] = v.z; t.b[it][3] = v.w;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                t.b[it][e] = (kr < k && col + e < n) ? b[kr * n + col + e] : 0.0f;
+                for (int e = 0; e < 4; e++)
+                    t.b[it][e] = (kr < k && col + e < n) ? b[kr * n + col + e] : 0.0f;
+            }
+        }
+    } else {
+        // W: 128 rows (output columns) x 16 k, loaded like A: four adjacent k
+        // of one row per thread (16 bytes of f32, 8 of bf16/f16), widened
+#pragma unroll
+        for (int it = 0; it < 2; it++) {
+            const int64_t col = n0 + (tid >> 2) + 64 * it;
+            const int64_t kk = k0 + 4 * (tid & 3);
+            if (VEC && col < n && kk + 3 < k) {
+                if (BT == QLL_W_F32) {
+                    const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(bv) + col * k + kk);
+                    t.b[it][0] = v.x; t.b[it][1] = v.y; t.b[it][2] = v.z; t.b[it][3] = v.w;
+                } else {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(bv) + col * k + kk);
+                    const uint32_t h[4] = {v.x & 0xffffu, v.x >> 16, v.y & 0xffffu, v.y >> 16};
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        t.b[it][e] = BT == QLL_W_BF16 ? __builtin_bit_cast(float, h[e] << 16) : half_bits_to_float(h[e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    t.b[it][e] = (col < n && kk + e < k) ? sgemm_w_elem<BT>(bv, col * k + kk + e) : 0.0f;
+            }
         }
     }
 }
 
+template <int BT>
 __device__ __forceinline__ void sgemm_store_tile(const SgemmTileRegs &t, float (*As)[BM + APAD],
                                                  float (*Bs)[BN + BPAD])
 {
@@ -223,17 +270,28 @@ __device__ __forceinline__ void sgemm_store_tile(const SgemmTileRegs &t, float (
         for (int e = 0; e < 4; e++)
             As[kq + e][row] = t.a[it][e];
     }
+    if (BT == kBNN) {
 #pragma unroll
-    for (int it = 0; it < 2; it++) {
-        const int kr = (tid >> 5) + 8 * it;
-        const int col = 4 * (tid & 31);
-        *reinterpret_cast<float4 *>(&Bs[kr][col]) = make_float4(t.b[it][0], t.b[it][1], t.b[it][2], t.b[it][3]);
+        for (int it = 0; it < 2; it++) {
+            const int kr = (tid >> 5) + 8 * it;
+            const int col = 4 * (tid & 31);
+            *reinterpret_cast<float4 *>(&Bs[kr][col]) = make_float4(t.b[it][0], t.b[it][1], t.b[it][2], t.b[it][3]);
+        }
+    } else { // k-major, like A
+#pragma unroll
+        for (int it = 0; it < 2; it++) {
+            const int col = (tid >> 2) + 64 * it;
+            const int kq = 4 * (tid & 3);
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                Bs[kq + e][col] = t.b[it][e];
+        }
     }
 }
 
-template <bool VEC>
+template <bool VEC, int BT>
 __global__ __launch_bounds__(kSgemmThreads) void sgemm_mfma_kernel(const float *__restrict__ a,
-                                                                   const float *__restrict__ b,
+                                                                   const void *__restrict__ b,
                                                                    float *__restrict__ c, int64_t m, int64_t n,
                                                                    int64_t k)
 {
@@ -256,14 +314,14 @@ __global__ __launch_bounds__(kSgemmThreads) void sgemm_mfma_kernel(const float *
 
     const int64_t nkt = (k + BK - 1) / BK;
     SgemmTileRegs regs;
-    sgemm_load_tile<VEC>(a, b, m, n, k, m0, n0, 0, regs);
-    sgemm_store_tile(regs, As[0], Bs[0]);
+    sgemm_load_tile<VEC, BT>(a, b, m, n, k, m0, n0, 0, regs);
+    sgemm_store_tile<BT>(regs, As[0], Bs[0]);
     __syncthreads();
 
     for (int64_t kt = 0; kt < nkt; kt++) {
         const int cur = (int)(kt & 1);
         if (kt + 1 < nkt)
-            sgemm_load_tile<VEC>(a, b, m, n, k, m0, n0, (kt + 1) * BK, regs);
+            sgemm_load_tile<VEC, BT>(a, b, m, n, k, m0, n0, (kt + 1) * BK, regs);
 #pragma unroll
         for (int s = 0; s < BK / 2; s++) {
             const int kk = 2 * s + lh; // lanes 0-31 take k = 2s, lanes 32-63 k = 2s+1
@@ -281,7 +339,7 @@ __global__ __launch_bounds__(kSgemmThreads) void sgemm_mfma_kernel(const float *
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
         if (kt + 1 < nkt)
-            sgemm_store_tile(regs, As[cur ^ 1], Bs[cur ^ 1]);
+            sgemm_store_tile<BT>(regs, As[cur ^ 1], Bs[cur ^ 1]);
         __syncthreads();
     }
 
@@ -304,10 +362,32 @@ hipError_t launch_sgemm(const float *a, const float *b, float *c, int64_t m, int
 {
     dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
     if (k % 4 == 0 && n % 4 == 0)
-        hipLaunchKernelGGL(sgemm_mfma_kernel<true>, grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<true, kBNN>), grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
     else
-        hipLaunchKernelGGL(sgemm_mfma_kernel<false>, grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<false, kBNN>), grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
     return hipGetLastError();
+}
+
+template <int BT>
+static hipError_t launch_sgemm_nt_t(const float *a, const void *w, float *c, int64_t m, int64_t n, int64_t k,
+                                    hipStream_t s)
+{
+    dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
+    if (k % 4 == 0)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<true, BT>), grid, dim3(kSgemmThreads), 0, s, a, w, c, m, n, k);
+    else
+        hipLaunchKernelGGL((sgemm_mfma_kernel<false, BT>), grid, dim3(kSgemmThreads), 0, s, a, w, c, m, n, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_sgemm_nt(const float *a, const void *w, int wfmt, float *c, int64_t m, int64_t n, int64_t k,
+                           hipStream_t s)
+{
+    if (wfmt == QLL_W_F32)
+        return launch_sgemm_nt_t<QLL_W_F32>(a, w, c, m, n, k, s);
+    if (wfmt == QLL_W_BF16)
+        return launch_sgemm_nt_t<QLL_W_BF16>(a, w, c, m, n, k, s);
+    return launch_sgemm_nt_t<QLL_W_F16>(a, w, c, m, n, k, s);
 }
 
 } // namespace qll

@@ -134,6 +134,14 @@ def test_q8w_errors(L):
         qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_REPACKED_GEMM, 512, 4096, 4096)
 
 
+def test_gemm_nt_errors(L):
+    assert L.qll_gemm_nt(NUL, GOOD, 0, GOOD, 2, 2, 2, None) == NULL
+    assert L.qll_gemm_nt(GOOD, GOOD, 3, GOOD, 2, 2, 2, None) == SHAPE
+    assert L.qll_gemm_nt(GOOD, GOOD, -1, GOOD, 2, 2, 2, None) == SHAPE
+    assert L.qll_gemm_nt(GOOD, GOOD, 1, GOOD, 2, 0, 2, None) == SHAPE
+    assert L.qll_gemm_nt(GOOD, MIS, 2, GOOD, 2, 2, 2, None) == ALIGN
+
+
 def test_repacked_sizes(L):
     L.qll_q4_0_repacked_bytes.restype = ctypes.c_size_t
     assert qll.qll_q4_0_repacked_bytes(1, 32) == 3328

@@ -1,0 +1,102 @@
+"""Parity of the transposed-B GEMV/GEMM (W stored [n][k]) with f32, bf16 and
+f16 weights against the oracle (f64 accumulation of exactly widened
+weights): |y - y_ref| <= 1e-5 * sum_p |x * w|.  Small-integer inputs give
+exact outputs in any order and are compared bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import quantized_linear_layer_amd as qll
+import synth
+from gpu_util import assert_within, dev, empty, host
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+DT = {"f32": qll.QLL_DTYPE_F32, "bf16": qll.QLL_DTYPE_BF16, "f16": qll.QLL_DTYPE_F16}
+
+
+def weights(w32, wdtype):
+    """Host weights in the requested element type: f32 as is, bf16 and f16
+    rounded to nearest even (torch's conversion), as uint16 bit patterns."""
+    if wdtype == "f32":
+        return np.ascontiguousarray(w32, np.float32)
+    t = torch.from_numpy(np.ascontiguousarray(w32, np.float32))
+    t = t.to(torch.bfloat16 if wdtype == "bf16" else torch.float16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def run(x, w, wdtype):
+    m, k = x.shape
+    n = w.shape[0]
+    y = empty(m * n, torch.float32)
+    qll.qll_gemm_nt(dev(x), dev(w), DT[wdtype], y, m, n, k)
+    return host(y).reshape(m, n)
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("n", [1, 7, 64, 257])
+@pytest.mark.parametrize("k", [1, 3, 8, 100, 256, 4096, 4100, 14336])
+def test_gemv_shapes(qll_gpu, wdtype, n, k):
+    rng = np.random.default_rng(n * 31 + k)
+    x = synth.uniform_f32(rng, (1, k))
+    w = weights(synth.uniform_f32(rng, (n, k)), wdtype)
+    y = run(x, w, wdtype)
+    y_ref, mag = O.gemm_nt(x, w, wdtype)
+    assert_within(y, y_ref, mag, TOL, f"NT GEMV {wdtype} n={n} k={k}")
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("m,n,k", [(2, 3, 5), (37, 68, 100), (130, 129, 320), (128, 128, 4096), (257, 131, 1001),
+                                   (64, 300, 4)])
+def test_gemm_shapes(qll_gpu, wdtype, m, n, k):
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    x = synth.uniform_f32(rng, (m, k))
+    w = weights(synth.uniform_f32(rng, (n, k)), wdtype)
+    y = run(x, w, wdtype)
+    y_ref, mag = O.gemm_nt(x, w, wdtype)
+    assert_within(y, y_ref, mag, TOL, f"NT GEMM {wdtype} m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("m", [1, 40])
+def test_small_integers_exact(qll_gpu, wdtype, m):
+    rng = np.random.default_rng(9 + m)
+    k, n = 640, 50
+    x = rng.integers(-4, 5, (m, k)).astype(np.float32)
+    w32 = rng.integers(-4, 5, (n, k)).astype(np.float32)
+    y = run(x, weights(w32, wdtype), wdtype)
+    assert np.array_equal(y.astype(np.float64), x.astype(np.float64) @ w32.astype(np.float64).T)
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16"])
+def test_full_size(qll_gpu, wdtype):
+    # the f32 workload's shapes in the transposed orientation: W = B^T of the
+    # 4096^3 GEMM; the GEMV on every output, the GEMM on a seeded sample
+    a, b, x = synth.f32_gemm()
+    w = weights(np.ascontiguousarray(b.T), wdtype)
+    del b
+    y1 = run(x, w, wdtype)
+    y_ref, mag = O.gemm_nt(x, w, wdtype)
+    assert_within(y1, y_ref, mag, TOL, f"NT GEMV 4096 {wdtype}")
+    y = run(a, w, wdtype)
+    rng = np.random.default_rng(17)
+    ii = np.concatenate([[0, 4095], rng.integers(0, 4096, 3000)])
+    jj = np.concatenate([[4095, 0], rng.integers(0, 4096, 3000)])
+    c_ref, cmag = O.gemm_nt_sampled(a, w, wdtype, ii, jj)
+    assert_within(y[ii, jj], c_ref, cmag, TOL, f"NT GEMM 4096^3 {wdtype}")
+    torch.cuda.empty_cache()
+
+
+def test_f32_nt_matches_nn(qll_gpu):
+    # the transposed orientation on W = B^T gives the plain GEMM's products
+    rng = np.random.default_rng(3)
+    a = synth.uniform_f32(rng, (70, 96))
+    b = synth.uniform_f32(rng, (96, 33))
+    y = run(a, np.ascontiguousarray(b.T), "f32")
+    c = empty(70 * 33, torch.float32)
+    ws = empty(max(16, qll.qll_workspace_bytes(qll.QLL_OP_SGEMM, 70, 33, 96)))
+    qll.qll_sgemm(dev(a), dev(b), c, 70, 33, 96, ws=ws)
+    c_ref, mag = O.sgemm(a, b)
+    assert_within(y, c_ref, mag, TOL, "NT vs oracle")
+    assert_within(host(c).reshape(70, 33), c_ref, mag, TOL, "NN vs oracle")
