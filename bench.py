@@ -6,17 +6,16 @@ size, on inputs already resident in HBM:
     (m = 1) on the four 8B-class linear shapes (k, n) = (4096, 14336),
     (14336, 4096), (4096, 4096), (4096, 128256);
   * Q8_0 quantization of the prefill activations and the Q4_0 x Q8_0 prefill
-    GEMM (m = 512) on the same four shapes and weights, once on the block_q4_0
-    bytes as they are and once on the same weights repacked at load time into
-    the matrix core's 6-bit operand form (the repack itself is load-time work
-    and is not part of a step);
-  * the same four shapes with Q8_0 weights: decode GEMV on the Q8_0 blocks
-    and prefill GEMM (m = 512) on the weights repacked at load time;
-  * the f32 GEMM 4096^3 and the f32 GEMV 4096 x 4096, and the same two in
-    the transposed-B orientation (W = B^T stored [n][k]) with f32, bf16 and
-    f16 weights (the GEMM with f32 and bf16 ones is in the step too);
+    GEMM (m = 512) on the same four shapes and weights;
+  * the f32 GEMM 4096^3 and the f32 GEMV 4096 x 4096;
   * the BitNet ternary layer 2560 -> 6912: int8 row quantization, GEMV (m = 1)
     and GEMM (m = 64).
+Measured in the same run, outside the step: the Q4_0 prefill GEMM on the same
+weights repacked at load time into the matrix core's 6-bit operand form (the
+repack itself is load-time work); the four shapes with Q8_0 weights (decode
+GEMV on the Q8_0 blocks, prefill GEMM on repacked weights); the f32 GEMV and
+GEMM in the transposed-B orientation (W = B^T stored [n][k]) with f32, bf16
+and f16 weights.
 Decode weights rotate through enough device copies (>= 1 GiB per shape) that
 no decode GEMV reads its weights from the 256 MiB Infinity Cache.
 
@@ -35,7 +34,9 @@ line's `value` is the Q4_0 x Q8_0 decode GEMV bandwidth over the four shapes
 (algorithmic bytes / summed average launch duration); `per_format` holds
 decode GB/s and prefill TOPS of every format with their fractions of the
 MI355X peaks, and `roofline` describes the kernel that takes the largest share
-of the step.
+of the step.  The operations of the widened rows (repacked weights, Q8_0
+weights, transposed-B) are measured in the same run, in passes of their own,
+and reported with `"in_step": false`; they are not part of a step.
 `cpu_baseline` times the oracle (the test suite's plain C reference, never
 tuned) on the same decode GEMVs on the host's cores.
 
@@ -68,10 +69,16 @@ def parse():
     return p.parse_args()
 
 
+# Operations of the rows beyond the hot path's core (small-m, repacked weights,
+# Q8_0 weights, transposed-B): timed the same way, but not part of a step.
+EXTRA_PREFIXES = ("q4r_gemm", "q8w_gemv", "q8r_gemm", "nt_")
+
+
 class Op:
     def __init__(self, name, fmt, kind, fn, nbytes, flops, bound, peak_key=None):
         self.name, self.fmt, self.kind, self.fn = name, fmt, kind, fn
         self.nbytes, self.flops, self.bound, self.peak_key = nbytes, flops, bound, peak_key
+        self.in_step = not name.startswith(EXTRA_PREFIXES)
         self.times_ms = []  # event pair around the op's single launch in each step
         self.batch_ms = []  # per launch, from runs of back-to-back launches
         self.reps = 1
@@ -329,23 +336,33 @@ def main():
             op.fn()
     torch.cuda.synchronize()
 
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for st in range(args.steps):
-        step_ref["i"] = args.warmup + st
-        for j, op in enumerate(ops):
-            evs[st][j][0].record(stream)
-            op.fn()
-            evs[st][j][1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    for st in range(args.steps):
-        for j, op in enumerate(ops):
-            op.times_ms.append(evs[st][j][0].elapsed_time(evs[st][j][1]))
+    def timed_passes(sel):
+        """`steps` passes over the ops in `sel`, each op between its own event
+        pair; returns the wall time per pass in ms."""
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sel]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for st in range(args.steps):
+            step_ref["i"] = args.warmup + st
+            for j, op in enumerate(sel):
+                evs[st][j][0].record(stream)
+                op.fn()
+                evs[st][j][1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for st in range(args.steps):
+            for j, op in enumerate(sel):
+                op.times_ms.append(evs[st][j][0].elapsed_time(evs[st][j][1]))
+        return (t1 - t0) * 1e3 / args.steps
+
+    step_ops = [op for op in ops if op.in_step]
+    extra_ops = [op for op in ops if not op.in_step]
+    ms_per_step = timed_passes(step_ops) if step_ops else 0.0
     print(f"bench: timed {args.steps} steps, {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    if extra_ops:
+        timed_passes(extra_ops)
+        print(f"bench: timed {len(extra_ops)} further ops outside the step", file=sys.stderr, flush=True)
 
     # Back-to-back launches: R launches of the op (decode ops on R successive
     # weight copies) captured once into a HIP graph, so that the host's
@@ -378,7 +395,8 @@ def main():
         t = np.array(op.batch_ms)
         ms = float(np.mean(t))
         rl = op.roofline(ms)
-        entry = {"op": op.name, "format": op.fmt, "kind": op.kind, "ms": ms, "ms_median": float(np.median(t)),
+        entry = {"op": op.name, "format": op.fmt, "kind": op.kind, "in_step": op.in_step, "ms": ms,
+                 "ms_median": float(np.median(t)),
                  "cv": float(np.std(t) / ms) if ms > 0 else 0.0, "reps": op.reps,
                  "ms_in_step": float(np.mean(op.times_ms)), "bytes": op.nbytes, "flops": op.flops, **rl}
         if op.kind == "prefill" and op.peak_key in ("f16", "bf6"):
@@ -416,7 +434,8 @@ def main():
         if any(d.values()):
             per_format[fmt] = d
 
-    dom = max(kernels, key=lambda e: e["ms"]) if kernels else None
+    in_step = [e for e in kernels if e["in_step"]] or kernels
+    dom = max(in_step, key=lambda e: e["ms"]) if in_step else None
     roofline = None
     if dom is not None:
         roofline = {"kernel": dom["op"], "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
@@ -433,10 +452,11 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "i8 (Q4_0 x Q8_0 int8 block dots, f32 scaling)", "data": "synthetic",
         "config": {"workload": "one pass of the whole path: Q4_0 x Q8_0 decode GEMV (m=1) and prefill GEMM (m=512) "
-                               "on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256), the prefill also on "
-                               "load-time repacked weights; the same shapes with Q8_0 weights (decode GEMV, prefill GEMM on repacked "
-                               "weights); f32 GEMM 4096^3 (also transposed-B with f32/bf16/f16 weights) "
+                               "on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256); f32 GEMM 4096^3 "
                                "and GEMV 4096x4096; BitNet ternary 2560->6912 at m=1 and m=64",
+                   "outside_step": "Q4_0 prefill on load-time repacked weights; Q8_0-weight decode GEMV and repacked "
+                                   "prefill GEMM on the same shapes; transposed-B f32 GEMV/GEMM 4096 with f32, bf16 "
+                                   "and f16 weights",
                    "value_is": "Q4_0 x Q8_0 decode GEMV algorithmic bytes / summed average launch duration (back-to-back "
                                "launches on rotating weight copies) over the four shapes",
                    "parallelism": "single GPU"},
