@@ -16,6 +16,8 @@
 
 namespace qll {
 
+#define QLL_LDS_T __attribute__((address_space(3)))
+
 // 16 activation bytes (dwords D0..D3, byte e of Dr = x[4r + e]) -> A0..A3 with
 // byte r of Aj = x[4r + j], the order of the code unpack: a 4x4 byte transpose
 // in two rounds of byte permutes (interleave pairs of dwords, then pairs of
@@ -309,11 +311,149 @@ __global__ __launch_bounds__(kTerGemmThreads) void ternary_gemm_kernel(
     }
 }
 
+// ------------------------------------------------------------------ GEMM, k % 64 == 0
+// The same MFMA and operand orders as above, restructured for latency: at the
+// workload's size (m = 64, 4.4 MB of weights) the kernel is bound by memory
+// round trips, not bytes or MFMAs.  One wave per workgroup owns 16 activation
+// rows x 32 weight rows (four times as many workgroups as the 64 x 32 tile
+// above), so no workgroup barrier is needed; every operand goes memory -> LDS
+// (global_load_lds) into a ring of kTer2Buf chunk buffers, issued
+// kTer2Buf - 1 chunks ahead, and the wave waits only for its own loads.  In
+// LDS the activation word w of row r sits in slot w ^ (r & 15) and weight
+// group g (4 words) of row r in group g ^ ((r >> 1) & 7), so the 16 rows an
+// MFMA operand reads fall in distinct banks; the 4x4 byte transpose of the
+// activation is applied after the LDS read.  Words past the end of the row
+// (a partial last chunk) are loaded from clamped addresses and their
+// activation operand is zeroed.
+constexpr int kTer2BM = 16, kTer2BN = 32, kTer2Buf = 3;
+constexpr int kTer2Dma = 12; // per chunk: 8 KB of activations + 4 KB of weights, 1 KB per wave-wide load
+
+struct Ter2Lds {
+    u32x4 x[kTer2BM][kTerWPC];  // [row][slot]
+    u32x4 w[kTer2BN][kTerWPC / 4]; // [row][group]
+};
+
+__device__ __forceinline__ void ter2_dma16(const void *base, uint32_t off, const QLL_LDS_T void *lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+                 "s"((uint32_t)(uintptr_t)lds)
+                 : "memory", "m0");
+}
+
+// Chunk c (activation words 32c .. 32c + 31 of every row) into buffer s.
+__device__ __forceinline__ void ter2_load(const uint32_t *__restrict__ w, const int8_t *__restrict__ xq, int64_t m,
+                                          int64_t n, int nw, int64_t m0, int64_t n0, int c, Ter2Lds &s)
+{
+    const int lane = threadIdx.x;
+    const QLL_LDS_T char *xs = (const QLL_LDS_T char *)&s.x[0][0];
+    const QLL_LDS_T char *ws = (const QLL_LDS_T char *)&s.w[0][0];
+#pragma unroll
+    for (int q = 0; q < 8; q++) { // rows 2q, 2q + 1: lane -> (row, slot)
+        const int rr = 2 * q + (lane >> 5), slot = lane & 31;
+        const int64_t gi = m0 + rr < m ? m0 + rr : m - 1;
+        int word = 32 * c + (slot ^ (rr & 15));
+        word = word < nw ? word : nw - 1;
+        ter2_dma16(xq, (uint32_t)((gi * nw + word) * 16), xs + 1024 * q);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) { // rows 8q .. 8q + 7: lane -> (row, group)
+        const int wr = 8 * q + (lane >> 3), grp = lane & 7;
+        const int64_t gj = n0 + wr < n ? n0 + wr : n - 1;
+        int word = 32 * c + 4 * (grp ^ ((wr >> 1) & 7));
+        word = word + 4 <= nw ? word : nw - 4;
+        ter2_dma16(w, (uint32_t)((gj * nw + word) * 4), ws + 1024 * q);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void ter2_wait()
+{
+    static_assert(N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4)); // vmcnt(N) expcnt(7) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(64) void ternary_gemm2_kernel(const uint32_t *__restrict__ w, float w_scale,
+                                                           const int8_t *__restrict__ xq,
+                                                           const float *__restrict__ act_scale,
+                                                           const int32_t *__restrict__ act_sum, float *__restrict__ y,
+                                                           int64_t m, int64_t n, int nw)
+{
+    __shared__ Ter2Lds lds[kTer2Buf];
+    const int64_t m0 = (int64_t)blockIdx.y * kTer2BM, n0 = (int64_t)blockIdx.x * kTer2BN;
+    const int lane = threadIdx.x, lr = lane & 15, lh = lane >> 4;
+    const int nch = (nw + kTerWPC - 1) / kTerWPC;
+
+    i32x4 acc[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+#pragma unroll
+    for (int c = 0; c < kTer2Buf - 1; c++)
+        if (c < nch)
+            ter2_load(w, xq, m, n, nw, m0, n0, c, lds[c]);
+    for (int c = 0; c < nch; c++) {
+        const int ahead = c + kTer2Buf - 1;
+        if (ahead < nch)
+            ter2_load(w, xq, m, n, nw, m0, n0, ahead, lds[ahead % kTer2Buf]);
+        // chunk c has landed once at most the loads of the later chunks remain
+        const int later = (nch - 1 - c) < (kTer2Buf - 1) ? (nch - 1 - c) : (kTer2Buf - 1);
+        if (later >= 2)
+            ter2_wait<2 * kTer2Dma>();
+        else if (later == 1)
+            ter2_wait<kTer2Dma>();
+        else
+            ter2_wait<0>();
+        const Ter2Lds &s = lds[c % kTer2Buf];
+        u32x4 wv[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int wr = 16 * j + lr, sw = (wr >> 1) & 7;
+            wv[j][0] = s.w[wr][(2 * lh) ^ sw];
+            wv[j][1] = s.w[wr][(2 * lh + 1) ^ sw];
+        }
+#pragma unroll
+        for (int st = 0; st < 8; st++) {
+            const int word = 32 * c + 8 * lh + st;
+            i32x4 a = __builtin_bit_cast(i32x4, transpose_4x4_bytes(s.x[lr][(8 * lh + st) ^ lr]));
+            if (word >= nw)
+                a = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const uint32_t cw = wv[j][st >> 2][st & 3];
+                const i32x4 b = {(int)(cw & 0x03030303u), (int)((cw >> 2) & 0x03030303u),
+                                 (int)((cw >> 4) & 0x03030303u), (int)((cw >> 6) & 0x03030303u)};
+                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[j], 0, 0, 0);
+            }
+        }
+    }
+    // D layout of a 16x16 tile: lane l, register v -> row 4*(l/16)+v, column l%16
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        const int64_t row = m0 + 4 * lh + v;
+        if (row >= m)
+            continue;
+        const float sc = act_scale[row];
+        const int asum = act_sum[row];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int64_t col = n0 + 16 * j + lr;
+            if (col < n)
+                y[row * n + col] = ternary_output(acc[j][v], asum, w_scale, sc);
+        }
+    }
+}
+
 hipError_t launch_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
                                const int32_t *act_sum, float *y, int64_t m, int64_t n, int64_t k, hipStream_t st)
 {
-    dim3 grid((unsigned)((n + TBN - 1) / TBN), (unsigned)((m + TBM - 1) / TBM));
     const int nw = (int)(k / 16);
+    // the restructured kernel addresses both operands with 32-bit offsets
+    const bool small = m * k < ((int64_t)1 << 32) && n * (k / 4) < ((int64_t)1 << 32);
+    if (nw % 4 == 0 && small) {
+        dim3 grid2((unsigned)((n + kTer2BN - 1) / kTer2BN), (unsigned)((m + kTer2BM - 1) / kTer2BM));
+        hipLaunchKernelGGL(ternary_gemm2_kernel, grid2, dim3(64), 0, st, w, w_scale, xq, act_scale, act_sum, y, m, n,
+                           nw);
+        return hipGetLastError();
+    }
+    dim3 grid((unsigned)((n + TBN - 1) / TBN), (unsigned)((m + TBM - 1) / TBM));
     if (nw % 4 == 0)
         hipLaunchKernelGGL(ternary_gemm_kernel<true>, grid, dim3(kTerGemmThreads), 0, st, w, w_scale, xq, act_scale,
                            act_sum, y, m, n, nw);
