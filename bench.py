@@ -52,7 +52,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"f16": 2500.0, "i8": 5000.0, "f32": 157.3, "bf6": 10100.0}
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0, "f32": 157.3, "bf6": 10100.0}
 METRIC = "decode GEMV HBM GB/s (% of peak) + prefill GEMM TOPS (% MFMA peak) per format"
 
 
@@ -241,9 +241,14 @@ def build_ops(qll, synth, torch, np, dev, only):
                               esz * N * K + 4 * K + 4 * N, 2 * N * K, "hbm"))
             if want(f"nt_gemm_{name}"):
                 cd = torch.empty(M * N, dtype=torch.float32, device=dev)
+                bf = name == "bf16"
+                need = qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, M, N, K) if bf else 0
+                wsn = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+                # bf16 weights run on the bf16 matrix core (three bf16 MFMAs per
+                # product of an f32 activation): fraction of the bf16 peak
                 ops.append(Op(f"nt_gemm_{name}_4096", f"{name}_nt", "prefill",
-                              lambda w=w, cd=cd, code=code: qll.qll_gemm_nt(ad, w, code, cd, M, N, K),
-                              4 * M * K + esz * N * K + 4 * M * N, 2 * M * N * K, "mfma", "f32"))
+                              lambda w=w, cd=cd, code=code, wsn=wsn: qll.qll_gemm_nt(ad, w, code, cd, M, N, K, ws=wsn),
+                              4 * M * K + esz * N * K + 4 * M * N, 2 * M * N * K, "mfma", "bf16" if bf else "f32"))
         del wt
 
     # ---------------------------------------------------------------- ternary

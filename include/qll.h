@@ -71,7 +71,8 @@ enum {
     QLL_OP_Q4_0_Q8_0_GEMM = 2,
     QLL_OP_TERNARY_GEMM = 3,
     QLL_OP_Q4_0_REPACKED_GEMM = 4,
-    QLL_OP_Q8_0_REPACKED_GEMM = 5
+    QLL_OP_Q8_0_REPACKED_GEMM = 5,
+    QLL_OP_GEMM_NT_BF16 = 6 /* qll_gemm_nt with QLL_DTYPE_BF16 weights */
 };
 
 /* Bytes of device workspace `op` needs at this shape (0 if none); SIZE_MAX if
@@ -221,15 +222,22 @@ int qll_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, in
 /* Transposed-B GEMM, the linear layer's own orientation ([FAST] 6.6: W stored
  * [n][k], each output a two-stream dot): Y[m][n] = X[m][k] . W^T, x f32
  * row-major, w of element type w_dtype (QLL_DTYPE_F32, _BF16 or _F16)
- * row-major [n][k], y f32 [m][n].  bf16 and f16 weights are widened to f32
- * exactly as they are read ([FAST] on reduced precision: bf16 is the top half
- * of an f32; f16 is converted once per load) and never stored as f32; the
- * activations are never rounded; accumulation in f32 (tolerance
- * 1e-5 * sum_p |x * w| against an f64 sum).  m == 1 runs a row-dot GEMV
- * (bandwidth-bound: W is read once), m > 1 the f32 matrix-core GEMM.  Any
- * k >= 1 (rows whose byte length is not a multiple of 16 take a scalar
- * path).  No workspace.  QLL_ERR_SHAPE for an unknown w_dtype. */
-int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m, int64_t n, int64_t k, void *stream);
+ * row-major [n][k], y f32 [m][n].  bf16 and f16 weights are used exactly as
+ * stored ([FAST] on reduced precision: bf16 is the top half of an f32; f16 is
+ * converted once per load) and never written back as f32; the activations are
+ * never rounded; accumulation in f32 (tolerance 1e-5 * sum_p |x * w| against
+ * an f64 sum).  m == 1 runs a row-dot GEMV (bandwidth-bound: W is read once).
+ * m > 1 runs a matrix-core GEMM: on the f32 matrix core with the weights
+ * widened in registers, or, for bf16 weights with k % 16 == 0, on the bf16
+ * matrix core with every activation split exactly into three bf16 parts (each
+ * bf16 x bf16 product is exact in f32, so the same products are accumulated).
+ * Any k >= 1.  ws/ws_bytes: at least
+ * qll_workspace_bytes(QLL_OP_GEMM_NT_BF16, m, n, k) bytes when w_dtype is
+ * QLL_DTYPE_BF16 (the split activations; 0 when that path does not run),
+ * none otherwise; contents on return unspecified.  QLL_ERR_SHAPE for an
+ * unknown w_dtype. */
+int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m, int64_t n, int64_t k, void *ws,
+                size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------- ternary */
 

@@ -20,6 +20,7 @@ QLL_OP_Q4_0_Q8_0_GEMM = 2
 QLL_OP_TERNARY_GEMM = 3
 QLL_OP_Q4_0_REPACKED_GEMM = 4
 QLL_OP_Q8_0_REPACKED_GEMM = 5
+QLL_OP_GEMM_NT_BF16 = 6
 QLL_DTYPE_F32, QLL_DTYPE_BF16, QLL_DTYPE_F16 = 0, 1, 2
 
 Q4_0_BLOCK_BYTES = 18
@@ -56,7 +57,7 @@ def load(path=LIB_PATH):
         "qll_q8_0_repack": [P, P, I, I, P],
         "qll_q8_0_repacked_q8_0_gemm": [P, P, P, I, I, I, P, S, P],
         "qll_sgemm": [P, P, P, I, I, I, P, S, P],
-        "qll_gemm_nt": [P, P, ctypes.c_int, P, I, I, I, P],
+        "qll_gemm_nt": [P, P, ctypes.c_int, P, I, I, I, P, S, P],
         "qll_quantize_i8_rows": [P, P, P, P, I, I, P],
         "qll_ternary_gemv": [P, F, P, P, P, P, I, I, P],
         "qll_ternary_gemm": [P, F, P, P, P, P, I, I, I, P],
@@ -218,11 +219,15 @@ def qll_sgemm(a, b, c, m, n, k, ws=None, stream=None):
           _stream(stream))
 
 
-def qll_gemm_nt(x, w, w_dtype, y, m, n, k, stream=None):
-    """Y = X.W^T with W [n][k] of element type w_dtype (QLL_DTYPE_F32/BF16/F16)."""
+def qll_gemm_nt(x, w, w_dtype, y, m, n, k, ws=None, stream=None):
+    """Y = X.W^T with W [n][k] of element type w_dtype (QLL_DTYPE_F32/BF16/F16);
+    bf16 weights at m > 1 may need a workspace (qll_workspace_bytes with
+    QLL_OP_GEMM_NT_BF16)."""
     esize = 4 if w_dtype == QLL_DTYPE_F32 else 2
+    need = qll_workspace_bytes(QLL_OP_GEMM_NT_BF16, m, n, k) if w_dtype == QLL_DTYPE_BF16 else 0
+    wsp, wsb = _ws(ws, need) if need != 2 ** 64 - 1 else (None, 0)
     _call("qll_gemm_nt", _ptr(x, m * k * 4, "x"), _ptr(w, n * k * esize, "w"), int(w_dtype), _ptr(y, m * n * 4, "y"),
-          m, n, k, _stream(stream))
+          m, n, k, wsp, wsb, _stream(stream))
 
 
 # ----------------------------------------------------------------- ternary

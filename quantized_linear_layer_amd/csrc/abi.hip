@@ -96,6 +96,10 @@ size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k)
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 16 != 0)
             return SIZE_MAX;
         return 0;
+    case QLL_OP_GEMM_NT_BF16:
+        if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n))
+            return SIZE_MAX;
+        return gemm_nt_workspace(QLL_W_BF16, m, n, k);
     case QLL_OP_Q4_0_REPACKED_GEMM:
     case QLL_OP_Q8_0_REPACKED_GEMM:
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
@@ -293,7 +297,8 @@ int qll_q8_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_
                                             n, k, ws, as_stream(stream)));
 }
 
-int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m, int64_t n, int64_t k, void *stream)
+int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m, int64_t n, int64_t k, void *ws,
+                size_t ws_bytes, void *stream)
 {
     if (!x || !w || !y)
         return QLL_ERR_NULL;
@@ -301,8 +306,10 @@ int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m,
         return QLL_ERR_SHAPE;
     if (m > 1 && ((n + 127) / 128 > 0x7fffffff || (m + 127) / 128 > 65535))
         return QLL_ERR_SHAPE;
-    if (!aligned16(x) || !aligned16(w) || !aligned16(y))
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (ws && !aligned16(ws)))
         return QLL_ERR_ALIGN;
+    if (gemm_nt_uses_bf16_mfma(w_dtype, m, k) && (!ws || ws_bytes < gemm_nt_workspace(w_dtype, m, n, k)))
+        return QLL_ERR_WORKSPACE;
     if (int rc = check_device())
         return rc;
     static_assert((int)QLL_DTYPE_F32 == (int)QLL_W_F32 && (int)QLL_DTYPE_BF16 == (int)QLL_W_BF16 &&
@@ -310,6 +317,13 @@ int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m,
                   "dtype codes");
     if (m == 1)
         return launched(launch_gemv_nt(x, w, w_dtype, y, n, k, as_stream(stream)));
+    if (gemm_nt_uses_bf16_mfma(w_dtype, m, k)) {
+        const size_t need = gemm_nt_workspace(w_dtype, m, n, k);
+        if (!ws || ws_bytes < need)
+            return QLL_ERR_WORKSPACE;
+        return launched(
+            launch_gemm_nt_bf16_mfma(x, static_cast<const uint16_t *>(w), y, m, n, k, ws, as_stream(stream)));
+    }
     return launched(launch_sgemm_nt(x, w, w_dtype, y, m, n, k, as_stream(stream)));
 }
 

@@ -155,6 +155,310 @@ static hipError_t launch_nt(const float *x, const uint8_t *w, float *y, int64_t 
     return launch_nt_l<WFMT, 64, 4, true>(x, w, y, n, k, s);
 }
 
+// ------------------------------------------------------------------ bf16 weights, m > 1
+// The bf16-weight GEMM on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16)
+// without rounding the activations: every f32 activation is split exactly
+// into three bf16 parts, x = x1 + x2 + x3 (x1 = bf16(x), x2 = bf16(x - x1),
+// x3 = x - x1 - x2: the residuals have at most 16 and 8 significant bits), and
+// each product of two bf16 values is exact in f32, so the three MFMAs per K
+// step accumulate exactly the products the f32 path forms, in f32.  A
+// prepass writes the three parts in the tile layout the kernel reads; the
+// weights are read as they are ([n][k] bf16, never widened in memory).
+//
+// Tiles: 128 x 128 outputs per workgroup, 4 waves of 64 x 64 (2 x 2 MFMA
+// tiles), K steps of 16, three LDS buffers filled by global_load_lds two
+// steps ahead.  A row of a 16-wide K step is 32 bytes (two 16-byte halves,
+// the two lane halves' operands); half h of row r sits at h ^ ((r >> 3) & 1),
+// so the 16 rows one ds_read_b128 serves fall in distinct banks.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define QLL_LDS_NT __attribute__((address_space(3)))
+
+constexpr int kNbM = 128, kNbK = 16, kNbBuf = 3, kNbThreads = 256;
+constexpr int kNbPlane = kNbM * kNbK * 2;  // 4096 bytes: one part of a 128-row K step
+constexpr int kNbAChunk = 3 * kNbPlane;    // the three parts
+// NJ = 32-column tiles per wave: the workgroup covers 64 NJ weight rows
+template <int NJ>
+struct NbCfg {
+    static constexpr int BN = 64 * NJ;
+    static constexpr int WChunk = BN * kNbK * 2; // weight bytes per K step
+    static constexpr int Dma = 3 + NJ / 2;        // loads per wave and stage (3 of activations, NJ/2 of weights)
+};
+
+struct NbPrep {
+    uint8_t *a; // [mp / 128][kp / 16] chunks of kNbAChunk bytes
+    int64_t mp, kp;
+};
+
+__device__ __forceinline__ int nb_half(int r, int h) { return h ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// One workgroup per chunk (128 rows x 16 k); thread (row r, half h) splits
+// the 8 activations x[row][16 kt + 8 h ..] (zero past m or k).
+__global__ __launch_bounds__(256) void nt_bf16_prep_kernel(const float *__restrict__ x, NbPrep p, int64_t m,
+                                                           int64_t k)
+{
+    const int64_t kts = p.kp / kNbK;
+    const int64_t mt = blockIdx.x / kts, kt = blockIdx.x % kts;
+    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+    const int64_t row = mt * kNbM + r, k0 = kt * kNbK + 8 * h;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        v[e] = (row < m && k0 + e < k) ? x[row * k + k0 + e] : 0.0f;
+    uint32_t part[3][4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        uint32_t b[3][2];
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const float x0 = v[e + q];
+            const uint32_t h1 = bf16_bits(x0);
+            const float r1 = x0 - __builtin_bit_cast(float, h1 << 16); // exact
+            const uint32_t h2 = bf16_bits(r1);
+            const float r2 = r1 - __builtin_bit_cast(float, h2 << 16); // exact, at most 8 significant bits
+            b[0][q] = h1;
+            b[1][q] = h2;
+            b[2][q] = bf16_bits(r2); // exact
+        }
+#pragma unroll
+        for (int pp = 0; pp < 3; pp++)
+            part[pp][e >> 1] = b[pp][0] | (b[pp][1] << 16);
+    }
+    uint8_t *chunk = p.a + (size_t)blockIdx.x * kNbAChunk + r * 32 + 16 * nb_half(r, h);
+#pragma unroll
+    for (int pp = 0; pp < 3; pp++)
+        *reinterpret_cast<u32x4 *>(chunk + pp * kNbPlane) = u32x4{part[pp][0], part[pp][1], part[pp][2], part[pp][3]};
+}
+
+template <int NJ>
+struct NbLds {
+    uint8_t a[kNbAChunk];
+    uint8_t w[NbCfg<NJ>::WChunk];
+};
+
+__device__ __forceinline__ void nb_dma16(const void *base, uint32_t off, const QLL_LDS_NT void *lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+                 "s"((uint32_t)(uintptr_t)lds)
+                 : "memory", "m0");
+}
+
+// K step kt into buffer s: the activation chunk (12 KB, three 1 KB loads per
+// wave) and the weight rows (32 bytes each, two lanes per row, 32 rows per
+// load; rows past n load row n - 1, whose outputs are dropped).
+template <int NJ>
+__device__ __forceinline__ void nb_load(const uint8_t *__restrict__ w, const NbPrep &p, int64_t mt, int64_t n0,
+                                        int64_t n, int64_t k, int64_t kt, NbLds<NJ> &s)
+{
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint8_t *ab = p.a + (mt * (p.kp / kNbK) + kt) * kNbAChunk;
+    const QLL_LDS_NT char *as = (const QLL_LDS_NT char *)&s.a[0];
+#pragma unroll
+    for (int j = 0; j < 3; j++) {
+        const int region = 3 * wave + j;
+        nb_dma16(ab + region * 1024, 16u * lane, as + region * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ / 2; j++) {
+        const int q = wave * (NJ / 2) + j; // 32-row group
+        const int row = 32 * q + (lane >> 1);
+        const int64_t grow = n0 + row < n ? n0 + row : n - 1;
+        const uint32_t off = (uint32_t)((grow - n0) * k * 2 + kt * 32 + 16 * nb_half(row, lane & 1));
+        nb_dma16(w + n0 * k * 2, off, (const QLL_LDS_NT char *)&s.w[0] + 1024 * q);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void nb_sync()
+{
+    __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4)); // vmcnt(N) expcnt(7) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// blockIdx.y = split: K steps [split * per, min(kts, (split + 1) * per)),
+// written to y + split * m * n (the workspace's partials when splitting).
+template <int NJ>
+__global__ __launch_bounds__(kNbThreads) void nt_bf16_gemm_kernel(const uint8_t *__restrict__ w, NbPrep p,
+                                                                  float *__restrict__ y, int64_t m, int64_t n,
+                                                                  int64_t k, int64_t per)
+{
+    constexpr int BN = NbCfg<NJ>::BN, DMA = NbCfg<NJ>::Dma;
+    __shared__ NbLds<NJ> lds[kNbBuf];
+    // consecutive workgroups share a weight tile (the row tiles of one column
+    // tile run together and meet its weights in L2)
+    const int64_t mtc = p.mp / kNbM;
+    const int64_t mt = blockIdx.x % mtc, ntile = blockIdx.x / mtc;
+    const int64_t m0 = mt * kNbM, n0 = ntile * BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 32 * NJ;
+    const int64_t kts_all = p.kp / kNbK;
+    const int64_t kb = (int64_t)blockIdx.y * per;
+    const int64_t ke = kb + per < kts_all ? kb + per : kts_all;
+    y += (int64_t)blockIdx.y * m * n;
+
+    f32x16 acc[2][NJ];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < NJ; j++)
+            acc[i][j] = f32x16{};
+
+    // per-lane LDS offsets of the operands (rows of the wave's tiles)
+    uint32_t ao[2], bo[NJ];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int r = wm + 32 * i + lr;
+        ao[i] = (uint32_t)(r * 32 + 16 * nb_half(r, lh));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+        const int c = wn + 32 * j + lr;
+        bo[j] = (uint32_t)(offsetof(NbLds<NJ>, w) + c * 32 + 16 * nb_half(c, lh));
+    }
+
+    nb_load<NJ>(w, p, mt, n0, n, k, kb, lds[0]);
+    nb_load<NJ>(w, p, mt, n0, n, k, kb + 1 < ke ? kb + 1 : ke - 1, lds[1]);
+    nb_sync<DMA>();
+    int cur = 0;
+    for (int64_t kt = kb; kt < ke; kt++) {
+        const int nx2 = cur == 0 ? 2 : cur - 1;
+        // steps past the range reload its last one (never computed)
+        nb_load<NJ>(w, p, mt, n0, n, k, kt + 2 < ke ? kt + 2 : ke - 1, lds[nx2]);
+        const QLL_LDS_NT char *base = (const QLL_LDS_NT char *)&lds[cur];
+        u32x4 a[2][3], b[NJ];
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int pp = 0; pp < 3; pp++)
+                a[i][pp] = *reinterpret_cast<const QLL_LDS_NT u32x4 *>(base + ao[i] + pp * kNbPlane);
+#pragma unroll
+        for (int j = 0; j < NJ; j++)
+            b[j] = *reinterpret_cast<const QLL_LDS_NT u32x4 *>(base + bo[j]);
+#pragma unroll
+        for (int pp = 0; pp < 3; pp++)
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < NJ; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i][pp]),
+                                                                         __builtin_bit_cast(bf16x8, b[j]), acc[i][j],
+                                                                         0, 0, 0);
+        nb_sync<DMA>();
+        cur = cur == 2 ? 0 : cur + 1;
+    }
+    __builtin_amdgcn_s_waitcnt(0x7 << 4); // no load may still be writing this workgroup's LDS
+
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < NJ; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
+                const int64_t col = n0 + wn + 32 * j + lr;
+                if (row < m && col < n)
+                    y[row * n + col] = acc[i][j][v];
+            }
+}
+
+// The bf16 matrix-core path is taken for bf16 weights at m > 1 when k % 16 == 0
+// (weight rows then 32-byte aligned and the K steps whole) and k < 2^23.
+bool gemm_nt_uses_bf16_mfma(int wfmt, int64_t m, int64_t k)
+{
+    return wfmt == QLL_W_BF16 && m > 1 && k % 16 == 0 && k < ((int64_t)1 << 23);
+}
+
+// 256-column tiles (one 64 x 128 tile per wave) when they still give two
+// workgroups per CU, else 128-column tiles; K is split (partials summed in
+// a fixed order by a second kernel) while the tiles leave workgroup slots
+// idle (two per CU), each split keeping at least 32 K steps.  Workspace: the split activations, then
+// the partials.
+struct NbPlan {
+    int nj, splits;
+    int64_t mp, per, tiles;
+    size_t parts_off, total;
+};
+
+static NbPlan nb_plan(int64_t m, int64_t n, int64_t k)
+{
+    NbPlan p;
+    p.mp = (m + kNbM - 1) / kNbM * kNbM;
+    const int64_t mt = p.mp / kNbM, kts = k / kNbK;
+    const int64_t tiles4 = mt * ((n + 255) / 256);
+    p.nj = tiles4 >= 512 ? 4 : 2;
+    p.tiles = p.nj == 4 ? tiles4 : mt * ((n + 127) / 128);
+    int64_t splits = 512 / p.tiles;
+    if (splits > kts / 32)
+        splits = kts / 32;
+    if (splits > 8)
+        splits = 8;
+    if (splits < 2)
+        splits = 1;
+    p.per = (kts + splits - 1) / splits;
+    p.splits = (int)((kts + p.per - 1) / p.per);
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    p.parts_off = up((size_t)mt * (size_t)kts * kNbAChunk);
+    p.total = p.parts_off + (p.splits > 1 ? up((size_t)p.splits * (size_t)(m * n) * sizeof(float)) : 0);
+    return p;
+}
+
+size_t gemm_nt_workspace(int wfmt, int64_t m, int64_t n, int64_t k)
+{
+    if (!gemm_nt_uses_bf16_mfma(wfmt, m, k))
+        return 0;
+    return nb_plan(m, n, k).total;
+}
+
+// y[i] = sum over s of parts[s][i], in split order.
+__global__ __launch_bounds__(256) void nb_sum_splits_kernel(const float *__restrict__ parts, float *__restrict__ y,
+                                                            int64_t count, int splits)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count)
+        return;
+    float v = parts[i];
+    for (int s = 1; s < splits; s++)
+        v += parts[s * count + i];
+    y[i] = v;
+}
+
+hipError_t launch_gemm_nt_bf16_mfma(const float *x, const uint16_t *w, float *y, int64_t m, int64_t n, int64_t k,
+                                    void *ws, hipStream_t s)
+{
+    const NbPlan plan = nb_plan(m, n, k);
+    NbPrep p;
+    p.a = static_cast<uint8_t *>(ws);
+    p.mp = plan.mp;
+    p.kp = k;
+    const int64_t chunks = (p.mp / kNbM) * (k / kNbK);
+    if (chunks > 0x7fffffff || plan.tiles > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(nt_bf16_prep_kernel, dim3((unsigned)chunks), dim3(256), 0, s, x, p, m, k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    float *out = plan.splits > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + plan.parts_off) : y;
+    const uint8_t *wb = reinterpret_cast<const uint8_t *>(w);
+    const dim3 grid((unsigned)plan.tiles, (unsigned)plan.splits);
+    if (plan.nj == 4)
+        hipLaunchKernelGGL(nt_bf16_gemm_kernel<4>, grid, dim3(kNbThreads), 0, s, wb, p, out, m, n, k, plan.per);
+    else
+        hipLaunchKernelGGL(nt_bf16_gemm_kernel<2>, grid, dim3(kNbThreads), 0, s, wb, p, out, m, n, k, plan.per);
+    e = hipGetLastError();
+    if (e != hipSuccess || plan.splits == 1)
+        return e;
+    const int64_t count = m * n;
+    hipLaunchKernelGGL(nb_sum_splits_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, out, y, count,
+                       plan.splits);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv_nt(const float *x, const void *w, int wfmt, float *y, int64_t n, int64_t k, hipStream_t s)
 {
     const uint8_t *wb = static_cast<const uint8_t *>(w);

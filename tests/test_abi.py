@@ -135,11 +135,20 @@ def test_q8w_errors(L):
 
 
 def test_gemm_nt_errors(L):
-    assert L.qll_gemm_nt(NUL, GOOD, 0, GOOD, 2, 2, 2, None) == NULL
-    assert L.qll_gemm_nt(GOOD, GOOD, 3, GOOD, 2, 2, 2, None) == SHAPE
-    assert L.qll_gemm_nt(GOOD, GOOD, -1, GOOD, 2, 2, 2, None) == SHAPE
-    assert L.qll_gemm_nt(GOOD, GOOD, 1, GOOD, 2, 0, 2, None) == SHAPE
-    assert L.qll_gemm_nt(GOOD, MIS, 2, GOOD, 2, 2, 2, None) == ALIGN
+    assert L.qll_gemm_nt(NUL, GOOD, 0, GOOD, 2, 2, 2, NUL, 0, None) == NULL
+    assert L.qll_gemm_nt(GOOD, GOOD, 3, GOOD, 2, 2, 2, NUL, 0, None) == SHAPE
+    assert L.qll_gemm_nt(GOOD, GOOD, -1, GOOD, 2, 2, 2, NUL, 0, None) == SHAPE
+    assert L.qll_gemm_nt(GOOD, GOOD, 1, GOOD, 2, 0, 2, NUL, 0, None) == SHAPE
+    assert L.qll_gemm_nt(GOOD, MIS, 2, GOOD, 2, 2, 2, NUL, 0, None) == ALIGN
+    # bf16 weights, m > 1, k % 16 == 0: the split activations need a workspace
+    assert L.qll_gemm_nt(GOOD, GOOD, 1, GOOD, 2, 8, 32, NUL, 0, None) == WORKSPACE
+    assert L.qll_gemm_nt(GOOD, GOOD, 1, GOOD, 2, 8, 32, MIS, 2 ** 40, None) == ALIGN
+    split_x = 4 * 256 * 3 * 128 * 16 * 2                            # three bf16 copies of X (512 x 4096)
+    assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, 4096, 4096, 4096) == 8 * split_x   # no K split
+    need = qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, 512, 4096, 4096)
+    assert need == split_x + 4 * 512 * 4096 * 4                      # 128 tiles: K split 4 ways, f32 partials
+    assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, 1, 4096, 4096) == 0   # the GEMV needs none
+    assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, 8, 4096, 4100) == 0   # k % 16 != 0: f32 path
 
 
 def test_repacked_sizes(L):

@@ -30,7 +30,8 @@ def run(x, w, wdtype):
     m, k = x.shape
     n = w.shape[0]
     y = empty(m * n, torch.float32)
-    qll.qll_gemm_nt(dev(x), dev(w), DT[wdtype], y, m, n, k)
+    need = qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, m, n, k) if wdtype == "bf16" else 0
+    qll.qll_gemm_nt(dev(x), dev(w), DT[wdtype], y, m, n, k, ws=empty(need) if need else None)
     return host(y).reshape(m, n)
 
 
@@ -56,6 +57,38 @@ def test_gemm_shapes(qll_gpu, wdtype, m, n, k):
     y = run(x, w, wdtype)
     y_ref, mag = O.gemm_nt(x, w, wdtype)
     assert_within(y, y_ref, mag, TOL, f"NT GEMM {wdtype} m={m} n={n} k={k}")
+
+
+# bf16 weights with k % 16 == 0 take the bf16 matrix-core path (three exact
+# bf16 parts of every activation): ragged tiles, one K step, many K steps
+# (33, 1, 4096), (130, 70, 14336) and (512, 256, 4096) split K eight ways;
+# (600, 1100, 64) takes 256-column tiles only if they are numerous enough
+@pytest.mark.parametrize("m,n,k", [(2, 3, 16), (129, 257, 48), (33, 1, 4096), (256, 128, 16), (300, 200, 1008),
+                                   (130, 70, 14336), (512, 256, 4096), (600, 1100, 64)])
+def test_bf16_mfma_shapes(qll_gpu, m, n, k):
+    rng = np.random.default_rng(m + n + k)
+    x = synth.normal_f32(rng, (m, k)) * np.float32(3.0)
+    w = weights(synth.uniform_f32(rng, (n, k)), "bf16")
+    y = run(x, w, "bf16")
+    y_ref, mag = O.gemm_nt(x, w, "bf16")
+    assert_within(y, y_ref, mag, TOL, f"bf16 MFMA m={m} n={n} k={k}")
+
+
+def test_bf16_mfma_activation_split_is_exact(qll_gpu):
+    # activations spanning many binades with full 24-bit significands, and a
+    # one-hot weight row: each output is one activation times a power of two,
+    # so any loss in the three-way split shows up as a bit difference
+    rng = np.random.default_rng(4)
+    m, k = 64, 256
+    x = (rng.uniform(1.0, 2.0, (m, k)) * 2.0 ** rng.integers(-30, 30, (m, k))).astype(np.float32)
+    x *= np.where(rng.random((m, k)) < 0.5, -1, 1).astype(np.float32)
+    n = 16
+    w32 = np.zeros((n, k), np.float32)
+    pos = rng.integers(0, k, n)
+    w32[np.arange(n), pos] = 2.0 ** rng.integers(-8, 8, n)
+    y = run(x, weights(w32, "bf16"), "bf16")
+    want = x[:, pos].astype(np.float64) * w32[np.arange(n), pos].astype(np.float64)
+    assert np.array_equal(y.astype(np.float64), want)
 
 
 @pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16"])
