@@ -64,6 +64,21 @@ def test_fused_f32_gemv(qll_gpu, m, n, k):
         assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
+# n >= 32768 takes the 4-rows-per-lane-group layout: odd block counts (one
+# block per unit), a ragged last row group, several k-chunks
+@pytest.mark.parametrize("m", [1, 2, 5, 8])
+@pytest.mark.parametrize("n,k", [(32771, 96), (40001, 4160), (32768, 1056)])
+def test_large_n_layout(qll_gpu, m, n, k):
+    codes, d_bits, x = _case(m * 31 + n + k, m, n, k)
+    w = pack_q4_0(codes, d_bits)
+    y = host(gemv_f32(w, x, m, n, k)).reshape(m, n)
+    y_ref, mag = _ref(codes, d_bits, x)
+    assert_within(y, y_ref, mag, TOL, f"fused large-n m={m} n={n} k={k}")
+    if m >= 2:
+        y2 = host(q4_gemm(w, quantize_q8_0(x), m, n, k)).reshape(m, n)
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
 def _unit_scale_x(rng, m, k):
     # a +-127 in every block (d = 1 exactly), integers and exact ties elsewhere
     x = rng.integers(-126, 127, (m, k)).astype(np.float32)
