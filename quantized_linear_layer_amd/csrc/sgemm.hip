@@ -194,12 +194,43 @@ __device__ __forceinline__ float sgemm_w_elem(const void *w, int64_t idx)
     return BT == QLL_W_BF16 ? __builtin_bit_cast(float, h << 16) : half_bits_to_float(h);
 }
 
-template <bool VEC, int BT>
+// FULL: the tile lies inside the matrices (m and n multiples of 128, k of 16),
+// so every load is an unconditional 16-byte (8-byte for 16-bit weights) load.
+// The per-element bounds checks of the general path compile to branches and
+// selects that cost more vector-ALU time per k-tile than the MFMAs leave free.
+template <bool VEC, int BT, bool FULL>
 __device__ __forceinline__ void sgemm_load_tile(const float *__restrict__ a, const void *__restrict__ bv, int64_t m,
                                                 int64_t n, int64_t k, int64_t m0, int64_t n0, int64_t k0,
                                                 SgemmTileRegs &t)
 {
     const int tid = threadIdx.x;
+    if (FULL) {
+#pragma unroll
+        for (int it = 0; it < 2; it++) {
+            const float4 v = *reinterpret_cast<const float4 *>(a + (m0 + (tid >> 2) + 64 * it) * k + k0 + 4 * (tid & 3));
+            t.a[it][0] = v.x; t.a[it][1] = v.y; t.a[it][2] = v.z; t.a[it][3] = v.w;
+        }
+#pragma unroll
+        for (int it = 0; it < 2; it++) {
+            if (BT == kBNN) {
+                const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(bv) +
+                                                                   (k0 + (tid >> 5) + 8 * it) * n + n0 + 4 * (tid & 31));
+                t.b[it][0] = v.x; t.b[it][1] = v.y; t.b[it][2] = v.z; t.b[it][3] = v.w;
+            } else if (BT == QLL_W_F32) {
+                const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(bv) +
+                                                                   (n0 + (tid >> 2) + 64 * it) * k + k0 + 4 * (tid & 3));
+                t.b[it][0] = v.x; t.b[it][1] = v.y; t.b[it][2] = v.z; t.b[it][3] = v.w;
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(bv) +
+                                                                 (n0 + (tid >> 2) + 64 * it) * k + k0 + 4 * (tid & 3));
+                const uint32_t h[4] = {v.x & 0xffffu, v.x >> 16, v.y & 0xffffu, v.y >> 16};
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    t.b[it][e] = BT == QLL_W_BF16 ? __builtin_bit_cast(float, h[e] << 16) : half_bits_to_float(h[e]);
+            }
+        }
+        return;
+    }
     // A: 128 rows x 16 k = 512 float4, two per thread
 #pragma unroll
     for (int it = 0; it < 2; it++) {
@@ -289,7 +320,7 @@ __device__ __forceinline__ void sgemm_store_tile(const SgemmTileRegs &t, float (
     }
 }
 
-template <bool VEC, int BT>
+template <bool VEC, int BT, bool FULL>
 __global__ __launch_bounds__(kSgemmThreads) void sgemm_mfma_kernel(const float *__restrict__ a,
                                                                    const void *__restrict__ b,
                                                                    float *__restrict__ c, int64_t m, int64_t n,
@@ -314,14 +345,14 @@ __global__ __launch_bounds__(kSgemmThreads) void sgemm_mfma_kernel(const float *
 
     const int64_t nkt = (k + BK - 1) / BK;
     SgemmTileRegs regs;
-    sgemm_load_tile<VEC, BT>(a, b, m, n, k, m0, n0, 0, regs);
+    sgemm_load_tile<VEC, BT, FULL>(a, b, m, n, k, m0, n0, 0, regs);
     sgemm_store_tile<BT>(regs, As[0], Bs[0]);
     __syncthreads();
 
     for (int64_t kt = 0; kt < nkt; kt++) {
         const int cur = (int)(kt & 1);
         if (kt + 1 < nkt)
-            sgemm_load_tile<VEC, BT>(a, b, m, n, k, m0, n0, (kt + 1) * BK, regs);
+            sgemm_load_tile<VEC, BT, FULL>(a, b, m, n, k, m0, n0, (kt + 1) * BK, regs);
 #pragma unroll
         for (int s = 0; s < BK / 2; s++) {
             const int kk = 2 * s + lh; // lanes 0-31 take k = 2s, lanes 32-63 k = 2s+1
@@ -353,7 +384,7 @@ __global__ __launch_bounds__(kSgemmThreads) void sgemm_mfma_kernel(const float *
             for (int v = 0; v < 16; v++) {
                 const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
                 const int64_t col = n0 + wn + 32 * j + li;
-                if (row < m && col < n)
+                if (FULL || (row < m && col < n))
                     c[row * n + col] = acc[i][j][v];
             }
 }
@@ -361,10 +392,12 @@ __global__ __launch_bounds__(kSgemmThreads) void sgemm_mfma_kernel(const float *
 hipError_t launch_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, int64_t k, hipStream_t s)
 {
     dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
-    if (k % 4 == 0 && n % 4 == 0)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<true, kBNN>), grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
+    if (m % BM == 0 && n % BN == 0 && k % BK == 0)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<true, kBNN, true>), grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
+    else if (k % 4 == 0 && n % 4 == 0)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<true, kBNN, false>), grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
     else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<false, kBNN>), grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<false, kBNN, false>), grid, dim3(kSgemmThreads), 0, s, a, b, c, m, n, k);
     return hipGetLastError();
 }
 
@@ -373,10 +406,12 @@ static hipError_t launch_sgemm_nt_t(const float *a, const void *w, float *c, int
                                     hipStream_t s)
 {
     dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
-    if (k % 4 == 0)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<true, BT>), grid, dim3(kSgemmThreads), 0, s, a, w, c, m, n, k);
+    if (m % BM == 0 && n % BN == 0 && k % BK == 0)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<true, BT, true>), grid, dim3(kSgemmThreads), 0, s, a, w, c, m, n, k);
+    else if (k % 4 == 0)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<true, BT, false>), grid, dim3(kSgemmThreads), 0, s, a, w, c, m, n, k);
     else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<false, BT>), grid, dim3(kSgemmThreads), 0, s, a, w, c, m, n, k);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<false, BT, false>), grid, dim3(kSgemmThreads), 0, s, a, w, c, m, n, k);
     return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@ def test_gemv_shapes(qll_gpu, wdtype, n, k):
 
 @pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("m,n,k", [(2, 3, 5), (37, 68, 100), (130, 129, 320), (128, 128, 4096), (257, 131, 1001),
-                                   (64, 300, 4)])
+                                   (64, 300, 4), (256, 384, 48)])
 def test_gemm_shapes(qll_gpu, wdtype, m, n, k):
     rng = np.random.default_rng(m * 7 + n * 3 + k)
     x = synth.uniform_f32(rng, (m, k))

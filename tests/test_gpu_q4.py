@@ -67,6 +67,15 @@ def test_gemv_adversarial_shapes(qll_gpu, n, k):
     _gemv_check(codes, d_bits, x, f"GEMV n={n} k={k}")
 
 
+@pytest.mark.parametrize("n,k", [(5, 49152), (9, 28672), (3, 16416)])
+def test_gemv_largest_k(qll_gpu, n, k):
+    # k = 49152 is the largest the entry accepts (60 KiB of staged activation
+    # in LDS); 16416 (513 blocks) is the first k past the two blocks per thread
+    # that the staging holds in registers
+    codes, d_bits, x = rand_case(n * 31 + k, 1, n, k)
+    _gemv_check(codes, d_bits, x, f"GEMV n={n} k={k}")
+
+
 @pytest.mark.parametrize("s", range(4))
 def test_gemv_8b_shapes_full(qll_gpu, s):
     codes, d_bits, x = synth.q4_decode(s)

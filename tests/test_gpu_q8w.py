@@ -57,6 +57,14 @@ def test_gemv_shapes(qll_gpu, n, k):
     assert_within(y, y_ref[0], mag[0], TOL, f"Q8_0 GEMV n={n} k={k}")
 
 
+@pytest.mark.parametrize("n,k", [(5, 49152), (4, 28704)])
+def test_gemv_largest_k(qll_gpu, n, k):
+    codes, d_bits, x = _case(n * 100 + k, 1, n, k)
+    y = host(gemv(upload_q8w(codes, d_bits), quantize_q8_0(x), n, k))
+    y_ref, mag = O.q8_0_q8_0(O.pack_q8_0(codes, d_bits), O.quantize_q8_0(x), 1, n, k)
+    assert_within(y, y_ref[0], mag[0], TOL, f"Q8_0 GEMV n={n} k={k}")
+
+
 @pytest.mark.parametrize("s", range(4))
 def test_gemv_8b_shapes_full(qll_gpu, s):
     codes, d_bits, x = synth.q8w_decode(s)

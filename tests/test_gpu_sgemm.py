@@ -22,7 +22,7 @@ def _check(a, b, what):
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 1), (2, 3, 5), (7, 11, 13), (33, 17, 23), (48, 192, 128), (130, 257, 300),
                                    (128, 128, 16), (129, 130, 17), (256, 64, 1000), (1, 7, 3), (1, 4096, 33),
-                                   (1, 300, 4096), (1, 1000, 1000)])
+                                   (1, 300, 4096), (1, 1000, 1000), (256, 384, 48), (384, 128, 1024)])
 def test_shapes(qll_gpu, m, n, k):
     rng = np.random.default_rng(m * 7919 + n * 31 + k)
     a = synth.uniform_f32(rng, (m, k))
