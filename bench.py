@@ -38,7 +38,11 @@ of the step.  The operations of the widened rows (repacked weights, Q8_0
 weights, transposed-B) are measured in the same run, in passes of their own,
 and reported with `"in_step": false`; they are not part of a step.
 `cpu_baseline` times the oracle (the test suite's plain C reference, never
-tuned) on the same decode GEMVs on the host's cores.
+tuned) on the same decode GEMVs on the host's cores.  `device` records the
+GPU, its compute-unit count, the HIP version and the bandwidth of a plain
+1 GiB device copy, which HBM-bound rows also report as a second denominator
+(`frac_of_copy`); a row whose launch times vary by more than 8% (coefficient
+of variation) is flagged `noisy`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -71,6 +75,7 @@ def parse():
 
 # Operations of the rows beyond the hot path's core (small-m, repacked weights,
 # Q8_0 weights, transposed-B): timed the same way, but not part of a step.
+NOISY_CV = 0.08  # coefficient of variation above which a row is flagged noisy
 EXTRA_PREFIXES = ("q4r_gemm", "q8w_gemv", "q8r_gemm", "nt_")
 
 
@@ -92,6 +97,17 @@ class Op:
         peak = PEAK_TFLOPS[self.peak_key]
         return {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s" if self.peak_key != "i8"
                 else "TOP/s", "frac": achieved / peak}
+
+
+def q8_0_block_bytes(np, codes, d_bits):
+    """The raw Q8_0 weight draws laid out as block_q8_0 records: little-endian
+    binary16 d, then the block's 32 int8 codes (34 bytes per block)."""
+    n, k = codes.shape
+    nb = k // 32
+    blk = np.empty((n, nb, 34), np.uint8)
+    blk[:, :, 0:2] = np.ascontiguousarray(d_bits.astype("<u2")).view(np.uint8).reshape(n, nb, 2)
+    blk[:, :, 2:] = codes.reshape(n, nb, 32).view(np.uint8)
+    return blk.reshape(-1)
 
 
 def build_ops(qll, synth, torch, np, dev, only):
@@ -165,13 +181,12 @@ def build_ops(qll, synth, torch, np, dev, only):
             qll.qll_quantize_q8_0(xd, xqd, 1, k)
 
     # ---------------------------------------------------------------- Q8_0 weights
-    import oracle as O  # host-side packing of the raw weight draws into Q8_0 blocks (set-up only)
     for s, (k, n) in enumerate(synth.SHAPES_8B):
         need_dec, need_pre = want(f"q8w_gemv_{s}"), want(f"q8r_gemm_{s}")
         if not (need_dec or need_pre):
             continue
         codes, d_bits, x = synth.q8w_decode(s)
-        w0 = to_dev(O.pack_q8_0(codes, d_bits).reshape(-1))
+        w0 = to_dev(q8_0_block_bytes(np, codes, d_bits))
         del codes, d_bits
         wbytes = w0.numel()
         if need_dec:
@@ -394,6 +409,7 @@ def main():
         op.batch_ms = [e0.elapsed_time(e1) / op.reps for e0, e1 in pairs]
         del graph
     print("bench: timed back-to-back launches (graph replays)", file=sys.stderr, flush=True)
+    copy_gbs = measured_copy_gbs(torch, dev, stream, args.steps)
 
     kernels = []
     for op in ops:
@@ -411,6 +427,9 @@ def main():
         if op.name == "ternary_gemm":
             entry["hbm_gbs"] = op.nbytes / (ms * 1e-3) / 1e9
             entry["hbm_frac"] = entry["hbm_gbs"] / PEAK_HBM_GBS
+        if rl["bound"] == "hbm" and copy_gbs:
+            entry["frac_of_copy"] = rl["achieved"] / copy_gbs
+        entry["noisy"] = entry["cv"] > NOISY_CV
         kernels.append(entry)
         print(f"  {op.name:22s} {ms * 1e3:10.2f} us (in step {entry['ms_in_step'] * 1e3:8.2f})  "
               f"{rl['achieved']:10.1f} {rl['unit']:8s} "
@@ -466,8 +485,37 @@ def main():
                                "launches on rotating weight copies) over the four shapes",
                    "parallelism": "single GPU"},
         "per_format": per_format, "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+        "device": device_record(torch, dev, copy_gbs),
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_copy_gbs(torch, dev, stream, reps):
+    """Secondary HBM denominator: a plain 1 GiB device-to-device copy (read +
+    write bytes over its time), median of `reps` event-timed copies."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(max(3, reps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    t = sorted(ts)[len(ts) // 2]
+    return 2 * (1 << 30) / (t * 1e-3) / 1e9
+
+
+def device_record(torch, dev, copy_gbs):
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_bytes": p.total_memory, "hip": torch.version.hip, "torch": torch.__version__,
+            "copy_1gib_gbs": copy_gbs, "date_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime())}
 
 
 def traffic_for(op_name):
