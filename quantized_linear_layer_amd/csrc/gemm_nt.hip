@@ -195,20 +195,9 @@ __device__ __forceinline__ int nb_half(int r, int h) { return h ^ ((r >> 3) & 1)
 
 __device__ __forceinline__ uint32_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-// One workgroup per chunk (128 rows x 16 k); thread (row r, half h) splits
-// the 8 activations x[row][16 kt + 8 h ..] (zero past m or k).
-__global__ __launch_bounds__(256) void nt_bf16_prep_kernel(const float *__restrict__ x, NbPrep p, int64_t m,
-                                                           int64_t k)
+// Three exact bf16 parts of 8 activations, packed two per dword per part.
+__device__ __forceinline__ void nb_split8(const float v[8], uint32_t part[3][4])
 {
-    const int64_t kts = p.kp / kNbK;
-    const int64_t mt = blockIdx.x / kts, kt = blockIdx.x % kts;
-    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
-    const int64_t row = mt * kNbM + r, k0 = kt * kNbK + 8 * h;
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++)
-        v[e] = (row < m && k0 + e < k) ? x[row * k + k0 + e] : 0.0f;
-    uint32_t part[3][4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
         uint32_t b[3][2];
@@ -227,10 +216,58 @@ __global__ __launch_bounds__(256) void nt_bf16_prep_kernel(const float *__restri
         for (int pp = 0; pp < 3; pp++)
             part[pp][e >> 1] = b[pp][0] | (b[pp][1] << 16);
     }
+}
+
+
+// One workgroup per chunk (128 rows x 16 k); thread (row r, half h) splits
+// the 8 activations x[row][16 kt + 8 h ..] (zero past m or k).
+__global__ __launch_bounds__(256) void nt_bf16_prep_kernel(const float *__restrict__ x, NbPrep p, int64_t m,
+                                                           int64_t k)
+{
+    const int64_t kts = p.kp / kNbK;
+    const int64_t mt = blockIdx.x / kts, kt = blockIdx.x % kts;
+    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+    const int64_t row = mt * kNbM + r, k0 = kt * kNbK + 8 * h;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        v[e] = (row < m && k0 + e < k) ? x[row * k + k0 + e] : 0.0f;
+    uint32_t part[3][4];
+    nb_split8(v, part);
     uint8_t *chunk = p.a + (size_t)blockIdx.x * kNbAChunk + r * 32 + 16 * nb_half(r, h);
 #pragma unroll
     for (int pp = 0; pp < 3; pp++)
         *reinterpret_cast<u32x4 *>(chunk + pp * kNbPlane) = u32x4{part[pp][0], part[pp][1], part[pp][2], part[pp][3]};
+}
+
+// Whole-tile form (m % 128 == 0, k % 32 == 0): one workgroup per pair of
+// chunks (128 rows x 32 k); thread (row r, half h) reads x[row][32 q + 16 h ..
+// + 15] with four 16-byte loads (a thread pair covers the row's 128-byte
+// line, where the form above splits it between two workgroups and loads it
+// one float at a time) and writes both of its 8-activation halves to chunk
+// 2 q + h, laid out as above.
+__global__ __launch_bounds__(256) void nt_bf16_prep_full_kernel(const float *__restrict__ x, NbPrep p, int64_t k)
+{
+    const int64_t kts = p.kp / kNbK, pairs = kts / 2;
+    const int64_t mt = blockIdx.x / pairs, q = blockIdx.x % pairs;
+    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+    const float *src = x + (mt * kNbM + r) * k + 32 * q + 16 * h;
+    float v[16];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        const float4 f = *reinterpret_cast<const float4 *>(src + 4 * c);
+        v[4 * c] = f.x; v[4 * c + 1] = f.y; v[4 * c + 2] = f.z; v[4 * c + 3] = f.w;
+    }
+    uint8_t *chunk = p.a + (size_t)(mt * kts + 2 * q + h) * kNbAChunk + r * 32;
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) {
+        uint32_t part[3][4];
+        nb_split8(v + 8 * hh, part);
+#pragma unroll
+        for (int pp = 0; pp < 3; pp++)
+            *reinterpret_cast<u32x4 *>(chunk + 16 * nb_half(r, hh) + pp * kNbPlane) =
+                u32x4{part[pp][0], part[pp][1], part[pp][2], part[pp][3]};
+    }
 }
 
 template <int NJ>
@@ -439,7 +476,10 @@ hipError_t launch_gemm_nt_bf16_mfma(const float *x, const uint16_t *w, float *y,
     const int64_t chunks = (p.mp / kNbM) * (k / kNbK);
     if (chunks > 0x7fffffff || plan.tiles > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(nt_bf16_prep_kernel, dim3((unsigned)chunks), dim3(256), 0, s, x, p, m, k);
+    if (m % kNbM == 0 && k % (2 * kNbK) == 0)
+        hipLaunchKernelGGL(nt_bf16_prep_full_kernel, dim3((unsigned)(chunks / 2)), dim3(256), 0, s, x, p, k);
+    else
+        hipLaunchKernelGGL(nt_bf16_prep_kernel, dim3((unsigned)chunks), dim3(256), 0, s, x, p, m, k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

@@ -126,26 +126,32 @@ __global__ __launch_bounds__(kSgemvThreads) void sgemv_partial_kernel(const floa
     }
 }
 
-// c[j] = sum over chunks of ws[s][j]: wave w adds chunks w, w+4, ... in order
-// (independent loads, unrolled), then the four waves combine in LDS.
+// c[j] = sum over chunks of ws[s][j]: wave w adds chunks w, w+4, ... in order,
+// then the four waves combine in LDS in a fixed order.  A wave issues the
+// loads of up to kFinishBatch of its chunks (clamped to valid rows) before the
+// first add, so the partial sums, which come from other XCDs' writes, cost one
+// memory round trip per batch rather than one per few chunks.
+constexpr int kFinishBatch = 16;
+
 __global__ __launch_bounds__(256) void sgemv_finish_kernel(const float *__restrict__ ws, float *__restrict__ c,
                                                            int64_t n, int64_t ks)
 {
     __shared__ float s_part[3][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t jc = j < n ? j : n - 1;
     float v = 0.0f;
-    if (j < n) {
-        int64_t s = wave;
-        for (; s + 12 < ks; s += 16) {
-            float t0 = ws[s * n + j], t1 = ws[(s + 4) * n + j], t2 = ws[(s + 8) * n + j], t3 = ws[(s + 12) * n + j];
-            v += t0;
-            v += t1;
-            v += t2;
-            v += t3;
+    for (int64_t s0 = wave; s0 < ks; s0 += 4 * kFinishBatch) {
+        float t[kFinishBatch];
+#pragma unroll
+        for (int u = 0; u < kFinishBatch; u++) {
+            const int64_t sc = s0 + 4 * u < ks ? s0 + 4 * u : ks - 1;
+            t[u] = ws[sc * n + jc];
         }
-        for (; s < ks; s += 4)
-            v += ws[s * n + j];
+#pragma unroll
+        for (int u = 0; u < kFinishBatch; u++)
+            if (s0 + 4 * u < ks)
+                v += t[u];
     }
     if (wave > 0)
         s_part[wave - 1][lane] = v;

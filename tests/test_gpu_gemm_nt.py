@@ -64,7 +64,7 @@ def test_gemm_shapes(qll_gpu, wdtype, m, n, k):
 # (33, 1, 4096), (130, 70, 14336) and (512, 256, 4096) split K eight ways;
 # (600, 1100, 64) takes 256-column tiles only if they are numerous enough
 @pytest.mark.parametrize("m,n,k", [(2, 3, 16), (129, 257, 48), (33, 1, 4096), (256, 128, 16), (300, 200, 1008),
-                                   (130, 70, 14336), (512, 256, 4096), (600, 1100, 64)])
+                                   (130, 70, 14336), (512, 256, 4096), (600, 1100, 64), (256, 200, 96), (128, 64, 32)])
 def test_bf16_mfma_shapes(qll_gpu, m, n, k):
     rng = np.random.default_rng(m + n + k)
     x = synth.normal_f32(rng, (m, k)) * np.float32(3.0)
