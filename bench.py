@@ -256,11 +256,13 @@ def build_ops(qll, synth, torch, np, dev, only):
                               esz * N * K + 4 * K + 4 * N, 2 * N * K, "hbm"))
             if want(f"nt_gemm_{name}"):
                 cd = torch.empty(M * N, dtype=torch.float32, device=dev)
-                bf = name == "bf16"
-                need = qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, M, N, K) if bf else 0
+                bf = name in ("bf16", "f16")
+                op_code = {"bf16": qll.QLL_OP_GEMM_NT_BF16, "f16": qll.QLL_OP_GEMM_NT_F16}.get(name)
+                need = qll.qll_workspace_bytes(op_code, M, N, K) if bf else 0
                 wsn = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
-                # bf16 weights run on the bf16 matrix core (three bf16 MFMAs per
-                # product of an f32 activation): fraction of the bf16 peak
+                # bf16 weights, and f16 weights given a workspace, run on the
+                # bf16 matrix core (three, resp. five, bf16 MFMAs per product of
+                # an f32 activation): fraction of the bf16 peak
                 ops.append(Op(f"nt_gemm_{name}_4096", f"{name}_nt", "prefill",
                               lambda w=w, cd=cd, code=code, wsn=wsn: qll.qll_gemm_nt(ad, w, code, cd, M, N, K, ws=wsn),
                               4 * M * K + esz * N * K + 4 * M * N, 2 * M * N * K, "mfma", "bf16" if bf else "f32"))

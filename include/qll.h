@@ -72,7 +72,8 @@ enum {
     QLL_OP_TERNARY_GEMM = 3,
     QLL_OP_Q4_0_REPACKED_GEMM = 4,
     QLL_OP_Q8_0_REPACKED_GEMM = 5,
-    QLL_OP_GEMM_NT_BF16 = 6 /* qll_gemm_nt with QLL_DTYPE_BF16 weights */
+    QLL_OP_GEMM_NT_BF16 = 6, /* qll_gemm_nt with QLL_DTYPE_BF16 weights */
+    QLL_OP_GEMM_NT_F16 = 7   /* qll_gemm_nt with QLL_DTYPE_F16 weights on the bf16 matrix core */
 };
 
 /* Bytes of device workspace `op` needs at this shape (0 if none); SIZE_MAX if
@@ -228,14 +229,19 @@ int qll_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, in
  * never rounded; accumulation in f32 (tolerance 1e-5 * sum_p |x * w| against
  * an f64 sum).  m == 1 runs a row-dot GEMV (bandwidth-bound: W is read once).
  * m > 1 runs a matrix-core GEMM: on the f32 matrix core with the weights
- * widened in registers, or, for bf16 weights with k % 16 == 0, on the bf16
- * matrix core with every activation split exactly into three bf16 parts (each
- * bf16 x bf16 product is exact in f32, so the same products are accumulated).
- * Any k >= 1.  ws/ws_bytes: at least
- * qll_workspace_bytes(QLL_OP_GEMM_NT_BF16, m, n, k) bytes when w_dtype is
- * QLL_DTYPE_BF16 (the split activations; 0 when that path does not run),
- * none otherwise; contents on return unspecified.  QLL_ERR_SHAPE for an
- * unknown w_dtype. */
+ * widened in registers, or, when k % 16 == 0, on the bf16 matrix core with
+ * every activation split exactly into three bf16 parts: bf16 weights as
+ * stored (each bf16 x bf16 product is exact in f32, so the same products are
+ * accumulated), and f16 weights, when a workspace is passed, split exactly
+ * into two bf16 parts (five of the six part products are accumulated; the
+ * sixth is at most 2^-27 of x * w).  Any k >= 1.  ws/ws_bytes: bf16 weights
+ * need at least qll_workspace_bytes(QLL_OP_GEMM_NT_BF16, m, n, k) bytes (the
+ * split activations and, when K is split, partial sums; 0 when that path does
+ * not run); f16 weights take the bf16 matrix core when ws is not NULL, which
+ * must then hold qll_workspace_bytes(QLL_OP_GEMM_NT_F16, m, n, k) bytes (also
+ * the two weight planes, 4 bytes per weight), and the f32 matrix core when ws
+ * is NULL; f32 weights ignore ws.  Contents on return unspecified.
+ * QLL_ERR_SHAPE for an unknown w_dtype. */
 int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                 size_t ws_bytes, void *stream);
 

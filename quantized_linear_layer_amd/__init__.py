@@ -21,6 +21,7 @@ QLL_OP_TERNARY_GEMM = 3
 QLL_OP_Q4_0_REPACKED_GEMM = 4
 QLL_OP_Q8_0_REPACKED_GEMM = 5
 QLL_OP_GEMM_NT_BF16 = 6
+QLL_OP_GEMM_NT_F16 = 7
 QLL_DTYPE_F32, QLL_DTYPE_BF16, QLL_DTYPE_F16 = 0, 1, 2
 
 Q4_0_BLOCK_BYTES = 18
@@ -222,9 +223,16 @@ def qll_sgemm(a, b, c, m, n, k, ws=None, stream=None):
 def qll_gemm_nt(x, w, w_dtype, y, m, n, k, ws=None, stream=None):
     """Y = X.W^T with W [n][k] of element type w_dtype (QLL_DTYPE_F32/BF16/F16);
     bf16 weights at m > 1 may need a workspace (qll_workspace_bytes with
-    QLL_OP_GEMM_NT_BF16)."""
+    QLL_OP_GEMM_NT_BF16); f16 weights run on the bf16 matrix core when a
+    workspace of qll_workspace_bytes(QLL_OP_GEMM_NT_F16, ...) bytes is passed,
+    on the f32 matrix core otherwise."""
     esize = 4 if w_dtype == QLL_DTYPE_F32 else 2
-    need = qll_workspace_bytes(QLL_OP_GEMM_NT_BF16, m, n, k) if w_dtype == QLL_DTYPE_BF16 else 0
+    if w_dtype == QLL_DTYPE_BF16:
+        need = qll_workspace_bytes(QLL_OP_GEMM_NT_BF16, m, n, k)
+    elif w_dtype == QLL_DTYPE_F16 and ws is not None:
+        need = qll_workspace_bytes(QLL_OP_GEMM_NT_F16, m, n, k)
+    else:
+        need = 0
     wsp, wsb = _ws(ws, need) if need != 2 ** 64 - 1 else (None, 0)
     _call("qll_gemm_nt", _ptr(x, m * k * 4, "x"), _ptr(w, n * k * esize, "w"), int(w_dtype), _ptr(y, m * n * 4, "y"),
           m, n, k, wsp, wsb, _stream(stream))

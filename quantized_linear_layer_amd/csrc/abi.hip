@@ -97,9 +97,10 @@ size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k)
             return SIZE_MAX;
         return 0;
     case QLL_OP_GEMM_NT_BF16:
+    case QLL_OP_GEMM_NT_F16:
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n))
             return SIZE_MAX;
-        return gemm_nt_workspace(QLL_W_BF16, m, n, k);
+        return gemm_nt_workspace(op == QLL_OP_GEMM_NT_BF16 ? QLL_W_BF16 : QLL_W_F16, m, n, k);
     case QLL_OP_Q4_0_REPACKED_GEMM:
     case QLL_OP_Q8_0_REPACKED_GEMM:
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
@@ -308,7 +309,12 @@ int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m,
         return QLL_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (ws && !aligned16(ws)))
         return QLL_ERR_ALIGN;
-    if (gemm_nt_uses_bf16_mfma(w_dtype, m, k) && (!ws || ws_bytes < gemm_nt_workspace(w_dtype, m, n, k)))
+    // bf16 weights at m > 1 always run on the bf16 matrix core and need the
+    // workspace; f16 weights do when a workspace is passed, else they are
+    // widened on the f32 matrix core
+    const bool core = gemm_nt_bf16_core_shape(m, k) &&
+                      (w_dtype == QLL_DTYPE_BF16 || (w_dtype == QLL_DTYPE_F16 && ws != nullptr));
+    if (core && (!ws || ws_bytes < gemm_nt_workspace(w_dtype, m, n, k)))
         return QLL_ERR_WORKSPACE;
     if (int rc = check_device())
         return rc;
@@ -317,13 +323,9 @@ int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m,
                   "dtype codes");
     if (m == 1)
         return launched(launch_gemv_nt(x, w, w_dtype, y, n, k, as_stream(stream)));
-    if (gemm_nt_uses_bf16_mfma(w_dtype, m, k)) {
-        const size_t need = gemm_nt_workspace(w_dtype, m, n, k);
-        if (!ws || ws_bytes < need)
-            return QLL_ERR_WORKSPACE;
-        return launched(
-            launch_gemm_nt_bf16_mfma(x, static_cast<const uint16_t *>(w), y, m, n, k, ws, as_stream(stream)));
-    }
+    if (core)
+        return launched(launch_gemm_nt_bf16_mfma(x, static_cast<const uint16_t *>(w), w_dtype, y, m, n, k, ws,
+                                                 as_stream(stream)));
     return launched(launch_sgemm_nt(x, w, w_dtype, y, m, n, k, as_stream(stream)));
 }
 

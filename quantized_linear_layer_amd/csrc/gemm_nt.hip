@@ -179,11 +179,13 @@ constexpr int kNbM = 128, kNbK = 16, kNbBuf = 3, kNbThreads = 256;
 constexpr int kNbPlane = kNbM * kNbK * 2;  // 4096 bytes: one part of a 128-row K step
 constexpr int kNbAChunk = 3 * kNbPlane;    // the three parts
 // NJ = 32-column tiles per wave: the workgroup covers 64 NJ weight rows
-template <int NJ>
+// NW weight planes: 1 for bf16 weights (used as stored), 2 for f16 weights
+// (each split exactly into two bf16 parts by nt_f16_split_kernel).
+template <int NJ, int NW>
 struct NbCfg {
     static constexpr int BN = 64 * NJ;
-    static constexpr int WChunk = BN * kNbK * 2; // weight bytes per K step
-    static constexpr int Dma = 3 + NJ / 2;        // loads per wave and stage (3 of activations, NJ/2 of weights)
+    static constexpr int WChunk = BN * kNbK * 2; // bytes of one weight plane per K step
+    static constexpr int Dma = 3 + NW * NJ / 2;   // loads per wave and stage (3 of activations, NJ/2 per plane)
 };
 
 struct NbPrep {
@@ -270,10 +272,10 @@ __global__ __launch_bounds__(256) void nt_bf16_prep_full_kernel(const float *__r
     }
 }
 
-template <int NJ>
+template <int NJ, int NW>
 struct NbLds {
     uint8_t a[kNbAChunk];
-    uint8_t w[NbCfg<NJ>::WChunk];
+    uint8_t w[NW][NbCfg<NJ, NW>::WChunk];
 };
 
 __device__ __forceinline__ void nb_dma16(const void *base, uint32_t off, const QLL_LDS_NT void *lds)
@@ -284,11 +286,12 @@ __device__ __forceinline__ void nb_dma16(const void *base, uint32_t off, const Q
 }
 
 // K step kt into buffer s: the activation chunk (12 KB, three 1 KB loads per
-// wave) and the weight rows (32 bytes each, two lanes per row, 32 rows per
-// load; rows past n load row n - 1, whose outputs are dropped).
-template <int NJ>
-__device__ __forceinline__ void nb_load(const uint8_t *__restrict__ w, const NbPrep &p, int64_t mt, int64_t n0,
-                                        int64_t n, int64_t k, int64_t kt, NbLds<NJ> &s)
+// wave) and the weight rows of each plane (32 bytes each, two lanes per row,
+// 32 rows per load; rows past n load row n - 1, whose outputs are dropped).
+// Plane ww starts at w + ww * plane bytes.
+template <int NJ, int NW>
+__device__ __forceinline__ void nb_load(const uint8_t *__restrict__ w, int64_t plane, const NbPrep &p, int64_t mt,
+                                        int64_t n0, int64_t n, int64_t k, int64_t kt, NbLds<NJ, NW> &s)
 {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t *ab = p.a + (mt * (p.kp / kNbK) + kt) * kNbAChunk;
@@ -299,13 +302,15 @@ __device__ __forceinline__ void nb_load(const uint8_t *__restrict__ w, const NbP
         nb_dma16(ab + region * 1024, 16u * lane, as + region * 1024);
     }
 #pragma unroll
-    for (int j = 0; j < NJ / 2; j++) {
-        const int q = wave * (NJ / 2) + j; // 32-row group
-        const int row = 32 * q + (lane >> 1);
-        const int64_t grow = n0 + row < n ? n0 + row : n - 1;
-        const uint32_t off = (uint32_t)((grow - n0) * k * 2 + kt * 32 + 16 * nb_half(row, lane & 1));
-        nb_dma16(w + n0 * k * 2, off, (const QLL_LDS_NT char *)&s.w[0] + 1024 * q);
-    }
+    for (int ww = 0; ww < NW; ww++)
+#pragma unroll
+        for (int j = 0; j < NJ / 2; j++) {
+            const int q = wave * (NJ / 2) + j; // 32-row group
+            const int row = 32 * q + (lane >> 1);
+            const int64_t grow = n0 + row < n ? n0 + row : n - 1;
+            const uint32_t off = (uint32_t)((grow - n0) * k * 2 + kt * 32 + 16 * nb_half(row, lane & 1));
+            nb_dma16(w + ww * plane + n0 * k * 2, off, (const QLL_LDS_NT char *)&s.w[ww][0] + 1024 * q);
+        }
 }
 
 template <int N>
@@ -319,13 +324,13 @@ __device__ __forceinline__ void nb_sync()
 
 // blockIdx.y = split: K steps [split * per, min(kts, (split + 1) * per)),
 // written to y + split * m * n (the workspace's partials when splitting).
-template <int NJ>
-__global__ __launch_bounds__(kNbThreads) void nt_bf16_gemm_kernel(const uint8_t *__restrict__ w, NbPrep p,
-                                                                  float *__restrict__ y, int64_t m, int64_t n,
-                                                                  int64_t k, int64_t per)
+template <int NJ, int NW>
+__global__ __launch_bounds__(kNbThreads) void nt_bf16_gemm_kernel(const uint8_t *__restrict__ w, int64_t plane,
+                                                                  NbPrep p, float *__restrict__ y, int64_t m,
+                                                                  int64_t n, int64_t k, int64_t per)
 {
-    constexpr int BN = NbCfg<NJ>::BN, DMA = NbCfg<NJ>::Dma;
-    __shared__ NbLds<NJ> lds[kNbBuf];
+    constexpr int BN = NbCfg<NJ, NW>::BN, DMA = NbCfg<NJ, NW>::Dma;
+    __shared__ NbLds<NJ, NW> lds[kNbBuf];
     // consecutive workgroups share a weight tile (the row tiles of one column
     // tile run together and meet its weights in L2)
     const int64_t mtc = p.mp / kNbM;
@@ -356,36 +361,44 @@ __global__ __launch_bounds__(kNbThreads) void nt_bf16_gemm_kernel(const uint8_t 
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
         const int c = wn + 32 * j + lr;
-        bo[j] = (uint32_t)(offsetof(NbLds<NJ>, w) + c * 32 + 16 * nb_half(c, lh));
+        using Lds = NbLds<NJ, NW>;
+        bo[j] = (uint32_t)(offsetof(Lds, w) + c * 32 + 16 * nb_half(c, lh));
     }
 
-    nb_load<NJ>(w, p, mt, n0, n, k, kb, lds[0]);
-    nb_load<NJ>(w, p, mt, n0, n, k, kb + 1 < ke ? kb + 1 : ke - 1, lds[1]);
+    nb_load<NJ, NW>(w, plane, p, mt, n0, n, k, kb, lds[0]);
+    nb_load<NJ, NW>(w, plane, p, mt, n0, n, k, kb + 1 < ke ? kb + 1 : ke - 1, lds[1]);
     nb_sync<DMA>();
     int cur = 0;
     for (int64_t kt = kb; kt < ke; kt++) {
         const int nx2 = cur == 0 ? 2 : cur - 1;
         // steps past the range reload its last one (never computed)
-        nb_load<NJ>(w, p, mt, n0, n, k, kt + 2 < ke ? kt + 2 : ke - 1, lds[nx2]);
+        nb_load<NJ, NW>(w, plane, p, mt, n0, n, k, kt + 2 < ke ? kt + 2 : ke - 1, lds[nx2]);
         const QLL_LDS_NT char *base = (const QLL_LDS_NT char *)&lds[cur];
-        u32x4 a[2][3], b[NJ];
+        u32x4 a[2][3], b[NW][NJ];
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
             for (int pp = 0; pp < 3; pp++)
                 a[i][pp] = *reinterpret_cast<const QLL_LDS_NT u32x4 *>(base + ao[i] + pp * kNbPlane);
 #pragma unroll
-        for (int j = 0; j < NJ; j++)
-            b[j] = *reinterpret_cast<const QLL_LDS_NT u32x4 *>(base + bo[j]);
+        for (int ww = 0; ww < NW; ww++)
 #pragma unroll
-        for (int pp = 0; pp < 3; pp++)
+            for (int j = 0; j < NJ; j++)
+                b[ww][j] = *reinterpret_cast<const QLL_LDS_NT u32x4 *>(base + bo[j] + ww * NbCfg<NJ, NW>::WChunk);
+        // activation part pp against weight plane ww; with two weight planes
+        // the product of the two smallest parts (at most 2^-27 of x * w, an
+        // eighth of one f32 rounding of the sum) is left out
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+        for (int ww = 0; ww < NW; ww++)
 #pragma unroll
-                for (int j = 0; j < NJ; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i][pp]),
-                                                                         __builtin_bit_cast(bf16x8, b[j]), acc[i][j],
-                                                                         0, 0, 0);
+            for (int pp = 0; pp < (ww == 0 ? 3 : 2); pp++)
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int j = 0; j < NJ; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i][pp]),
+                                                                             __builtin_bit_cast(bf16x8, b[ww][j]),
+                                                                             acc[i][j], 0, 0, 0);
         nb_sync<DMA>();
         cur = cur == 2 ? 0 : cur + 1;
     }
@@ -404,31 +417,34 @@ __global__ __launch_bounds__(kNbThreads) void nt_bf16_gemm_kernel(const uint8_t 
             }
 }
 
-// The bf16 matrix-core path is taken for bf16 weights at m > 1 when k % 16 == 0
-// (weight rows then 32-byte aligned and the K steps whole) and k < 2^23.
-bool gemm_nt_uses_bf16_mfma(int wfmt, int64_t m, int64_t k)
+// The bf16 matrix-core path needs m > 1, k % 16 == 0 (weight rows then
+// 32-byte aligned and the K steps whole) and k < 2^23.
+bool gemm_nt_bf16_core_shape(int64_t m, int64_t k)
 {
-    return wfmt == QLL_W_BF16 && m > 1 && k % 16 == 0 && k < ((int64_t)1 << 23);
+    return m > 1 && k % 16 == 0 && k < ((int64_t)1 << 23);
 }
 
 // 256-column tiles (one 64 x 128 tile per wave) when they still give two
-// workgroups per CU, else 128-column tiles; K is split (partials summed in
-// a fixed order by a second kernel) while the tiles leave workgroup slots
-// idle (two per CU), each split keeping at least 32 K steps.  Workspace: the split activations, then
-// the partials.
+// workgroups per CU and there is one weight plane, else 128-column tiles (two
+// planes of 256-column tiles would leave room for one workgroup per CU); K is
+// split (partials summed in a fixed order by a second kernel) while the tiles
+// leave workgroup slots idle (two per CU), each split keeping at least 32 K
+// steps.  Workspace: the split activations, the two weight planes (f16
+// weights), then the partials.
 struct NbPlan {
-    int nj, splits;
+    int nj, nw, splits;
     int64_t mp, per, tiles;
-    size_t parts_off, total;
+    size_t w_off, parts_off, total;
 };
 
-static NbPlan nb_plan(int64_t m, int64_t n, int64_t k)
+static NbPlan nb_plan(int64_t m, int64_t n, int64_t k, int nw)
 {
     NbPlan p;
+    p.nw = nw;
     p.mp = (m + kNbM - 1) / kNbM * kNbM;
     const int64_t mt = p.mp / kNbM, kts = k / kNbK;
     const int64_t tiles4 = mt * ((n + 255) / 256);
-    p.nj = tiles4 >= 512 ? 4 : 2;
+    p.nj = nw == 1 && tiles4 >= 512 ? 4 : 2;
     p.tiles = p.nj == 4 ? tiles4 : mt * ((n + 127) / 128);
     int64_t splits = 512 / p.tiles;
     if (splits > kts / 32)
@@ -440,16 +456,45 @@ static NbPlan nb_plan(int64_t m, int64_t n, int64_t k)
     p.per = (kts + splits - 1) / splits;
     p.splits = (int)((kts + p.per - 1) / p.per);
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    p.parts_off = up((size_t)mt * (size_t)kts * kNbAChunk);
+    p.w_off = up((size_t)mt * (size_t)kts * kNbAChunk);
+    p.parts_off = p.w_off + (nw == 2 ? up(2 * (size_t)n * (size_t)k * 2) : 0);
     p.total = p.parts_off + (p.splits > 1 ? up((size_t)p.splits * (size_t)(m * n) * sizeof(float)) : 0);
     return p;
 }
 
 size_t gemm_nt_workspace(int wfmt, int64_t m, int64_t n, int64_t k)
 {
-    if (!gemm_nt_uses_bf16_mfma(wfmt, m, k))
+    if (wfmt == QLL_W_F32 || !gemm_nt_bf16_core_shape(m, k))
         return 0;
-    return nb_plan(m, n, k).total;
+    return nb_plan(m, n, k, wfmt == QLL_W_F16 ? 2 : 1).total;
+}
+
+// f16 weights -> two bf16 planes with w = hi + lo exactly: hi = bf16(w) keeps
+// 8 of the 11 significant bits, the rest (at most 4 bits, within bf16's
+// exponent range since f16's is narrower) is lo.  Eight weights per thread.
+__global__ __launch_bounds__(256) void nt_f16_split_kernel(const uint16_t *__restrict__ w, uint8_t *__restrict__ hi,
+                                                           uint8_t *__restrict__ lo, int64_t count8)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count8)
+        return;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(w + 8 * i);
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const uint32_t word = v[e];
+        uint32_t hb[2], lb[2];
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const float f = half_bits_to_float(q ? word >> 16 : word & 0xffffu);
+            hb[q] = bf16_bits(f);
+            lb[q] = bf16_bits(f - __builtin_bit_cast(float, hb[q] << 16)); // exact
+        }
+        h[e] = hb[0] | (hb[1] << 16);
+        l[e] = lb[0] | (lb[1] << 16);
+    }
+    *reinterpret_cast<u32x4 *>(hi + 16 * i) = u32x4{h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<u32x4 *>(lo + 16 * i) = u32x4{l[0], l[1], l[2], l[3]};
 }
 
 // y[i] = sum over s of parts[s][i], in split order.
@@ -465,16 +510,17 @@ __global__ __launch_bounds__(256) void nb_sum_splits_kernel(const float *__restr
     y[i] = v;
 }
 
-hipError_t launch_gemm_nt_bf16_mfma(const float *x, const uint16_t *w, float *y, int64_t m, int64_t n, int64_t k,
-                                    void *ws, hipStream_t s)
+hipError_t launch_gemm_nt_bf16_mfma(const float *x, const uint16_t *w, int wfmt, float *y, int64_t m, int64_t n,
+                                    int64_t k, void *ws, hipStream_t s)
 {
-    const NbPlan plan = nb_plan(m, n, k);
+    const NbPlan plan = nb_plan(m, n, k, wfmt == QLL_W_F16 ? 2 : 1);
     NbPrep p;
     p.a = static_cast<uint8_t *>(ws);
     p.mp = plan.mp;
     p.kp = k;
     const int64_t chunks = (p.mp / kNbM) * (k / kNbK);
-    if (chunks > 0x7fffffff || plan.tiles > 0x7fffffff)
+    const int64_t count8 = n * k / 8;
+    if (chunks > 0x7fffffff || plan.tiles > 0x7fffffff || (count8 + 255) / 256 > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     if (m % kNbM == 0 && k % (2 * kNbK) == 0)
         hipLaunchKernelGGL(nt_bf16_prep_full_kernel, dim3((unsigned)(chunks / 2)), dim3(256), 0, s, x, p, k);
@@ -483,13 +529,29 @@ hipError_t launch_gemm_nt_bf16_mfma(const float *x, const uint16_t *w, float *y,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    float *out = plan.splits > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + plan.parts_off) : y;
     const uint8_t *wb = reinterpret_cast<const uint8_t *>(w);
+    int64_t plane = 0;
+    if (plan.nw == 2) {
+        uint8_t *hi = static_cast<uint8_t *>(ws) + plan.w_off;
+        plane = n * k * 2;
+        hipLaunchKernelGGL(nt_f16_split_kernel, dim3((unsigned)((count8 + 255) / 256)), dim3(256), 0, s, w, hi,
+                           hi + plane, count8);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        wb = hi;
+    }
+    float *out = plan.splits > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + plan.parts_off) : y;
     const dim3 grid((unsigned)plan.tiles, (unsigned)plan.splits);
-    if (plan.nj == 4)
-        hipLaunchKernelGGL(nt_bf16_gemm_kernel<4>, grid, dim3(kNbThreads), 0, s, wb, p, out, m, n, k, plan.per);
+    if (plan.nw == 2)
+        hipLaunchKernelGGL((nt_bf16_gemm_kernel<2, 2>), grid, dim3(kNbThreads), 0, s, wb, plane, p, out, m, n, k,
+                           plan.per);
+    else if (plan.nj == 4)
+        hipLaunchKernelGGL((nt_bf16_gemm_kernel<4, 1>), grid, dim3(kNbThreads), 0, s, wb, plane, p, out, m, n, k,
+                           plan.per);
     else
-        hipLaunchKernelGGL(nt_bf16_gemm_kernel<2>, grid, dim3(kNbThreads), 0, s, wb, p, out, m, n, k, plan.per);
+        hipLaunchKernelGGL((nt_bf16_gemm_kernel<2, 1>), grid, dim3(kNbThreads), 0, s, wb, plane, p, out, m, n, k,
+                           plan.per);
     e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
         return e;

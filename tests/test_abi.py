@@ -149,6 +149,14 @@ def test_gemm_nt_errors(L):
     assert need == split_x + 4 * 512 * 4096 * 4                      # 128 tiles: K split 4 ways, f32 partials
     assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, 1, 4096, 4096) == 0   # the GEMV needs none
     assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, 8, 4096, 4100) == 0   # k % 16 != 0: f32 path
+    # f16 weights: a passed workspace selects the bf16 matrix core, and must
+    # then also hold the two bf16 weight planes; without one they are widened
+    assert L.qll_gemm_nt(GOOD, GOOD, 2, GOOD, 2, 8, 32, GOOD, 16, None) == WORKSPACE
+    planes = 2 * 4096 * 4096 * 2
+    assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F16, 4096, 4096, 4096) == 8 * split_x + planes
+    assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F16, 512, 4096, 4096) == split_x + planes + 4 * 512 * 4096 * 4
+    assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F16, 1, 4096, 4096) == 0
+    assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F16, 8, 4096, 4100) == 0
 
 
 def test_repacked_sizes(L):

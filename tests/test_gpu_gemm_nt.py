@@ -26,11 +26,18 @@ def weights(w32, wdtype):
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def run(x, w, wdtype):
+def run(x, w, wdtype, f16_core=False):
+    """f16_core: pass a workspace with f16 weights, which puts them on the bf16
+    matrix core (split exactly into two bf16 parts) instead of widening them."""
     m, k = x.shape
     n = w.shape[0]
     y = empty(m * n, torch.float32)
-    need = qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, m, n, k) if wdtype == "bf16" else 0
+    if wdtype == "bf16":
+        need = qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, m, n, k)
+    elif wdtype == "f16" and f16_core:
+        need = max(16, qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F16, m, n, k))
+    else:
+        need = 0
     qll.qll_gemm_nt(dev(x), dev(w), DT[wdtype], y, m, n, k, ws=empty(need) if need else None)
     return host(y).reshape(m, n)
 
@@ -91,28 +98,66 @@ def test_bf16_mfma_activation_split_is_exact(qll_gpu):
     assert np.array_equal(y.astype(np.float64), want)
 
 
-@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("m,n,k", [(2, 3, 16), (129, 257, 48), (33, 1, 4096), (256, 128, 16), (300, 200, 1008),
+                                   (130, 70, 14336), (512, 256, 4096), (256, 200, 96), (128, 64, 32)])
+def test_f16_bf16_core_shapes(qll_gpu, m, n, k):
+    rng = np.random.default_rng(3 * m + n + k)
+    x = synth.normal_f32(rng, (m, k)) * np.float32(3.0)
+    w = weights(synth.uniform_f32(rng, (n, k)), "f16")
+    y = run(x, w, "f16", f16_core=True)
+    y_ref, mag = O.gemm_nt(x, w, "f16")
+    assert_within(y, y_ref, mag, TOL, f"f16 on the bf16 core m={m} n={n} k={k}")
+
+
+def test_f16_weight_split_is_exact(qll_gpu):
+    # bf16-representable activations (their second and third parts are zero)
+    # against one-hot f16 weight rows with full 11-bit significands, including
+    # subnormal f16 values: each output is one exact product x * w, so a lost
+    # bit of the two-way weight split shows up
+    rng = np.random.default_rng(6)
+    m, k, n = 64, 256, 24
+    x = weights((rng.uniform(1.0, 2.0, (m, k)) * 2.0 ** rng.integers(-20, 20, (m, k))).astype(np.float32), "bf16")
+    x = (x.astype(np.uint32) << 16).view(np.float32)
+    x *= np.where(rng.random((m, k)) < 0.5, -1, 1).astype(np.float32)
+    w32 = np.zeros((n, k), np.float32)
+    pos = rng.integers(0, k, n)
+    sig = 1.0 + rng.integers(0, 1024, n) / 1024.0
+    w32[np.arange(n), pos] = sig * 2.0 ** rng.integers(-14, 15, n)
+    w32[0, pos[0]] = 2.0 ** -24 * 1023  # largest subnormal pattern family
+    w32[1, pos[1]] = -(2.0 ** -24) * 5
+    w = weights(w32, "f16")
+    wv = torch.from_numpy(w.view(np.int16)).view(torch.float16).float().numpy()
+    assert np.array_equal(wv, w32), "test weights must be exact in f16"
+    y = run(x, w, "f16", f16_core=True)
+    want = x[:, pos].astype(np.float64) * w32[np.arange(n), pos].astype(np.float64)
+    assert np.array_equal(y.astype(np.float64), want)
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16", "f16core"])
 @pytest.mark.parametrize("m", [1, 40])
 def test_small_integers_exact(qll_gpu, wdtype, m):
     rng = np.random.default_rng(9 + m)
     k, n = 640, 50
     x = rng.integers(-4, 5, (m, k)).astype(np.float32)
     w32 = rng.integers(-4, 5, (n, k)).astype(np.float32)
-    y = run(x, weights(w32, wdtype), wdtype)
+    wd = "f16" if wdtype == "f16core" else wdtype
+    y = run(x, weights(w32, wd), wd, f16_core=wdtype == "f16core")
     assert np.array_equal(y.astype(np.float64), x.astype(np.float64) @ w32.astype(np.float64).T)
 
 
-@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16", "f16core"])
 def test_full_size(qll_gpu, wdtype):
     # the f32 workload's shapes in the transposed orientation: W = B^T of the
     # 4096^3 GEMM; the GEMV on every output, the GEMM on a seeded sample
+    core = wdtype == "f16core"
+    wdtype = "f16" if core else wdtype
     a, b, x = synth.f32_gemm()
     w = weights(np.ascontiguousarray(b.T), wdtype)
     del b
-    y1 = run(x, w, wdtype)
+    y1 = run(x, w, wdtype, f16_core=core)
     y_ref, mag = O.gemm_nt(x, w, wdtype)
     assert_within(y1, y_ref, mag, TOL, f"NT GEMV 4096 {wdtype}")
-    y = run(a, w, wdtype)
+    y = run(a, w, wdtype, f16_core=core)
     rng = np.random.default_rng(17)
     ii = np.concatenate([[0, 4095], rng.integers(0, 4096, 3000)])
     jj = np.concatenate([[4095, 0], rng.integers(0, 4096, 3000)])
