@@ -76,7 +76,7 @@ def parse():
 # Operations of the rows beyond the hot path's core (small-m, repacked weights,
 # Q8_0 weights, transposed-B): timed the same way, but not part of a step.
 NOISY_CV = 0.08  # coefficient of variation above which a row is flagged noisy
-EXTRA_PREFIXES = ("q4r_gemm", "q8w_gemv", "q8r_gemm", "nt_")
+EXTRA_PREFIXES = ("q4r_gemm", "q8w_gemv", "q8r_gemm", "nt_", "sgemm_core")
 
 
 class Op:
@@ -224,6 +224,15 @@ def build_ops(qll, synth, torch, np, dev, only):
             cd = torch.empty(M * N, dtype=torch.float32, device=dev)
             ops.append(Op("sgemm_4096", "f32", "prefill", lambda: qll.qll_sgemm(ad, bd, cd, M, N, K),
                           4 * (M * K + K * N + M * N), 2 * M * N * K, "mfma", "f32"))
+        if want("sgemm_core"):
+            # the same GEMM given a workspace: both operands split into three
+            # exact bf16 parts on the bf16 matrix core (fraction of the bf16
+            # peak; outside the step, which keeps the f32 matrix core)
+            wsc = torch.empty(qll.qll_workspace_bytes(qll.QLL_OP_SGEMM_BF16, M, N, K), dtype=torch.uint8, device=dev)
+            cdc = torch.empty(M * N, dtype=torch.float32, device=dev)
+            ops.append(Op("sgemm_core_4096", "f32_core", "prefill",
+                          lambda: qll.qll_sgemm(ad, bd, cdc, M, N, K, ws=wsc),
+                          4 * (M * K + K * N + M * N), 2 * M * N * K, "mfma", "bf16"))
         if want("sgemv"):
             copies = [bd] + [bd.clone() for _ in range(max(1, -(-gib // (4 * K * N))) - 1)]
             xd = to_dev(x)
@@ -256,13 +265,16 @@ def build_ops(qll, synth, torch, np, dev, only):
                               esz * N * K + 4 * K + 4 * N, 2 * N * K, "hbm"))
             if want(f"nt_gemm_{name}"):
                 cd = torch.empty(M * N, dtype=torch.float32, device=dev)
-                bf = name in ("bf16", "f16")
-                op_code = {"bf16": qll.QLL_OP_GEMM_NT_BF16, "f16": qll.QLL_OP_GEMM_NT_F16}.get(name)
-                need = qll.qll_workspace_bytes(op_code, M, N, K) if bf else 0
+                op_code = {"bf16": qll.QLL_OP_GEMM_NT_BF16, "f16": qll.QLL_OP_GEMM_NT_F16,
+                           "f32": qll.QLL_OP_GEMM_NT_F32}[name]
+                need = qll.qll_workspace_bytes(op_code, M, N, K)
                 wsn = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
-                # bf16 weights, and f16 weights given a workspace, run on the
-                # bf16 matrix core (three, resp. five, bf16 MFMAs per product of
-                # an f32 activation): fraction of the bf16 peak
+                bf = True
+                # given a workspace, every weight type runs on the bf16 matrix
+                # core (three, five or six bf16 MFMAs per product of an f32
+                # activation for bf16, f16 or f32 weights): fraction of the
+                # bf16 peak; the widened f32-matrix-core path is the plain
+                # orientation's sgemm kernel
                 ops.append(Op(f"nt_gemm_{name}_4096", f"{name}_nt", "prefill",
                               lambda w=w, cd=cd, code=code, wsn=wsn: qll.qll_gemm_nt(ad, w, code, cd, M, N, K, ws=wsn),
                               4 * M * K + esz * N * K + 4 * M * N, 2 * M * N * K, "mfma", "bf16" if bf else "f32"))
@@ -455,7 +467,7 @@ def main():
         return out
 
     per_format = {}
-    for fmt in ("q4_0", "q4_0_repacked", "q8_0", "f32", "f32_nt", "bf16_nt", "f16_nt", "ternary"):
+    for fmt in ("q4_0", "q4_0_repacked", "q8_0", "f32", "f32_core", "f32_nt", "bf16_nt", "f16_nt", "ternary"):
         d = {"decode": agg(fmt, "decode"), "prefill": agg(fmt, "prefill")}
         if any(d.values()):
             per_format[fmt] = d
@@ -481,8 +493,9 @@ def main():
                                "on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256); f32 GEMM 4096^3 "
                                "and GEMV 4096x4096; BitNet ternary 2560->6912 at m=1 and m=64",
                    "outside_step": "Q4_0 prefill on load-time repacked weights; Q8_0-weight decode GEMV and repacked "
-                                   "prefill GEMM on the same shapes; transposed-B f32 GEMV/GEMM 4096 with f32, bf16 "
-                                   "and f16 weights",
+                                   "prefill GEMM on the same shapes; the f32 GEMM 4096^3 on the bf16 matrix core "
+                                   "(operands split into exact bf16 parts); transposed-B f32 GEMV/GEMM 4096 with "
+                                   "f32, bf16 and f16 weights (GEMMs on the bf16 matrix core)",
                    "value_is": "Q4_0 x Q8_0 decode GEMV algorithmic bytes / summed average launch duration (back-to-back "
                                "launches on rotating weight copies) over the four shapes",
                    "parallelism": "single GPU"},

@@ -73,7 +73,9 @@ enum {
     QLL_OP_Q4_0_REPACKED_GEMM = 4,
     QLL_OP_Q8_0_REPACKED_GEMM = 5,
     QLL_OP_GEMM_NT_BF16 = 6, /* qll_gemm_nt with QLL_DTYPE_BF16 weights */
-    QLL_OP_GEMM_NT_F16 = 7   /* qll_gemm_nt with QLL_DTYPE_F16 weights on the bf16 matrix core */
+    QLL_OP_GEMM_NT_F16 = 7,  /* qll_gemm_nt with QLL_DTYPE_F16 weights on the bf16 matrix core */
+    QLL_OP_GEMM_NT_F32 = 8,  /* qll_gemm_nt with QLL_DTYPE_F32 weights on the bf16 matrix core */
+    QLL_OP_SGEMM_BF16 = 9    /* qll_sgemm at m > 1 on the bf16 matrix core */
 };
 
 /* Bytes of device workspace `op` needs at this shape (0 if none); SIZE_MAX if
@@ -215,8 +217,15 @@ int qll_q8_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_
 /* C[m][n] = A[m][k] . B[k][n], all f32 row-major (the plain orientation of
  * [FAST] 6.4), accumulated in f32 (tolerance 1e-5 * sum_p |a*b| against an
  * f64 sum).  m == 1 runs a split-k GEMV whose partial sums go to ws in a
- * fixed order (results are bit-identical from run to run).  ws: at least
- * qll_workspace_bytes(QLL_OP_SGEMM, m, n, k) bytes. */
+ * fixed order (results are bit-identical from run to run); ws: at least
+ * qll_workspace_bytes(QLL_OP_SGEMM, 1, n, k) bytes.  m > 1 runs on the bf16
+ * matrix core when ws holds at least qll_workspace_bytes(QLL_OP_SGEMM_BF16, m,
+ * n, k) bytes and k % 16 == 0 (the workspace size selects the algorithm, as
+ * in BLAS libraries): A and B (transposed on the way) are each split exactly
+ * into three bf16 parts and the part products a_i b_j with i + j <= 4 are
+ * accumulated (each one left out is at most 2^-27 of a * b); otherwise (ws
+ * NULL or smaller) on the f32 matrix core.  Contents of ws on return
+ * unspecified. */
 int qll_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, int64_t k, void *ws, size_t ws_bytes,
               void *stream);
 
@@ -232,16 +241,17 @@ int qll_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, in
  * widened in registers, or, when k % 16 == 0, on the bf16 matrix core with
  * every activation split exactly into three bf16 parts: bf16 weights as
  * stored (each bf16 x bf16 product is exact in f32, so the same products are
- * accumulated), and f16 weights, when a workspace is passed, split exactly
- * into two bf16 parts (five of the six part products are accumulated; the
- * sixth is at most 2^-27 of x * w).  Any k >= 1.  ws/ws_bytes: bf16 weights
- * need at least qll_workspace_bytes(QLL_OP_GEMM_NT_BF16, m, n, k) bytes (the
- * split activations and, when K is split, partial sums; 0 when that path does
- * not run); f16 weights take the bf16 matrix core when ws is not NULL, which
- * must then hold qll_workspace_bytes(QLL_OP_GEMM_NT_F16, m, n, k) bytes (also
- * the two weight planes, 4 bytes per weight), and the f32 matrix core when ws
- * is NULL; f32 weights ignore ws.  Contents on return unspecified.
- * QLL_ERR_SHAPE for an unknown w_dtype. */
+ * accumulated), and, when a workspace is passed, f16 weights split exactly
+ * into two bf16 parts and f32 weights into three, accumulating the part
+ * products x_i w_j with i + j <= 4 (five of six, resp. six of nine; each one
+ * left out is at most 2^-27 of x * w).  Any k >= 1.  ws/ws_bytes: bf16
+ * weights need at least qll_workspace_bytes(QLL_OP_GEMM_NT_BF16, m, n, k)
+ * bytes (the split activations and, when K is split, partial sums; 0 when
+ * that path does not run); f16 and f32 weights take the bf16 matrix core when
+ * ws holds at least qll_workspace_bytes(QLL_OP_GEMM_NT_F16, resp.
+ * QLL_OP_GEMM_NT_F32, m, n, k) bytes (also the weight planes, 2 bytes per
+ * weight and plane), and the f32 matrix core otherwise (ws NULL or smaller).
+ * Contents on return unspecified.  QLL_ERR_SHAPE for an unknown w_dtype. */
 int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                 size_t ws_bytes, void *stream);
 

@@ -22,6 +22,8 @@ QLL_OP_Q4_0_REPACKED_GEMM = 4
 QLL_OP_Q8_0_REPACKED_GEMM = 5
 QLL_OP_GEMM_NT_BF16 = 6
 QLL_OP_GEMM_NT_F16 = 7
+QLL_OP_GEMM_NT_F32 = 8
+QLL_OP_SGEMM_BF16 = 9
 QLL_DTYPE_F32, QLL_DTYPE_BF16, QLL_DTYPE_F16 = 0, 1, 2
 
 Q4_0_BLOCK_BYTES = 18
@@ -214,8 +216,14 @@ def qll_q8_0_repacked_q8_0_gemm(wp, xq, y, m, n, k, ws=None, stream=None):
 # ----------------------------------------------------------------- f32
 
 def qll_sgemm(a, b, c, m, n, k, ws=None, stream=None):
-    need = qll_workspace_bytes(QLL_OP_SGEMM, m, n, k)
-    wsp, wsb = _ws(ws, need) if need != 2 ** 64 - 1 else (None, 0)
+    """C = A.B; m == 1 needs a workspace (QLL_OP_SGEMM); at m > 1 a workspace
+    of at least qll_workspace_bytes(QLL_OP_SGEMM_BF16, ...) bytes selects the
+    bf16 matrix core, none or a smaller one the f32 one."""
+    if m > 1 and ws is not None:  # the workspace's size selects the algorithm
+        wsp, wsb = _ptr(ws, 0, "ws"), ws.numel() * ws.element_size()
+    else:
+        need = qll_workspace_bytes(QLL_OP_SGEMM, m, n, k)
+        wsp, wsb = _ws(ws, need) if need != 2 ** 64 - 1 else (None, 0)
     _call("qll_sgemm", _ptr(a, m * k * 4, "a"), _ptr(b, k * n * 4, "b"), _ptr(c, m * n * 4, "c"), m, n, k, wsp, wsb,
           _stream(stream))
 
@@ -223,17 +231,18 @@ def qll_sgemm(a, b, c, m, n, k, ws=None, stream=None):
 def qll_gemm_nt(x, w, w_dtype, y, m, n, k, ws=None, stream=None):
     """Y = X.W^T with W [n][k] of element type w_dtype (QLL_DTYPE_F32/BF16/F16);
     bf16 weights at m > 1 may need a workspace (qll_workspace_bytes with
-    QLL_OP_GEMM_NT_BF16); f16 weights run on the bf16 matrix core when a
-    workspace of qll_workspace_bytes(QLL_OP_GEMM_NT_F16, ...) bytes is passed,
-    on the f32 matrix core otherwise."""
+    QLL_OP_GEMM_NT_BF16); f16 and f32 weights run on the bf16 matrix core when
+    the workspace holds at least qll_workspace_bytes(QLL_OP_GEMM_NT_F16 / _F32,
+    ...) bytes, on the f32 matrix core otherwise."""
     esize = 4 if w_dtype == QLL_DTYPE_F32 else 2
     if w_dtype == QLL_DTYPE_BF16:
         need = qll_workspace_bytes(QLL_OP_GEMM_NT_BF16, m, n, k)
-    elif w_dtype == QLL_DTYPE_F16 and ws is not None:
-        need = qll_workspace_bytes(QLL_OP_GEMM_NT_F16, m, n, k)
     else:
         need = 0
-    wsp, wsb = _ws(ws, need) if need != 2 ** 64 - 1 else (None, 0)
+    if w_dtype != QLL_DTYPE_BF16 and ws is not None:  # the workspace's size selects the algorithm
+        wsp, wsb = _ptr(ws, 0, "ws"), ws.numel() * ws.element_size()
+    else:
+        wsp, wsb = _ws(ws, need) if need != 2 ** 64 - 1 else (None, 0)
     _call("qll_gemm_nt", _ptr(x, m * k * 4, "x"), _ptr(w, n * k * esize, "w"), int(w_dtype), _ptr(y, m * n * 4, "y"),
           m, n, k, wsp, wsb, _stream(stream))
 

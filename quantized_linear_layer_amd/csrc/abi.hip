@@ -96,11 +96,17 @@ size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k)
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 16 != 0)
             return SIZE_MAX;
         return 0;
-    case QLL_OP_GEMM_NT_BF16:
-    case QLL_OP_GEMM_NT_F16:
+    case QLL_OP_SGEMM_BF16:
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n))
             return SIZE_MAX;
-        return gemm_nt_workspace(op == QLL_OP_GEMM_NT_BF16 ? QLL_W_BF16 : QLL_W_F16, m, n, k);
+        return gemm_nt_workspace(QLL_W_F32, m, n, k);
+    case QLL_OP_GEMM_NT_BF16:
+    case QLL_OP_GEMM_NT_F16:
+    case QLL_OP_GEMM_NT_F32:
+        if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n))
+            return SIZE_MAX;
+        return gemm_nt_workspace(op == QLL_OP_GEMM_NT_BF16 ? QLL_W_BF16 : op == QLL_OP_GEMM_NT_F16 ? QLL_W_F16 : QLL_W_F32,
+                                 m, n, k);
     case QLL_OP_Q4_0_REPACKED_GEMM:
     case QLL_OP_Q8_0_REPACKED_GEMM:
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
@@ -310,12 +316,12 @@ int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m,
     if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (ws && !aligned16(ws)))
         return QLL_ERR_ALIGN;
     // bf16 weights at m > 1 always run on the bf16 matrix core and need the
-    // workspace; f16 weights do when a workspace is passed, else they are
-    // widened on the f32 matrix core
-    const bool core = gemm_nt_bf16_core_shape(m, k) &&
-                      (w_dtype == QLL_DTYPE_BF16 || (w_dtype == QLL_DTYPE_F16 && ws != nullptr));
-    if (core && (!ws || ws_bytes < gemm_nt_workspace(w_dtype, m, n, k)))
+    // workspace; f16 and f32 weights do when the workspace passed holds their
+    // split parts, else they run (widened) on the f32 matrix core
+    const bool core_shape = gemm_nt_bf16_core_shape(m, k);
+    if (core_shape && w_dtype == QLL_DTYPE_BF16 && (!ws || ws_bytes < gemm_nt_workspace(w_dtype, m, n, k)))
         return QLL_ERR_WORKSPACE;
+    const bool core = core_shape && ws != nullptr && ws_bytes >= gemm_nt_workspace(w_dtype, m, n, k);
     if (int rc = check_device())
         return rc;
     static_assert((int)QLL_DTYPE_F32 == (int)QLL_W_F32 && (int)QLL_DTYPE_BF16 == (int)QLL_W_BF16 &&
@@ -324,8 +330,7 @@ int qll_gemm_nt(const float *x, const void *w, int w_dtype, float *y, int64_t m,
     if (m == 1)
         return launched(launch_gemv_nt(x, w, w_dtype, y, n, k, as_stream(stream)));
     if (core)
-        return launched(launch_gemm_nt_bf16_mfma(x, static_cast<const uint16_t *>(w), w_dtype, y, m, n, k, ws,
-                                                 as_stream(stream)));
+        return launched(launch_gemm_nt_bf16_mfma(x, w, w_dtype, y, m, n, k, ws, as_stream(stream)));
     return launched(launch_sgemm_nt(x, w, w_dtype, y, m, n, k, as_stream(stream)));
 }
 
@@ -348,8 +353,17 @@ int qll_sgemm(const float *a, const float *b, float *c, int64_t m, int64_t n, in
             return rc;
         return launched(launch_sgemv(a, b, c, n, k, static_cast<float *>(ws), as_stream(stream)));
     }
+    // m > 1: given a workspace that holds the split operands (and k % 16 ==
+    // 0), on the bf16 matrix core with both operands split exactly into three
+    // bf16 parts; otherwise on the f32 one
+    const bool core = ws != nullptr && gemm_nt_bf16_core_shape(m, k) &&
+                      ws_bytes >= gemm_nt_workspace(QLL_W_F32, m, n, k);
+    if (core && !aligned16(ws))
+        return QLL_ERR_ALIGN;
     if (int rc = check_device())
         return rc;
+    if (core)
+        return launched(launch_gemm_nt_bf16_mfma(a, b, QLL_W_F32, c, m, n, k, ws, as_stream(stream), true));
     return launched(launch_sgemm(a, b, c, m, n, k, as_stream(stream)));
 }
 

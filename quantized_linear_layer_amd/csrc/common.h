@@ -115,8 +115,8 @@ hipError_t launch_sgemm_nt(const float *a, const void *w, int wfmt, float *c, in
                            hipStream_t s);
 bool gemm_nt_bf16_core_shape(int64_t m, int64_t k);
 size_t gemm_nt_workspace(int wfmt, int64_t m, int64_t n, int64_t k);
-hipError_t launch_gemm_nt_bf16_mfma(const float *x, const uint16_t *w, int wfmt, float *y, int64_t m, int64_t n,
-                                    int64_t k, void *ws, hipStream_t s);
+hipError_t launch_gemm_nt_bf16_mfma(const float *x, const void *w, int wfmt, float *y, int64_t m, int64_t n,
+                                    int64_t k, void *ws, hipStream_t s, bool b_kn = false);
 // Load-time repack of Q4_0 weights and the GEMM on them (6-bit matrix-core path).
 size_t q4_0_repacked_bytes(int64_t n, int64_t k);
 hipError_t launch_q4_0_repack(const uint8_t *w, uint8_t *wp, int64_t n, int64_t k, hipStream_t s);

@@ -180,7 +180,8 @@ constexpr int kNbPlane = kNbM * kNbK * 2;  // 4096 bytes: one part of a 128-row 
 constexpr int kNbAChunk = 3 * kNbPlane;    // the three parts
 // NJ = 32-column tiles per wave: the workgroup covers 64 NJ weight rows
 // NW weight planes: 1 for bf16 weights (used as stored), 2 for f16 weights
-// (each split exactly into two bf16 parts by nt_f16_split_kernel).
+// and 3 for f32 weights (each split exactly into that many bf16 parts by
+// nt_w_split_kernel).
 template <int NJ, int NW>
 struct NbCfg {
     static constexpr int BN = 64 * NJ;
@@ -385,13 +386,14 @@ __global__ __launch_bounds__(kNbThreads) void nt_bf16_gemm_kernel(const uint8_t 
 #pragma unroll
             for (int j = 0; j < NJ; j++)
                 b[ww][j] = *reinterpret_cast<const QLL_LDS_NT u32x4 *>(base + bo[j] + ww * NbCfg<NJ, NW>::WChunk);
-        // activation part pp against weight plane ww; with two weight planes
-        // the product of the two smallest parts (at most 2^-27 of x * w, an
-        // eighth of one f32 rounding of the sum) is left out
+        // activation part pp against weight plane ww, for pp + ww <= 2: the
+        // products left out (x3 w2 for f16 weights; x2 w3, x3 w2, x3 w3 for
+        // f32 weights) are each at most 2^-27 of x * w, an eighth of one f32
+        // rounding of the sum
 #pragma unroll
         for (int ww = 0; ww < NW; ww++)
 #pragma unroll
-            for (int pp = 0; pp < (ww == 0 ? 3 : 2); pp++)
+            for (int pp = 0; pp < 3 - ww; pp++)
 #pragma unroll
                 for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -457,44 +459,126 @@ static NbPlan nb_plan(int64_t m, int64_t n, int64_t k, int nw)
     p.splits = (int)((kts + p.per - 1) / p.per);
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     p.w_off = up((size_t)mt * (size_t)kts * kNbAChunk);
-    p.parts_off = p.w_off + (nw == 2 ? up(2 * (size_t)n * (size_t)k * 2) : 0);
+    p.parts_off = p.w_off + (nw > 1 ? up((size_t)nw * (size_t)n * (size_t)k * 2) : 0);
     p.total = p.parts_off + (p.splits > 1 ? up((size_t)p.splits * (size_t)(m * n) * sizeof(float)) : 0);
     return p;
 }
 
+static int nb_planes(int wfmt) { return wfmt == QLL_W_BF16 ? 1 : wfmt == QLL_W_F16 ? 2 : 3; }
+
 size_t gemm_nt_workspace(int wfmt, int64_t m, int64_t n, int64_t k)
 {
-    if (wfmt == QLL_W_F32 || !gemm_nt_bf16_core_shape(m, k))
+    if (!gemm_nt_bf16_core_shape(m, k))
         return 0;
-    return nb_plan(m, n, k, wfmt == QLL_W_F16 ? 2 : 1).total;
+    return nb_plan(m, n, k, nb_planes(wfmt)).total;
 }
 
-// f16 weights -> two bf16 planes with w = hi + lo exactly: hi = bf16(w) keeps
-// 8 of the 11 significant bits, the rest (at most 4 bits, within bf16's
-// exponent range since f16's is narrower) is lo.  Eight weights per thread.
-__global__ __launch_bounds__(256) void nt_f16_split_kernel(const uint16_t *__restrict__ w, uint8_t *__restrict__ hi,
-                                                           uint8_t *__restrict__ lo, int64_t count8)
+// Weights -> NW bf16 planes whose sum is the weight exactly.  f16 (NW = 2):
+// the first part keeps 8 of the 11 significant bits, the rest (at most 4 bits,
+// within bf16's exponent range since f16's is narrower) is the second.  f32
+// (NW = 3): 8 + 8 + 8 of the 24 bits, as for the activations.  Eight weights
+// per thread.
+template <int NW>
+__global__ __launch_bounds__(256) void nt_w_split_kernel(const void *__restrict__ w, uint8_t *__restrict__ planes,
+                                                         int64_t plane, int64_t count8)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= count8)
         return;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(w + 8 * i);
-    uint32_t h[4], l[4];
+    float f[8];
+    if (NW == 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(w) + 8 * i);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const uint32_t word = v[e];
+            f[2 * e] = half_bits_to_float(word & 0xffffu);
+            f[2 * e + 1] = half_bits_to_float(word >> 16);
+        }
+    } else {
+        const float *src = static_cast<const float *>(w) + 8 * i;
+        const float4 a = *reinterpret_cast<const float4 *>(src), b = *reinterpret_cast<const float4 *>(src + 4);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    }
+    uint32_t out[NW][4];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-        const uint32_t word = v[e];
-        uint32_t hb[2], lb[2];
+        uint32_t b[NW][2];
 #pragma unroll
         for (int q = 0; q < 2; q++) {
-            const float f = half_bits_to_float(q ? word >> 16 : word & 0xffffu);
-            hb[q] = bf16_bits(f);
-            lb[q] = bf16_bits(f - __builtin_bit_cast(float, hb[q] << 16)); // exact
+            float r = f[2 * e + q];
+#pragma unroll
+            for (int pp = 0; pp < NW; pp++) {
+                b[pp][q] = bf16_bits(r);
+                r -= __builtin_bit_cast(float, b[pp][q] << 16); // exact
+            }
         }
-        h[e] = hb[0] | (hb[1] << 16);
-        l[e] = lb[0] | (lb[1] << 16);
+#pragma unroll
+        for (int pp = 0; pp < NW; pp++)
+            out[pp][e] = b[pp][0] | (b[pp][1] << 16);
     }
-    *reinterpret_cast<u32x4 *>(hi + 16 * i) = u32x4{h[0], h[1], h[2], h[3]};
-    *reinterpret_cast<u32x4 *>(lo + 16 * i) = u32x4{l[0], l[1], l[2], l[3]};
+#pragma unroll
+    for (int pp = 0; pp < NW; pp++)
+        *reinterpret_cast<u32x4 *>(planes + pp * plane + 16 * i) = u32x4{out[pp][0], out[pp][1], out[pp][2], out[pp][3]};
+}
+
+// The plain orientation's B[k][n] (f32) -> three bf16 planes laid out as
+// W[n][k] = B^T, split like nt_w_split_kernel<3>.  64 x 64 tiles through LDS:
+// rows of B are read 16 bytes per thread along n, and each thread writes 16
+// consecutive k of one output row per plane (32 bytes, four threads per row).
+__global__ __launch_bounds__(256) void nn_b_split_t_kernel(const float *__restrict__ b, uint8_t *__restrict__ planes,
+                                                           int64_t plane, int64_t n, int64_t k)
+{
+    __shared__ float t[64][65];
+    const int64_t n0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < 4; it++) {
+        const int r = (tid >> 4) + 16 * it, c = 4 * (tid & 15);
+        const int64_t kr = k0 + r, nc = n0 + c;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (kr < k) {
+            if (nc + 3 < n && n % 4 == 0) {
+                const float4 f = *reinterpret_cast<const float4 *>(b + kr * n + nc);
+                v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    v[e] = nc + e < n ? b[kr * n + nc + e] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            t[r][c + e] = v[e];
+    }
+    __syncthreads();
+    const int nr = tid >> 2, kq = 16 * (tid & 3);
+    const int64_t row = n0 + nr, kk = k0 + kq;
+    if (row >= n || kk >= k) // k is a multiple of 16, so a 16-wide piece is whole
+        return;
+    uint32_t out[3][8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        uint32_t bb[3][2];
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            float r = t[kq + 2 * e + q][nr];
+#pragma unroll
+            for (int pp = 0; pp < 3; pp++) {
+                bb[pp][q] = bf16_bits(r);
+                r -= __builtin_bit_cast(float, bb[pp][q] << 16); // exact
+            }
+        }
+#pragma unroll
+        for (int pp = 0; pp < 3; pp++)
+            out[pp][e] = bb[pp][0] | (bb[pp][1] << 16);
+    }
+#pragma unroll
+    for (int pp = 0; pp < 3; pp++) {
+        uint8_t *dst = planes + pp * plane + (row * k + kk) * 2;
+        *reinterpret_cast<u32x4 *>(dst) = u32x4{out[pp][0], out[pp][1], out[pp][2], out[pp][3]};
+        *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{out[pp][4], out[pp][5], out[pp][6], out[pp][7]};
+    }
 }
 
 // y[i] = sum over s of parts[s][i], in split order.
@@ -510,17 +594,19 @@ __global__ __launch_bounds__(256) void nb_sum_splits_kernel(const float *__restr
     y[i] = v;
 }
 
-hipError_t launch_gemm_nt_bf16_mfma(const float *x, const uint16_t *w, int wfmt, float *y, int64_t m, int64_t n,
-                                    int64_t k, void *ws, hipStream_t s)
+// b_kn: w is the plain orientation's B[k][n] (f32), transposed by the split.
+hipError_t launch_gemm_nt_bf16_mfma(const float *x, const void *w, int wfmt, float *y, int64_t m, int64_t n,
+                                    int64_t k, void *ws, hipStream_t s, bool b_kn)
 {
-    const NbPlan plan = nb_plan(m, n, k, wfmt == QLL_W_F16 ? 2 : 1);
+    const NbPlan plan = nb_plan(m, n, k, nb_planes(wfmt));
     NbPrep p;
     p.a = static_cast<uint8_t *>(ws);
     p.mp = plan.mp;
     p.kp = k;
     const int64_t chunks = (p.mp / kNbM) * (k / kNbK);
     const int64_t count8 = n * k / 8;
-    if (chunks > 0x7fffffff || plan.tiles > 0x7fffffff || (count8 + 255) / 256 > 0x7fffffff)
+    if (chunks > 0x7fffffff || plan.tiles > 0x7fffffff || (count8 + 255) / 256 > 0x7fffffff ||
+        (b_kn && ((n + 63) / 64 > 0x7fffffff || (k + 63) / 64 > 65535)))
         return hipErrorInvalidConfiguration;
     if (m % kNbM == 0 && k % (2 * kNbK) == 0)
         hipLaunchKernelGGL(nt_bf16_prep_full_kernel, dim3((unsigned)(chunks / 2)), dim3(256), 0, s, x, p, k);
@@ -529,21 +615,30 @@ hipError_t launch_gemm_nt_bf16_mfma(const float *x, const uint16_t *w, int wfmt,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const uint8_t *wb = reinterpret_cast<const uint8_t *>(w);
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
     int64_t plane = 0;
-    if (plan.nw == 2) {
-        uint8_t *hi = static_cast<uint8_t *>(ws) + plan.w_off;
+    if (plan.nw > 1) {
+        uint8_t *planes = static_cast<uint8_t *>(ws) + plan.w_off;
         plane = n * k * 2;
-        hipLaunchKernelGGL(nt_f16_split_kernel, dim3((unsigned)((count8 + 255) / 256)), dim3(256), 0, s, w, hi,
-                           hi + plane, count8);
+        const dim3 g((unsigned)((count8 + 255) / 256));
+        if (b_kn)
+            hipLaunchKernelGGL(nn_b_split_t_kernel, dim3((unsigned)((n + 63) / 64), (unsigned)((k + 63) / 64)),
+                               dim3(256), 0, s, static_cast<const float *>(w), planes, plane, n, k);
+        else if (plan.nw == 2)
+            hipLaunchKernelGGL(nt_w_split_kernel<2>, g, dim3(256), 0, s, w, planes, plane, count8);
+        else
+            hipLaunchKernelGGL(nt_w_split_kernel<3>, g, dim3(256), 0, s, w, planes, plane, count8);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        wb = hi;
+        wb = planes;
     }
     float *out = plan.splits > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + plan.parts_off) : y;
     const dim3 grid((unsigned)plan.tiles, (unsigned)plan.splits);
-    if (plan.nw == 2)
+    if (plan.nw == 3)
+        hipLaunchKernelGGL((nt_bf16_gemm_kernel<2, 3>), grid, dim3(kNbThreads), 0, s, wb, plane, p, out, m, n, k,
+                           plan.per);
+    else if (plan.nw == 2)
         hipLaunchKernelGGL((nt_bf16_gemm_kernel<2, 2>), grid, dim3(kNbThreads), 0, s, wb, plane, p, out, m, n, k,
                            plan.per);
     else if (plan.nj == 4)

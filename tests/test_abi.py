@@ -149,14 +149,16 @@ def test_gemm_nt_errors(L):
     assert need == split_x + 4 * 512 * 4096 * 4                      # 128 tiles: K split 4 ways, f32 partials
     assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, 1, 4096, 4096) == 0   # the GEMV needs none
     assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, 8, 4096, 4100) == 0   # k % 16 != 0: f32 path
-    # f16 weights: a passed workspace selects the bf16 matrix core, and must
-    # then also hold the two bf16 weight planes; without one they are widened
-    assert L.qll_gemm_nt(GOOD, GOOD, 2, GOOD, 2, 8, 32, GOOD, 16, None) == WORKSPACE
+    # f16 and f32 weights: a workspace holding the split activations and the
+    # bf16 weight planes selects the bf16 matrix core (a smaller one or none:
+    # widened on the f32 one, which no call here may reach: the pointers are
+    # fake, so every call below must fail its host-side checks)
     planes = 2 * 4096 * 4096 * 2
     assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F16, 4096, 4096, 4096) == 8 * split_x + planes
     assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F16, 512, 4096, 4096) == split_x + planes + 4 * 512 * 4096 * 4
     assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F16, 1, 4096, 4096) == 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F16, 8, 4096, 4100) == 0
+    assert qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F32, 4096, 4096, 4096) == 8 * split_x + 3 * 4096 * 4096 * 2
 
 
 def test_repacked_sizes(L):
@@ -180,6 +182,10 @@ def test_sgemm_errors(L):
     need = qll.qll_workspace_bytes(qll.QLL_OP_SGEMM, 1, 4096, 4096)
     assert L.qll_sgemm(GOOD, GOOD, GOOD, 1, 4096, 4096, NUL, 0, None) == WORKSPACE
     assert L.qll_sgemm(GOOD, GOOD, GOOD, 1, 4096, 4096, GOOD, need - 1, None) == WORKSPACE
+    # m > 1: a workspace of this size selects the bf16 matrix core
+    need_core = qll.qll_workspace_bytes(qll.QLL_OP_SGEMM_BF16, 4096, 4096, 4096)
+    assert need_core == 8 * (4 * 256 * 3 * 128 * 16 * 2) + 3 * 4096 * 4096 * 2
+    assert L.qll_sgemm(GOOD, GOOD, GOOD, 4096, 4096, 4096, MIS, need_core, None) == ALIGN
     assert L.qll_sgemm(GOOD, GOOD, GOOD, 1, 4096, 4096, MIS, need, None) == ALIGN
 
 

@@ -26,16 +26,18 @@ def weights(w32, wdtype):
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def run(x, w, wdtype, f16_core=False):
-    """f16_core: pass a workspace with f16 weights, which puts them on the bf16
-    matrix core (split exactly into two bf16 parts) instead of widening them."""
+def run(x, w, wdtype, core=False):
+    """core: pass a workspace with f16 or f32 weights, which puts them on the
+    bf16 matrix core (split exactly into two or three bf16 parts) instead of
+    widening them on the f32 one."""
     m, k = x.shape
     n = w.shape[0]
     y = empty(m * n, torch.float32)
     if wdtype == "bf16":
         need = qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_BF16, m, n, k)
-    elif wdtype == "f16" and f16_core:
-        need = max(16, qll.qll_workspace_bytes(qll.QLL_OP_GEMM_NT_F16, m, n, k))
+    elif core:
+        op = qll.QLL_OP_GEMM_NT_F16 if wdtype == "f16" else qll.QLL_OP_GEMM_NT_F32
+        need = max(16, qll.qll_workspace_bytes(op, m, n, k))
     else:
         need = 0
     qll.qll_gemm_nt(dev(x), dev(w), DT[wdtype], y, m, n, k, ws=empty(need) if need else None)
@@ -100,13 +102,14 @@ def test_bf16_mfma_activation_split_is_exact(qll_gpu):
 
 @pytest.mark.parametrize("m,n,k", [(2, 3, 16), (129, 257, 48), (33, 1, 4096), (256, 128, 16), (300, 200, 1008),
                                    (130, 70, 14336), (512, 256, 4096), (256, 200, 96), (128, 64, 32)])
-def test_f16_bf16_core_shapes(qll_gpu, m, n, k):
+@pytest.mark.parametrize("wdtype", ["f16", "f32"])
+def test_bf16_core_split_weight_shapes(qll_gpu, wdtype, m, n, k):
     rng = np.random.default_rng(3 * m + n + k)
     x = synth.normal_f32(rng, (m, k)) * np.float32(3.0)
-    w = weights(synth.uniform_f32(rng, (n, k)), "f16")
-    y = run(x, w, "f16", f16_core=True)
-    y_ref, mag = O.gemm_nt(x, w, "f16")
-    assert_within(y, y_ref, mag, TOL, f"f16 on the bf16 core m={m} n={n} k={k}")
+    w = weights(synth.uniform_f32(rng, (n, k)), wdtype)
+    y = run(x, w, wdtype, core=True)
+    y_ref, mag = O.gemm_nt(x, w, wdtype)
+    assert_within(y, y_ref, mag, TOL, f"{wdtype} on the bf16 core m={m} n={n} k={k}")
 
 
 def test_f16_weight_split_is_exact(qll_gpu):
@@ -128,36 +131,54 @@ def test_f16_weight_split_is_exact(qll_gpu):
     w = weights(w32, "f16")
     wv = torch.from_numpy(w.view(np.int16)).view(torch.float16).float().numpy()
     assert np.array_equal(wv, w32), "test weights must be exact in f16"
-    y = run(x, w, "f16", f16_core=True)
+    y = run(x, w, "f16", core=True)
     want = x[:, pos].astype(np.float64) * w32[np.arange(n), pos].astype(np.float64)
     assert np.array_equal(y.astype(np.float64), want)
 
 
-@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16", "f16core"])
+def test_f32_weight_split_is_exact(qll_gpu):
+    # power-of-two activations against one-hot f32 weight rows with full
+    # 24-bit significands: every output x * w is exact in f32, and equals the
+    # sum of the three weight parts' products only if the split lost no bit.
+    # (With activations of more significant bits x * w would need rounding,
+    # which the matrix core does toward zero, not to nearest.)
+    rng = np.random.default_rng(8)
+    m, k, n = 64, 256, 24
+    x = (2.0 ** rng.integers(-20, 20, (m, k)) * np.where(rng.random((m, k)) < 0.5, -1, 1)).astype(np.float32)
+    w32 = np.zeros((n, k), np.float32)
+    pos = rng.integers(0, k, n)
+    w32[np.arange(n), pos] = ((1.0 + rng.integers(0, 1 << 23, n) / 2.0 ** 23) * 2.0 ** rng.integers(-30, 30, n)
+                              * np.where(rng.random(n) < 0.5, -1, 1)).astype(np.float32)
+    y = run(x, w32, "f32", core=True)
+    want = x[:, pos].astype(np.float64) * w32[np.arange(n), pos].astype(np.float64)
+    assert np.array_equal(y.astype(np.float64), want)
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16", "f16core", "f32core"])
 @pytest.mark.parametrize("m", [1, 40])
 def test_small_integers_exact(qll_gpu, wdtype, m):
     rng = np.random.default_rng(9 + m)
     k, n = 640, 50
     x = rng.integers(-4, 5, (m, k)).astype(np.float32)
     w32 = rng.integers(-4, 5, (n, k)).astype(np.float32)
-    wd = "f16" if wdtype == "f16core" else wdtype
-    y = run(x, weights(w32, wd), wd, f16_core=wdtype == "f16core")
+    wd = wdtype.replace("core", "")
+    y = run(x, weights(w32, wd), wd, core=wdtype.endswith("core"))
     assert np.array_equal(y.astype(np.float64), x.astype(np.float64) @ w32.astype(np.float64).T)
 
 
-@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16", "f16core"])
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16", "f16core", "f32core"])
 def test_full_size(qll_gpu, wdtype):
     # the f32 workload's shapes in the transposed orientation: W = B^T of the
     # 4096^3 GEMM; the GEMV on every output, the GEMM on a seeded sample
-    core = wdtype == "f16core"
-    wdtype = "f16" if core else wdtype
+    core = wdtype.endswith("core")
+    wdtype = wdtype.replace("core", "")
     a, b, x = synth.f32_gemm()
     w = weights(np.ascontiguousarray(b.T), wdtype)
     del b
-    y1 = run(x, w, wdtype, f16_core=core)
+    y1 = run(x, w, wdtype, core=core)
     y_ref, mag = O.gemm_nt(x, w, wdtype)
     assert_within(y1, y_ref, mag, TOL, f"NT GEMV 4096 {wdtype}")
-    y = run(a, w, wdtype, f16_core=core)
+    y = run(a, w, wdtype, core=core)
     rng = np.random.default_rng(17)
     ii = np.concatenate([[0, 4095], rng.integers(0, 4096, 3000)])
     jj = np.concatenate([[4095, 0], rng.integers(0, 4096, 3000)])

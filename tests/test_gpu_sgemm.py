@@ -5,16 +5,28 @@ import pytest
 
 import oracle as O
 import synth
-from gpu_util import assert_within, dev, host, sgemm
+import torch
+
+import quantized_linear_layer_amd as qll
+from gpu_util import assert_within, dev, empty, host, sgemm
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
 
-def _check(a, b, what):
+def sgemm_core(a_t, b_t, m, n, k):
+    """m > 1 with a workspace: the bf16 matrix core, both operands split into
+    three exact bf16 parts (B transposed on the way)."""
+    c = empty(m * n, torch.float32)
+    ws = empty(max(16, qll.qll_workspace_bytes(qll.QLL_OP_SGEMM_BF16, m, n, k)))
+    qll.qll_sgemm(a_t, b_t, c, m, n, k, ws=ws)
+    return c
+
+
+def _check(a, b, what, core=False):
     m, k = a.shape
     n = b.shape[1]
-    c = host(sgemm(dev(a), dev(b), m, n, k)).reshape(m, n)
+    c = host((sgemm_core if core else sgemm)(dev(a), dev(b), m, n, k)).reshape(m, n)
     c_ref, mag = O.sgemm(a, b)
     assert_within(c, c_ref, mag, TOL, what)
     return c
@@ -76,3 +88,40 @@ def test_gemm_row_matches_gemv(qll_gpu):
         ci = host(sgemm(dev(a[i:i + 1]), dev(b), 1, 300, 512))
         _, mag = O.sgemm(a[i:i + 1], b)
         assert np.all(np.abs(ci - c[i]) <= 2 * TOL * mag[0])
+
+
+@pytest.mark.parametrize("m,n,k", [(2, 3, 16), (48, 192, 128), (128, 128, 16), (130, 257, 304), (256, 384, 48),
+                                   (384, 128, 1024), (70, 33, 4096), (129, 65, 80)])
+def test_bf16_core_shapes(qll_gpu, m, n, k):
+    rng = np.random.default_rng(m * 7919 + n * 31 + k + 5)
+    a = synth.uniform_f32(rng, (m, k))
+    b = synth.uniform_f32(rng, (k, n))
+    _check(a, b, f"sgemm on the bf16 core {m}x{n}x{k}", core=True)
+
+
+def test_bf16_core_exact_cases(qll_gpu):
+    # A . I = A: the three parts of every a add up to a exactly; small
+    # integers are exact in the first part and give exact sums
+    rng = np.random.default_rng(12)
+    a = synth.uniform_f32(rng, (70, 96)) * np.float32(1e3)
+    c = _check(a, np.eye(96, dtype=np.float32), "identity", core=True)
+    assert np.array_equal(c, a)
+    ai = rng.integers(-2, 3, (150, 208)).astype(np.float32)
+    bi = rng.integers(-2, 3, (208, 90)).astype(np.float32)
+    c = _check(ai, bi, "small integers", core=True)
+    assert np.array_equal(c.astype(np.int64), ai.astype(np.int64) @ bi.astype(np.int64))
+
+
+def test_bf16_core_config_sampled(qll_gpu):
+    a, b, _ = synth.f32_gemm()
+    m, k = a.shape
+    n = b.shape[1]
+    c = host(sgemm_core(dev(a), dev(b), m, n, k)).reshape(m, n)
+    rng = np.random.default_rng(98)
+    ii = np.concatenate([[0, 0, m - 1, m - 1], rng.integers(0, m, 4000)])
+    jj = np.concatenate([[0, n - 1, 0, n - 1], rng.integers(0, n, 4000)])
+    c_ref, mag = O.sgemm_sampled(a, b, ii, jj)
+    assert_within(c[ii, jj], c_ref, mag, TOL, "f32 GEMM 4096^3 on the bf16 core (sampled)")
+    c_ref, mag = O.sgemm_sampled(a, b, np.full(n, 777), np.arange(n))
+    assert_within(c[777], c_ref, mag, TOL, "row 777")
+    torch.cuda.empty_cache()
