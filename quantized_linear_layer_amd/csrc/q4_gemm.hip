@@ -46,14 +46,27 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define QLL_LDS __attribute__((address_space(3)))
 
-constexpr int QBM = 128, QBN = 128, QKB = 2, QNBUF = 3;
+constexpr int QBN = 128, QKB = 2, QNBUF = 3;
+
+// Row-tile heights: 128 (four waves in a 2 x 2 grid of 64 x 64 tiles) or, for
+// small m, 32 (four waves side by side, one 32 x 32 tile each), which pads m
+// to 32 instead of 128.
+template <int BM>
+struct QCfg {
+    static constexpr int TI = BM == 128 ? 2 : 1;            // 32-row tiles per wave
+    static constexpr int TJ = BM == 128 ? 2 : 1;            // 32-column tiles per wave
+    static constexpr int XLoads = QKB * BM / 16 / 4;        // 1 KB activation loads per wave and stage
+    static constexpr int Dma = XLoads + 1 + 2;              // + d_x or C0, + weight codes and d_w
+    __device__ static int wm(int wave) { return BM == 128 ? (wave >> 1) * 64 : 0; }
+    __device__ static int wn(int wave) { return BM == 128 ? (wave & 1) * 64 : wave * 32; }
+};
 constexpr int kQ4GemmThreads = 256;
 
 // Prepared activations: per (row, block) 32 halves = 4 chunks of 16 bytes.
 // Chunk c holds the elements paired with weight dword c, in the order the
 // weight fragment produces them: codes 4c, 4c+2, 4c+1, 4c+3 (low nibbles),
 // then 16+4c, 18+4c, 17+4c, 19+4c (high nibbles, activations divided by 16).
-// Rows are padded to a multiple of QBM and blocks to the end of the last
+// Rows are padded to a multiple of the row tile and blocks to the end of the last
 // split's range, plus two stages, with zeros (zero activations and d_x = 0
 // contribute nothing), so the main loop never tests a row or block edge on
 // the activation side.
@@ -152,22 +165,23 @@ __device__ __forceinline__ int q4gemm_slot(int kb, int row, int c)
     return c ^ (((row >> 1) ^ (row >> 3)) & 3) ^ (kb ? 3 : 0);
 }
 
+template <int BM>
 struct Q4GemmLds {
-    u32x4 xs[QKB][QBM][4]; // prepared activations, slots swizzled
+    u32x4 xs[QKB][BM][4];  // prepared activations, slots swizzled
     u32x4 wq[QKB][QBN];    // weight code dwords 0..3 of (block, row)
-    u32x2 dx[QKB][QBM];    // {binary16 bits of d_x, 0}
-    float c0[QKB][QBM];
+    u32x2 dx[QKB][BM];     // {binary16 bits of d_x, 0}
+    float c0[QKB][BM];
     uint32_t dw[QKB][QBN]; // binary16 bits of d_w, zero-extended
 };
 
 // Every byte a stage needs goes straight from memory to LDS
-// (global_load_lds), seven wave-wide loads per wave and stage:
-//   * the 16 KB of prepared activations, four 1 KB loads per wave (lane l
-//     of a load writes LDS byte 16 l, so it fetches the chunk that belongs
-//     in that slot);
-//   * waves 0 and 1: the {d_x, 0} pairs of block kb = wave (1 KB, two rows
-//     per lane); waves 2 and 3: C0 of block kb = wave - 2 (512 B, lanes
-//     0..31);
+// (global_load_lds), QCfg<BM>::Dma wave-wide loads per wave and stage (7 for
+// BM = 128, 4 for BM = 32):
+//   * the prepared activations (16 KB, resp. 4 KB), four, resp. one, 1 KB
+//     loads per wave (lane l of a load writes LDS byte 16 l, so it fetches
+//     the chunk that belongs in that slot);
+//   * waves 0 and 1: the {d_x, 0} pairs of block kb = wave (8 BM bytes, two
+//     rows per lane); waves 2 and 3: C0 of block kb = wave - 2 (4 BM bytes);
 //   * weight rows (wave & 1) * 64 + lane of block kb = wave >> 1: the 16
 //     code bytes (block + 2) and d_w (block + 0, a 16-bit load, which the
 //     hardware writes to LDS as a zero-extended dword).  Weight blocks are
@@ -175,23 +189,23 @@ struct Q4GemmLds {
 //     global -> LDS path takes.
 // No stage data passes through registers, so the compiler has no loads of
 // its own to wait for; the end-of-stage wait (q4gemm_sync) counts these.
-constexpr int kQ4GemmDmaPerStage = 7;
-
 struct Q4GemmSrc {
     uint32_t xo[4]; // byte offset of this lane's activation chunk for each 1 KB load, from (m0, block b)
     uint32_t so;    // byte offset of this lane's d_x pair / C0 entries, from (block b, m0)
     uint32_t wo;    // byte offset of this lane's weight block, from (row n0, block b)
 };
 
+template <int BM>
 __device__ __forceinline__ Q4GemmSrc q4gemm_src(const Q4GemmPrep &p, int64_t n0, int64_t n, int nb)
 {
+    constexpr int XL = QCfg<BM>::XLoads, RPB = BM / 16; // 1 KB regions per block
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     Q4GemmSrc c;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int region = wave * 4 + j; // 1 KB = 16 rows of one block
-        const int kb = region >> 3;
-        const int row = (region & 7) * 16 + (lane >> 2);
+    for (int j = 0; j < XL; j++) {
+        const int region = wave * XL + j; // 1 KB = 16 rows of one block
+        const int kb = region / RPB;
+        const int row = (region % RPB) * 16 + (lane >> 2);
         c.xo[j] = (uint32_t)((row * p.nbp + kb) * 64 + q4gemm_slot(kb, row, lane & 3) * 16);
     }
     c.so = (uint32_t)(16 * lane);
@@ -222,20 +236,25 @@ __device__ __forceinline__ void q4gemm_dma2(const void *base, uint32_t off, cons
 // The loads of stage st (blocks b = b_begin + QKB st + 0, 1).  Weight blocks
 // at or past nb load block nb - 1 of the row instead: their activations
 // and d_x are zero in the prepared arrays, so they add nothing.
+template <int BM>
 __device__ __forceinline__ void q4gemm_load_stage(const uint8_t *__restrict__ w, const Q4GemmPrep &p,
                                                   const Q4GemmSrc &c, int64_t m0, int64_t n0, int nb, int b,
-                                                  Q4GemmLds &s)
+                                                  Q4GemmLds<BM> &s)
 {
+    constexpr int XL = QCfg<BM>::XLoads, RPB = BM / 16;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t *xb = reinterpret_cast<const uint8_t *>(p.x) + (m0 * p.nbp + b) * 64;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int region = wave * 4 + j;
-        q4gemm_dma16(xb, c.xo[j], (const QLL_LDS void *)&s.xs[region >> 3][(region & 7) * 16][0]);
+    for (int j = 0; j < XL; j++) {
+        const int region = wave * XL + j;
+        q4gemm_dma16(xb, c.xo[j], (const QLL_LDS void *)&s.xs[region / RPB][(region % RPB) * 16][0]);
     }
+    // every wave issues exactly one of these (lanes past the data masked), so
+    // the per-wave load count stays QCfg<BM>::Dma
     if (wave < 2) {
-        q4gemm_dma16(p.dx + ((int64_t)(b + wave) * p.mp + m0), c.so, (const QLL_LDS void *)&s.dx[wave][0]);
-    } else if (lane < 32) {
+        if (lane < BM / 2)
+            q4gemm_dma16(p.dx + ((int64_t)(b + wave) * p.mp + m0), c.so, (const QLL_LDS void *)&s.dx[wave][0]);
+    } else if (lane < BM / 4) {
         q4gemm_dma16(p.c0 + ((int64_t)(b + wave - 2) * p.mp + m0), c.so, (const QLL_LDS void *)&s.c0[wave - 2][0]);
     }
     const int kb = wave >> 1, rbase = (wave & 1) * 64;
@@ -272,20 +291,22 @@ struct Q4GemmLaneOff {
     uint32_t dx, dw, c0;
 };
 
+template <int BM>
 __device__ __forceinline__ Q4GemmLaneOff q4gemm_lane_offsets(int wm, int wn, int lane)
 {
+    using Lds = Q4GemmLds<BM>;
     const int lr = lane & 31, lh = lane >> 5;
     Q4GemmLaneOff o;
 #pragma unroll
     for (int kb = 0; kb < QKB; kb++)
 #pragma unroll
         for (int st = 0; st < 2; st++)
-            o.x[kb][st] = (uint32_t)(offsetof(Q4GemmLds, xs) + (kb * QBM + wm + lr) * 64 +
+            o.x[kb][st] = (uint32_t)(offsetof(Lds, xs) + (kb * BM + wm + lr) * 64 +
                                      q4gemm_slot(kb, wm + lr, 2 * lh + st) * 16);
-    o.w = (uint32_t)(offsetof(Q4GemmLds, wq) + (wn + lr) * 16 + lh * 8);
-    o.dx = (uint32_t)(offsetof(Q4GemmLds, dx) + (wm + lr) * 8);
-    o.dw = (uint32_t)(offsetof(Q4GemmLds, dw) + (wn + lr) * 4);
-    o.c0 = (uint32_t)(offsetof(Q4GemmLds, c0) + (wm + 4 * lh) * 4);
+    o.w = (uint32_t)(offsetof(Lds, wq) + (wn + lr) * 16 + lh * 8);
+    o.dx = (uint32_t)(offsetof(Lds, dx) + (wm + lr) * 8);
+    o.dw = (uint32_t)(offsetof(Lds, dw) + (wn + lr) * 4);
+    o.c0 = (uint32_t)(offsetof(Lds, c0) + (wm + 4 * lh) * 4);
     // opaque to the compiler: it would otherwise split off the constant
     // parts again and re-add them per read (read2 pairs take 8-bit offsets)
 #pragma unroll
@@ -303,8 +324,8 @@ __device__ __forceinline__ T q4gemm_lds(const QLL_LDS char *base, uint32_t off)
     return *reinterpret_cast<const QLL_LDS T *>(base + off);
 }
 
-// One stage: for each of its blocks, the block sums of the wave's 64 x 64
-// tile on the matrix core -- 2 x 2 tiles of 32 x 32, each two K = 16 steps
+// One stage: for each of its blocks, the block sums of the wave's tile on the
+// matrix core -- 2 x 2 (BM = 128) or one (BM = 32) tiles of 32 x 32, each two K = 16 steps
 // started from C0 -- and the scale tiles, then acc += S * P.  MFMA operand
 // lanes: lane l holds row (column) l % 32 of its tile and chunk
 // 2 (l / 32) + s of the block in step s (one 8-byte read of a weight row
@@ -317,37 +338,40 @@ __device__ __forceinline__ T q4gemm_lds(const QLL_LDS char *base, uint32_t off)
 // both d_x[r] d_w[c]: S = 2 d_x d_w exactly (a product of two halves is
 // exact in f32, and so is its double).  The factor 2 leaves the kernel as an
 // exact halving of the outputs.
+template <int BM>
 __device__ __forceinline__ void q4gemm_compute(const QLL_LDS char *base, const Q4GemmLaneOff &o, uint32_t bias,
-                                               f32x16 acc[2][2])
+                                               f32x16 acc[QCfg<BM>::TI][QCfg<BM>::TJ])
 {
+    constexpr int TI = QCfg<BM>::TI, TJ = QCfg<BM>::TJ, NT = TI * TJ;
 #pragma unroll
     for (int kb = 0; kb < QKB; kb++) {
         // keeps the two blocks' reads apart (hoisted together they spill)
         __builtin_amdgcn_sched_barrier(0);
-        f16x8 a[2][2], bm[2][2];
-        f16x4 sa[2], sb[2];
-        f32x16 c0[2];
+        f16x8 a[TI][2], bm[TJ][2];
+        f16x4 sa[TI], sb[TJ];
+        f32x16 c0[TI];
+        static_assert(TI == TJ, "reads interleave row and column tiles");
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
+        for (int i = 0; i < TI; i++) {
             const u32x2 wv = q4gemm_lds<u32x2>(base, o.w + kb * QBN * 16 + 512 * i);
 #pragma unroll
             for (int st = 0; st < 2; st++) {
                 a[i][st] = __builtin_bit_cast(f16x8, q4gemm_lds<u32x4>(base, o.x[kb][st] + 2048 * i));
                 bm[i][st] = q4gemm_wfrag(wv[st], bias);
             }
-            sa[i] = __builtin_bit_cast(f16x4, q4gemm_lds<u32x2>(base, o.dx + kb * QBM * 8 + 256 * i));
+            sa[i] = __builtin_bit_cast(f16x4, q4gemm_lds<u32x2>(base, o.dx + kb * BM * 8 + 256 * i));
             sb[i] = __builtin_bit_cast(f16x4, u32x2{q4gemm_lds<uint32_t>(base, o.dw + kb * QBN * 4 + 128 * i), 0u});
             // D layout of a 32 x 32 tile: lane l, register v -> row
             // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const f32x4 t = q4gemm_lds<f32x4>(base, o.c0 + kb * QBM * 4 + 128 * i + 32 * q);
+                const f32x4 t = q4gemm_lds<f32x4>(base, o.c0 + kb * BM * 4 + 128 * i + 32 * q);
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     c0[i][4 * q + e] = t[e];
             }
         }
-        // Software pipeline over the four tiles: the matrix core works on
+        // Software pipeline over the wave's tiles: the matrix core works on
         // tile t while the vector ALU applies tile t-1's scales.  Per tile,
         // in issue order: the first K step and the scale product, half of
         // the previous tile's fmas, the second K step (by then the first has
@@ -355,15 +379,15 @@ __device__ __forceinline__ void q4gemm_compute(const QLL_LDS char *base, const Q
         __builtin_amdgcn_sched_barrier(0);
         f32x16 p[2], sc[2];
 #pragma unroll
-        for (int t = 0; t <= 4; t++) {
-            if (t < 4) {
-                const int i = t >> 1, j = t & 1;
+        for (int t = 0; t <= NT; t++) {
+            if (t < NT) {
+                const int i = t / TJ, j = t % TJ;
                 p[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][0], bm[j][0], c0[i], 0, 0, 0);
                 sc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], f32x16{}, 0, 0, 0);
                 p[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][1], bm[j][1], p[t & 1], 0, 0, 0);
             }
             if (t > 0) {
-                const int u = t - 1, i = u >> 1, j = u & 1;
+                const int u = t - 1, i = u / TJ, j = u % TJ;
 #pragma unroll
                 for (int v = 0; v < 16; v++)
                     acc[i][j][v] = fmaf(sc[u & 1][v], p[u & 1][v], acc[i][j][v]);
@@ -371,7 +395,7 @@ __device__ __forceinline__ void q4gemm_compute(const QLL_LDS char *base, const Q
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 3, 0); // tile 0
 #pragma unroll
-        for (int t = 1; t < 4; t++) {
+        for (int t = 1; t < NT; t++) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -410,32 +434,34 @@ __device__ __forceinline__ void q4gemm_sync()
     asm volatile("" ::: "memory");
 }
 
+template <int BM>
 __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const uint8_t *__restrict__ w, Q4GemmPrep prep,
                                                                            float *__restrict__ y, int64_t m,
                                                                            int64_t n, int nb, int per_split)
 {
-    __shared__ Q4GemmLds lds[QNBUF];
+    constexpr int TI = QCfg<BM>::TI, TJ = QCfg<BM>::TJ, DMA = QCfg<BM>::Dma;
+    __shared__ Q4GemmLds<BM> lds[QNBUF];
     int64_t m_tile, n_tile;
-    q4gemm_tile(prep.mp / QBM, (n + QBN - 1) / QBN, m_tile, n_tile);
-    const int64_t m0 = m_tile * QBM, n0 = n_tile * QBN;
+    q4gemm_tile(prep.mp / BM, (n + QBN - 1) / QBN, m_tile, n_tile);
+    const int64_t m0 = m_tile * BM, n0 = n_tile * QBN;
     // split-k: blockIdx.y takes blocks [b_begin, b_begin + per_split) and
     // writes its partial tile to y + blockIdx.y * m * n (the workspace when
     // there are splits); blocks past nb have d_x = 0 in the prepared arrays
     const int b_begin = blockIdx.y * per_split;
     y += (int64_t)blockIdx.y * m * n;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int wm = QCfg<BM>::wm(wave), wn = QCfg<BM>::wn(wave);
 
-    f32x16 acc[2][2];
+    f32x16 acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < TJ; j++)
             acc[i][j] = f32x16{};
 
-    const Q4GemmSrc src = q4gemm_src(prep, n0, n, nb);
+    const Q4GemmSrc src = q4gemm_src<BM>(prep, n0, n, nb);
     const int nstages = per_split / QKB;
-    const Q4GemmLaneOff lo = q4gemm_lane_offsets(wm, wn, lane);
+    const Q4GemmLaneOff lo = q4gemm_lane_offsets<BM>(wm, wn, lane);
     uint32_t bias; // 0x64006400, opaque to the compiler (see q4gemm_wfrag)
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));
 
@@ -445,24 +471,24 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
     // st-1; the end-of-stage wait leaves exactly them in flight, so each
     // stage's loads have two stages of compute to land.  Stages past the
     // range load padding and are never computed.
-    q4gemm_load_stage(w, prep, src, m0, n0, nb, b_begin, lds[0]);
-    q4gemm_load_stage(w, prep, src, m0, n0, nb, b_begin + QKB, lds[1]);
-    q4gemm_sync<kQ4GemmDmaPerStage>();
+    q4gemm_load_stage<BM>(w, prep, src, m0, n0, nb, b_begin, lds[0]);
+    q4gemm_load_stage<BM>(w, prep, src, m0, n0, nb, b_begin + QKB, lds[1]);
+    q4gemm_sync<DMA>();
     int cur = 0; // buffer of stage st
     for (int st = 0; st < nstages; st++) {
         const int nx2 = cur == 0 ? 2 : cur - 1;
-        q4gemm_load_stage(w, prep, src, m0, n0, nb, b_begin + (st + 2) * QKB, lds[nx2]);
-        q4gemm_compute((const QLL_LDS char *)&lds[cur], lo, bias, acc);
-        q4gemm_sync<kQ4GemmDmaPerStage>();
+        q4gemm_load_stage<BM>(w, prep, src, m0, n0, nb, b_begin + (st + 2) * QKB, lds[nx2]);
+        q4gemm_compute<BM>((const QLL_LDS char *)&lds[cur], lo, bias, acc);
+        q4gemm_sync<DMA>();
         cur = cur == 2 ? 0 : cur + 1;
     }
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(0x7 << 4); // vmcnt(0) expcnt(7) lgkmcnt(0)
 
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < TJ; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -490,17 +516,22 @@ __global__ __launch_bounds__(256) void q4gemm_sum_splits_kernel(const float *__r
 // of 2 QKB of them.  The workspace holds the split partials (if any), then
 // the prepared activations, d_x and C0.
 struct Q4GemmPlan {
-    int splits, per_split;
-    int64_t mp, nbp;
+    int bm, splits, per_split;
+    int64_t mp, nbp, tiles;
     size_t x_off, dx_off, c0_off, total;
 };
+
+// Row tiles of 32 for m <= kQ4SmallTileM, else 128.
+constexpr int64_t kQ4SmallTileM = 32;
 
 static Q4GemmPlan q4gemm_plan(int64_t m, int64_t n, int64_t k)
 {
     Q4GemmPlan p;
     const int64_t nb = k / 32;
-    p.mp = (m + QBM - 1) / QBM * QBM;
-    const int64_t tiles = ((n + QBN - 1) / QBN) * (p.mp / QBM);
+    p.bm = m <= kQ4SmallTileM ? 32 : 128;
+    p.mp = (m + p.bm - 1) / p.bm * p.bm;
+    const int64_t tiles = ((n + QBN - 1) / QBN) * (p.mp / p.bm);
+    p.tiles = tiles;
     int64_t s = 512 / tiles;
     if (s > nb / 16)
         s = nb / 16;
@@ -548,10 +579,14 @@ hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const int64_t tiles = ((n + QBN - 1) / QBN) * (plan.mp / QBM);
     float *out = plan.splits > 1 ? reinterpret_cast<float *>(base) : y;
-    hipLaunchKernelGGL(q4_0_q8_0_gemm_kernel, dim3((unsigned)tiles, (unsigned)plan.splits), dim3(kQ4GemmThreads), 0,
-                       s, w, prep, out, m, n, (int)nb, plan.per_split);
+    const dim3 grid((unsigned)plan.tiles, (unsigned)plan.splits);
+    if (plan.bm == 32)
+        hipLaunchKernelGGL(q4_0_q8_0_gemm_kernel<32>, grid, dim3(kQ4GemmThreads), 0, s, w, prep, out, m, n, (int)nb,
+                           plan.per_split);
+    else
+        hipLaunchKernelGGL(q4_0_q8_0_gemm_kernel<128>, grid, dim3(kQ4GemmThreads), 0, s, w, prep, out, m, n,
+                           (int)nb, plan.per_split);
     e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
         return e;

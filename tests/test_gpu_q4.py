@@ -163,7 +163,9 @@ def _gemm_check(codes, d_bits, x, what):
 # block and 19 of padding; (257, 131, 608): odd block count, three row tiles
 # with a one-row tail, weight buffer length 2 mod 4 (131 x 19 blocks)
 @pytest.mark.parametrize("m,n,k", [(2, 1, 32), (3, 7, 96), (17, 64, 512), (130, 129, 320), (128, 128, 4096),
-                                   (200, 300, 64), (64, 33, 14336), (128, 256, 3232), (257, 131, 608)])
+                                   (200, 300, 64), (64, 33, 14336), (128, 256, 3232), (257, 131, 608),
+                                   # 9 <= m <= 32: 32-row tiles
+                                   (9, 257, 4096), (32, 1000, 1024), (31, 128, 96), (20, 33, 14336), (12, 129, 32)])
 def test_gemm_shapes(qll_gpu, m, n, k):
     codes, d_bits, x = rand_case(m * 1000 + n + k, m, n, k)
     _gemm_check(codes, d_bits, x, f"GEMM m={m} n={n} k={k}")
@@ -176,6 +178,18 @@ def test_gemm_unit_scales_bit_exact(qll_gpu):
     d_bits = np.full((n, k // 32), 0x3c00, np.uint16)
     x = _unit_scale_x(rng, m, k)
     y, _, _, _ = _gemm_check(codes, d_bits, x, "GEMM unit scales")
+    want = x.astype(np.int64) @ (codes.astype(np.int64) - 8).T
+    assert np.array_equal(y.astype(np.float64), want.astype(np.float64))
+
+
+def test_gemm_small_tile_unit_scales_bit_exact(qll_gpu):
+    # the 32-row tile path (9 <= m <= 32) on integer-valued outputs
+    rng = np.random.default_rng(18)
+    m, n, k = 20, 300, 2048
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    d_bits = np.full((n, k // 32), 0x3c00, np.uint16)
+    x = _unit_scale_x(rng, m, k)
+    y, _, _, _ = _gemm_check(codes, d_bits, x, "GEMM m=20 unit scales")
     want = x.astype(np.int64) @ (codes.astype(np.int64) - 8).T
     assert np.array_equal(y.astype(np.float64), want.astype(np.float64))
 
