@@ -194,6 +194,15 @@ def test_gemm_small_tile_unit_scales_bit_exact(qll_gpu):
     assert np.array_equal(y.astype(np.float64), want.astype(np.float64))
 
 
+@pytest.mark.parametrize("s,m", [(0, 16), (1, 9), (2, 32)])
+def test_gemm_small_tile_8b_shapes_full(qll_gpu, s, m):
+    # the 32-row tile path at an 8B-class layer's full size, every output
+    # checked: the shape's weights with the first m rows of its prefill input
+    codes, d_bits, _ = synth.q4_decode(s)
+    x = synth.q4_prefill_x(s, m=m)
+    _gemm_check(codes, d_bits, x, f"GEMM m={m} 8B shape {synth.SHAPES_8B[s]}")
+
+
 def test_gemm_rows_match_gemv(qll_gpu):
     codes, d_bits, x = rand_case(9, 24, 96, 512)
     y, y_ref, w, xq = _gemm_check(codes, d_bits, x, "GEMM")
