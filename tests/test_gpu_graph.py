@@ -1,5 +1,5 @@
-"""Every entry point captured into a HIP graph (torch.cuda.CUDAGraph) and
-replayed: each replay, with eager work and synchronisations between replays,
+"""Every compute entry point, on each of its kernel paths, captured into a
+HIP graph (torch.cuda.CUDAGraph) and replayed: each replay, with eager work and synchronisations between replays,
 must reproduce the eager call's outputs bit for bit (the kernels are
 deterministic: fixed reduction orders, split-k partials summed in split
 order).  The library records kernel launches only -- no memset or copy nodes
@@ -48,6 +48,76 @@ def _setup():
         ws = empty(need) if need else None
         bufs[f"f32_{tag}_c"] = c
         calls.append(lambda a=a, b=b, c=c, m=m, n=n, k=k, ws=ws: qll.qll_sgemm(a, b, c, m, n, k, ws=ws))
+
+    # Q4_0 at small m: the GEMV-style kernel (m = 4), its quantize-fused
+    # entry (m = 3), and the 32-row GEMM with paired weight rows (even block
+    # count) and without (odd)
+    for tag, (m, n, k) in {"m4": (4, 200, 1024), "m16": (16, 300, 2048), "m12odd": (12, 140, 96)}.items():
+        codes, d_bits = synth.q4_0_weights(rng, n, k)
+        w = empty(n * (k // 32) * 18)
+        qll.qll_pack_q4_0(dev(codes), dev(np.asarray(d_bits, np.uint16).view(np.int16)), w, n, k)
+        xq = empty(m * (k // 32) * 34)
+        qll.qll_quantize_q8_0(dev(synth.normal_f32(rng, (m, k))), xq, m, k)
+        y = empty(m * n, torch.float32)
+        need = qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, m, n, k)
+        ws = empty(need) if need else None
+        bufs[f"q4_{tag}_y"] = y
+        calls.append(lambda w=w, xq=xq, y=y, m=m, n=n, k=k, ws=ws: qll.qll_q4_0_q8_0_gemm(w, xq, y, m, n, k,
+                                                                                       ws=ws))
+        if tag == "m4":
+            xf = dev(synth.normal_f32(rng, (3, k)))
+            yf = empty(3 * n, torch.float32)
+            bufs["q4_fused_y"] = yf
+            calls.append(lambda w=w, xf=xf, yf=yf, n=n, k=k: qll.qll_q4_0_q8_0_gemv_f32(w, xf, yf, 3, n, k))
+
+    # weights repacked at load time (Q4_0 and Q8_0) and the Q8_0-weight GEMV
+    m, n, k = 64, 200, 512
+    codes, d_bits = synth.q4_0_weights(rng, n, k)
+    w4 = empty(n * (k // 32) * 18)
+    qll.qll_pack_q4_0(dev(codes), dev(np.asarray(d_bits, np.uint16).view(np.int16)), w4, n, k)
+    w4p = empty(qll.qll_q4_0_repacked_bytes(n, k))
+    qll.qll_q4_0_repack(w4, w4p, n, k)
+    w8 = empty(n * (k // 32) * 34)
+    qll.qll_quantize_q8_0(dev(synth.normal_f32(rng, (n, k))), w8, n, k)
+    w8p = empty(qll.qll_q8_0_repacked_bytes(n, k))
+    qll.qll_q8_0_repack(w8, w8p, n, k)
+    xq = empty(m * (k // 32) * 34)
+    qll.qll_quantize_q8_0(dev(synth.normal_f32(rng, (m, k))), xq, m, k)
+    for tag, fn, op in (("q4r", qll.qll_q4_0_repacked_q8_0_gemm, qll.QLL_OP_Q4_0_REPACKED_GEMM),
+                        ("q8r", qll.qll_q8_0_repacked_q8_0_gemm, qll.QLL_OP_Q8_0_REPACKED_GEMM)):
+        wp = w4p if tag == "q4r" else w8p
+        y = empty(m * n, torch.float32)
+        ws = empty(max(16, qll.qll_workspace_bytes(op, m, n, k)))
+        bufs[f"{tag}_y"] = y
+        calls.append(lambda fn=fn, wp=wp, y=y, ws=ws, xq=xq, m=m, n=n, k=k: fn(wp, xq, y, m, n, k, ws=ws))
+    y8 = empty(n, torch.float32)
+    bufs["q8w_gemv_y"] = y8
+    calls.append(lambda w8=w8, xq=xq, y8=y8, n=n, k=k: qll.qll_q8_0_q8_0_gemv(w8, xq, y8, n, k))
+
+    # transposed-B: every weight type at m = 1 and m = 64, on the f32 matrix
+    # core (no workspace) and on the bf16 one (a workspace); and the plain
+    # f32 GEMM on the bf16 matrix core
+    m, n, k = 64, 144, 320
+    x = dev(synth.normal_f32(rng, (m, k)))
+    w32 = synth.uniform_f32(rng, (n, k))
+    for dt, code in (("f32", qll.QLL_DTYPE_F32), ("bf16", qll.QLL_DTYPE_BF16), ("f16", qll.QLL_DTYPE_F16)):
+        wt = dev(w32)
+        wt = wt if dt == "f32" else wt.to(torch.bfloat16 if dt == "bf16" else torch.float16)
+        op = {"f32": qll.QLL_OP_GEMM_NT_F32, "bf16": qll.QLL_OP_GEMM_NT_BF16, "f16": qll.QLL_OP_GEMM_NT_F16}[dt]
+        for core in ((False, True) if dt != "bf16" else (True,)):
+            y = empty(m * n, torch.float32)
+            ws = empty(max(16, qll.qll_workspace_bytes(op, m, n, k))) if core else None
+            bufs[f"nt_{dt}_{core}_y"] = y
+            calls.append(lambda wt=wt, code=code, y=y, ws=ws, x=x, m=m, n=n, k=k: qll.qll_gemm_nt(x, wt, code, y, m, n,
+                                                                                              k, ws=ws))
+        y1 = empty(n, torch.float32)
+        bufs[f"nt_{dt}_gemv_y"] = y1
+        calls.append(lambda wt=wt, code=code, y1=y1, x=x, n=n, k=k: qll.qll_gemm_nt(x[:1], wt, code, y1, 1, n, k))
+    b = dev(synth.uniform_f32(rng, (k, n)))
+    c = empty(m * n, torch.float32)
+    wsc = empty(qll.qll_workspace_bytes(qll.QLL_OP_SGEMM_BF16, m, n, k))
+    bufs["sgemm_core_c"] = c
+    calls.append(lambda x=x, b=b, c=c, m=m, n=n, k=k, wsc=wsc: qll.qll_sgemm(x, b, c, m, n, k, ws=wsc))
 
     # ternary: int8 row quantization, GEMV and GEMM
     n, k = 640, 2560
