@@ -35,6 +35,12 @@
 // the 2-byte aligned addresses of 18-byte weight blocks), two stages ahead.
 // Weights stay as nibbles in LDS (a quarter of the bytes of f16) and are
 // widened when the fragments are read.
+//
+// Small m (9 <= m <= 32; m <= 8 runs as a GEMV): the same kernel with 32-row
+// tiles (4 waves side by side, one 32 x 32 tile each), and, when the block
+// count is even, each weight row's two blocks of a stage loaded as the 36
+// bytes they are (nine lanes, seven rows per load) instead of one 16-byte
+// load per row, which at this compute per weight byte would bound the kernel.
 #include "common.h"
 
 namespace qll {
