@@ -45,6 +45,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define QLL_LDS __attribute__((address_space(3)))
 
 constexpr int PBM = 128, PBN = 128, PKB = 2, PNBUF = 3;
+constexpr int PDIST = PNBUF - 1; // stages in flight ahead of the one computed
 constexpr int kPThreads = 256;
 constexpr int kPWChunk = 3072; // codes of 128 weight rows x one block
 constexpr int kPXChunk = 6144; // h and l codes of 128 activation rows x one block
@@ -224,6 +225,64 @@ __device__ __forceinline__ void q4p_dma16(const void *base, uint32_t off, const 
                  : "memory", "m0");
 }
 
+// Row-tile and column-tile bases of the stage loads, set once per workgroup.
+struct Q4pSrc {
+    const uint8_t *x;  // activation chunks of the row tile
+    const uint8_t *dx; // d_x chunks of the row tile
+    const uint8_t *w;  // weight code chunks of the column tile
+    const uint8_t *dw; // d_w chunks of the column tile
+};
+
+// One wave's loads of a stage.  The wave index is a template argument so
+// that every region, block and part number below is a constant; only the
+// block offsets (32-bit: the largest is nb chunks of at most 6 KB) and the
+// clamp at nb - 1 remain per stage.
+template <bool Q8W, int WAVE>
+__device__ __forceinline__ void q4p_load_wave(const Q4pSrc &src, int nb, int b, Q4pLds<Q8W> &s)
+{
+    constexpr int WC = PFmt<Q8W>::kWChunk;
+    const int lane = threadIdx.x & 63;
+    const uint32_t lo = 16u * (uint32_t)lane;
+    const uint8_t *xb = src.x + (uint32_t)b * (uint32_t)kPXChunk;
+    const QLL_LDS char *xs = (const QLL_LDS char *)&s.xs[0][0];
+    const QLL_LDS char *wq = (const QLL_LDS char *)&s.wq[0][0];
+    const auto wblock = [&](int kb) { return (uint32_t)(b + kb < nb ? b + kb : nb - 1); };
+#pragma unroll
+    for (int j = 0; j < 3; j++) {
+        constexpr int r0 = 3 * WAVE;
+        q4p_dma16(xb + (r0 + j) * 1024, lo, xs + (r0 + j) * 1024);
+    }
+    if (Q8W) {
+#pragma unroll
+        for (int j = 0; j < 3; j++) {
+            const int region = 3 * WAVE + j, kb = region / 6, part = region % 6;
+            q4p_dma16(src.w + wblock(kb) * (uint32_t)WC + part * 1024, lo, wq + kb * WC + part * 1024);
+        }
+        if (lane < 16) {
+            if (WAVE < 2)
+                q4p_dma16(src.dx + (uint32_t)(b + WAVE) * (uint32_t)kPSChunk, lo, (const QLL_LDS void *)&s.dx[WAVE][0]);
+            else
+                q4p_dma16(src.dw + wblock(WAVE - 2) * (uint32_t)kPSChunk, lo,
+                          (const QLL_LDS void *)&s.dw[WAVE - 2][0]);
+        }
+    } else {
+        constexpr int nw = WAVE < 2 ? 2 : 1;
+#pragma unroll
+        for (int j = 0; j < nw; j++) {
+            const int region = WAVE < 2 ? 2 * WAVE + j : 2 + WAVE;
+            const int kb = region / 3, part = region % 3;
+            q4p_dma16(src.w + wblock(kb) * (uint32_t)WC + part * 1024, lo, wq + kb * WC + part * 1024);
+        }
+        if (WAVE == 2 && lane < 32) {
+            q4p_dma16(src.dx + (uint32_t)b * (uint32_t)kPSChunk, lo, (const QLL_LDS void *)&s.dx[0][0]);
+        } else if (WAVE == 3 && lane < 32) {
+            const int bb = b + (lane >> 4) < nb ? b + (lane >> 4) : nb - 1;
+            q4p_dma16(src.dw, (uint32_t)bb * kPSChunk + 16u * (uint32_t)(lane & 15),
+                      (const QLL_LDS void *)&s.dw[0][0]);
+        }
+    }
+}
+
 // The loads of the stage holding blocks b and b + 1.  Q4_0 weights, five
 // per wave:
 //   * activations: the two blocks' chunks are adjacent (12 KB), three 1 KB
@@ -237,58 +296,13 @@ __device__ __forceinline__ void q4p_dma16(const void *base, uint32_t off, const 
 // (12 KB) as three 1 KB loads per wave, and d_x (waves 0, 1) and d_w
 // (waves 2, 3) one block per wave on lanes 0..15.
 template <bool Q8W>
-__device__ __forceinline__ void q4p_load_stage(const uint8_t *__restrict__ wcodes, const uint16_t *__restrict__ dws,
-                                               const Q4pPrep &p, int64_t mt, int64_t nt, int nb, int b,
-                                               Q4pLds<Q8W> &s)
+__device__ __forceinline__ void q4p_load_stage(const Q4pSrc &src, int nb, int b, int wave, Q4pLds<Q8W> &s)
 {
-    constexpr int WC = PFmt<Q8W>::kWChunk;
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t lo = 16u * (uint32_t)lane;
-    const uint8_t *xb = p.x + (mt * p.nbp + b) * kPXChunk;
-    const QLL_LDS char *xs = (const QLL_LDS char *)&s.xs[0][0];
-    const QLL_LDS char *wq = (const QLL_LDS char *)&s.wq[0][0];
-#pragma unroll
-    for (int j = 0; j < 3; j++) {
-        const int region = 3 * wave + j;
-        q4p_dma16(xb + region * 1024, lo, xs + region * 1024);
-    }
-    const uint8_t *wt = wcodes + nt * nb * (int64_t)WC;
-    const uint8_t *dwt = reinterpret_cast<const uint8_t *>(dws) + nt * nb * (int64_t)kPSChunk;
-    if (Q8W) {
-#pragma unroll
-        for (int j = 0; j < 3; j++) {
-            const int region = 3 * wave + j;
-            const int kb = region / 6, part = region % 6;
-            const int bb = b + kb < nb ? b + kb : nb - 1;
-            q4p_dma16(wt + (int64_t)bb * WC + part * 1024, lo, wq + kb * WC + part * 1024);
-        }
-        if (lane < 16) {
-            if (wave < 2) {
-                q4p_dma16(reinterpret_cast<const uint8_t *>(p.dx) + (mt * p.nbp + b + wave) * kPSChunk, lo,
-                          (const QLL_LDS void *)&s.dx[wave][0]);
-            } else {
-                const int bb = b + wave - 2 < nb ? b + wave - 2 : nb - 1;
-                q4p_dma16(dwt + (int64_t)bb * kPSChunk, lo, (const QLL_LDS void *)&s.dw[wave - 2][0]);
-            }
-        }
-    } else {
-        const int nw = wave < 2 ? 2 : 1;
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            if (j < nw) {
-                const int region = wave < 2 ? 2 * wave + j : 2 + wave;
-                const int kb = region / 3, part = region % 3;
-                const int bb = b + kb < nb ? b + kb : nb - 1;
-                q4p_dma16(wt + (int64_t)bb * WC + part * 1024, lo, wq + kb * WC + part * 1024);
-            }
-        }
-        if (wave == 2 && lane < 32) {
-            q4p_dma16(reinterpret_cast<const uint8_t *>(p.dx) + (mt * p.nbp + b) * kPSChunk, lo,
-                      (const QLL_LDS void *)&s.dx[0][0]);
-        } else if (wave == 3 && lane < 32) {
-            const int bb = b + (lane >> 4) < nb ? b + (lane >> 4) : nb - 1;
-            q4p_dma16(dwt, (uint32_t)bb * kPSChunk + 16u * (uint32_t)(lane & 15), (const QLL_LDS void *)&s.dw[0][0]);
-        }
+    switch (wave) {
+    case 0: q4p_load_wave<Q8W, 0>(src, nb, b, s); break;
+    case 1: q4p_load_wave<Q8W, 1>(src, nb, b, s); break;
+    case 2: q4p_load_wave<Q8W, 2>(src, nb, b, s); break;
+    default: q4p_load_wave<Q8W, 3>(src, nb, b, s); break;
     }
 }
 
@@ -333,11 +347,9 @@ __device__ __forceinline__ void q4p_compute(const QLL_LDS char *base, const Q4pL
                                             f32x16 acc[2][2])
 {
     constexpr int WC = PFmt<Q8W>::kWChunk;
-#pragma unroll
-    for (int kb = 0; kb < PKB; kb++) {
-        __builtin_amdgcn_sched_barrier(0);
-        i32x8 a[2], bm[2], bl[2];
-        f16x4 sa[2], sb[2];
+    i32x8 a[2], bm[2], bl[2];
+    f16x4 sa[2], sb[2];
+    const auto operands = [&](int kb) {
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             const u32x4 x0 = q4p_lds<u32x4>(base, o.x0 + kb * kPXChunk + 512 * i);
@@ -356,40 +368,41 @@ __device__ __forceinline__ void q4p_compute(const QLL_LDS char *base, const Q4pL
             sa[i] = __builtin_bit_cast(f16x4, u32x2{dxb, 0u});
             sb[i] = __builtin_bit_cast(f16x4, u32x2{dwb, 0u});
         }
+    };
+    // Software pipeline over the stage's eight (block, tile) steps: the
+    // matrix core works on step t while the vector ALU applies the scales of
+    // step t - 1, and the second block's operands are read once the first
+    // block's last MFMAs are issued.  The scheduling fences keep that order:
+    // left free, the compiler fills the gap with step t's own fmas, which
+    // wait for the MFMAs just issued.
+    operands(0);
+    f32x16 p[2], sc[2];
+#pragma unroll
+    for (int t = 0; t <= 4 * PKB; t++) {
+        if (t < 4 * PKB) {
+            const int i = (t >> 1) & 1, j = t & 1;
+            if (Q8W) { // sum 16 h_w (16 h_x + l_x) + l_w (16 h_x + l_x)
+                p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bm[j], f32x16{}, 3, 3, 0, scale_a, 0,
+                                                                          kE8M0Sixteen);
+                p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bl[j], p[t & 1], 3, 3, 0, scale_a, 0,
+                                                                          kE8M0One);
+            } else {
+                p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bm[j], f32x16{}, 3, 3, 0, scale_a, 0,
+                                                                          kE8M0One);
+            }
+            sc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], f32x16{}, 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        // Software pipeline over the four tiles: the matrix core works on
-        // tile t while the vector ALU applies tile t-1's scales.
-        f32x16 p[2], sc[2];
+        if ((t & 3) == 3 && t + 1 < 4 * PKB)
+            operands((t + 1) >> 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t > 0) {
+            const int u = t - 1, i = (u >> 1) & 1, j = u & 1;
 #pragma unroll
-        for (int t = 0; t <= 4; t++) {
-            if (t < 4) {
-                const int i = t >> 1, j = t & 1;
-                if (Q8W) { // sum 16 h_w (16 h_x + l_x) + l_w (16 h_x + l_x)
-                    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bm[j], f32x16{}, 3, 3, 0, scale_a,
-                                                                              0, kE8M0Sixteen);
-                    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bl[j], p[t & 1], 3, 3, 0, scale_a,
-                                                                              0, kE8M0One);
-                } else {
-                    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bm[j], f32x16{}, 3, 3, 0, scale_a,
-                                                                              0, kE8M0One);
-                }
-                sc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], f32x16{}, 0, 0, 0);
-            }
-            if (t > 0) {
-                const int u = t - 1, i = u >> 1, j = u & 1;
-#pragma unroll
-                for (int v = 0; v < 16; v++)
-                    acc[i][j][v] = fmaf(sc[u & 1][v], p[u & 1][v], acc[i][j][v]);
-            }
+            for (int v = 0; v < 16; v++)
+                acc[i][j][v] = fmaf(sc[u & 1][v], p[u & 1][v], acc[i][j][v]);
         }
-        constexpr int NM = Q8W ? 3 : 2; // MFMAs per tile
-        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0); // tile 0
-#pragma unroll
-        for (int t = 1; t < 4; t++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -449,17 +462,25 @@ __global__ __launch_bounds__(kPThreads) void packed_gemm_kernel(const uint8_t *_
     // Stage st is computed from buffer st % 3; the loads of stage st + 2 go
     // out at its start into the buffer that stage st - 1 used (every wave
     // left it at the barrier that ended stage st - 1).  Stages past the range
-    // load padding and are never computed.
-    q4p_load_stage<Q8W>(wcodes, dws, prep, m_tile, n_tile, nb, b_begin, lds[0]);
-    q4p_load_stage<Q8W>(wcodes, dws, prep, m_tile, n_tile, nb, b_begin + PKB, lds[1]);
-    q4p_sync<DMA>();
+    // load padding and are never computed.  Wave roles in the loads are
+    // uniform per wave, so the wave index goes through a scalar register.
+    Q4pSrc src;
+    src.x = prep.x + m_tile * prep.nbp * kPXChunk;
+    src.dx = reinterpret_cast<const uint8_t *>(prep.dx) + m_tile * prep.nbp * kPSChunk;
+    src.w = wcodes + n_tile * nb * (int64_t)PFmt<Q8W>::kWChunk;
+    src.dw = reinterpret_cast<const uint8_t *>(dws) + n_tile * nb * (int64_t)kPSChunk;
+    const int swave = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int s0 = 0; s0 < PDIST; s0++)
+        q4p_load_stage<Q8W>(src, nb, b_begin + s0 * PKB, swave, lds[s0]);
+    q4p_sync<DMA * (PDIST - 1)>();
     int cur = 0;
     for (int st = 0; st < nstages; st++) {
-        const int nx2 = cur == 0 ? 2 : cur - 1;
-        q4p_load_stage<Q8W>(wcodes, dws, prep, m_tile, n_tile, nb, b_begin + (st + 2) * PKB, lds[nx2]);
+        const int nxt = cur + PDIST < PNBUF ? cur + PDIST : cur + PDIST - PNBUF;
+        q4p_load_stage<Q8W>(src, nb, b_begin + (st + PDIST) * PKB, swave, lds[nxt]);
         q4p_compute<Q8W>((const QLL_LDS char *)&lds[cur], lo, scale_a, acc);
-        q4p_sync<DMA>();
-        cur = cur == 2 ? 0 : cur + 1;
+        q4p_sync<DMA * (PDIST - 1)>();
+        cur = cur + 1 < PNBUF ? cur + 1 : 0;
     }
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(0x7 << 4); // vmcnt(0) expcnt(7) lgkmcnt(0)
