@@ -279,44 +279,69 @@ __device__ __forceinline__ void q4gemm_dma2(const void *base, uint32_t off, cons
                  : "memory", "m0");
 }
 
-// The loads of stage st (blocks b = b_begin + QKB st + 0, 1).  Weight blocks
-// at or past nb load block nb - 1 of the row instead: their activations
-// and d_x are zero in the prepared arrays, so they add nothing.
-template <int BM, bool PW>
-__device__ __forceinline__ void q4gemm_load_stage(const uint8_t *__restrict__ w, const Q4GemmPrep &p,
-                                                  const Q4GemmSrc &c, int64_t m0, int64_t n0, int nb, int b,
-                                                  Q4GemmLds<BM, PW> &s)
+// Row-tile and column-tile bases of the stage loads, set once per workgroup.
+struct Q4GemmBase {
+    const uint8_t *x;  // prepared activations of row m0, block 0
+    const uint8_t *dx; // {d_x, 0} pairs of block 0, row m0
+    const uint8_t *c0; // C0 of block 0, row m0
+    const uint8_t *w;  // weight blocks of row n0
+    int64_t sblk;      // bytes from one block to the next in dx (c0: half of it)
+};
+
+// One wave's loads of stage st (blocks b = b_begin + QKB st + 0, 1).  The
+// wave index is a template argument, so that the regions and blocks it
+// loads are constants and only the block offsets remain per stage (32-bit
+// within a row of prepared activations or of weight blocks, which k < 2^24
+// keeps far below 4 GiB; 64-bit across the d_x and C0 arrays).  Weight
+// blocks at or past nb load block nb - 1 of the row instead: their
+// activations and d_x are zero in the prepared arrays, so they add nothing.
+template <int BM, bool PW, int WAVE>
+__device__ __forceinline__ void q4gemm_load_wave(const Q4GemmBase &g, const Q4GemmSrc &c, int nb, int b,
+                                                 Q4GemmLds<BM, PW> &s)
 {
     constexpr int XL = QCfg<BM, PW>::XLoads, RPB = BM / 16;
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint8_t *xb = reinterpret_cast<const uint8_t *>(p.x) + (m0 * p.nbp + b) * 64;
+    const int lane = threadIdx.x & 63;
+    const uint8_t *xb = g.x + (uint32_t)b * 64u;
 #pragma unroll
     for (int j = 0; j < XL; j++) {
-        const int region = wave * XL + j;
-        q4gemm_dma16(xb, c.xo[j], (const QLL_LDS void *)&s.xs[region / RPB][(region % RPB) * 16][0]);
+        constexpr int r0 = WAVE * XL;
+        q4gemm_dma16(xb, c.xo[j], (const QLL_LDS void *)&s.xs[(r0 + j) / RPB][((r0 + j) % RPB) * 16][0]);
     }
     // every wave issues exactly one of these (lanes past the data masked), so
     // the per-wave load count stays QCfg<BM, PW>::Dma
-    if (wave < 2) {
+    if (WAVE < 2) {
         if (lane < BM / 2)
-            q4gemm_dma16(p.dx + ((int64_t)(b + wave) * p.mp + m0), c.so, (const QLL_LDS void *)&s.dx[wave][0]);
+            q4gemm_dma16(g.dx + (int64_t)(b + WAVE) * g.sblk, c.so, (const QLL_LDS void *)&s.dx[WAVE][0]);
     } else if (lane < BM / 4) {
-        q4gemm_dma16(p.c0 + ((int64_t)(b + wave - 2) * p.mp + m0), c.so, (const QLL_LDS void *)&s.c0[wave - 2][0]);
+        q4gemm_dma16(g.c0 + (int64_t)(b + WAVE - 2) * (g.sblk / 2), c.so, (const QLL_LDS void *)&s.c0[WAVE - 2][0]);
     }
     if constexpr (PW) {
         // the pair (b, b + 1): b is even and so is nb, so a pair in range
         // lies wholly inside the row; stages past the range load the last pair
-        const uint8_t *wb = w + 18 * (n0 * nb + (b < nb ? b : nb - 2));
+        const uint8_t *wb = g.w + 18u * (uint32_t)(b < nb ? b : nb - 2);
 #pragma unroll
         for (int j = 0; j < 5; j++)
             if (lane < 63) // every wave issues all five loads
-                q4gemm_dma4(wb, c.wpo[j], (const QLL_LDS void *)&s.wp[(wave + 4 * j) * kPwRowsPerLoad * 9]);
+                q4gemm_dma4(wb, c.wpo[j], (const QLL_LDS void *)&s.wp[(WAVE + 4 * j) * kPwRowsPerLoad * 9]);
     } else {
-        const int kb = wave >> 1, rbase = (wave & 1) * 64;
+        constexpr int kb = WAVE >> 1, rbase = (WAVE & 1) * 64;
         const int bw = (b + kb < nb) ? b + kb : nb - 1;
-        const uint8_t *wb = w + 18 * (n0 * nb + bw);
+        const uint8_t *wb = g.w + 18u * (uint32_t)bw;
         q4gemm_dma16(wb + 2, c.wo, (const QLL_LDS void *)&s.wq[kb][rbase]);
         q4gemm_dma2(wb, c.wo, (const QLL_LDS void *)&s.dw[kb][rbase]);
+    }
+}
+
+// The loads of a stage; `wave` is uniform (a scalar register).
+template <int BM, bool PW>
+__device__ __forceinline__ void q4gemm_load_stage(const Q4GemmBase &g, const Q4GemmSrc &c, int nb, int b, int wave,
+                                                  Q4GemmLds<BM, PW> &s)
+{
+    switch (wave) {
+    case 0: q4gemm_load_wave<BM, PW, 0>(g, c, nb, b, s); break;
+    case 1: q4gemm_load_wave<BM, PW, 1>(g, c, nb, b, s); break;
+    case 2: q4gemm_load_wave<BM, PW, 2>(g, c, nb, b, s); break;
+    default: q4gemm_load_wave<BM, PW, 3>(g, c, nb, b, s); break;
     }
 }
 
@@ -552,13 +577,20 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
     // st-1; the end-of-stage wait leaves exactly them in flight, so each
     // stage's loads have two stages of compute to land.  Stages past the
     // range load padding and are never computed.
-    q4gemm_load_stage<BM, PW>(w, prep, src, m0, n0, nb, b_begin, lds[0]);
-    q4gemm_load_stage<BM, PW>(w, prep, src, m0, n0, nb, b_begin + QKB, lds[1]);
+    Q4GemmBase g;
+    g.x = reinterpret_cast<const uint8_t *>(prep.x) + m0 * prep.nbp * 64;
+    g.dx = reinterpret_cast<const uint8_t *>(prep.dx + m0);
+    g.c0 = reinterpret_cast<const uint8_t *>(prep.c0 + m0);
+    g.w = w + 18 * n0 * (int64_t)nb;
+    g.sblk = prep.mp * 8;
+    const int swave = __builtin_amdgcn_readfirstlane(wave);
+    q4gemm_load_stage<BM, PW>(g, src, nb, b_begin, swave, lds[0]);
+    q4gemm_load_stage<BM, PW>(g, src, nb, b_begin + QKB, swave, lds[1]);
     q4gemm_sync<DMA>();
     int cur = 0; // buffer of stage st
     for (int st = 0; st < nstages; st++) {
         const int nx2 = cur == 0 ? 2 : cur - 1;
-        q4gemm_load_stage<BM, PW>(w, prep, src, m0, n0, nb, b_begin + (st + 2) * QKB, lds[nx2]);
+        q4gemm_load_stage<BM, PW>(g, src, nb, b_begin + (st + 2) * QKB, swave, lds[nx2]);
         q4gemm_compute<BM, PW>((const QLL_LDS char *)&lds[cur], lo, bias, acc);
         q4gemm_sync<DMA>();
         cur = cur == 2 ? 0 : cur + 1;
