@@ -10,11 +10,16 @@ Kinds of pin used (the pages print no worked numeric example for this path):
     activations (the output is one weight times 127), identity matrices;
   * invariants: round trips of the byte formats, quantizer bounds,
     idempotence, the ternary identity;
-  * special cases: exact ties, zero blocks, zero rows.
+  * special cases: exact ties, zero blocks, zero rows;
+  * exact rational arithmetic (Python fractions): the quantizers' IEEE f32
+    quotient and product, rounded to binary32 from the exact value, on inputs
+    chosen so that this rounding lands on a .5 the exact value misses.
 The byte layouts are built here with numpy from their definitions (Q4_0:
 fp16 d little-endian then 16 bytes, low nibble = element t, high nibble =
 element t + 16; Q8_0: fp16 d then 32 int8; ternary: code s at bits 2s).
 """
+from fractions import Fraction
+
 import numpy as np
 
 import oracle as O
@@ -50,6 +55,56 @@ def np_pack_ternary(codes):
 
 def np_half(d_bits):
     return d_bits.astype(np.uint16).view(np.float16).astype(np.float64)
+
+
+def rne_binary32(r):
+    """The binary32 value nearest to the rational r (ties to even), as a
+    Fraction: 24 significant bits in the normal range, multiples of 2^-149
+    below it (IEEE 754 round-to-nearest-even; overflow is not reached here)."""
+    if r == 0:
+        return Fraction(0)
+    a = abs(r)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)  # 2^e <= a < 2^(e+1), or the subnormal range
+    scale = Fraction(2) ** (23 - e)
+    v = a * scale
+    n = v.numerator // v.denominator
+    rem = v - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return (Fraction(n) / scale) * (1 if r > 0 else -1)
+
+
+def round_half_away(r):
+    """Nearest integer to the rational r, halves away from zero."""
+    a = abs(r)
+    n = a.numerator // a.denominator
+    if a - n >= Fraction(1, 2):
+        n += 1
+    return n if r >= 0 else -n
+
+
+def _f32_tie_crossings(rng, count, quotient):
+    """`count` (amax, [x...]) sets whose f32 step (x / d with d = f32(amax/127)
+    when `quotient`, else x * s with s = f32(127/amax)) rounds onto k + 1/2
+    while the exact value lies strictly below it, so rounding the exact value
+    and rounding the f32 result give different codes."""
+    out = []
+    while len(out) < count:
+        amax = np.float32(rng.uniform(0.5, 100.0))
+        scale = rne_binary32(Fraction(float(amax)) / 127 if quotient else Fraction(127) / Fraction(float(amax)))
+        xs = []
+        while len(xs) < 31:
+            k = int(rng.integers(0, 126))
+            target = (k + Fraction(1, 2)) * scale if quotient else (k + Fraction(1, 2)) / scale
+            x = Fraction(float(np.float32(float(target))))
+            exact = x / scale if quotient else x * scale
+            if abs(x) < Fraction(float(amax)) and round_half_away(exact) != round_half_away(rne_binary32(exact)):
+                xs.append(float(x) * (1 if rng.integers(0, 2) else -1))
+        out.append((amax, xs))
+    return out
 
 
 def rand_q4(rng, n, k):
@@ -169,6 +224,29 @@ def check_q8_0_quantize_invariants(L):
             assert np.all((qb[i, b] == 0) | (np.sign(qb[i, b]) == np.sign(xb[i, b])))
             # the stored scale is the nearest fp16 of amax/127
             assert abs(np_half(np.array([d[i, b]]))[0] - dd) <= max(dd * 2.0 ** -11, 2.0 ** -25) * 1.0001
+
+
+def check_q8_0_quantize_f32_quotient(L):
+    # The code is round-half-away of the IEEE f32 quotient x/d, d = f32(amax/127).
+    # Each x below sits where that quotient rounds to k + 1/2 but the exact
+    # x/d lies below it: f32 division gives k + 1, an exact (or f64) division
+    # gives k.  The expected code is derived with exact rationals.
+    rng = np.random.default_rng(15)
+    sets = _f32_tie_crossings(rng, 6, quotient=True)
+    x = np.zeros((1, 32 * len(sets)), np.float32)
+    want = np.zeros(x.shape[1], np.int64)
+    want_d = []
+    for b, (amax, xs) in enumerate(sets):
+        d = rne_binary32(Fraction(float(amax)) / 127)
+        x[0, 32 * b] = -amax if b % 2 else amax
+        x[0, 32 * b + 1:32 * b + 32] = xs
+        for t in range(32):
+            xt = Fraction(float(x[0, 32 * b + t]))
+            want[32 * b + t] = max(-127, min(127, round_half_away(rne_binary32(xt / d))))
+        want_d.append(np.float32(float(d)).astype(np.float16).view(np.uint16))
+    q, dbits = O.unpack_q8_0(O.quantize_q8_0(x, L=L), 1, x.shape[1], L=L)
+    assert np.array_equal(q[0].astype(np.int64), want)
+    assert np.array_equal(dbits[0], np.array(want_d, np.uint16))
 
 
 def check_q8_0_idempotent(L):
@@ -472,6 +550,26 @@ def check_quantize_i8_rows(L):
     assert s[0] == 1.0
     assert q[0, :8].tolist() == [127, 1, -1, 3, -3, 127, -127, -127]
     assert t[0] == 127 + 1 - 1 + 3 - 3 + 127 - 127 - 127
+
+
+def check_quantize_i8_rows_f32_product(L):
+    # q = round-half-away of the IEEE f32 product x*s, s = f32(127/amax).
+    # Each x below makes that product round to k + 1/2 while the exact x*s
+    # lies below it (f32: k + 1, exact or f64: k).  Expected values from
+    # exact rationals.
+    rng = np.random.default_rng(16)
+    sets = _f32_tie_crossings(rng, 4, quotient=False)
+    x = np.zeros((len(sets), 48), np.float32)
+    for i, (amax, xs) in enumerate(sets):
+        x[i, 5] = -amax if i % 2 else amax
+        x[i, 6:37] = xs
+    q, s, t = O.quantize_i8_rows(x, L=L)
+    for i, (amax, _) in enumerate(sets):
+        sc = rne_binary32(Fraction(127) / Fraction(float(amax)))
+        want = [max(-127, min(127, round_half_away(rne_binary32(Fraction(float(v)) * sc)))) for v in x[i]]
+        assert Fraction(float(s[i])) == sc
+        assert q[i].astype(np.int64).tolist() == want
+        assert int(t[i]) == sum(want)
 
 
 def check_ternary_brute_force(L):

@@ -40,6 +40,20 @@ def test_quantize_q8_0_bit_exact(qll_gpu, m, k):
     assert np.array_equal(host(xq), O.quantize_q8_0(x).reshape(-1))
 
 
+def test_quantize_q8_0_f32_quotient_ties(qll_gpu):
+    # Inputs whose IEEE f32 quotient x/d rounds onto k + 1/2 while the exact
+    # quotient lies below it: only a kernel that divides in f32 and rounds
+    # half away from zero gives the oracle's codes.
+    import pins
+    sets = pins._f32_tie_crossings(np.random.default_rng(25), 64, quotient=True)
+    x = np.zeros((2, 32 * 32), np.float32)
+    for b, (amax, xs) in enumerate(sets):
+        row, col = divmod(b, 32)
+        x[row, 32 * col] = -amax if b % 3 == 0 else amax
+        x[row, 32 * col + 1:32 * col + 32] = xs
+    assert np.array_equal(host(quantize_q8_0(x)), O.quantize_q8_0(x).reshape(-1))
+
+
 def test_quantize_q8_0_prefill_size(qll_gpu):
     x = synth.q4_prefill_x(0)
     assert np.array_equal(host(quantize_q8_0(x)), O.quantize_q8_0(x).reshape(-1))

@@ -34,6 +34,23 @@ def test_quantize_i8_rows_bit_exact(qll_gpu, m, k):
     assert np.array_equal(host(t), t_ref)
 
 
+def test_quantize_i8_rows_f32_product_ties(qll_gpu):
+    # Rows whose f32 product x * (127/amax) rounds onto k + 1/2 while the exact
+    # product lies below it (f32 product, then half away from zero).
+    import pins
+    sets = pins._f32_tie_crossings(np.random.default_rng(26), 16, quotient=False)
+    x = np.zeros((len(sets), 2560), np.float32)
+    for i, (amax, xs) in enumerate(sets):
+        x[i, 7 * i] = -amax if i % 2 else amax
+        x[i, 100:100 + 31] = xs
+        x[i, 2000:2031] = xs[::-1]
+    q, s, t = quantize_i8_rows(x)
+    q_ref, s_ref, t_ref = O.quantize_i8_rows(x)
+    assert np.array_equal(host(q).reshape(x.shape), q_ref)
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(t), t_ref)
+
+
 def _check(codes, w_scale, x, what):
     n, k = codes.shape
     m = x.shape[0]

@@ -38,6 +38,7 @@ MUTATIONS = {
     "q8_scale_128": ("float d = amax / 127.0f;", "float d = amax / 128.0f;"),
     "q8_round_floor_half": ("float r = roundf(xb[t] / d);", "float r = floorf(xb[t] / d + 0.5f);"),
     "q8_round_even": ("float r = roundf(xb[t] / d);", "float r = rintf(xb[t] / d);"),
+    "q8_quotient_f64": ("float r = roundf(xb[t] / d);", "float r = (float)round((double)xb[t] / (double)d);"),
     "q8_small_block_zeroed": ("if (d != 0.0f) {\n                    float r = roundf(xb[t] / d);",
                               "if (d > 1e-3f) {\n                    float r = roundf(xb[t] / d);"),
     # Q4_0 x Q8_0 dot
@@ -79,6 +80,7 @@ MUTATIONS = {
     "i8_scale_inverted": ("float s = (amax == 0.0f) ? 0.0f : 127.0f / amax;",
                           "float s = (amax == 0.0f) ? 0.0f : amax / 127.0f;"),
     "i8_round_trunc": ("float r = roundf(xr[t] * s);", "float r = truncf(xr[t] * s);"),
+    "i8_product_f64": ("float r = roundf(xr[t] * s);", "float r = (float)round((double)xr[t] * (double)s);"),
     "i8_sum_dropped": ("sum += v;", "sum += (v > 0) ? v : 0;"),
 }
 
