@@ -20,7 +20,8 @@
  *  - Data pointers are DEVICE pointers owned by the caller.  The library never
  *    allocates, frees or retains them.  Base addresses must be 16-byte aligned
  *    (every PyTorch/hipMalloc allocation is).  Tensors are dense, row-major.
- *  - `stream` is a hipStream_t (NULL = the default stream).  Every call checks
+ *  - `stream` is a hipStream_t passed as `void *` (NULL = the default stream),
+ *    so that this header needs no HIP include.  Every call checks
  *    its arguments on the host in O(1), enqueues its kernel(s) on `stream` and
  *    returns without synchronising.  On error nothing is enqueued.  Faults
  *    during execution surface at the caller's next synchronisation.
@@ -113,7 +114,8 @@ int qll_quantize_q8_0(const float *x, void *xq, int64_t m, int64_t k, void *stre
  * sumi[j,b] = sum_t (qw[j,b,t] - 8) * qx[b,t] exact in int32 [CPU]; the float
  * sum over b is accumulated in f32 in an order of the kernel's choosing
  * (tolerance 1e-4 * sum_b |term_b| against an f64 sum).  w: block_q4_0[n][k/32],
- * xq: block_q8_0[k/32], y: float[n].  k % 32 == 0.  Bandwidth-bound: every
+ * xq: block_q8_0[k/32], y: float[n].  k % 32 == 0 and k <= 49152 (else
+ * QLL_ERR_SHAPE: the activation row is staged in LDS).  Bandwidth-bound: every
  * weight byte is read once ([FAST] 6.1). */
 int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64_t k, void *stream);
 
@@ -129,7 +131,7 @@ int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64
  * GEMV kernel; 2 <= m <= 8 (the small-m decode band that [BACK] 9.9 gates
  * apart from the general GEMM, one row-dot per weight row in 9.9.2) runs a
  * GEMV-shaped kernel that loads every weight once for all m rows; neither
- * needs a workspace. */
+ * needs a workspace.  At m == 1 the GEMV's limit k <= 49152 applies. */
 int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                        size_t ws_bytes, void *stream);
 
@@ -165,7 +167,8 @@ int qll_q4_0_repack(const void *w, void *wp, int64_t n, int64_t k, void *stream)
  * f32 scaling; tolerance 1e-4 * sum_b |term_b| against an f64 sum), computed
  * on the matrix core's 6-bit block-scaled path.  wp: the output of
  * qll_q4_0_repack for (n, k); xq: block_q8_0[m][k/32]; y: float[m][n];
- * k % 32 == 0, m >= 1.  ws/ws_bytes: at least
+ * k % 32 == 0 and k < 2^24 (else QLL_ERR_SHAPE: the kernel addresses the
+ * blocks of a row with 32-bit offsets), m >= 1.  ws/ws_bytes: at least
  * qll_workspace_bytes(QLL_OP_Q4_0_REPACKED_GEMM, m, n, k) bytes: the call
  * writes the activations there in operand form (6-bit codes of h and l with
  * q = 16h + l, and d), then split-k partial sums when it splits k; contents on
@@ -205,8 +208,9 @@ int qll_q8_0_repack(const void *w, void *wp, int64_t n, int64_t k, void *stream)
 /* Prefill GEMM on repacked Q8_0 weights: Y[m][n] = X.W^T with the per-block
  * arithmetic above, the exact block sum taken by two 6-bit block-scaled MFMAs
  * (16 h_w and l_w against 16 h_x + l_x).  wp: the output of qll_q8_0_repack;
- * xq: block_q8_0[m][k/32]; y: float[m][n]; k % 32 == 0, m >= 1.  ws/ws_bytes:
- * at least qll_workspace_bytes(QLL_OP_Q8_0_REPACKED_GEMM, m, n, k) bytes
+ * xq: block_q8_0[m][k/32]; y: float[m][n]; k % 32 == 0 and k < 2^24 (else
+ * QLL_ERR_SHAPE), m >= 1.  ws/ws_bytes: at least
+ * qll_workspace_bytes(QLL_OP_Q8_0_REPACKED_GEMM, m, n, k) bytes
  * (prepared activations, then split-k partials); contents on return are
  * unspecified. */
 int qll_q8_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
@@ -270,7 +274,8 @@ int qll_quantize_i8_rows(const float *x, int8_t *xq, float *act_scale, int32_t *
  * (exact int32; equal to sum_t (code - 1) * xq by the ternary identity), then
  * y[i,j] = dot * w_scale / act_scale[i] (0 where act_scale[i] == 0).
  * w: uint32[n][k/16], xq: int8[m][k], y: float[m][n].  k % 16 == 0.
- * The GEMV is the m = 1 case. */
+ * The GEMV is the m = 1 case (qll_ternary_gemm with m == 1 runs it): there
+ * k <= 65536 (else QLL_ERR_SHAPE: the activation row is staged in LDS). */
 int qll_ternary_gemv(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
                      const int32_t *act_sum, float *y, int64_t n, int64_t k, void *stream);
 int qll_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,

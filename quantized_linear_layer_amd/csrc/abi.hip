@@ -18,7 +18,7 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;    // every dimension below 2^31
 constexpr int64_t kMaxElems = (int64_t)1 << 40;  // and every tensor below 2^40 elements
-constexpr int64_t kMaxGemmK = (int64_t)1 << 24;  // Q4_0 GEMM (m > 1): per-lane 32-bit load offsets
+constexpr int64_t kMaxGemmK = (int64_t)1 << 24;  // Q4_0/Q8_0 GEMMs (m > 8, repacked): 32-bit load offsets
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -109,7 +109,7 @@ size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k)
                                  m, n, k);
     case QLL_OP_Q4_0_REPACKED_GEMM:
     case QLL_OP_Q8_0_REPACKED_GEMM:
-        if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
+        if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0 || k >= kMaxGemmK)
             return SIZE_MAX;
         return q4_0_packed_gemm_workspace(m, n, k);
     default:
@@ -240,7 +240,7 @@ int qll_q4_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_
 {
     if (!wp || !xq || !y || !ws)
         return QLL_ERR_NULL;
-    if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
+    if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0 || k >= kMaxGemmK)
         return QLL_ERR_SHAPE;
     if (!aligned16(wp) || !aligned16(xq) || !aligned16(y) || !aligned16(ws))
         return QLL_ERR_ALIGN;
@@ -292,7 +292,7 @@ int qll_q8_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_
 {
     if (!wp || !xq || !y || !ws)
         return QLL_ERR_NULL;
-    if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
+    if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0 || k >= kMaxGemmK)
         return QLL_ERR_SHAPE;
     if (!aligned16(wp) || !aligned16(xq) || !aligned16(y) || !aligned16(ws))
         return QLL_ERR_ALIGN;

@@ -92,6 +92,7 @@ def test_q4_errors(L):
     assert L.qll_q4_0_q8_0_gemv(GOOD, GOOD, NUL, 8, 64, None) == NULL
     assert L.qll_q4_0_q8_0_gemv(GOOD, GOOD, GOOD, 8, 65, None) == SHAPE
     assert L.qll_q4_0_q8_0_gemv(GOOD, GOOD, GOOD, 8, 49152 + 32, None) == SHAPE  # beyond the LDS-staged k
+    assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, GOOD, 1, 8, 49152 + 32, NUL, 0, None) == SHAPE  # m = 1: the GEMV
     assert L.qll_q4_0_q8_0_gemv(GOOD, GOOD, GOOD, 2 ** 31, 64, None) == SHAPE
     assert L.qll_q4_0_q8_0_gemv(MIS, GOOD, GOOD, 8, 64, None) == ALIGN
     assert L.qll_q4_0_q8_0_gemm(GOOD, NUL, GOOD, 4, 8, 64, NUL, 0, None) == NULL
@@ -110,6 +111,11 @@ def test_q4_errors(L):
     assert L.qll_q4_0_repack(GOOD, MIS, 8, 64, None) == ALIGN
     assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 64, NUL, 0, None) == NULL
     assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 80, GOOD, 2 ** 40, None) == SHAPE
+    # 32-bit block offsets inside the kernel: k below 2^24
+    assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 2 ** 24, GOOD, 2 ** 40, None) == SHAPE
+    assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 2 ** 25 - 32, GOOD, 2 ** 40, None) == SHAPE
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_REPACKED_GEMM, 4, 8, 2 ** 24) == SIZE_MAX
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_REPACKED_GEMM, 4, 8, 2 ** 24 - 32) < SIZE_MAX
     assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, MIS, 4, 8, 64, GOOD, 2 ** 40, None) == ALIGN
     assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 64, MIS, 2 ** 40, None) == ALIGN
     assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 64, GOOD, 16, None) == WORKSPACE
@@ -125,6 +131,8 @@ def test_q8w_errors(L):
     assert L.qll_q8_0_repack(MIS, GOOD, 8, 64, None) == ALIGN
     assert L.qll_q8_0_repacked_q8_0_gemm(GOOD, GOOD, NUL, 4, 8, 64, GOOD, 2 ** 40, None) == NULL
     assert L.qll_q8_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 0, 8, 64, GOOD, 2 ** 40, None) == SHAPE
+    assert L.qll_q8_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 2 ** 24, GOOD, 2 ** 40, None) == SHAPE
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q8_0_REPACKED_GEMM, 4, 8, 2 ** 24) == SIZE_MAX
     assert L.qll_q8_0_repacked_q8_0_gemm(GOOD, MIS, GOOD, 4, 8, 64, GOOD, 2 ** 40, None) == ALIGN
     assert L.qll_q8_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 64, GOOD, 1, None) == WORKSPACE
     assert qll.qll_q8_0_repacked_bytes(1, 32) == 6400
@@ -197,6 +205,7 @@ def test_ternary_errors(L):
     assert L.qll_ternary_gemv(GOOD, f, GOOD, GOOD, NUL, GOOD, 4, 32, None) == NULL
     assert L.qll_ternary_gemv(GOOD, f, GOOD, GOOD, GOOD, GOOD, 4, 40, None) == SHAPE
     assert L.qll_ternary_gemv(GOOD, f, GOOD, GOOD, GOOD, GOOD, 4, 65536 + 16, None) == SHAPE
+    assert L.qll_ternary_gemm(GOOD, f, GOOD, GOOD, GOOD, GOOD, 1, 4, 65536 + 16, None) == SHAPE  # m = 1: the GEMV
     assert L.qll_ternary_gemv(GOOD, f, MIS, GOOD, GOOD, GOOD, 4, 32, None) == ALIGN
     assert L.qll_ternary_gemm(GOOD, f, GOOD, GOOD, GOOD, NUL, 4, 4, 32, None) == NULL
     assert L.qll_ternary_gemm(GOOD, f, GOOD, GOOD, GOOD, GOOD, 4, 4, 8, None) == SHAPE
