@@ -2,6 +2,7 @@
 
 One step is one pass of every operation of the path at its full workload
 size, on inputs already resident in HBM:
+  * the Q4_0 x Q8_0 GEMV of the 512 x 512 layer (m = 1);
   * Q8_0 quantization of the decode activation and Q4_0 x Q8_0 decode GEMV
     (m = 1) on the four 8B-class linear shapes (k, n) = (4096, 14336),
     (14336, 4096), (4096, 4096), (4096, 128256);
@@ -11,38 +12,36 @@ size, on inputs already resident in HBM:
   * the BitNet ternary layer 2560 -> 6912: int8 row quantization, GEMV (m = 1)
     and GEMM (m = 64).
 Measured in the same run, outside the step: the Q4_0 prefill GEMM on the same
-weights repacked at load time into the matrix core's 6-bit operand form (the
-repack itself is load-time work); the four shapes with Q8_0 weights (decode
-GEMV on the Q8_0 blocks, prefill GEMM on repacked weights); the f32 GEMV and
-GEMM in the transposed-B orientation (W = B^T stored [n][k]) with f32, bf16
-and f16 weights.
+weights repacked at load time into the matrix core's 6-bit operand form; the
+four shapes with Q8_0 weights (decode GEMV, prefill GEMM on repacked
+weights); the f32 GEMV and GEMM in the transposed-B orientation (W = B^T
+stored [n][k]) with f32, bf16 and f16 weights; the (4096 -> 14336) layer over
+prompt lengths m = 1, 2, 4, 8, 16, 32, 64, 129, 256, 512; and the
+quantize-fused decode entry against quantize + decode at m = 1 and 8.
 Decode weights rotate through enough device copies (>= 1 GiB per shape) that
 no decode GEMV reads its weights from the 256 MiB Infinity Cache.
 
 Timing uses HIP events recorded on the stream the library launches on
 (torch's current stream).  `ms_per_step` is the wall time of the timed steps,
-each op bracketed by its own event pair (`ms_in_step` per kernel).  An event
-pair around one lone launch also holds the event and dispatch latency (about
-2-3 us, which is a third of a small decode GEMV), so each op's average launch
-duration (`ms` per kernel) is taken as well from runs of R back-to-back
-launches between one event pair, R chosen per op for about a millisecond per
-run, the decode ops still rotating through their weight copies.  The R
-launches are captured once into a HIP graph and replayed, so that the host's
-per-call overhead (Python argument checks, the launch itself: longer than a
-small kernel) cannot leave the GPU idle between them.  The JSON
-line's `value` is the Q4_0 x Q8_0 decode GEMV bandwidth over the four shapes
-(algorithmic bytes / summed average launch duration); `per_format` holds
-decode GB/s and prefill TOPS of every format with their fractions of the
-MI355X peaks, and `roofline` describes the kernel that takes the largest share
-of the step.  The operations of the widened rows (repacked weights, Q8_0
-weights, transposed-B) are measured in the same run, in passes of their own,
-and reported with `"in_step": false`; they are not part of a step.
+each op bracketed by its own event pair.  An event pair around one lone
+launch also holds the event and dispatch latency (2-3 us, a third of a small
+decode GEMV), so each op's average launch duration is taken from R
+back-to-back launches captured once into a HIP graph (the decode ops still
+rotating through their weight copies) and replayed between one event pair,
+R chosen for about a millisecond per replay, with at least 7 replays and 200
+launches per op.
+
+Output: the per-kernel table goes to stderr (and to --kernels-out), and stdout
+ends with ONE short JSON line: `value` is the Q4_0 x Q8_0 decode GEMV
+bandwidth over the four shapes (algorithmic bytes / summed average launch
+duration); `roofline` describes the kernel with the largest share of the
+step; `per_format` holds decode GB/s and prefill TOPS of every format with
+their fractions of the MI355X peaks; `rows` the per-workload times;
 `cpu_baseline` times the oracle (the test suite's plain C reference, never
-tuned) on the same decode GEMVs on the host's cores.  `device` records the
-GPU, its compute-unit count, the HIP version and the bandwidth of a plain
-1 GiB device copy, which HBM-bound rows also report as a second denominator
-(`frac_of_copy`); a row whose launch times vary by more than 8% (coefficient
-of variation) is flagged `noisy`.
+tuned) on every workload on the host's physical cores; `device` records the
+GPU, the bandwidth of a plain 1 GiB device copy (a second HBM denominator)
+and a hash of the kernel sources.  A row whose launch times vary by more than
+8% (coefficient of variation) is flagged noisy.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -68,6 +67,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's CPU sample")
     p.add_argument("--only", default="", help="comma-separated op-name prefixes to run (profiling)")
+    p.add_argument("--kernels-out", default="", help="also write the per-kernel table (JSON) to this file")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy per step (counter calibration)")
     return p.parse_args()
@@ -76,7 +76,8 @@ def parse():
 # Operations of the rows beyond the hot path's core (small-m, repacked weights,
 # Q8_0 weights, transposed-B): timed the same way, but not part of a step.
 NOISY_CV = 0.08  # coefficient of variation above which a row is flagged noisy
-EXTRA_PREFIXES = ("q4r_gemm", "q8w_gemv", "q8r_gemm", "nt_", "sgemm_core")
+EXTRA_PREFIXES = ("q4r_gemm", "q8w_gemv", "q8r_gemm", "nt_", "sgemm_core", "msweep_", "f1_")
+M_SWEEP = (1, 2, 4, 8, 16, 32, 64, 129, 256, 512)  # prompt lengths straddling the tile edges
 
 
 class Op:
@@ -179,6 +180,64 @@ def build_ops(qll, synth, torch, np, dev, only):
                               wp.numel() + m * (k // 32) * 34 + 4 * m * n, 2 * m * n * k, "mfma", "bf6"))
         if need_dec and want(f"q4_gemv_{s}") and not want(f"q8_quant_decode_{s}"):
             qll.qll_quantize_q8_0(xd, xqd, 1, k)
+
+    # ---------------------------------------------------------------- Q4_0 512 x 512 layer (m = 1)
+    if want("q4_gemv_small"):
+        codes, d_bits, x = synth.q4_small()
+        n1, k1 = codes.shape
+        w1 = torch.empty(n1 * (k1 // 32) * 18, dtype=torch.uint8, device=dev)
+        qll.qll_pack_q4_0(to_dev(codes), to_dev(d_bits.view(np.int16)), w1, n1, k1)
+        xq1 = torch.empty((k1 // 32) * 34, dtype=torch.uint8, device=dev)
+        qll.qll_quantize_q8_0(to_dev(x), xq1, 1, k1)
+        y1 = torch.empty(n1, dtype=torch.float32, device=dev)
+        ops.append(Op("q4_gemv_small", "q4_0_small", "decode",
+                      lambda: qll.qll_q4_0_q8_0_gemv(w1, xq1, y1, n1, k1),
+                      w1.numel() + xq1.numel() + 4 * n1, 2 * n1 * k1, "hbm"))
+
+    # ---------------------------------------------------------------- prompt-length sweep, fused decode
+    # (4096 -> 14336): m over prompt lengths that straddle the kernels' row
+    # tiles (m = 1 GEMV, 2..8 small-m decode, 9..32 the 32-row GEMM, above it
+    # the 128-row GEMM), and the quantize-fused decode entry against the
+    # quantize + decode pair at m = 1 and m = 8 on every 8B-class shape.
+    for s, (k, n) in enumerate(synth.SHAPES_8B):
+        sweep = s == 0 and any(want(f"msweep_q4_m{m}") for m in M_SWEEP)
+        fused = any(want(f"f1_{kind}_m{m}_{s}") for kind in ("fused", "pair") for m in (1, 8))
+        if not (sweep or fused):
+            continue
+        codes, d_bits, _ = synth.q4_decode(s)
+        w0 = torch.empty(n * (k // 32) * 18, dtype=torch.uint8, device=dev)
+        qll.qll_pack_q4_0(to_dev(codes), to_dev(d_bits.view(np.int16)), w0, n, k)
+        del codes, d_bits
+        wbytes = w0.numel()
+        copies = [w0] + [w0.clone() for _ in range(max(1, -(-gib // wbytes)) - 1)]
+        xall = to_dev(synth.q4_prefill_x(s))
+        ms = [m for m in M_SWEEP if sweep and want(f"msweep_q4_m{m}")]
+        for m in ms:
+            xqm = torch.empty(m * (k // 32) * 34, dtype=torch.uint8, device=dev)
+            qll.qll_quantize_q8_0(xall[:m].contiguous(), xqm, m, k)
+            ym = torch.empty(m * n, dtype=torch.float32, device=dev)
+            need = qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, m, n, k)
+            wsm = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+            ops.append(Op(f"msweep_q4_m{m}", "q4_0_msweep", "sweep",
+                          lambda c=copies, xqm=xqm, ym=ym, m=m, n=n, k=k, wsm=wsm: qll.qll_q4_0_q8_0_gemm(
+                              c[step_ref["i"] % len(c)], xqm, ym, m, n, k, ws=wsm),
+                          wbytes + m * (k // 32) * 34 + 4 * m * n, 2 * m * n * k, "hbm" if m <= 8 else "mfma",
+                          None if m <= 8 else "f16"))
+        for m in ((1, 8) if fused else ()):
+            xm = xall[:m].contiguous()
+            xqm = torch.empty(m * (k // 32) * 34, dtype=torch.uint8, device=dev)
+            ym = torch.empty(m * n, dtype=torch.float32, device=dev)
+            if want(f"f1_fused_m{m}_{s}"):
+                ops.append(Op(f"f1_fused_m{m}_{s}", "q4_0_fused", "decode",
+                              lambda c=copies, xm=xm, ym=ym, m=m, n=n, k=k: qll.qll_q4_0_q8_0_gemv_f32(
+                                  c[step_ref["i"] % len(c)], xm, ym, m, n, k),
+                              wbytes + 4 * m * k + 4 * m * n, 2 * m * n * k, "hbm"))
+            if want(f"f1_pair_m{m}_{s}"):
+                def pair(c=copies, xm=xm, xqm=xqm, ym=ym, m=m, n=n, k=k):
+                    qll.qll_quantize_q8_0(xm, xqm, m, k)
+                    qll.qll_q4_0_q8_0_gemm(c[step_ref["i"] % len(c)], xqm, ym, m, n, k)
+                ops.append(Op(f"f1_pair_m{m}_{s}", "q4_0_pair", "decode", pair,
+                              wbytes + 4 * m * k + 4 * m * n, 2 * m * n * k, "hbm"))
 
     # ---------------------------------------------------------------- Q8_0 weights
     for s, (k, n) in enumerate(synth.SHAPES_8B):
@@ -317,26 +376,110 @@ def build_ops(qll, synth, torch, np, dev, only):
     return ops, step_ref
 
 
+def host_cpus():
+    """(physical cores, logical CPUs, model name) of this process's affinity
+    mask: logical CPUs that share a (package, core) pair are SMT siblings and
+    count once."""
+    cpus = sorted(os.sched_getaffinity(0))
+    cores = set()
+    for c in cpus:
+        base = f"/sys/devices/system/cpu/cpu{c}/topology/"
+        try:
+            cores.add((open(base + "physical_package_id").read().strip(), open(base + "core_id").read().strip()))
+        except OSError:
+            cores.add(("?", str(c)))
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return len(cores), len(cpus), model
+
+
 def cpu_baseline(synth, np, seconds):
-    """The oracle's Q4_0 x Q8_0 decode GEMV on the four 8B-class shapes, on
-    the host's cores, repeated until `seconds` of wall time have passed."""
+    """The oracle (plain C: exact int32 block sums with f64 scaling, f64
+    accumulation; never tuned) on every workload, on the physical cores of
+    this process's affinity mask.  Small workloads run whole, repeated until
+    a share of `seconds` has passed; the large GEMMs run on their first rows
+    only (the oracle's cost is linear in the rows), which the entry states.
+    `value` is the decode GEMV rate over the four 8B-class shapes, in the
+    unit of the GPU's `value`."""
     import oracle as O
-    data = []
+    phys, logical, model = host_cpus()
+    O.set_num_threads(phys)
+
+    def timed(fn, budget):
+        t_total, passes = 0.0, 0
+        while passes < 1 or (t_total < budget and passes < 10000):
+            t0 = time.perf_counter()
+            fn()
+            t_total += time.perf_counter() - t0
+            passes += 1
+        return t_total / passes, passes
+
+    out = {}
+
+    def rec(name, per_pass_s, passes, nbytes=None, ops=None, sample="whole"):
+        e = {"s": round(per_pass_s, 6), "passes": passes, "sample": sample}
+        if nbytes is not None:
+            e.update(value=round(nbytes / per_pass_s / 1e9, 3), unit="GB/s")
+        else:
+            e.update(value=round(ops / per_pass_s / 1e9, 3), unit="GOP/s")
+        out[name] = e
+
+    # 512 x 512 Q4_0 layer, m = 1
+    codes, d_bits, x = synth.q4_small()
+    w, xq = O.pack_q4_0(codes, d_bits), O.quantize_q8_0(x)
+    t, p = timed(lambda: O.q4_0_q8_0(w, xq, 1, 512, 512), 0.05 * seconds)
+    rec("q4_gemv_512", t, p, nbytes=w.size + xq.size + 4 * 512)
+    # 8B-class decode GEMVs (the four shapes together) and prefill GEMMs (first rows)
+    dec, pre_rows = [], 4
+    pre_ops, pre_t = 0, 0.0
     for s, (k, n) in enumerate(synth.SHAPES_8B):
         codes, d_bits, x = synth.q4_decode(s)
-        data.append((O.pack_q4_0(codes, d_bits), O.quantize_q8_0(x), n, k))
+        w = O.pack_q4_0(codes, d_bits)
         del codes, d_bits
-    nbytes = sum(w.size + xq.size + 4 * n for w, xq, n, k in data)
-    t_total, passes = 0.0, 0
-    while passes < 1 or (t_total < seconds and passes < 5000):
+        dec.append((w, O.quantize_q8_0(x), n, k))
+        xp = O.quantize_q8_0(synth.q4_prefill_x(s, m=pre_rows))
         t0 = time.perf_counter()
-        for w, xq, n, k in data:
-            O.q4_0_q8_0(w, xq, 1, n, k)
-        t_total += time.perf_counter() - t0
-        passes += 1
-    return {"value": nbytes * passes / t_total / 1e9, "unit": "GB/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{passes} pass(es) of the Q4_0 x Q8_0 decode GEMV oracle (int32 block sums, f64 scaling) "
-                      f"over the four 8B-class shapes, {nbytes / 1e6:.1f} MB per pass, {t_total:.1f} s"}
+        O.q4_0_q8_0(w, xp, pre_rows, n, k)
+        pre_t += time.perf_counter() - t0
+        pre_ops += 2 * pre_rows * n * k
+    dec_bytes = sum(w.size + xq.size + 4 * n for w, xq, n, k in dec)
+    t, p = timed(lambda: [O.q4_0_q8_0(w, xq, 1, n, k) for w, xq, n, k in dec], 0.35 * seconds)
+    rec("q4_gemv_8b", t, p, nbytes=dec_bytes)
+    rec("q4_gemm_8b_m512", pre_t, 1, ops=pre_ops, sample=f"rows 0..{pre_rows - 1} of 512, four shapes")
+    del dec
+    # f32 GEMM 4096^3 (first rows) and GEMV 4096 x 4096
+    a, b, x = synth.f32_gemm()
+    rows = 16
+    t0 = time.perf_counter()
+    O.sgemm(a[:rows], b)
+    rec("sgemm_4096", time.perf_counter() - t0, 1, ops=2 * rows * 4096 * 4096, sample=f"rows 0..{rows - 1} of 4096")
+    t, p = timed(lambda: O.sgemm(x, b), 0.1 * seconds)
+    rec("sgemv_4096", t, p, nbytes=4 * (4096 + 4096 * 4096 + 4096))
+    del a, b
+    # BitNet ternary 2560 -> 6912, m = 1 and m = 64 (quantization included)
+    codes, w_scale, x = synth.ternary_layer()
+    n, k = codes.shape
+    words = O.pack_ternary(codes)
+
+    def tern(xr):
+        q, sc, sm = O.quantize_i8_rows(xr)
+        O.ternary(words, w_scale, q, sc, sm, n, k)
+
+    t, p = timed(lambda: tern(x[:1]), 0.1 * seconds)
+    rec("ternary_m1", t, p, nbytes=words.size * 4 + 4 * k + 4 * n)
+    t, p = timed(lambda: tern(x), 0.1 * seconds)
+    rec("ternary_m64", t, p, ops=2 * 64 * n * k)
+    return {"value": out["q4_gemv_8b"]["value"], "unit": "GB/s", "cores": phys, "logical_cpus": logical,
+            "cpu_model": model, "kind": "oracle",
+            "sample": "the oracle on every workload on the physical cores; GEMMs on their first rows (stated per "
+                      "config); value = Q4_0 x Q8_0 decode GEMV over the four 8B-class shapes",
+            "configs": out}
 
 
 def main():
@@ -413,8 +556,10 @@ def main():
                 op.fn()
         graph.replay()
         torch.cuda.synchronize()
+        # at least 7 replays and 200 launches per op
+        replays = max(args.steps, 7, -(-200 // op.reps))
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(args.steps)]
+                 for _ in range(replays)]
         for e0, e1 in pairs:
             e0.record(stream)
             graph.replay()
@@ -432,9 +577,9 @@ def main():
         rl = op.roofline(ms)
         entry = {"op": op.name, "format": op.fmt, "kind": op.kind, "in_step": op.in_step, "ms": ms,
                  "ms_median": float(np.median(t)),
-                 "cv": float(np.std(t) / ms) if ms > 0 else 0.0, "reps": op.reps,
+                 "cv": float(np.std(t) / ms) if ms > 0 else 0.0, "reps": op.reps, "launches": op.reps * len(t),
                  "ms_in_step": float(np.mean(op.times_ms)), "bytes": op.nbytes, "flops": op.flops, **rl}
-        if op.kind == "prefill" and op.peak_key in ("f16", "bf6"):
+        if op.kind in ("prefill", "sweep") and op.peak_key in ("f16", "bf6"):
             entry["frac_int8_peak"] = rl["achieved"] / PEAK_TFLOPS["i8"]
         if op.kind == "prefill" and op.peak_key == "bf6":
             entry["frac_f16_peak"] = rl["achieved"] / PEAK_TFLOPS["f16"]
@@ -448,6 +593,13 @@ def main():
         print(f"  {op.name:22s} {ms * 1e3:10.2f} us (in step {entry['ms_in_step'] * 1e3:8.2f})  "
               f"{rl['achieved']:10.1f} {rl['unit']:8s} "
               f"{100 * rl['frac']:6.1f}% of {rl['bound']} peak  (cv {entry['cv']:.3f})", file=sys.stderr)
+    # the whole per-kernel table, on stderr (and in a file when asked), so
+    # that stdout ends with one short line
+    table = json.dumps({"kernels": kernels})
+    print("bench kernels: " + table, file=sys.stderr, flush=True)
+    if args.kernels_out:
+        with open(args.kernels_out, "w") as f:
+            f.write(table + "\n")
 
     def agg(fmt, kind):
         sel = [(op, e) for op, e in zip(ops, kernels) if op.fmt == fmt and op.kind == kind]
@@ -456,28 +608,50 @@ def main():
         t = sum(e["ms"] for _, e in sel) * 1e-3
         if kind == "decode":
             v = sum(op.nbytes for op, _ in sel) / t / 1e9
-            return {"gbs": v, "frac_hbm": v / PEAK_HBM_GBS}
+            return {"gbs": r4(v), "frac": r4(v / PEAK_HBM_GBS)}
         v = sum(op.flops for op, _ in sel) / t / 1e12
         key = sel[0][0].peak_key
-        out = {"tops": v, "mfma_dtype": key, "frac_mfma": v / PEAK_TFLOPS[key]}
+        out = {"tops": r4(v), "peak": key, "frac": r4(v / PEAK_TFLOPS[key])}
         if key in ("f16", "bf6"):
-            out["frac_int8_peak"] = v / PEAK_TFLOPS["i8"]
+            out["frac_i8"] = r4(v / PEAK_TFLOPS["i8"])
         if key == "bf6":
-            out["frac_f16_peak"] = v / PEAK_TFLOPS["f16"]
+            out["frac_f16"] = r4(v / PEAK_TFLOPS["f16"])
         return out
 
     per_format = {}
     for fmt in ("q4_0", "q4_0_repacked", "q8_0", "f32", "f32_core", "f32_nt", "bf16_nt", "f16_nt", "ternary"):
-        d = {"decode": agg(fmt, "decode"), "prefill": agg(fmt, "prefill")}
-        if any(d.values()):
+        d = {kind: agg(fmt, kind) for kind in ("decode", "prefill")}
+        d = {kind: v for kind, v in d.items() if v}
+        if d:
             per_format[fmt] = d
 
+    by_name = {e["op"]: e for e in kernels}
     in_step = [e for e in kernels if e["in_step"]] or kernels
     dom = max(in_step, key=lambda e: e["ms"]) if in_step else None
     roofline = None
     if dom is not None:
-        roofline = {"kernel": dom["op"], "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
-                    "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic_for(dom["op"])}
+        roofline = {"kernel": dom["op"], "bound": dom["bound"], "achieved": r4(dom["achieved"]), "peak": dom["peak"],
+                    "unit": dom["unit"], "frac": r4(dom["frac"]), "traffic": traffic_for(dom["op"]),
+                    "algorithmic_per_launch": dom["bytes"] if dom["bound"] == "hbm" else dom["flops"],
+                    "algorithmic_unit": "bytes" if dom["bound"] == "hbm" else "flop",
+                    "us_per_launch": r4(dom["ms"] * 1e3), "launches_timed": dom["launches"]}
+
+    def us(name):
+        e = by_name.get(name)
+        return r4(e["ms"] * 1e3) if e else None
+
+    rows = {
+        "q4_gemv_512x512_us": us("q4_gemv_small"),
+        "q4_decode_us": [us(f"q4_gemv_{s}") for s in range(4)],
+        "q4_prefill_us": [us(f"q4_gemm_{s}") for s in range(4)],
+        "q4_prefill_repacked_us": [us(f"q4r_gemm_{s}") for s in range(4)],
+        "sgemm_4096_us": us("sgemm_4096"), "sgemv_4096_us": us("sgemv_4096"),
+        "ternary_m1_us": us("ternary_gemv"), "ternary_m64_us": us("ternary_gemm"),
+        "m_sweep_4096x14336_us": {str(m): us(f"msweep_q4_m{m}") for m in M_SWEEP if f"msweep_q4_m{m}" in by_name},
+        "fused_vs_pair_us": {f"m{m}": [[us(f"f1_fused_m{m}_{s}"), us(f"f1_pair_m{m}_{s}")] for s in range(4)]
+                             for m in (1, 8)},
+        "noisy": [e["op"] for e in kernels if e["noisy"]],
+    }
 
     value = per_format.get("q4_0", {}).get("decode", {}) or {}
     cpu = None
@@ -486,23 +660,25 @@ def main():
         cpu = cpu_baseline(synth, np, args.cpu_seconds)
 
     line = {
-        "metric": METRIC, "value": value.get("gbs"), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "i8 (Q4_0 x Q8_0 int8 block dots, f32 scaling)", "data": "synthetic",
-        "config": {"workload": "one pass of the whole path: Q4_0 x Q8_0 decode GEMV (m=1) and prefill GEMM (m=512) "
-                               "on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256); f32 GEMM 4096^3 "
-                               "and GEMV 4096x4096; BitNet ternary 2560->6912 at m=1 and m=64",
-                   "outside_step": "Q4_0 prefill on load-time repacked weights; Q8_0-weight decode GEMV and repacked "
-                                   "prefill GEMM on the same shapes; the f32 GEMM 4096^3 on the bf16 matrix core "
-                                   "(operands split into exact bf16 parts); transposed-B f32 GEMV/GEMM 4096 with "
-                                   "f32, bf16 and f16 weights (GEMMs on the bf16 matrix core)",
-                   "value_is": "Q4_0 x Q8_0 decode GEMV algorithmic bytes / summed average launch duration (back-to-back "
-                               "launches on rotating weight copies) over the four shapes",
+        "metric": METRIC, "value": r4(value.get("gbs")), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r4(ms_per_step), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": "one pass of the path: Q4_0 x Q8_0 GEMV 512x512; decode GEMV (m=1) and prefill GEMM "
+                               "(m=512) on (k,n) = (4096,14336), (14336,4096), (4096,4096), (4096,128256) with their "
+                               "Q8_0 quantization; f32 GEMM 4096^3 and GEMV 4096^2; BitNet ternary 2560->6912 at "
+                               "m=1 and m=64 with int8 quantization",
+                   "value_is": "Q4_0 x Q8_0 decode GEMV algorithmic bytes / summed average launch time over "
+                               "the four 8B-class shapes (weights rotating through >= 1 GiB of copies)",
                    "parallelism": "single GPU"},
-        "per_format": per_format, "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+        "roofline": roofline, "per_format": per_format, "rows": rows, "cpu_baseline": cpu,
         "device": device_record(torch, dev, copy_gbs),
     }
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line, separators=(",", ":")), flush=True)
+
+
+def r4(v):
+    """Four significant digits (keeps the result line short)."""
+    return None if v is None else float(f"{v:.4g}")
 
 
 def measured_copy_gbs(torch, dev, stream, reps):
@@ -527,10 +703,27 @@ def measured_copy_gbs(torch, dev, stream, reps):
 
 
 def device_record(torch, dev, copy_gbs):
+    import glob
+    import hashlib
     p = torch.cuda.get_device_properties(dev)
-    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
-            "memory_bytes": p.total_memory, "hip": torch.version.hip, "torch": torch.__version__,
-            "copy_1gib_gbs": copy_gbs, "date_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime())}
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "quantized_linear_layer_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "hip": torch.version.hip, "copy_1gib_gbs": r4(copy_gbs), "sclk_mhz": sclk_mhz(),
+            "csrc_sha256_16": h.hexdigest()[:16], "date_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime())}
+
+
+def sclk_mhz():
+    """The GPU's current shader clock as amd-smi reports it (None if unavailable)."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "-g", "0"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    m = re.search(r"GFX_0:.*?CLK:\s*([0-9]+)\s*MHz", r.stdout, re.S)
+    return int(m.group(1)) if m else None
 
 
 def traffic_for(op_name):

@@ -68,6 +68,7 @@ def load(path):
         "orc_ternary": [_P, ctypes.c_float, _P, _P, _P, _I, _I, _I, _P, _P, _P],
         "orc_ternary_sampled": [_P, ctypes.c_float, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _P],
         "orc_num_threads": [],
+        "orc_set_num_threads": [ctypes.c_int],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -95,6 +96,13 @@ def _check(rc, what):
 
 def num_threads(L=None):
     return (L or lib()).orc_num_threads()
+
+
+def set_num_threads(count, L=None):
+    """Threads for the oracle's later calls (results are the same for any)."""
+    L = L or lib()
+    L.orc_set_num_threads.restype = None
+    L.orc_set_num_threads(int(count))
 
 
 # --------------------------------------------------------------------------- fp16

@@ -239,25 +239,43 @@ int orc_unpack_q8_0(const uint8_t *xq, int8_t *q, uint16_t *d_bits, int64_t m, i
 /* y = sum_b term_b in b order (f64), mag = sum_b |term_b|.                  */
 /* ------------------------------------------------------------------------ */
 
+/* Elements t = 0..15 are the low nibbles of qs[t], t = 16..31 the high
+ * nibbles of qs[t - 16]: the sum runs over t in order, in two loops. */
 static int32_t q4_0_q8_0_block_sum(const uint8_t *wblk, const uint8_t *xblk)
 {
     int32_t s = 0;
-    for (int t = 0; t < 32; t++) {
-        int qw = (t < 16) ? (wblk[2 + t] & 0x0f) : (wblk[2 + t - 16] >> 4);
-        int qx = (int8_t)xblk[2 + t];
-        s += (qw - 8) * qx;
+    for (int t = 0; t < 16; t++) {
+        int qw = wblk[2 + t] & 0x0f;
+        s += (qw - 8) * (int8_t)xblk[2 + t];
+    }
+    for (int t = 16; t < 32; t++) {
+        int qw = wblk[2 + t - 16] >> 4;
+        s += (qw - 8) * (int8_t)xblk[2 + t];
     }
     return s;
 }
 
-static void q4_0_q8_0_one(const uint8_t *wrow, const uint8_t *xrow, int64_t nb, double *y, double *mag)
+/* Every binary16 bit pattern decoded once by orc_half_to_double, so that a
+ * large product does not decode the same scale bits again for each output
+ * (the values are those of orc_half_to_double; NULL when out of memory). */
+static double *half_table(void)
+{
+    double *t = malloc(sizeof(double) * 65536);
+    if (t)
+        for (int h = 0; h < 65536; h++)
+            t[h] = orc_half_to_double((uint16_t)h);
+    return t;
+}
+
+static void q4_0_q8_0_one(const uint8_t *wrow, const uint8_t *xrow, int64_t nb, const double *half, double *y,
+                          double *mag)
 {
     double acc = 0.0, m = 0.0;
     for (int64_t b = 0; b < nb; b++) {
         const uint8_t *wb = wrow + b * 18;
         const uint8_t *xb = xrow + b * 34;
         int32_t sumi = q4_0_q8_0_block_sum(wb, xb);
-        double s = orc_half_to_double(load_u16le(wb)) * orc_half_to_double(load_u16le(xb));
+        double s = half[load_u16le(wb)] * half[load_u16le(xb)];
         double term = s * (double)sumi;
         acc += term;
         m += fabs(term);
@@ -272,10 +290,14 @@ int orc_q4_0_q8_0(const uint8_t *w, const uint8_t *xq, int64_t m, int64_t n, int
     if (k % 32 != 0 || m < 0 || n < 0 || k < 0)
         return ORC_ERR_ARG;
     int64_t nb = k / 32;
+    double *half = half_table();
+    if (!half)
+        return ORC_ERR_ARG;
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < n; j++)
         for (int64_t i = 0; i < m; i++)
-            q4_0_q8_0_one(w + j * nb * 18, xq + i * nb * 34, nb, &y[i * n + j], &mag[i * n + j]);
+            q4_0_q8_0_one(w + j * nb * 18, xq + i * nb * 34, nb, half, &y[i * n + j], &mag[i * n + j]);
+    free(half);
     return ORC_OK;
 }
 
@@ -289,9 +311,13 @@ int orc_q4_0_q8_0_sampled(const uint8_t *w, const uint8_t *xq, int64_t m, int64_
         if (ii[s] < 0 || ii[s] >= m || jj[s] < 0 || jj[s] >= n)
             return ORC_ERR_ARG;
     int64_t nb = k / 32;
+    double *half = half_table();
+    if (!half)
+        return ORC_ERR_ARG;
 #pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < count; s++)
-        q4_0_q8_0_one(w + jj[s] * nb * 18, xq + ii[s] * nb * 34, nb, &y[s], &mag[s]);
+        q4_0_q8_0_one(w + jj[s] * nb * 18, xq + ii[s] * nb * 34, nb, half, &y[s], &mag[s]);
+    free(half);
     return ORC_OK;
 }
 
@@ -408,11 +434,13 @@ int orc_q8_0_q8_0_block_sums(const uint8_t *w, const uint8_t *xq, int64_t m, int
 /*   mag[i][j] = sum_p |A[i][p] * B[p][j]|.                                 */
 /* ------------------------------------------------------------------------ */
 
-static void sgemm_one(const float *a, const float *b, int64_t n, int64_t k, int64_t i, int64_t j, double *c, double *mag)
+/* bt is B transposed (bt[j][p] = B[p][j]), so that one output streams two
+ * contiguous rows; the products and their order are those of the definition. */
+static void sgemm_one(const float *a, const float *bt, int64_t k, int64_t i, int64_t j, double *c, double *mag)
 {
     double acc = 0.0, m = 0.0;
     for (int64_t p = 0; p < k; p++) {
-        double prod = (double)a[i * k + p] * (double)b[p * n + j];
+        double prod = (double)a[i * k + p] * (double)bt[j * k + p];
         acc += prod;
         m += fabs(prod);
     }
@@ -420,14 +448,30 @@ static void sgemm_one(const float *a, const float *b, int64_t n, int64_t k, int6
     *mag = m;
 }
 
+/* A private copy of b[rows][cols] transposed to [cols][rows] (NULL when out
+ * of memory or empty). */
+static float *transposed(const float *b, int64_t rows, int64_t cols)
+{
+    float *t = malloc(sizeof(float) * (size_t)(rows * cols > 0 ? rows * cols : 1));
+    if (t)
+        for (int64_t p = 0; p < rows; p++)
+            for (int64_t j = 0; j < cols; j++)
+                t[j * rows + p] = b[p * cols + j];
+    return t;
+}
+
 int orc_sgemm(const float *a, const float *b, int64_t m, int64_t n, int64_t k, double *c, double *mag)
 {
     if (m < 0 || n < 0 || k < 0)
         return ORC_ERR_ARG;
+    float *bt = transposed(b, k, n);
+    if (!bt && n * k > 0)
+        return ORC_ERR_ARG;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < m; i++)
         for (int64_t j = 0; j < n; j++)
-            sgemm_one(a, b, n, k, i, j, &c[i * n + j], &mag[i * n + j]);
+            sgemm_one(a, bt, k, i, j, &c[i * n + j], &mag[i * n + j]);
+    free(bt);
     return ORC_OK;
 }
 
@@ -439,9 +483,13 @@ int orc_sgemm_sampled(const float *a, const float *b, int64_t m, int64_t n, int6
     for (int64_t s = 0; s < count; s++)
         if (ii[s] < 0 || ii[s] >= m || jj[s] < 0 || jj[s] >= n)
             return ORC_ERR_ARG;
+    float *bt = transposed(b, k, n);
+    if (!bt && n * k > 0)
+        return ORC_ERR_ARG;
 #pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < count; s++)
-        sgemm_one(a, b, n, k, ii[s], jj[s], &c[s], &mag[s]);
+        sgemm_one(a, bt, k, ii[s], jj[s], &c[s], &mag[s]);
+    free(bt);
     return ORC_OK;
 }
 
@@ -652,6 +700,19 @@ int orc_ternary_sampled(const uint32_t *w, float w_scale, const int8_t *q, const
         }
     }
     return status;
+}
+
+/* Threads of the next parallel loops (the bench runs the oracle on the
+ * physical cores only); results do not depend on it. */
+void orc_set_num_threads(int count)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (count > 0)
+        omp_set_num_threads(count);
+#else
+    (void)count;
+#endif
 }
 
 int orc_num_threads(void)

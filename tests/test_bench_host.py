@@ -29,3 +29,12 @@ def test_gpus_above_one_exit_with_message(capsys):
     finally:
         sys.argv = argv
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_host_cpus_counts_physical_cores():
+    phys, logical, _ = bench.host_cpus()
+    assert 1 <= phys <= logical
+
+
+def test_r4_keeps_four_significant_digits():
+    assert bench.r4(1234.5678) == 1235.0 and bench.r4(0.000123456) == 0.0001235 and bench.r4(None) is None

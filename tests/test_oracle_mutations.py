@@ -42,12 +42,18 @@ MUTATIONS = {
     "q8_small_block_zeroed": ("if (d != 0.0f) {\n                    float r = roundf(xb[t] / d);",
                               "if (d > 1e-3f) {\n                    float r = roundf(xb[t] / d);"),
     # Q4_0 x Q8_0 dot
-    "dot_nibble_order": ("int qw = (t < 16) ? (wblk[2 + t] & 0x0f) : (wblk[2 + t - 16] >> 4);",
-                         "int qw = (t < 16) ? (wblk[2 + t] >> 4) : (wblk[2 + t - 16] & 0x0f);"),
-    "dot_dropped_offset": ("s += (qw - 8) * qx;", "s += qw * qx;"),
-    "dot_offset_sign": ("s += (qw - 8) * qx;", "s += (qw + 8) * qx;"),
-    "dot_scale_dw_twice": ("double s = orc_half_to_double(load_u16le(wb)) * orc_half_to_double(load_u16le(xb));",
-                           "double s = orc_half_to_double(load_u16le(wb)) * orc_half_to_double(load_u16le(wb));"),
+    "dot_nibble_order": ("int qw = wblk[2 + t] & 0x0f;\n        s += (qw - 8) * (int8_t)xblk[2 + t];\n    }\n"
+                         "    for (int t = 16; t < 32; t++) {\n        int qw = wblk[2 + t - 16] >> 4;",
+                         "int qw = wblk[2 + t] >> 4;\n        s += (qw - 8) * (int8_t)xblk[2 + t];\n    }\n"
+                         "    for (int t = 16; t < 32; t++) {\n        int qw = wblk[2 + t - 16] & 0x0f;"),
+    "dot_high_nibble_index": ("int qw = wblk[2 + t - 16] >> 4;", "int qw = wblk[2 + t - 15] >> 4;"),
+    "dot_dropped_offset": ("int qw = wblk[2 + t] & 0x0f;\n        s += (qw - 8) * (int8_t)xblk[2 + t];",
+                           "int qw = wblk[2 + t] & 0x0f;\n        s += qw * (int8_t)xblk[2 + t];"),
+    "dot_offset_sign": ("int qw = wblk[2 + t - 16] >> 4;\n        s += (qw - 8) * (int8_t)xblk[2 + t];",
+                        "int qw = wblk[2 + t - 16] >> 4;\n        s += (qw + 8) * (int8_t)xblk[2 + t];"),
+    "dot_scale_dw_twice": ("double s = half[load_u16le(wb)] * half[load_u16le(xb)];",
+                           "double s = half[load_u16le(wb)] * half[load_u16le(wb)];"),
+    "dot_half_table": ("t[h] = orc_half_to_double((uint16_t)h);", "t[h] = orc_half_to_double((uint16_t)(h ^ 1));"),
     "dot_mag_signed": ("m += fabs(term);", "m += term;"),
     "dot_x_block_index": ("const uint8_t *xb = xrow + b * 34;", "const uint8_t *xb = xrow + (nb - 1 - b) * 34;"),
     # Q8_0 x Q8_0 dot
@@ -64,10 +70,11 @@ MUTATIONS = {
     "nt_f16_read_as_bf16": ("    return orc_half_to_double(h);\n}", "    return (double)h;\n}"),
     "nt_mag_signed": ("sum_abs += fabs(prod);", "sum_abs += prod;"),
     # f32 GEMM
-    "sgemm_b_column": ("double prod = (double)a[i * k + p] * (double)b[p * n + j];",
-                       "double prod = (double)a[i * k + p] * (double)b[p * n + (n - 1 - j)];"),
-    "sgemm_a_column": ("double prod = (double)a[i * k + p] * (double)b[p * n + j];",
-                       "double prod = (double)a[i * k + (k - 1 - p)] * (double)b[p * n + j];"),
+    "sgemm_b_column": ("double prod = (double)a[i * k + p] * (double)bt[j * k + p];",
+                       "double prod = (double)a[i * k + p] * (double)bt[(j ^ 1) * k + p];"),
+    "sgemm_a_column": ("double prod = (double)a[i * k + p] * (double)bt[j * k + p];",
+                       "double prod = (double)a[i * k + (k - 1 - p)] * (double)bt[j * k + p];"),
+    "sgemm_transpose_index": ("t[j * rows + p] = b[p * cols + j];", "t[j * rows + p] = b[j * cols + p];"),
     "sgemm_f32_accumulate": ("double acc = 0.0, m = 0.0;\n    for (int64_t p = 0; p < k; p++) {",
                              "float acc = 0.0f; double m = 0.0;\n    for (int64_t p = 0; p < k; p++) {"),
     # ternary
