@@ -504,7 +504,8 @@ int orc_sgemm_sampled(const float *a, const float *b, int64_t m, int64_t n, int6
 
 enum { ORC_W_F32 = 0, ORC_W_BF16 = 1, ORC_W_F16 = 2 };
 
-static double widen_weight(const void *w, int wtype, int64_t idx)
+/* half: orc_half_to_double of every binary16 pattern (half_table). */
+static double widen_weight(const void *w, int wtype, int64_t idx, const double *half)
 {
     if (wtype == ORC_W_F32)
         return (double)((const float *)w)[idx];
@@ -515,15 +516,15 @@ static double widen_weight(const void *w, int wtype, int64_t idx)
         memcpy(&f, &bits, sizeof f);
         return (double)f;
     }
-    return orc_half_to_double(h);
+    return half[h];
 }
 
-static void gemm_nt_one(const float *a, const void *w, int wtype, int64_t k, int64_t i, int64_t j, double *c,
-                        double *mag)
+static void gemm_nt_one(const float *a, const void *w, int wtype, int64_t k, int64_t i, int64_t j,
+                        const double *half, double *c, double *mag)
 {
     double sum = 0.0, sum_abs = 0.0;
     for (int64_t p = 0; p < k; p++) {
-        double prod = (double)a[i * k + p] * widen_weight(w, wtype, j * k + p);
+        double prod = (double)a[i * k + p] * widen_weight(w, wtype, j * k + p, half);
         sum += prod;
         sum_abs += fabs(prod);
     }
@@ -535,10 +536,14 @@ int orc_gemm_nt(const float *a, const void *w, int wtype, int64_t m, int64_t n, 
 {
     if (m < 0 || n < 0 || k < 0 || wtype < ORC_W_F32 || wtype > ORC_W_F16)
         return ORC_ERR_ARG;
+    double *half = half_table();
+    if (!half)
+        return ORC_ERR_ARG;
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < n; j++)
         for (int64_t i = 0; i < m; i++)
-            gemm_nt_one(a, w, wtype, k, i, j, &c[i * n + j], &mag[i * n + j]);
+            gemm_nt_one(a, w, wtype, k, i, j, half, &c[i * n + j], &mag[i * n + j]);
+    free(half);
     return ORC_OK;
 }
 
@@ -550,9 +555,13 @@ int orc_gemm_nt_sampled(const float *a, const void *w, int wtype, int64_t m, int
     for (int64_t s = 0; s < count; s++)
         if (ii[s] < 0 || ii[s] >= m || jj[s] < 0 || jj[s] >= n)
             return ORC_ERR_ARG;
+    double *half = half_table();
+    if (!half)
+        return ORC_ERR_ARG;
 #pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < count; s++)
-        gemm_nt_one(a, w, wtype, k, ii[s], jj[s], &c[s], &mag[s]);
+        gemm_nt_one(a, w, wtype, k, ii[s], jj[s], half, &c[s], &mag[s]);
+    free(half);
     return ORC_OK;
 }
 

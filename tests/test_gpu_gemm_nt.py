@@ -169,21 +169,38 @@ def test_small_integers_exact(qll_gpu, wdtype, m):
 @pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16", "f16core", "f32core"])
 def test_full_size(qll_gpu, wdtype):
     # the f32 workload's shapes in the transposed orientation: W = B^T of the
-    # 4096^3 GEMM; the GEMV on every output, the GEMM on a seeded sample
+    # 4096^3 GEMM; the GEMV and the GEMM on every output
+    import full_refs
     core = wdtype.endswith("core")
     wdtype = wdtype.replace("core", "")
-    a, b, x = synth.f32_gemm()
-    w = weights(np.ascontiguousarray(b.T), wdtype)
-    del b
+    a, w, y_ref, mag = full_refs.gemm_nt_4096(wdtype)
+    _, _, x = synth.f32_gemm()
     y1 = run(x, w, wdtype, core=core)
-    y_ref, mag = O.gemm_nt(x, w, wdtype)
-    assert_within(y1, y_ref, mag, TOL, f"NT GEMV 4096 {wdtype}")
+    r1, m1 = O.gemm_nt(x, w, wdtype)
+    assert_within(y1, r1, m1, TOL, f"NT GEMV 4096 {wdtype}")
     y = run(a, w, wdtype, core=core)
-    rng = np.random.default_rng(17)
-    ii = np.concatenate([[0, 4095], rng.integers(0, 4096, 3000)])
-    jj = np.concatenate([[4095, 0], rng.integers(0, 4096, 3000)])
-    c_ref, cmag = O.gemm_nt_sampled(a, w, wdtype, ii, jj)
-    assert_within(y[ii, jj], c_ref, cmag, TOL, f"NT GEMM 4096^3 {wdtype}")
+    assert_within(y, y_ref, mag, TOL, f"NT GEMM 4096^3 {wdtype}")
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "f16", "f16core", "f32core"])
+def test_same_sign_4096(qll_gpu, wdtype):
+    # operands of one sign (U(0, 1)) at 4096^3 (no K split): a rounding that
+    # always goes one way adds up along the k = 4096 chain instead of
+    # cancelling.  Whole rows and columns are checked.
+    core = wdtype.endswith("core")
+    wdtype = wdtype.replace("core", "")
+    rng = np.random.default_rng(2025)
+    a = synth.uniform_f32(rng, (4096, 4096), 0.0, 1.0)
+    w = weights(synth.uniform_f32(rng, (4096, 4096), 0.0, 1.0), wdtype)
+    y = run(a, w, wdtype, core=core)
+    rows = np.array([0, 1, 777, 4095])
+    cols = np.array([0, 100, 4095])
+    ii = np.concatenate([np.repeat(rows, 4096), np.tile(np.arange(4096), len(cols))])
+    jj = np.concatenate([np.tile(np.arange(4096), len(rows)), np.repeat(cols, 4096)])
+    y_ref, mag = O.gemm_nt_sampled(a, w, wdtype, ii, jj)
+    err = assert_within(y[ii, jj], y_ref, mag, TOL, f"same-sign NT 4096^3 {wdtype}{' core' if core else ''}")
+    print(f"same-sign NT 4096^3 {wdtype}{' core' if core else ''}: max |err|/mag = {err:.3g}")
     torch.cuda.empty_cache()
 
 

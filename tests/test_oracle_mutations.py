@@ -65,9 +65,9 @@ MUTATIONS = {
     "q8w_pack_d_big_endian": ("store_u16le(out, d_bits[j * nb + b]);",
                               "out[0] = (uint8_t)(d_bits[j * nb + b] >> 8); out[1] = (uint8_t)d_bits[j * nb + b];"),
     # NT GEMM, f32/bf16/f16 weights
-    "nt_weight_index_nn": ("widen_weight(w, wtype, j * k + p)", "widen_weight(w, wtype, p * k + j)"),
+    "nt_weight_index_nn": ("widen_weight(w, wtype, j * k + p, half)", "widen_weight(w, wtype, p * k + j, half)"),
     "nt_bf16_shift_15": ("uint32_t bits = (uint32_t)h << 16;", "uint32_t bits = (uint32_t)h << 15;"),
-    "nt_f16_read_as_bf16": ("    return orc_half_to_double(h);\n}", "    return (double)h;\n}"),
+    "nt_f16_read_as_bf16": ("    return half[h];\n}", "    return (double)h;\n}"),
     "nt_mag_signed": ("sum_abs += fabs(prod);", "sum_abs += prod;"),
     # f32 GEMM
     "sgemm_b_column": ("double prod = (double)a[i * k + p] * (double)bt[j * k + p];",
