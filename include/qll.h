@@ -63,7 +63,8 @@ enum {
     QLL_ERR_ALIGN = -3,     /* a base address is not 16-byte aligned */
     QLL_ERR_WORKSPACE = -4, /* ws is NULL or smaller than qll_workspace_bytes() */
     QLL_ERR_LAUNCH = -5,    /* the HIP launch itself failed */
-    QLL_ERR_DEVICE = -6     /* no usable device, or the current device is not gfx950 */
+    QLL_ERR_DEVICE = -6,    /* no usable device, or the current device is not gfx950 */
+    QLL_ERR_SCRATCH = -7    /* qll_q4_0_q8_0_gemm_noalloc: the shape needs more than its static scratch */
 };
 
 /* Operations that may need a caller-owned device workspace. */
@@ -134,6 +135,25 @@ int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64
  * needs a workspace.  At m == 1 the GEMV's limit k <= 49152 applies. */
 int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                        size_t ws_bytes, void *stream);
+
+/* Bytes of the static device scratch of qll_q4_0_q8_0_gemm_noalloc (per device). */
+#define QLL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* qll_q4_0_q8_0_gemm for callers that cannot allocate device memory or pass
+ * a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels, the same results bit for bit,
+ * with the workspace taken from a static device array of
+ * QLL_NOALLOC_SCRATCH_BYTES (64 MiB) that each device holds from the first
+ * call until the process ends.  The call itself allocates nothing.  Shapes
+ * whose qll_workspace_bytes(QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) exceeds that
+ * size return QLL_ERR_SCRATCH with nothing enqueued (every 8B-class layer at
+ * m = 512 fits); m <= 8 needs no scratch.  All calls on one device share its
+ * array and leave their contents there: two calls whose executions overlap
+ * on one device (different streams, or graphs replayed concurrently) race
+ * and give undefined results, so serialise them.  Other arguments and
+ * errors as qll_q4_0_q8_0_gemm. */
+int qll_q4_0_q8_0_gemm_noalloc(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k,
+                               void *stream);
 
 /* Quantize-fused decode: Y[m][n] = Q8_0(X).W^T for 1 <= m <= 8, where the f32
  * activation rows x: float[m][k] are quantized to Q8_0 inside the launch with

@@ -54,6 +54,7 @@ def load(path=LIB_PATH):
         "qll_q4_0_q8_0_gemv": [P, P, P, I, I, P],
         "qll_q4_0_q8_0_gemm": [P, P, P, I, I, I, P, S, P],
         "qll_q4_0_q8_0_gemv_f32": [P, P, P, I, I, I, P],
+        "qll_q4_0_q8_0_gemm_noalloc": [P, P, P, I, I, I, P],
         "qll_q4_0_repack": [P, P, I, I, P],
         "qll_q4_0_repacked_q8_0_gemm": [P, P, P, I, I, I, P, S, P],
         "qll_q8_0_q8_0_gemv": [P, P, P, I, I, P],
@@ -152,6 +153,17 @@ def qll_q4_0_q8_0_gemm(w, xq, y, m, n, k, ws=None, stream=None):
     _call("qll_q4_0_q8_0_gemm", _ptr(w, n * (k // 32) * Q4_0_BLOCK_BYTES, "w"),
           _ptr(xq, m * (k // 32) * Q8_0_BLOCK_BYTES, "xq"), _ptr(y, m * n * 4, "y"), m, n, k, wsp, wsb,
           _stream(stream))
+
+
+QLL_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def qll_q4_0_q8_0_gemm_noalloc(w, xq, y, m, n, k, stream=None):
+    """qll_q4_0_q8_0_gemm with its workspace in the library's static device
+    scratch (no allocation, no workspace argument); calls on one device must
+    not overlap."""
+    _call("qll_q4_0_q8_0_gemm_noalloc", _ptr(w, n * (k // 32) * Q4_0_BLOCK_BYTES, "w"),
+          _ptr(xq, m * (k // 32) * Q8_0_BLOCK_BYTES, "xq"), _ptr(y, m * n * 4, "y"), m, n, k, _stream(stream))
 
 
 def qll_q4_0_q8_0_gemv_f32(w, x, y, m, n, k, stream=None):

@@ -11,8 +11,16 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 using namespace qll;
+
+// Scratch of qll_q4_0_q8_0_gemm_noalloc, for callers that cannot allocate:
+// one array per device, held until the process ends.  In host code the name
+// `scratch` only stands for the symbol; its device address on the current
+// device comes from hipGetSymbolAddress (once per device, below), and only
+// that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[QLL_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -53,6 +61,30 @@ int check_device()
 
 int launched(hipError_t e) { return e == hipSuccess ? QLL_OK : QLL_ERR_LAUNCH; }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[64];
+
+int scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return QLL_ERR_DEVICE;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return QLL_ERR_DEVICE;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return QLL_OK;
+}
+
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 } // namespace
@@ -76,6 +108,8 @@ const char *qll_status_string(int status)
         return "kernel launch failed";
     case QLL_ERR_DEVICE:
         return "no usable device or the current device is not gfx950";
+    case QLL_ERR_SCRATCH:
+        return "the shape needs more scratch than the allocation-free entry's static array holds";
     default:
         return "unknown status";
     }
@@ -209,6 +243,30 @@ int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64
     if (ws && !aligned16(ws))
         return QLL_ERR_ALIGN;
     if (int rc = check_device())
+        return rc;
+    return launched(launch_q4_0_q8_0_gemm(static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(xq), y, m,
+                                          n, k, ws, as_stream(stream)));
+}
+
+int qll_q4_0_q8_0_gemm_noalloc(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k,
+                               void *stream)
+{
+    if (!w || !xq || !y)
+        return QLL_ERR_NULL;
+    if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
+        return QLL_ERR_SHAPE;
+    if (m <= kMaxMSmall) // the decode kernels need no scratch
+        return qll_q4_0_q8_0_gemm(w, xq, y, m, n, k, nullptr, 0, stream);
+    if (k >= kMaxGemmK)
+        return QLL_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(xq) || !aligned16(y))
+        return QLL_ERR_ALIGN;
+    if (q4_0_q8_0_gemm_workspace(m, n, k) > QLL_NOALLOC_SCRATCH_BYTES)
+        return QLL_ERR_SCRATCH;
+    if (int rc = check_device())
+        return rc;
+    void *ws = nullptr;
+    if (int rc = scratch_address(&ws))
         return rc;
     return launched(launch_q4_0_q8_0_gemm(static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(xq), y, m,
                                           n, k, ws, as_stream(stream)));

@@ -121,6 +121,21 @@ def test_q4_errors(L):
     assert L.qll_q4_0_repacked_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 64, GOOD, 16, None) == WORKSPACE
 
 
+def test_noalloc_gemm_errors(L):
+    SCRATCH = -7
+    assert L.qll_q4_0_q8_0_gemm_noalloc(NUL, GOOD, GOOD, 16, 8, 64, None) == NULL
+    assert L.qll_q4_0_q8_0_gemm_noalloc(GOOD, GOOD, GOOD, 16, 8, 48, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemm_noalloc(GOOD, GOOD, GOOD, 16, 8, 2 ** 24, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemm_noalloc(GOOD, GOOD, MIS, 16, 8, 64, None) == ALIGN
+    # a shape whose workspace exceeds the static scratch is refused before any device call
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 4096, 64, 14336) > qll.QLL_NOALLOC_SCRATCH_BYTES
+    assert L.qll_q4_0_q8_0_gemm_noalloc(GOOD, GOOD, GOOD, 4096, 64, 14336, None) == SCRATCH
+    assert "static" in qll.qll_status_string(SCRATCH)
+    # every 8B-class prefill layer at m = 512 fits
+    for k, n in ((4096, 14336), (14336, 4096), (4096, 4096), (4096, 128256)):
+        assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 512, n, k) <= qll.QLL_NOALLOC_SCRATCH_BYTES
+
+
 def test_q8w_errors(L):
     assert L.qll_q8_0_q8_0_gemv(GOOD, NUL, GOOD, 8, 64, None) == NULL
     assert L.qll_q8_0_q8_0_gemv(GOOD, GOOD, GOOD, 8, 65, None) == SHAPE
