@@ -45,7 +45,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define QLL_LDS __attribute__((address_space(3)))
 
 constexpr int PBM = 128, PBN = 128, PKB = 2, PNBUF = 3;
-constexpr int PDIST = PNBUF - 1; // stages in flight ahead of the one computed
 constexpr int kPThreads = 256;
 constexpr int kPWChunk = 3072; // codes of 128 weight rows x one block
 constexpr int kPXChunk = 6144; // h and l codes of 128 activation rows x one block
@@ -315,8 +314,8 @@ __device__ __forceinline__ T q4p_lds(const QLL_LDS char *base, uint32_t off)
 // Per-lane LDS byte offsets from the start of a stage buffer; reads add only
 // immediates (block, tile) to them.
 struct Q4pLaneOff {
-    uint32_t x0, x1; // this lane's activation planes (h for lanes 0..31, l for 32..63), tile row 0, block 0
-    uint32_t w0, w1; // weight planes, tile column 0, block 0
+    uint32_t x0, x1[2]; // this lane's activation planes (h for lanes 0..31, l for 32..63), tile rows 0 and 1
+    uint32_t w0, w1[2]; // weight planes, tile columns 0 and 1, block 0
     uint32_t dx, dw;
 };
 
@@ -327,83 +326,76 @@ __device__ __forceinline__ Q4pLaneOff q4p_lane_offsets(int wm, int wn, int lane)
     const int lr = lane & 31, lh = lane >> 5;
     Q4pLaneOff o;
     o.x0 = (uint32_t)(offsetof(Lds, xs) + lh * 3072 + 16 * (wm + lr));
-    o.x1 = (uint32_t)(offsetof(Lds, xs) + lh * 3072 + 2048 + 8 * (wm + lr));
     o.w0 = (uint32_t)(offsetof(Lds, wq) + 16 * (wn + lr));
-    o.w1 = (uint32_t)(offsetof(Lds, wq) + 2048 + 8 * (wn + lr));
     o.dx = (uint32_t)(offsetof(Lds, dx) + 2 * (wm + lr));
     o.dw = (uint32_t)(offsetof(Lds, dw) + 2 * (wn + lr));
-    asm volatile("" : "+v"(o.x0), "+v"(o.x1), "+v"(o.w0), "+v"(o.w1), "+v"(o.dx), "+v"(o.dw));
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        o.x1[i] = (uint32_t)(offsetof(Lds, xs) + lh * 3072 + 2048 + 8 * (wm + 32 * i + lr));
+        o.w1[i] = (uint32_t)(offsetof(Lds, wq) + 2048 + 8 * (wn + 32 * i + lr));
+    }
+    // Opaque to the compiler, so that the two 8-byte reads of a block (tiles
+    // 0 and 1, different base registers) are not merged into one read of
+    // four registers, which would then have to be copied into the two
+    // six-register MFMA operands.
+    asm volatile("" : "+v"(o.x0), "+v"(o.x1[0]), "+v"(o.x1[1]), "+v"(o.w0), "+v"(o.w1[0]), "+v"(o.w1[1]),
+                 "+v"(o.dx), "+v"(o.dw));
     return o;
 }
 
-// One stage: for each of its two blocks, the wave's 64 x 64 tile (2 x 2
-// tiles of 32 x 32).  Operand lanes: lane l holds row (column) l % 32 of
-// its tile and K half l / 32: the h codes (A, scale 2^4) or l codes (A,
-// scale 1) of its row, and the same 32 weight codes (B) in both halves.
-// The scale tile takes {d_x, 0, 0, 0} and {d_w, 0, 0, 0} in both lane
-// halves, so S = 2 d_x d_w exactly; the outputs are halved at the end.
+// Operand fragments of the wave's 64 x 64 tile (2 x 2 tiles of 32 x 32) for
+// one block.  Lane l holds row (column) l % 32 of its tile and K half l / 32:
+// the h codes (A, scale 2^4) or l codes (A, scale 1) of its row, and the
+// same 32 weight codes (B) in both halves.  The scale tile takes
+// {d_x, 0, 0, 0} and {d_w, 0, 0, 0} in both lane halves, so S = 2 d_x d_w
+// exactly; the outputs are halved at the end.
+struct Q4pA {
+    i32x8 x;   // activation codes of tile row i
+    f16x4 s;   // {d_x, 0, 0, 0}
+};
 template <bool Q8W>
-__device__ __forceinline__ void q4p_compute(const QLL_LDS char *base, const Q4pLaneOff &o, uint32_t scale_a,
-                                            f32x16 acc[2][2])
+struct Q4pB {
+    i32x8 m, l; // weight codes of tile column j (Q8_0 weights: h and l groups; Q4_0: m only)
+    f16x4 s;    // {d_w, 0, 0, 0}
+};
+
+__device__ __forceinline__ void q4p_read_a(const QLL_LDS char *base, const Q4pLaneOff &o, int kb, int i, Q4pA &a)
+{
+    const u32x4 x0 = q4p_lds<u32x4>(base, o.x0 + kb * kPXChunk + 512 * i);
+    const u32x2 x1 = q4p_lds<u32x2>(base, o.x1[i] + kb * kPXChunk);
+    a.x = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], 0, 0};
+    const uint32_t d = q4p_lds<uint16_t>(base, o.dx + kb * 2 * PBM + 64 * i);
+    a.s = __builtin_bit_cast(f16x4, u32x2{d, 0u});
+}
+
+template <bool Q8W>
+__device__ __forceinline__ void q4p_read_b(const QLL_LDS char *base, const Q4pLaneOff &o, int kb, int j,
+                                           Q4pB<Q8W> &b)
 {
     constexpr int WC = PFmt<Q8W>::kWChunk;
-    i32x8 a[2], bm[2], bl[2];
-    f16x4 sa[2], sb[2];
-    const auto operands = [&](int kb) {
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const u32x4 x0 = q4p_lds<u32x4>(base, o.x0 + kb * kPXChunk + 512 * i);
-            const u32x2 x1 = q4p_lds<u32x2>(base, o.x1 + kb * kPXChunk + 256 * i);
-            a[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], 0, 0};
-            const u32x4 w0 = q4p_lds<u32x4>(base, o.w0 + kb * WC + 512 * i);
-            const u32x2 w1 = q4p_lds<u32x2>(base, o.w1 + kb * WC + 256 * i);
-            bm[i] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], 0, 0};
-            if (Q8W) { // the l half of the weight codes, 3072 bytes further
-                const u32x4 v0 = q4p_lds<u32x4>(base, o.w0 + kb * WC + 3072 + 512 * i);
-                const u32x2 v1 = q4p_lds<u32x2>(base, o.w1 + kb * WC + 3072 + 256 * i);
-                bl[i] = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3], (int)v1[0], (int)v1[1], 0, 0};
-            }
-            const uint32_t dxb = q4p_lds<uint16_t>(base, o.dx + kb * 2 * PBM + 64 * i);
-            const uint32_t dwb = q4p_lds<uint16_t>(base, o.dw + kb * 2 * PBN + 64 * i);
-            sa[i] = __builtin_bit_cast(f16x4, u32x2{dxb, 0u});
-            sb[i] = __builtin_bit_cast(f16x4, u32x2{dwb, 0u});
-        }
-    };
-    // Software pipeline over the stage's eight (block, tile) steps: the
-    // matrix core works on step t while the vector ALU applies the scales of
-    // step t - 1, and the second block's operands are read once the first
-    // block's last MFMAs are issued.  The scheduling fences keep that order:
-    // left free, the compiler fills the gap with step t's own fmas, which
-    // wait for the MFMAs just issued.
-    operands(0);
-    f32x16 p[2], sc[2];
-#pragma unroll
-    for (int t = 0; t <= 4 * PKB; t++) {
-        if (t < 4 * PKB) {
-            const int i = (t >> 1) & 1, j = t & 1;
-            if (Q8W) { // sum 16 h_w (16 h_x + l_x) + l_w (16 h_x + l_x)
-                p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bm[j], f32x16{}, 3, 3, 0, scale_a, 0,
-                                                                          kE8M0Sixteen);
-                p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bl[j], p[t & 1], 3, 3, 0, scale_a, 0,
-                                                                          kE8M0One);
-            } else {
-                p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bm[j], f32x16{}, 3, 3, 0, scale_a, 0,
-                                                                          kE8M0One);
-            }
-            sc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[i], sb[j], f32x16{}, 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if ((t & 3) == 3 && t + 1 < 4 * PKB)
-            operands((t + 1) >> 2);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t > 0) {
-            const int u = t - 1, i = (u >> 1) & 1, j = u & 1;
-#pragma unroll
-            for (int v = 0; v < 16; v++)
-                acc[i][j][v] = fmaf(sc[u & 1][v], p[u & 1][v], acc[i][j][v]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    const u32x4 w0 = q4p_lds<u32x4>(base, o.w0 + kb * WC + 512 * j);
+    const u32x2 w1 = q4p_lds<u32x2>(base, o.w1[j] + kb * WC);
+    b.m = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], 0, 0};
+    if (Q8W) { // the l half of the weight codes, 3072 bytes further
+        const u32x4 v0 = q4p_lds<u32x4>(base, o.w0 + kb * WC + 3072 + 512 * j);
+        const u32x2 v1 = q4p_lds<u32x2>(base, o.w1[j] + kb * WC + 3072);
+        b.l = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3], (int)v1[0], (int)v1[1], 0, 0};
     }
+    const uint32_t d = q4p_lds<uint16_t>(base, o.dw + kb * 2 * PBN + 64 * j);
+    b.s = __builtin_bit_cast(f16x4, u32x2{d, 0u});
+}
+
+// The block sum P and the scale tile S of one 32 x 32 tile.
+template <bool Q8W>
+__device__ __forceinline__ void q4p_mfma(const Q4pA &a, const Q4pB<Q8W> &b, uint32_t scale_a, f32x16 &p, f32x16 &sc)
+{
+    if (Q8W) { // sum 16 h_w (16 h_x + l_x) + l_w (16 h_x + l_x)
+        p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.x, b.m, f32x16{}, 3, 3, 0, scale_a, 0, kE8M0Sixteen);
+        p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.x, b.l, p, 3, 3, 0, scale_a, 0, kE8M0One);
+    } else {
+        p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.x, b.m, f32x16{}, 3, 3, 0, scale_a, 0, kE8M0One);
+    }
+    sc = __builtin_amdgcn_mfma_f32_32x32x8f16(a.s, b.s, f32x16{}, 0, 0, 0);
 }
 
 // Consecutive workgroup ids go to the 8 XCDs in turn; each XCD walks a
@@ -430,6 +422,63 @@ __device__ __forceinline__ void q4p_sync()
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// One stage, computed from buffer CUR: steps t = 0..7 take block t / 4,
+// tile (i, j) = ((t / 2) % 2, t % 2), whose fragments are A[i], B[j].  Each
+// step issues its MFMAs, then the reads that refill the fragments just
+// finished with (A[0] after step 1 of a block, B[0] after step 2, A[1] and
+// B[1] after step 3) with those of the next block, two or three steps
+// before their use, then the scale fmas of the step before it; the
+// scheduling fences keep that order, so the vector ALU works on step t - 1
+// while the matrix core works on step t.  After step 4 each wave waits for
+// its loads of the next stage and the workgroup meets: every wave has then
+// read this buffer whole (block 1 is in registers) and the next one is
+// complete, so the loads of the stage three ahead go into this buffer at
+// once, and steps 5..7 read the next stage's block 0.
+template <bool Q8W, int CUR>
+__device__ __forceinline__ void q4p_stage(Q4pLds<Q8W> *lds, const Q4pLaneOff &lo, uint32_t scale_a,
+                                          f32x16 (&acc)[2][2], Q4pA (&A)[2], Q4pB<Q8W> (&B)[2], const Q4pSrc &src,
+                                          int nb, int b_load, int swave)
+{
+    constexpr int DMA = PFmt<Q8W>::kDma;
+    const QLL_LDS char *cur = (const QLL_LDS char *)&lds[CUR];
+    const QLL_LDS char *nxt = (const QLL_LDS char *)&lds[(CUR + 1) % PNBUF];
+    f32x16 p[2], sc[2];
+#pragma unroll
+    for (int t = 0; t <= 4 * PKB; t++) {
+        if (t < 4 * PKB)
+            q4p_mfma<Q8W>(A[(t >> 1) & 1], B[t & 1], scale_a, p[t & 1], sc[t & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t == 4) {
+            q4p_sync<DMA>();
+            q4p_load_stage<Q8W>(src, nb, b_load, swave, lds[CUR]);
+        }
+        if (t < 4 * PKB) {
+            const QLL_LDS char *rb = t < 4 ? cur : nxt;
+            const int rkb = t < 4 ? 1 : 0;
+            if ((t & 3) == 1)
+                q4p_read_a(rb, lo, rkb, 0, A[0]);
+            if ((t & 3) == 2)
+                q4p_read_b<Q8W>(rb, lo, rkb, 0, B[0]);
+            if ((t & 3) == 3) {
+                q4p_read_a(rb, lo, rkb, 1, A[1]);
+                q4p_read_b<Q8W>(rb, lo, rkb, 1, B[1]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (t > 0) {
+            const int u = t - 1, ui = (u >> 1) & 1, uj = u & 1;
+#pragma unroll
+            for (int v = 0; v < 16; v++)
+                acc[ui][uj][v] = fmaf(sc[u & 1][v], p[u & 1][v], acc[ui][uj][v]);
+            // keeps these fmas in this step: the loads' branches split the
+            // stage into blocks, and the compiler would otherwise sink each
+            // fma to the next use of its accumulator
+            asm volatile("" : "+v"(acc[ui][uj]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 template <bool Q8W>
@@ -459,11 +508,12 @@ __global__ __launch_bounds__(kPThreads) void packed_gemm_kernel(const uint8_t *_
     const Q4pLaneOff lo = q4p_lane_offsets<Q8W>(wm, wn, lane);
     const uint32_t scale_a = lane < 32 ? kE8M0Sixteen : kE8M0One;
 
-    // Stage st is computed from buffer st % 3; the loads of stage st + 2 go
-    // out at its start into the buffer that stage st - 1 used (every wave
-    // left it at the barrier that ended stage st - 1).  Stages past the range
-    // load padding and are never computed.  Wave roles in the loads are
-    // uniform per wave, so the wave index goes through a scalar register.
+    // Three stage buffers, stage st computed from buffer st % 3 (the loop
+    // runs three stages per trip, so every LDS address is a lane offset plus
+    // an immediate).  The loads run three stages ahead; stages past the
+    // range load padding (zero activations, clamped weights) and are never
+    // computed.  Wave roles in the loads are uniform per wave, so the wave
+    // index goes through a scalar register.
     Q4pSrc src;
     src.x = prep.x + m_tile * prep.nbp * kPXChunk;
     src.dx = reinterpret_cast<const uint8_t *>(prep.dx) + m_tile * prep.nbp * kPSChunk;
@@ -471,17 +521,26 @@ __global__ __launch_bounds__(kPThreads) void packed_gemm_kernel(const uint8_t *_
     src.dw = reinterpret_cast<const uint8_t *>(dws) + n_tile * nb * (int64_t)kPSChunk;
     const int swave = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-    for (int s0 = 0; s0 < PDIST; s0++)
+    for (int s0 = 0; s0 < PNBUF; s0++)
         q4p_load_stage<Q8W>(src, nb, b_begin + s0 * PKB, swave, lds[s0]);
-    q4p_sync<DMA * (PDIST - 1)>();
-    int cur = 0;
-    for (int st = 0; st < nstages; st++) {
-        const int nxt = cur + PDIST < PNBUF ? cur + PDIST : cur + PDIST - PNBUF;
-        q4p_load_stage<Q8W>(src, nb, b_begin + (st + PDIST) * PKB, swave, lds[nxt]);
-        q4p_compute<Q8W>((const QLL_LDS char *)&lds[cur], lo, scale_a, acc);
-        q4p_sync<DMA * (PDIST - 1)>();
-        cur = cur + 1 < PNBUF ? cur + 1 : 0;
+    q4p_sync<DMA * (PNBUF - 1)>();
+    Q4pA A[2];
+    Q4pB<Q8W> B[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        q4p_read_a((const QLL_LDS char *)&lds[0], lo, 0, i, A[i]);
+        q4p_read_b<Q8W>((const QLL_LDS char *)&lds[0], lo, 0, i, B[i]);
     }
+    int st = 0;
+    for (; st + PNBUF <= nstages; st += PNBUF) {
+        q4p_stage<Q8W, 0>(lds, lo, scale_a, acc, A, B, src, nb, b_begin + (st + 3) * PKB, swave);
+        q4p_stage<Q8W, 1>(lds, lo, scale_a, acc, A, B, src, nb, b_begin + (st + 4) * PKB, swave);
+        q4p_stage<Q8W, 2>(lds, lo, scale_a, acc, A, B, src, nb, b_begin + (st + 5) * PKB, swave);
+    }
+    if (st < nstages)
+        q4p_stage<Q8W, 0>(lds, lo, scale_a, acc, A, B, src, nb, b_begin + (st + 3) * PKB, swave);
+    if (st + 1 < nstages)
+        q4p_stage<Q8W, 1>(lds, lo, scale_a, acc, A, B, src, nb, b_begin + (st + 4) * PKB, swave);
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(0x7 << 4); // vmcnt(0) expcnt(7) lgkmcnt(0)
 
@@ -540,8 +599,8 @@ static Q4pPlan q4p_plan(int64_t m, int64_t n, int64_t k)
     s = (nb + per - 1) / per;
     p.splits = (int)s;
     p.per_split = (int)per;
-    // the last split's range plus the stages the pipeline reads past it
-    p.nbp = per * s + (PNBUF - 1) * PKB;
+    // the last split's range plus the stages the pipeline loads past it
+    p.nbp = per * s + PNBUF * PKB;
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     const size_t parts = s > 1 ? up((size_t)s * (size_t)(m * n) * sizeof(float)) : 0;
     const size_t chunks = (size_t)(p.mp / PBM) * (size_t)p.nbp;
