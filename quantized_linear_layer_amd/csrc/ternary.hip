@@ -169,6 +169,107 @@ static hipError_t launch_ter_l(const uint32_t *w, float w_scale, const int8_t *x
     return hipGetLastError();
 }
 
+// m = 1, k % 64 == 0: 256-thread workgroups, so the activation staging is
+// shared by four waves and each lane transposes at most a few 16-byte
+// pieces.  Per lane, in issue order: its activation pieces (so that waiting
+// for them does not wait for the weights: loads retire in order), the
+// weight units of its first chunk, then the transposes into LDS while the
+// weights are in flight.  L lanes per row (R = 64 / L rows per wave), U
+// units of four words per lane and chunk; the next chunk's weights are
+// loaded while the current one is dotted, into four independent
+// accumulators (one per dword of a word's activation) rather than one chain.
+constexpr int kTg2Threads = 256;
+constexpr int kTg2ActRegs = 4; // activation pieces per thread held in registers (k <= 16384)
+
+template <int L, int U>
+__global__ __launch_bounds__(kTg2Threads) void ternary_gemv2_kernel(
+    const uint32_t *__restrict__ w, float w_scale, const int8_t *__restrict__ xq, const float *__restrict__ act_scale,
+    const int32_t *__restrict__ act_sum, float *__restrict__ y, int64_t n, int nw)
+{
+    extern __shared__ u32x4 s_x[]; // [nw] transposed activation words
+    constexpr int R = 64 / L, WAVES = kTg2Threads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / L, r = lane % L;
+    const int nu = nw / 4;
+    const int chunk = U * L, chunks = (nu + chunk - 1) / chunk;
+    const int64_t row = ((int64_t)blockIdx.x * WAVES + wave) * R + g;
+    const u32x4 *wr = reinterpret_cast<const u32x4 *>(w + (row < n ? row : 0) * nw);
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(xq);
+    const float s = act_scale[0];
+    const int asum = act_sum[0];
+
+    u32x4 a[kTg2ActRegs];
+#pragma unroll
+    for (int j = 0; j < kTg2ActRegs; j++) {
+        const int i = threadIdx.x + j * kTg2Threads;
+        a[j] = xv[i < nw ? i : 0];
+    }
+    asm volatile("" ::: "memory"); // the activation loads go out first
+
+    u32x4 cur[U], nxt[U];
+    const auto load = [&](u32x4 (&d)[U], int c) {
+#pragma unroll
+        for (int i = 0; i < U; i++) {
+            const int u = c * chunk + r + i * L;
+            d[i] = wr[u < nu ? u : 0];
+        }
+    };
+    load(cur, 0);
+
+#pragma unroll
+    for (int j = 0; j < kTg2ActRegs; j++) {
+        const int i = threadIdx.x + j * kTg2Threads;
+        if (i < nw)
+            s_x[i] = transpose_4x4_bytes(a[j]);
+    }
+    for (int i = threadIdx.x + kTg2ActRegs * kTg2Threads; i < nw; i += kTg2Threads)
+        s_x[i] = transpose_4x4_bytes(xv[i]);
+    __syncthreads();
+
+    int acc[4] = {0, 0, 0, 0};
+    for (int c = 0; c < chunks; c++) {
+        if (c + 1 < chunks)
+            load(nxt, c + 1);
+#pragma unroll
+        for (int i = 0; i < U; i++) {
+            const int u = c * chunk + r + i * L;
+            if (u < nu) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const u32x4 t = s_x[4 * u + e];
+                    const uint32_t word = cur[i][e];
+                    acc[0] = sdot4(word & 0x03030303u, t[0], acc[0]);
+                    acc[1] = sdot4((word >> 2) & 0x03030303u, t[1], acc[1]);
+                    acc[2] = sdot4((word >> 4) & 0x03030303u, t[2], acc[2]);
+                    acc[3] = sdot4((word >> 6) & 0x03030303u, t[3], acc[3]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < U; i++)
+            cur[i] = nxt[i];
+    }
+    int dot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+    for (int off = L / 2; off > 0; off >>= 1)
+        dot += __shfl_xor(dot, off);
+    if (row < n && r == 0)
+        y[row] = ternary_output(dot, asum, w_scale, s);
+}
+
+template <int L, int U>
+static hipError_t launch_tg2(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
+                             const int32_t *act_sum, float *y, int64_t n, int nw, hipStream_t st)
+{
+    constexpr int R = 64 / L, RPW = R * (kTg2Threads / 64);
+    const int64_t grid = (n + RPW - 1) / RPW;
+    if (grid > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((ternary_gemv2_kernel<L, U>), dim3((unsigned)grid), dim3(kTg2Threads), (size_t)nw * 16, st, w,
+                       w_scale, xq, act_scale, act_sum, y, n, nw);
+    return hipGetLastError();
+}
+
 template <int VEC>
 static hipError_t launch_ter_vec(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
                                  const int32_t *act_sum, float *y, int64_t n, int nw, hipStream_t st)
@@ -187,8 +288,19 @@ hipError_t launch_ternary_gemv(const uint32_t *w, float w_scale, const int8_t *x
                                const int32_t *act_sum, float *y, int64_t n, int64_t k, hipStream_t st)
 {
     const int nw = (int)(k / 16);
-    if (nw % 4 == 0)
-        return launch_ter_vec<4>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+    if (nw % 4 == 0) {
+        // units of four words per row, about three per lane (2560 -> 6912:
+        // 16 lanes x 3 units 3.9 us; 32 x 2 4.1, 64 x 1 4.4, 8 x 5 4.0,
+        // 16 x 4 4.0, 8 x 8 4.2)
+        const int nu = nw / 4;
+        if (nu > 96)
+            return launch_tg2<64, 3>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+        if (nu > 48)
+            return launch_tg2<32, 3>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+        if (nu > 24)
+            return launch_tg2<16, 3>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+        return launch_tg2<8, 3>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
+    }
     return launch_ter_vec<1>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
 }
 

@@ -72,7 +72,10 @@ def test_bitnet_layer_full(qll_gpu, m):
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (1, 7, 48), (1, 33, 160), (1, 257, 1024), (2, 5, 16), (3, 17, 48),
                                    (17, 31, 160), (65, 40, 2560), (130, 70, 1024), (64, 16, 64),
                                    (5, 70, 14336), (33, 9, 4112),  # long k: several register buffers per wave
-                                   (2, 33, 1088), (16, 32, 2048), (40, 100, 192), (100, 3, 4160)])  # partial last chunks
+                                   (2, 33, 1088), (16, 32, 2048), (40, 100, 192), (100, 3, 4160),  # partial last chunks
+                                   # m = 1, k % 64 == 0: several chunks per row, a partial chunk, and
+                                   # activations beyond the pieces a thread stages from registers (k > 16384)
+                                   (1, 37, 16384), (1, 19, 65536), (1, 5, 4160), (1, 70, 6208), (1, 130, 192)])
 def test_shapes(qll_gpu, m, n, k):
     rng = np.random.default_rng(m * 100 + n * 7 + k)
     codes = synth.ternary_codes(rng, n, k)
