@@ -553,6 +553,141 @@ __global__ __launch_bounds__(64) void ternary_gemm2_kernel(const uint32_t *__res
     }
 }
 
+// The same tile per wave (16 activation rows x 32 weight rows, the same
+// MFMA and LDS layouts) with WN waves per workgroup side by side, so the
+// activation chunk a workgroup loads serves WN * 32 weight rows (a quarter
+// or half of the activation bytes the one-wave kernel reads per output), and
+// a ring of NB chunk buffers, all filled at the start: with the workload's
+// five chunks every load is requested before the first wait, so the kernel
+// pays one memory round trip instead of one per ring turn.  The loads of a
+// chunk are spread over the waves (per wave: its share of the activation
+// rows and its own weight rows), so each wave waits for its own loads of the
+// chunk and the workgroup then meets; after that meeting every wave is done
+// with the previous chunk, whose buffer then takes the next chunk past the
+// ring.
+template <int WN>
+struct Ter3Lds {
+    u32x4 x[kTer2BM][kTerWPC];          // [row][slot]
+    u32x4 w[WN * kTer2BN][kTerWPC / 4]; // [row][group]
+};
+
+template <int WN>
+__device__ __forceinline__ void ter3_load(const uint32_t *__restrict__ w, const int8_t *__restrict__ xq, int64_t m,
+                                          int64_t n, int nw, int64_t m0, int64_t n0, int c, int wave, Ter3Lds<WN> &s)
+{
+    const int lane = threadIdx.x & 63;
+    const QLL_LDS_T char *xs = (const QLL_LDS_T char *)&s.x[0][0];
+    const QLL_LDS_T char *ws = (const QLL_LDS_T char *)&s.w[0][0];
+#pragma unroll
+    for (int q0 = 0; q0 < 8 / WN; q0++) { // activation rows 2q, 2q + 1 for q = wave, wave + WN, ...
+        const int q = wave + WN * q0;
+        const int rr = 2 * q + (lane >> 5), slot = lane & 31;
+        const int64_t gi = m0 + rr < m ? m0 + rr : m - 1;
+        int word = 32 * c + (slot ^ (rr & 15));
+        word = word < nw ? word : nw - 1;
+        ter2_dma16(xq, (uint32_t)((gi * nw + word) * 16), xs + 1024 * q);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) { // this wave's weight rows 32 wave + 8q .. + 7
+        const int wr = 8 * q + (lane >> 3), grp = lane & 7;
+        const int64_t gj = n0 + 32 * wave + wr < n ? n0 + 32 * wave + wr : n - 1;
+        int word = 32 * c + 4 * (grp ^ ((wr >> 1) & 7));
+        word = word + 4 <= nw ? word : nw - 4;
+        ter2_dma16(w, (uint32_t)((gj * nw + word) * 4), ws + 4096 * wave + 1024 * q);
+    }
+}
+
+// Wait until at most `later` chunks of this wave's loads are outstanding.
+template <int D, int NB>
+__device__ __forceinline__ void ter3_wait(int later)
+{
+    static_assert(D * (NB - 1) < 64, "vmcnt field");
+    switch (later) {
+    case 0: ter2_wait<0>(); break;
+    case 1: ter2_wait<D>(); break;
+    case 2: ter2_wait<(NB > 2 ? 2 * D : 0)>(); break;
+    case 3: ter2_wait<(NB > 3 ? 3 * D : 0)>(); break;
+    default: ter2_wait<(NB > 4 ? 4 * D : 0)>(); break;
+    }
+}
+
+template <int WN, int NB>
+__global__ __launch_bounds__(64 * WN) void ternary_gemm3_kernel(const uint32_t *__restrict__ w, float w_scale,
+                                                                 const int8_t *__restrict__ xq,
+                                                                 const float *__restrict__ act_scale,
+                                                                 const int32_t *__restrict__ act_sum,
+                                                                 float *__restrict__ y, int64_t m, int64_t n, int nw)
+{
+    static_assert(NB >= 2 && NB <= 5, "ring depth");
+    constexpr int D = 8 / WN + 4; // loads per wave and chunk
+    __shared__ Ter3Lds<WN> lds[NB];
+    const int64_t m0 = (int64_t)blockIdx.y * kTer2BM, n0 = (int64_t)blockIdx.x * (kTer2BN * WN);
+    const int lane = threadIdx.x & 63, lr = lane & 15, lh = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nch = (nw + kTerWPC - 1) / kTerWPC;
+
+    i32x4 acc[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+    // the scales and code sums of this lane's four output rows, requested
+    // first so that the epilogue does not wait for another round trip
+    float scs[4];
+    int asums[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        const int64_t rw = m0 + 4 * lh + v < m ? m0 + 4 * lh + v : m - 1;
+        scs[v] = act_scale[rw];
+        asums[v] = act_sum[rw];
+    }
+#pragma unroll
+    for (int c = 0; c < NB; c++)
+        if (c < nch)
+            ter3_load<WN>(w, xq, m, n, nw, m0, n0, c, wave, lds[c]);
+    for (int c = 0; c < nch; c++) {
+        // chunks requested so far: the first NB, then one more per turn from c = 1
+        const int issued = (NB + (c > 0 ? c - 1 : 0)) < nch ? NB + (c > 0 ? c - 1 : 0) : nch;
+        ter3_wait<D, NB>(issued - c - 1);
+        __syncthreads();
+        if (c > 0 && c - 1 + NB < nch)
+            ter3_load<WN>(w, xq, m, n, nw, m0, n0, c - 1 + NB, wave, lds[(c - 1) % NB]);
+        const Ter3Lds<WN> &s = lds[c % NB];
+        u32x4 wv[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int wr = 32 * wave + 16 * j + lr, sw = ((16 * j + lr) >> 1) & 7;
+            wv[j][0] = s.w[wr][(2 * lh) ^ sw];
+            wv[j][1] = s.w[wr][(2 * lh + 1) ^ sw];
+        }
+#pragma unroll
+        for (int st = 0; st < 8; st++) {
+            const int word = 32 * c + 8 * lh + st;
+            i32x4 a = __builtin_bit_cast(i32x4, transpose_4x4_bytes(s.x[lr][(8 * lh + st) ^ lr]));
+            if (word >= nw)
+                a = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const uint32_t cw = wv[j][st >> 2][st & 3];
+                const i32x4 b = {(int)(cw & 0x03030303u), (int)((cw >> 2) & 0x03030303u),
+                                 (int)((cw >> 4) & 0x03030303u), (int)((cw >> 6) & 0x03030303u)};
+                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[j], 0, 0, 0);
+            }
+        }
+    }
+    // no load may still be writing this workgroup's LDS when it ends
+    ter2_wait<0>();
+    // D layout of a 16x16 tile: lane l, register v -> row 4*(l/16)+v, column l%16
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        const int64_t row = m0 + 4 * lh + v;
+        if (row >= m)
+            continue;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int64_t col = n0 + 32 * wave + 16 * j + lr;
+            if (col < n)
+                y[row * n + col] = ternary_output(acc[j][v], asums[v], w_scale, scs[v]);
+        }
+    }
+}
+
 hipError_t launch_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
                                const int32_t *act_sum, float *y, int64_t m, int64_t n, int64_t k, hipStream_t st)
 {
@@ -560,9 +695,10 @@ hipError_t launch_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *x
     // the restructured kernel addresses both operands with 32-bit offsets
     const bool small = m * k < ((int64_t)1 << 32) && n * (k / 4) < ((int64_t)1 << 32);
     if (nw % 4 == 0 && small) {
-        dim3 grid2((unsigned)((n + kTer2BN - 1) / kTer2BN), (unsigned)((m + kTer2BM - 1) / kTer2BM));
-        hipLaunchKernelGGL(ternary_gemm2_kernel, grid2, dim3(64), 0, st, w, w_scale, xq, act_scale, act_sum, y, m, n,
-                           nw);
+        constexpr int WN = 2, NB = 5;
+        dim3 grid3((unsigned)((n + WN * kTer2BN - 1) / (WN * kTer2BN)), (unsigned)((m + kTer2BM - 1) / kTer2BM));
+        hipLaunchKernelGGL((ternary_gemm3_kernel<WN, NB>), grid3, dim3(64 * WN), 0, st, w, w_scale, xq, act_scale,
+                           act_sum, y, m, n, nw);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((n + TBN - 1) / TBN), (unsigned)((m + TBM - 1) / TBM));
