@@ -228,9 +228,11 @@ def build_ops(qll, synth, torch, np, dev, only):
             xqm = torch.empty(m * (k // 32) * 34, dtype=torch.uint8, device=dev)
             ym = torch.empty(m * n, dtype=torch.float32, device=dev)
             if want(f"f1_fused_m{m}_{s}"):
+                need = qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_GEMV_F32, m, n, k)
+                fws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
                 ops.append(Op(f"f1_fused_m{m}_{s}", "q4_0_fused", "decode",
-                              lambda c=copies, xm=xm, ym=ym, m=m, n=n, k=k: qll.qll_q4_0_q8_0_gemv_f32(
-                                  c[step_ref["i"] % len(c)], xm, ym, m, n, k),
+                              lambda c=copies, xm=xm, ym=ym, m=m, n=n, k=k, fws=fws: qll.qll_q4_0_q8_0_gemv_f32(
+                                  c[step_ref["i"] % len(c)], xm, ym, m, n, k, ws=fws),
                               wbytes + 4 * m * k + 4 * m * n, 2 * m * n * k, "hbm"))
             if want(f"f1_pair_m{m}_{s}"):
                 def pair(c=copies, xm=xm, xqm=xqm, ym=ym, m=m, n=n, k=k):

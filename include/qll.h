@@ -77,7 +77,8 @@ enum {
     QLL_OP_GEMM_NT_BF16 = 6, /* qll_gemm_nt with QLL_DTYPE_BF16 weights */
     QLL_OP_GEMM_NT_F16 = 7,  /* qll_gemm_nt with QLL_DTYPE_F16 weights on the bf16 matrix core */
     QLL_OP_GEMM_NT_F32 = 8,  /* qll_gemm_nt with QLL_DTYPE_F32 weights on the bf16 matrix core */
-    QLL_OP_SGEMM_BF16 = 9    /* qll_sgemm at m > 1 on the bf16 matrix core */
+    QLL_OP_SGEMM_BF16 = 9,   /* qll_sgemm at m > 1 on the bf16 matrix core */
+    QLL_OP_Q4_0_GEMV_F32 = 10 /* qll_q4_0_q8_0_gemv_f32's optional workspace */
 };
 
 /* Bytes of device workspace `op` needs at this shape (0 if none); SIZE_MAX if
@@ -155,14 +156,23 @@ int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64
 int qll_q4_0_q8_0_gemm_noalloc(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k,
                                void *stream);
 
-/* Quantize-fused decode: Y[m][n] = Q8_0(X).W^T for 1 <= m <= 8, where the f32
- * activation rows x: float[m][k] are quantized to Q8_0 inside the launch with
- * exactly the arithmetic of qll_quantize_q8_0 ([BACK] 9.7 quantizes the
- * activation per call), then dotted as in qll_q4_0_q8_0_gemm: the result is
- * that of qll_quantize_q8_0 followed by qll_q4_0_q8_0_gemm, in one launch and
- * without the intermediate buffer.  w: block_q4_0[n][k/32], y: float[m][n],
- * k % 32 == 0; QLL_ERR_SHAPE for m outside [1, 8].  No workspace. */
-int qll_q4_0_q8_0_gemv_f32(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k, void *stream);
+/* Quantize-fused decode: Y[m][n] = Q8_0(X).W^T for 1 <= m <= 8, from the f32
+ * activation rows x: float[m][k] ([BACK] 9.7 quantizes the activation per
+ * call), quantized to Q8_0 with exactly the arithmetic of qll_quantize_q8_0
+ * and dotted as in qll_q4_0_q8_0_gemm: the result is that of
+ * qll_quantize_q8_0 followed by qll_q4_0_q8_0_gemm, bit for bit, on either
+ * route below.  w: block_q4_0[n][k/32], y: float[m][n], k % 32 == 0;
+ * QLL_ERR_SHAPE for m outside [1, 8].
+ * ws is optional.  Where qll_workspace_bytes(QLL_OP_Q4_0_GEMV_F32, m, n, k)
+ * is nonzero and ws (16-byte aligned, caller-owned, contents not preserved)
+ * holds at least that many bytes, the rows are quantized once into ws and
+ * the Q8_0 decode kernel runs on them: two launches from this one call, as
+ * fast as the pair.  Otherwise (ws NULL or smaller, or no workspace needed:
+ * m == 1 with a short row and a matrix that one pass of the resident
+ * workgroups covers) a single launch quantizes the rows inside every
+ * workgroup, which is faster only at that size. */
+int qll_q4_0_q8_0_gemv_f32(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k, void *ws,
+                           size_t ws_bytes, void *stream);
 
 /* ------------------------------------- Q4_0 repacked for the matrix core (prefill) */
 

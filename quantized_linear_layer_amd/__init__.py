@@ -24,6 +24,7 @@ QLL_OP_GEMM_NT_BF16 = 6
 QLL_OP_GEMM_NT_F16 = 7
 QLL_OP_GEMM_NT_F32 = 8
 QLL_OP_SGEMM_BF16 = 9
+QLL_OP_Q4_0_GEMV_F32 = 10
 QLL_DTYPE_F32, QLL_DTYPE_BF16, QLL_DTYPE_F16 = 0, 1, 2
 
 Q4_0_BLOCK_BYTES = 18
@@ -53,7 +54,7 @@ def load(path=LIB_PATH):
         "qll_quantize_q8_0": [P, P, I, I, P],
         "qll_q4_0_q8_0_gemv": [P, P, P, I, I, P],
         "qll_q4_0_q8_0_gemm": [P, P, P, I, I, I, P, S, P],
-        "qll_q4_0_q8_0_gemv_f32": [P, P, P, I, I, I, P],
+        "qll_q4_0_q8_0_gemv_f32": [P, P, P, I, I, I, P, S, P],
         "qll_q4_0_q8_0_gemm_noalloc": [P, P, P, I, I, I, P],
         "qll_q4_0_repack": [P, P, I, I, P],
         "qll_q4_0_repacked_q8_0_gemm": [P, P, P, I, I, I, P, S, P],
@@ -166,10 +167,14 @@ def qll_q4_0_q8_0_gemm_noalloc(w, xq, y, m, n, k, stream=None):
           _ptr(xq, m * (k // 32) * Q8_0_BLOCK_BYTES, "xq"), _ptr(y, m * n * 4, "y"), m, n, k, _stream(stream))
 
 
-def qll_q4_0_q8_0_gemv_f32(w, x, y, m, n, k, stream=None):
-    """Quantize-fused decode, 1 <= m <= 8: y[m][n] = Q8_0(x).W^T in one launch."""
+def qll_q4_0_q8_0_gemv_f32(w, x, y, m, n, k, ws=None, stream=None):
+    """Quantize-fused decode, 1 <= m <= 8: y[m][n] = Q8_0(x).W^T.  A workspace
+    of at least qll_workspace_bytes(QLL_OP_Q4_0_GEMV_F32, ...) bytes (when
+    that is nonzero) selects quantize-once-then-decode; none or a smaller
+    one the single launch that quantizes in every workgroup."""
+    wsp, wsb = (None, 0) if ws is None else (_ptr(ws, 0, "ws"), ws.numel() * ws.element_size())
     _call("qll_q4_0_q8_0_gemv_f32", _ptr(w, n * (k // 32) * Q4_0_BLOCK_BYTES, "w"), _ptr(x, m * k * 4, "x"),
-          _ptr(y, m * n * 4, "y"), m, n, k, _stream(stream))
+          _ptr(y, m * n * 4, "y"), m, n, k, wsp, wsb, _stream(stream))
 
 
 def qll_q4_0_repacked_bytes(n, k):

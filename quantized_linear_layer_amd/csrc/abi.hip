@@ -141,6 +141,10 @@ size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k)
             return SIZE_MAX;
         return gemm_nt_workspace(op == QLL_OP_GEMM_NT_BF16 ? QLL_W_BF16 : op == QLL_OP_GEMM_NT_F16 ? QLL_W_F16 : QLL_W_F32,
                                  m, n, k);
+    case QLL_OP_Q4_0_GEMV_F32:
+        if (m < 1 || m > kMaxMSmall || !dims_ok(n, k) || k % 32 != 0)
+            return SIZE_MAX;
+        return q4_0_gemv_f32_workspace(m, n, k);
     case QLL_OP_Q4_0_REPACKED_GEMM:
     case QLL_OP_Q8_0_REPACKED_GEMM:
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0 || k >= kMaxGemmK)
@@ -204,18 +208,22 @@ int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64
                                           k, as_stream(stream)));
 }
 
-int qll_q4_0_q8_0_gemv_f32(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k, void *stream)
+int qll_q4_0_q8_0_gemv_f32(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k, void *ws,
+                           size_t ws_bytes, void *stream)
 {
     if (!w || !x || !y)
         return QLL_ERR_NULL;
     if (m < 1 || m > kMaxMSmall || !dims_ok(n, k) || k % 32 != 0)
         return QLL_ERR_SHAPE;
-    if (!aligned16(w) || !aligned16(x) || !aligned16(y))
+    // a workspace too small, or not needed, selects the single launch
+    const size_t need = q4_0_gemv_f32_workspace(m, n, k);
+    uint8_t *wsp = (ws && need && ws_bytes >= need) ? static_cast<uint8_t *>(ws) : nullptr;
+    if (!aligned16(w) || !aligned16(x) || !aligned16(y) || (wsp && !aligned16(wsp)))
         return QLL_ERR_ALIGN;
     if (int rc = check_device())
         return rc;
     return launched(
-        launch_q4_0_q8_0_gemv_f32(static_cast<const uint8_t *>(w), x, y, m, n, k, as_stream(stream)));
+        launch_q4_0_q8_0_gemv_f32(static_cast<const uint8_t *>(w), x, y, m, n, k, wsp, as_stream(stream)));
 }
 
 int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,

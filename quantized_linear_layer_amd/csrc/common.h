@@ -102,8 +102,12 @@ hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, 
 constexpr int64_t kMaxMSmall = 8;
 hipError_t launch_q4_0_q8_0_gemv_m(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                    hipStream_t s);
+// With ws (at least q4_0_gemv_f32_workspace bytes, nonzero), the rows are
+// quantized into ws by the quantize kernel and the Q8_0 decode kernel runs
+// on them; with ws == nullptr, one launch quantizes inside each workgroup.
 hipError_t launch_q4_0_q8_0_gemv_f32(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
-                                     hipStream_t s);
+                                     uint8_t *ws, hipStream_t s);
+size_t q4_0_gemv_f32_workspace(int64_t m, int64_t n, int64_t k);
 size_t q4_0_q8_0_gemm_workspace(int64_t m, int64_t n, int64_t k);
 // Decode GEMV with Q8_0 weights.
 hipError_t launch_q8_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int64_t k, hipStream_t s);

@@ -198,6 +198,83 @@ __device__ __forceinline__ ActLds stage_q8_finish(const uint8_t *xq, int nb, con
     return ActLds{s_qs, s_dx, s_c8};
 }
 
+// The f32 activation row of the quantize-fused entry, quantized to Q8_0
+// while it is staged, with exactly the arithmetic of quantize_q8_0_kernel:
+// eight lanes per block (four values each; groups of eight consecutive
+// threads share a block), amax by xor-shuffles over the eight, d = amax / 127
+// and codes round-half-away(x / d) in IEEE f32, the stored binary16 d widened
+// back to f32 for the dot.  The LDS layout is stage_q8_finish's, so the dot
+// that follows sees the same values as after qll_quantize_q8_0.
+constexpr int kStageF32Regs = 4; // 16-byte pieces per thread held in registers (k <= 4096 at 256 threads)
+
+struct ActRawF32 {
+    u32x4 v[kStageF32Regs];
+};
+
+__device__ __forceinline__ void stage_f32_load(const float *x, int nb, ActRawF32 &raw)
+{
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    const int pieces = nb * 8;
+#pragma unroll
+    for (int j = 0; j < kStageF32Regs; j++) {
+        const int p = threadIdx.x + j * blockDim.x;
+        raw.v[j] = xv[p < pieces ? p : 0]; // unconditional (see stage_q8_load)
+    }
+}
+
+__device__ __forceinline__ void stage_f32_piece(u32x4 raw, int p, int nb, void *smem)
+{
+    u32x4 *s_qs = reinterpret_cast<u32x4 *>(smem);
+    float *s_dx = reinterpret_cast<float *>(s_qs + 2 * nb);
+    int *s_c8 = reinterpret_cast<int *>(s_dx + nb);
+    const int b = p >> 3, sub = p & 7;
+    const bool ok = b < nb;
+    // named components: a bit-cast of raw[e] inside an unrolled loop read
+    // component 0 for every e in this compiler's output
+    const float v[4] = {ok ? __uint_as_float(raw.x) : 0.0f, ok ? __uint_as_float(raw.y) : 0.0f,
+                        ok ? __uint_as_float(raw.z) : 0.0f, ok ? __uint_as_float(raw.w) : 0.0f};
+    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    a = fmaxf(a, __shfl_xor(a, 4));
+    const float d = a / 127.0f;
+    uint32_t q = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+        q |= ((uint32_t)quant_code(v[e], d) & 0xffu) << (8 * e);
+    int sx = sdot4(q, 0x01010101u, 0);
+    sx += __shfl_xor(sx, 1);
+    sx += __shfl_xor(sx, 2);
+    sx += __shfl_xor(sx, 4);
+    if (ok) {
+        reinterpret_cast<uint32_t *>(s_qs)[8 * b + sub] = q; // codes 4 sub .. 4 sub + 3 of block b
+        if (sub == 0) {
+            s_dx[b] = half_bits_to_float(float_to_half_bits(d));
+            s_c8[b] = -8 * sx;
+        }
+    }
+}
+
+__device__ __forceinline__ ActLds stage_f32_finish(const float *x, int nb, const ActRawF32 &raw, void *smem)
+{
+#pragma unroll
+    for (int j = 0; j < kStageF32Regs; j++)
+        stage_f32_piece(raw.v[j], threadIdx.x + j * blockDim.x, nb, smem);
+    // every thread of the workgroup runs the same trip count, so the
+    // eight-lane shuffles always see whole groups
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    const int pieces = nb * 8;
+    for (int p0 = kStageF32Regs * blockDim.x; p0 < pieces; p0 += blockDim.x) {
+        const int p = p0 + threadIdx.x;
+        stage_f32_piece(xv[p < pieces ? p : 0], p, nb, smem);
+    }
+    __syncthreads();
+    u32x4 *s_qs = reinterpret_cast<u32x4 *>(smem);
+    float *s_dx = reinterpret_cast<float *>(s_qs + 2 * nb);
+    int *s_c8 = reinterpret_cast<int *>(s_dx + nb);
+    return ActLds{s_qs, s_dx, s_c8};
+}
+
 constexpr int kGemvThreads = 256;
 
 // One work item of a wave: a group of R = 64/L rows and a chunk of U * L
@@ -260,9 +337,9 @@ __device__ __forceinline__ float gemv_compute(const GemvRaw<U> &raw, int64_t row
 // order, so the staging waits only for its own bytes and HBM traffic starts
 // at once.  (xq is deliberately not __restrict__: with it, the compiler may
 // move the activation loads past the barrier that keeps them ahead.)
-template <int L, int U, bool PAIR>
+template <int L, int U, bool PAIR, bool F32>
 __global__ __launch_bounds__(kGemvThreads) void q4_0_q8_0_gemv_kernel(const uint8_t *__restrict__ w,
-                                                                      const uint8_t *xq,
+                                                                      const void *xin,
                                                                       float *__restrict__ y, int64_t n, int nb)
 {
     extern __shared__ u32x4 smem[];
@@ -277,8 +354,14 @@ __global__ __launch_bounds__(kGemvThreads) void q4_0_q8_0_gemv_kernel(const uint
     const int64_t n_groups = (n + R - 1) / R;
     const int64_t stride = (int64_t)gridDim.x * WAVES;
 
+    const uint8_t *xq = static_cast<const uint8_t *>(xin);
+    const float *xf = static_cast<const float *>(xin);
     ActRaw araw;
-    stage_q8_load(xq, nb, araw);
+    ActRawF32 fraw;
+    if (F32)
+        stage_f32_load(xf, nb, fraw);
+    else
+        stage_q8_load(xq, nb, araw);
     asm volatile("" ::: "memory"); // keep these loads ahead of the weight loads
 
     int64_t grp = (int64_t)blockIdx.x * WAVES + wave;
@@ -287,7 +370,7 @@ __global__ __launch_bounds__(kGemvThreads) void q4_0_q8_0_gemv_kernel(const uint
     // unconditional (a wave without work loads masked dummies): see gemv_load
     gemv_load<L, U, PAIR>(w, grp * R + g, n, row_bytes, nu, 0, r, cur);
 
-    const ActLds act = stage_q8_finish(xq, nb, araw, smem);
+    const ActLds act = F32 ? stage_f32_finish(xf, nb, fraw, smem) : stage_q8_finish(xq, nb, araw, smem);
 
     float acc = 0.0f;
     while (grp < n_groups) {
@@ -318,25 +401,33 @@ __global__ __launch_bounds__(kGemvThreads) void q4_0_q8_0_gemv_kernel(const uint
 
 size_t q4_gemv_lds_bytes(int nb) { return (size_t)nb * 40; }
 
+constexpr int64_t kF32GemvGrid = 512;
+
 // One work item per wave: the dispatcher starts new workgroups as others
 // finish, which measured faster on the 296 MB vocabulary projection than
 // looping resident waves over items (47 vs 53 us), and equal on one-pass
 // shapes.  The kernel still loops if the grid limit were ever reached.
-template <int L, int U, bool PAIR>
-static hipError_t launch_l(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int nb, hipStream_t s)
+template <int L, int U, bool PAIR, bool F32>
+static hipError_t launch_l(const uint8_t *w, const void *xin, float *y, int64_t n, int nb, hipStream_t s)
 {
     constexpr int R = 64 / L;
     const int64_t groups = (n + R - 1) / R;
     int64_t grid = (groups + kGemvThreads / 64 - 1) / (kGemvThreads / 64);
+    // f32 rows: every workgroup quantizes the whole row, so at most two
+    // workgroups per CU, each looping over its rows, quantize it (measured
+    // against one item per wave: 11 vs 14 us on 4096 -> 14336, 57 vs 72 us
+    // on the 296 MB vocabulary projection)
+    if (F32 && grid > kF32GemvGrid)
+        grid = kF32GemvGrid;
     if (grid > 0x7fffffff)
         grid = 0x7fffffff;
-    hipLaunchKernelGGL((q4_0_q8_0_gemv_kernel<L, U, PAIR>), dim3((unsigned)grid), dim3(kGemvThreads),
-                       q4_gemv_lds_bytes(nb), s, w, xq, y, n, nb);
+    hipLaunchKernelGGL((q4_0_q8_0_gemv_kernel<L, U, PAIR, F32>), dim3((unsigned)grid), dim3(kGemvThreads),
+                       q4_gemv_lds_bytes(nb), s, w, xin, y, n, nb);
     return hipGetLastError();
 }
 
-template <bool PAIR>
-static hipError_t launch_pair(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int nb, hipStream_t s)
+template <bool PAIR, bool F32 = false>
+static hipError_t launch_pair(const uint8_t *w, const void *xq, float *y, int64_t n, int nb, hipStream_t s)
 {
     const int nu = PAIR ? nb / 2 : nb;
     // Lanes per row (8..64).  A matrix that fits in one pass of the resident
@@ -345,20 +436,20 @@ static hipError_t launch_pair(const uint8_t *w, const uint8_t *xq, float *y, int
     // per-row overhead in the persistent loop).
     if (n <= 16384) {
         if (nu > 64)
-            return launch_l<64, 4, PAIR>(w, xq, y, n, nb, s);
+            return launch_l<64, 4, PAIR, F32>(w, xq, y, n, nb, s);
         if (nu > 32)
-            return launch_l<32, 2, PAIR>(w, xq, y, n, nb, s);
+            return launch_l<32, 2, PAIR, F32>(w, xq, y, n, nb, s);
         if (nu > 16)
-            return launch_l<16, 2, PAIR>(w, xq, y, n, nb, s);
-        return launch_l<8, 2, PAIR>(w, xq, y, n, nb, s);
+            return launch_l<16, 2, PAIR, F32>(w, xq, y, n, nb, s);
+        return launch_l<8, 2, PAIR, F32>(w, xq, y, n, nb, s);
     }
     if (nu > 128)
-        return launch_l<64, 4, PAIR>(w, xq, y, n, nb, s);
+        return launch_l<64, 4, PAIR, F32>(w, xq, y, n, nb, s);
     if (nu > 64)
-        return launch_l<32, 4, PAIR>(w, xq, y, n, nb, s);
+        return launch_l<32, 4, PAIR, F32>(w, xq, y, n, nb, s);
     if (nu > 32)
-        return launch_l<16, 4, PAIR>(w, xq, y, n, nb, s);
-    return launch_l<8, 4, PAIR>(w, xq, y, n, nb, s);
+        return launch_l<16, 4, PAIR, F32>(w, xq, y, n, nb, s);
+    return launch_l<8, 4, PAIR, F32>(w, xq, y, n, nb, s);
 }
 
 hipError_t launch_q4_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int64_t k,
@@ -619,7 +710,7 @@ __device__ __forceinline__ void gm_act_load(const void *xin, int64_t m, int nb, 
 #pragma unroll
     for (int t = 0; t < GmRaw<M, U, PAIR, F32>::T; t++) {
         const int task = threadIdx.x + t * kGmThreads;
-        if (F32) {
+        if constexpr (F32) {
             const int blk = task >> 3, sub = task & 7;
             const int r = blk / CB, b = chunk * CB + blk % CB;
             const bool ok = task < TASKS && r < m && b < nb;
@@ -653,7 +744,7 @@ __device__ __forceinline__ void gm_act_store(const GmRaw<M, U, PAIR, F32> &raw, 
 #pragma unroll
     for (int t = 0; t < GmRaw<M, U, PAIR, F32>::T; t++) {
         const int task = threadIdx.x + t * kGmThreads;
-        if (F32) {
+        if constexpr (F32) {
             // every lane computes (the shuffles need all of them); tasks past
             // the chunk only skip their stores
             const int blk = task >> 3, sub = task & 7;
@@ -869,9 +960,41 @@ hipError_t launch_q4_0_q8_0_gemv_m(const uint8_t *w, const uint8_t *xq, float *y
     return launch_gm<false>(w, xq, y, m, n, k, s);
 }
 
-hipError_t launch_q4_0_q8_0_gemv_f32(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
-                                     hipStream_t s)
+// The single launch wins only where the weights take one pass of the
+// resident workgroups and the row is short: every workgroup then quantizes
+// the row once, in the shadow of its first weight loads (4096 x 4096 at
+// m = 1: 6.1 against 6.7 us for the two launches).  Elsewhere the repeated
+// quantization costs more than a second launch (4096 -> 14336 at m = 1:
+// 11.2 against 10.4 us; 14336 -> 4096: 18 against 11.7; every shape at
+// m = 8, where each workgroup would quantize eight rows: 38 to 178 against
+// 13 to 112 us), so given a workspace the rows are quantized once by the
+// quantize kernel and the Q8_0 decode kernels run on them.
+size_t q4_0_gemv_f32_workspace(int64_t m, int64_t n, int64_t k)
 {
+    if (m == 1 && k <= 4096 && n * k <= ((int64_t)1 << 24))
+        return 0;
+    return ((size_t)(m * (k / 32) * 34) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_q4_0_q8_0_gemv_f32(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
+                                     uint8_t *ws, hipStream_t s)
+{
+    if (ws) {
+        hipError_t e = launch_quantize_q8_0(x, ws, m * (k / 32), s);
+        if (e != hipSuccess)
+            return e;
+        if (m == 1 && k <= kMaxKQ4Gemv)
+            return launch_q4_0_q8_0_gemv(w, ws, y, n, k, s);
+        return launch_gm<false>(w, ws, y, m, n, k, s);
+    }
+    // m = 1: the GEMV kernel, quantizing the row while it stages it (the
+    // whole row fits in LDS up to kMaxKQ4Gemv; longer rows stage by chunks)
+    if (m == 1 && k <= kMaxKQ4Gemv) {
+        const int nb = (int)(k / 32);
+        if (nb % 2 == 0)
+            return launch_pair<true, true>(w, x, y, n, nb, s);
+        return launch_pair<false, true>(w, x, y, n, nb, s);
+    }
     return launch_gm<true>(w, x, y, m, n, k, s);
 }
 

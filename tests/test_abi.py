@@ -65,6 +65,12 @@ def test_workspace_sizes(L):
     assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 9, 4096, 14336) > 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_TERNARY_GEMM, 64, 6912, 2560) == 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_TERNARY_GEMM, 64, 6912, 2561) == SIZE_MAX
+    # the fused entry: none where its single launch is the faster route
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_GEMV_F32, 1, 4096, 4096) == 0
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_GEMV_F32, 1, 14336, 4096) >= 128 * 34
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_GEMV_F32, 8, 4096, 14336) >= 8 * 448 * 34
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_GEMV_F32, 9, 4096, 4096) == SIZE_MAX
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_GEMV_F32, 2, 8, 48) == SIZE_MAX
     assert qll.qll_workspace_bytes(99, 1, 1, 1) == SIZE_MAX
     assert qll.qll_workspace_bytes(qll.QLL_OP_SGEMM, 0, 4, 4) == SIZE_MAX
 
@@ -99,11 +105,12 @@ def test_q4_errors(L):
     assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, GOOD, 4, 8, 16, NUL, 0, None) == SHAPE
     assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, MIS, 4, 8, 64, NUL, 0, None) == ALIGN
     assert L.qll_q4_0_q8_0_gemm(GOOD, GOOD, GOOD, 16, 8, 2 ** 24, GOOD, 2 ** 40, None) == SHAPE
-    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, NUL, GOOD, 1, 8, 64, None) == NULL
-    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 0, 8, 64, None) == SHAPE
-    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 9, 8, 64, None) == SHAPE
-    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 2, 8, 48, None) == SHAPE
-    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, MIS, GOOD, 2, 8, 64, None) == ALIGN
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, NUL, GOOD, 1, 8, 64, NUL, 0, None) == NULL
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 0, 8, 64, NUL, 0, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 9, 8, 64, NUL, 0, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 2, 8, 48, NUL, 0, None) == SHAPE
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, MIS, GOOD, 2, 8, 64, NUL, 0, None) == ALIGN
+    assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 2, 8, 64, MIS, 2 ** 20, None) == ALIGN  # a workspace in use
     # repacked weights: the repack and the GEMM on them
     assert L.qll_q4_0_repack(NUL, GOOD, 8, 64, None) == NULL
     assert L.qll_q4_0_repack(GOOD, GOOD, 8, 48, None) == SHAPE

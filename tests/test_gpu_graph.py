@@ -69,6 +69,11 @@ def _setup():
             yf = empty(3 * n, torch.float32)
             bufs["q4_fused_y"] = yf
             calls.append(lambda w=w, xf=xf, yf=yf, n=n, k=k: qll.qll_q4_0_q8_0_gemv_f32(w, xf, yf, 3, n, k))
+            yfw = empty(3 * n, torch.float32)
+            fws = empty(qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_GEMV_F32, 3, n, k))
+            bufs["q4_fused_ws_y"] = yfw
+            calls.append(lambda w=w, xf=xf, yfw=yfw, n=n, k=k, fws=fws: qll.qll_q4_0_q8_0_gemv_f32(w, xf, yfw, 3, n,
+                                                                                                  k, ws=fws))
 
     # weights repacked at load time (Q4_0 and Q8_0) and the Q8_0-weight GEMV
     m, n, k = 64, 200, 512

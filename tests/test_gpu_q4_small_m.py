@@ -1,7 +1,7 @@
 """Parity of the small-m decode kernels against the oracle: the Q4_0 x Q8_0
 GEMM entry at 2 <= m <= 8 (weights loaded once for all rows) and the
 quantize-fused entry (f32 activations quantized to Q8_0 inside the launch)
-at 1 <= m <= 8.  Float outputs within 1e-4 * sum_b |term_b|; integer cases
+at 1 <= m <= 8, with and without its workspace.  Float outputs within 1e-4 * sum_b |term_b|; integer cases
 bit-exact; the fused quantization is checked bit for bit through the results
 it must reproduce."""
 import numpy as np
@@ -21,9 +21,17 @@ TOL = 1e-4
 SHAPES = [(300, 4096), (33, 14336), (7, 96), (129, 608), (64, 4160), (5, 32), (17, 8224)]
 
 
-def gemv_f32(w, x, m, n, k):
+def gemv_f32(w, x, m, n, k, route="single"):
+    """The fused entry without a workspace ("single": one launch quantizing
+    in every workgroup) or with one of the size it asks for ("ws": quantize
+    once, then the Q8_0 decode kernel; the single launch where it asks for
+    none)."""
     y = empty(m * n, torch.float32)
-    qll.qll_q4_0_q8_0_gemv_f32(w, dev(np.asarray(x, np.float32)), y, m, n, k)
+    ws = None
+    if route == "ws":
+        need = qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_GEMV_F32, m, n, k)
+        ws = empty(need) if need else None
+    qll.qll_q4_0_q8_0_gemv_f32(w, dev(np.asarray(x, np.float32)), y, m, n, k, ws=ws)
     return y
 
 
@@ -48,20 +56,53 @@ def test_small_m_gemm(qll_gpu, m, n, k):
     assert_within(y, y_ref, mag, TOL, f"small-m GEMM m={m} n={n} k={k}")
 
 
+@pytest.mark.parametrize("route", ["single", "ws"])
 @pytest.mark.parametrize("m", [1, 2, 4, 7, 8])
 @pytest.mark.parametrize("n,k", SHAPES)
-def test_fused_f32_gemv(qll_gpu, m, n, k):
+def test_fused_f32_gemv(qll_gpu, m, n, k, route):
     codes, d_bits, x = _case(m * 577 + n * 11 + k, m, n, k)
     w = pack_q4_0(codes, d_bits)
-    y = host(gemv_f32(w, x, m, n, k)).reshape(m, n)
+    y = host(gemv_f32(w, x, m, n, k, route)).reshape(m, n)
     y_ref, mag = _ref(codes, d_bits, x)
     assert_within(y, y_ref, mag, TOL, f"fused GEMV m={m} n={n} k={k}")
-    if m >= 2:
-        # the same kernel on Q8_0 input from qll_quantize_q8_0: identical
-        # arithmetic after the staging, so any difference in the in-launch
-        # quantization shows up as a bit difference
-        y2 = host(q4_gemm(w, quantize_q8_0(x), m, n, k)).reshape(m, n)
-        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    # the same dot on Q8_0 input from qll_quantize_q8_0 (the GEMV at m = 1,
+    # the small-m kernel above it): identical arithmetic after the staging,
+    # so any difference in the in-launch quantization shows up as a bit
+    # difference
+    y2 = host(q4_gemm(w, quantize_q8_0(x), m, n, k)).reshape(m, n)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("route", ["single", "ws"])
+@pytest.mark.parametrize("n,k", [(5, 49152), (7, 49184), (3, 65536)])
+def test_fused_f32_gemv_long_rows(qll_gpu, n, k, route):
+    # m = 1 stages the whole row in LDS up to k = 49152 and by chunks beyond
+    # (with a workspace: the GEMV up to 49152, the small-m kernel beyond)
+    codes, d_bits, x = _case(n * 13 + k, 1, n, k)
+    w = pack_q4_0(codes, d_bits)
+    y = host(gemv_f32(w, x, 1, n, k, route)).reshape(1, n)
+    y_ref, mag = _ref(codes, d_bits, x)
+    assert_within(y, y_ref, mag, TOL, f"fused GEMV m=1 n={n} k={k} {route}")
+    y2 = host(gemv_f32(w, x, 1, n, k, "single" if route == "ws" else "ws")).reshape(1, n)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+def test_fused_workspace_short_or_absent(qll_gpu):
+    # a workspace one byte short, or none, selects the single launch: the
+    # same bits as the two-launch route
+    op = qll.QLL_OP_Q4_0_GEMV_F32
+    m, n, k = 3, 70, 8192
+    codes, d_bits, x = _case(4242, m, n, k)
+    w = pack_q4_0(codes, d_bits)
+    need = qll.qll_workspace_bytes(op, m, n, k)
+    assert need >= m * (k // 32) * 34
+    outs = []
+    for ws in (None, empty(need - 1), empty(need)):
+        y = empty(m * n, torch.float32)
+        qll.qll_q4_0_q8_0_gemv_f32(w, dev(x), y, m, n, k, ws=ws)
+        outs.append(host(y))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
 
 
 # n >= 32768 takes the 4-rows-per-lane-group layout: odd block counts (one
@@ -129,8 +170,9 @@ def test_fused_zero_rows(qll_gpu):
 
 @pytest.mark.parametrize("s", range(4))
 def test_8b_shapes_fused_m1_and_m8(qll_gpu, s):
-    # full decode sizes: the fused entry at m = 1 against the oracle on every
-    # output; the small-m GEMM at m = 8 on a sample of outputs
+    # full decode sizes: the fused entry at m = 1 (both routes) against the
+    # oracle on every output; at m = 8 the small-m GEMM on a sample of
+    # outputs and the fused entry's routes bit for bit against it
     codes, d_bits, x1 = synth.q4_decode(s)
     n, k = codes.shape
     w = pack_q4_0(codes, d_bits)
@@ -138,8 +180,12 @@ def test_8b_shapes_fused_m1_and_m8(qll_gpu, s):
     y = host(gemv_f32(w, x1, 1, n, k))
     y_ref, mag = O.q4_0_q8_0(wq, O.quantize_q8_0(x1), 1, n, k)
     assert_within(y, y_ref[0], mag[0], TOL, f"fused m=1 {synth.SHAPES_8B[s]}")
+    assert np.array_equal(y.view(np.uint32), host(gemv_f32(w, x1, 1, n, k, "ws")).view(np.uint32))
     x8 = synth.q4_prefill_x(s)[:8]
     y8 = host(q4_gemm(w, quantize_q8_0(x8), 8, n, k)).reshape(8, n)
+    for route in ("single", "ws"):
+        yf = host(gemv_f32(w, x8, 8, n, k, route)).reshape(8, n)
+        assert np.array_equal(yf.view(np.uint32), y8.view(np.uint32)), route
     rng = np.random.default_rng(300 + s)
     ii = np.concatenate([[0, 7], rng.integers(0, 8, 2000)])
     jj = np.concatenate([[0, n - 1], rng.integers(0, n, 2000)])
