@@ -424,267 +424,235 @@ __global__ __launch_bounds__(kTerGemmThreads) void ternary_gemm_kernel(
 }
 
 // ------------------------------------------------------------------ GEMM, k % 64 == 0
-// The same MFMA and operand orders as above, restructured for latency: at the
-// workload's size (m = 64, 4.4 MB of weights) the kernel is bound by memory
-// round trips, not bytes or MFMAs.  One wave per workgroup owns 16 activation
-// rows x 32 weight rows (four times as many workgroups as the 64 x 32 tile
-// above), so no workgroup barrier is needed; every operand goes memory -> LDS
-// (global_load_lds) into a ring of kTer2Buf chunk buffers, issued
-// kTer2Buf - 1 chunks ahead, and the wave waits only for its own loads.  In
-// LDS the activation word w of row r sits in slot w ^ (r & 15) and weight
-// group g (4 words) of row r in group g ^ ((r >> 1) & 7), so the 16 rows an
-// MFMA operand reads fall in distinct banks; the 4x4 byte transpose of the
-// activation is applied after the LDS read.  Words past the end of the row
-// (a partial last chunk) are loaded from clamped addresses and their
-// activation operand is zeroed.
-constexpr int kTer2BM = 16, kTer2BN = 32, kTer2Buf = 3;
-constexpr int kTer2Dma = 12; // per chunk: 8 KB of activations + 4 KB of weights, 1 KB per wave-wide load
-
-struct Ter2Lds {
-    u32x4 x[kTer2BM][kTerWPC];  // [row][slot]
-    u32x4 w[kTer2BN][kTerWPC / 4]; // [row][group]
-};
-
-__device__ __forceinline__ void ter2_dma16(const void *base, uint32_t off, const QLL_LDS_T void *lds)
+// At the workload's size (m = 64, 4.4 MB of weights, 2.3 GOP) the GEMM is
+// bound neither by bytes nor by the matrix core but by each SIMD's
+// instruction stream and by memory round trips, so this kernel spends few
+// instructions per multiply-add and spreads k over the waves:
+//   * 32x32x32 int8 MFMA.  Per instruction a lane brings 16 activation bytes
+//     (one code word's worth, transposed into the unpack order) and one
+//     code word, so each transposed activation fragment feeds two MFMAs of
+//     32K multiply-adds (the wave's two 32-row weight groups) and each
+//     unpacked word a 32-row product.
+//   * Tile 32 activation rows x 64 weight rows per workgroup; the row's
+//     32-word chunks (512 codes) are dealt round-robin to its KS waves,
+//     each with its own LDS region; the exact int32 partial tiles are added
+//     in LDS in a fixed order at the end, so the result does not depend on
+//     KS.  KS is chosen so that the grid has about a wave per SIMD.
+//   * Operands go memory -> LDS by 16-byte DMA (global_load_lds), coalesced
+//     in 128-byte runs; per-lane loads of the MFMA fragments themselves
+//     would touch 64 cache lines per instruction.  Lane (r, h) at step s
+//     takes word 16h + s of the chunk, so half p of the chunk (steps 8p ..
+//     8p + 7) is words 8p .. 8p + 7 and 16 + 8p .. 16 + 8p + 7 of each row:
+//     both halves are requested at once and the first is dotted while the
+//     second lands.  The lane offsets (row, slot swizzle, clamps for ragged
+//     m and n) are computed once; chunk and half enter only through the
+//     scalar base address.
+//   * LDS slot swizzles: activation slot ^ (row & 15) and code group ^
+//     ((row >> 2) & 3), so the 16 rows one fragment read touches fall in
+//     distinct banks.
+// Words past the end of a row (a partial last chunk) are loaded from
+// clamped addresses and their code word is zeroed: code 0 adds nothing to
+// sum c q, and act_sum counts the row's real words only.
+__device__ __forceinline__ void ter_dma16(const void *base, uint32_t off, const QLL_LDS_T void *lds)
 {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
                  "s"((uint32_t)(uintptr_t)lds)
                  : "memory", "m0");
 }
 
-// Chunk c (activation words 32c .. 32c + 31 of every row) into buffer s.
-__device__ __forceinline__ void ter2_load(const uint32_t *__restrict__ w, const int8_t *__restrict__ xq, int64_t m,
-                                          int64_t n, int nw, int64_t m0, int64_t n0, int c, Ter2Lds &s)
-{
-    const int lane = threadIdx.x;
-    const QLL_LDS_T char *xs = (const QLL_LDS_T char *)&s.x[0][0];
-    const QLL_LDS_T char *ws = (const QLL_LDS_T char *)&s.w[0][0];
-#pragma unroll
-    for (int q = 0; q < 8; q++) { // rows 2q, 2q + 1: lane -> (row, slot)
-        const int rr = 2 * q + (lane >> 5), slot = lane & 31;
-        const int64_t gi = m0 + rr < m ? m0 + rr : m - 1;
-        int word = 32 * c + (slot ^ (rr & 15));
-        word = word < nw ? word : nw - 1;
-        ter2_dma16(xq, (uint32_t)((gi * nw + word) * 16), xs + 1024 * q);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; q++) { // rows 8q .. 8q + 7: lane -> (row, group)
-        const int wr = 8 * q + (lane >> 3), grp = lane & 7;
-        const int64_t gj = n0 + wr < n ? n0 + wr : n - 1;
-        int word = 32 * c + 4 * (grp ^ ((wr >> 1) & 7));
-        word = word + 4 <= nw ? word : nw - 4;
-        ter2_dma16(w, (uint32_t)((gj * nw + word) * 4), ws + 1024 * q);
-    }
-}
-
+// Wait until at most N vector-memory operations of this wave are
+// outstanding (and all LDS operations have completed).
 template <int N>
-__device__ __forceinline__ void ter2_wait()
+__device__ __forceinline__ void ter_wait()
 {
     static_assert(N < 64, "vmcnt field");
     __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4)); // vmcnt(N) expcnt(7) lgkmcnt(0)
     asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(64) void ternary_gemm2_kernel(const uint32_t *__restrict__ w, float w_scale,
-                                                           const int8_t *__restrict__ xq,
-                                                           const float *__restrict__ act_scale,
-                                                           const int32_t *__restrict__ act_sum, float *__restrict__ y,
-                                                           int64_t m, int64_t n, int nw)
-{
-    __shared__ Ter2Lds lds[kTer2Buf];
-    const int64_t m0 = (int64_t)blockIdx.y * kTer2BM, n0 = (int64_t)blockIdx.x * kTer2BN;
-    const int lane = threadIdx.x, lr = lane & 15, lh = lane >> 4;
-    const int nch = (nw + kTerWPC - 1) / kTerWPC;
+constexpr int kTerKsRows = 32, kTerKsCols = 64, kTerKsMaxSplit = 6; // 24 KB of LDS per wave
+constexpr int64_t kTerKsTargetWaves = 1024;
 
-    i32x4 acc[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
-#pragma unroll
-    for (int c = 0; c < kTer2Buf - 1; c++)
-        if (c < nch)
-            ter2_load(w, xq, m, n, nw, m0, n0, c, lds[c]);
-    for (int c = 0; c < nch; c++) {
-        const int ahead = c + kTer2Buf - 1;
-        if (ahead < nch)
-            ter2_load(w, xq, m, n, nw, m0, n0, ahead, lds[ahead % kTer2Buf]);
-        // chunk c has landed once at most the loads of the later chunks remain
-        const int later = (nch - 1 - c) < (kTer2Buf - 1) ? (nch - 1 - c) : (kTer2Buf - 1);
-        if (later >= 2)
-            ter2_wait<2 * kTer2Dma>();
-        else if (later == 1)
-            ter2_wait<kTer2Dma>();
-        else
-            ter2_wait<0>();
-        const Ter2Lds &s = lds[c % kTer2Buf];
-        u32x4 wv[2][2];
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int wr = 16 * j + lr, sw = (wr >> 1) & 7;
-            wv[j][0] = s.w[wr][(2 * lh) ^ sw];
-            wv[j][1] = s.w[wr][(2 * lh + 1) ^ sw];
-        }
-#pragma unroll
-        for (int st = 0; st < 8; st++) {
-            const int word = 32 * c + 8 * lh + st;
-            i32x4 a = __builtin_bit_cast(i32x4, transpose_4x4_bytes(s.x[lr][(8 * lh + st) ^ lr]));
-            if (word >= nw)
-                a = i32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const uint32_t cw = wv[j][st >> 2][st & 3];
-                const i32x4 b = {(int)(cw & 0x03030303u), (int)((cw >> 2) & 0x03030303u),
-                                 (int)((cw >> 4) & 0x03030303u), (int)((cw >> 6) & 0x03030303u)};
-                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[j], 0, 0, 0);
-            }
-        }
-    }
-    // D layout of a 16x16 tile: lane l, register v -> row 4*(l/16)+v, column l%16
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-        const int64_t row = m0 + 4 * lh + v;
-        if (row >= m)
-            continue;
-        const float sc = act_scale[row];
-        const int asum = act_sum[row];
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t col = n0 + 16 * j + lr;
-            if (col < n)
-                y[row * n + col] = ternary_output(acc[j][v], asum, w_scale, sc);
-        }
-    }
-}
-
-// The same tile per wave (16 activation rows x 32 weight rows, the same
-// MFMA and LDS layouts) with WN waves per workgroup side by side, so the
-// activation chunk a workgroup loads serves WN * 32 weight rows (a quarter
-// or half of the activation bytes the one-wave kernel reads per output), and
-// a ring of NB chunk buffers, all filled at the start: with the workload's
-// five chunks every load is requested before the first wait, so the kernel
-// pays one memory round trip instead of one per ring turn.  The loads of a
-// chunk are spread over the waves (per wave: its share of the activation
-// rows and its own weight rows), so each wave waits for its own loads of the
-// chunk and the workgroup then meets; after that meeting every wave is done
-// with the previous chunk, whose buffer then takes the next chunk past the
-// ring.
-template <int WN>
-struct Ter3Lds {
-    u32x4 x[kTer2BM][kTerWPC];          // [row][slot]
-    u32x4 w[WN * kTer2BN][kTerWPC / 4]; // [row][group]
+struct TerKsLds {
+    u32x4 x[2][kTerKsRows][16]; // [half][row][slot]: slot ^ (row & 15) = 8 hh + s8 -> word 32c + 16 hh + 8 half + s8
+    u32x4 w[2][kTerKsCols][4];  // [half][row][group]: group ^ ((row >> 2) & 3) = 2 hh + g2 -> words 32c + 16 hh + 8 half + 4 g2 ..
 };
 
-template <int WN>
-__device__ __forceinline__ void ter3_load(const uint32_t *__restrict__ w, const int8_t *__restrict__ xq, int64_t m,
-                                          int64_t n, int nw, int64_t m0, int64_t n0, int c, int wave, Ter3Lds<WN> &s)
+struct TerKsOff {
+    uint32_t x[8]; // byte offset of the lane's 16 bytes in activation load q (rows 4q .. 4q + 3), first half of chunk 0
+    uint32_t w[4]; // the same for code load q (rows 16q .. 16q + 15)
+};
+
+__device__ __forceinline__ void ter_ks_offsets(int64_t m, int64_t n, int nw, int64_t m0, int64_t n0, TerKsOff &o)
 {
     const int lane = threadIdx.x & 63;
-    const QLL_LDS_T char *xs = (const QLL_LDS_T char *)&s.x[0][0];
-    const QLL_LDS_T char *ws = (const QLL_LDS_T char *)&s.w[0][0];
+    // m * k and n * k / 4 are below 2^32 - 4096 (checked at launch)
+    const uint32_t xrow = (uint32_t)nw * 16u, wrow = (uint32_t)nw * 4u;
 #pragma unroll
-    for (int q0 = 0; q0 < 8 / WN; q0++) { // activation rows 2q, 2q + 1 for q = wave, wave + WN, ...
-        const int q = wave + WN * q0;
-        const int rr = 2 * q + (lane >> 5), slot = lane & 31;
-        const int64_t gi = m0 + rr < m ? m0 + rr : m - 1;
-        int word = 32 * c + (slot ^ (rr & 15));
-        word = word < nw ? word : nw - 1;
-        ter2_dma16(xq, (uint32_t)((gi * nw + word) * 16), xs + 1024 * q);
+    for (int q = 0; q < 8; q++) { // 16 lanes per row
+        const int row = 4 * q + (lane >> 4), lam = (lane & 15) ^ (row & 15);
+        const uint32_t gi = (uint32_t)(m0 + row < m ? m0 + row : m - 1);
+        o.x[q] = gi * xrow + (uint32_t)(16 * (lam >> 3) + (lam & 7)) * 16u;
     }
 #pragma unroll
-    for (int q = 0; q < 4; q++) { // this wave's weight rows 32 wave + 8q .. + 7
-        const int wr = 8 * q + (lane >> 3), grp = lane & 7;
-        const int64_t gj = n0 + 32 * wave + wr < n ? n0 + 32 * wave + wr : n - 1;
-        int word = 32 * c + 4 * (grp ^ ((wr >> 1) & 7));
-        word = word + 4 <= nw ? word : nw - 4;
-        ter2_dma16(w, (uint32_t)((gj * nw + word) * 4), ws + 4096 * wave + 1024 * q);
+    for (int q = 0; q < 4; q++) { // 4 lanes per row
+        const int row = 16 * q + (lane >> 2), gam = (lane & 3) ^ ((row >> 2) & 3);
+        const uint32_t gj = (uint32_t)(n0 + row < n ? n0 + row : n - 1);
+        o.w[q] = gj * wrow + (uint32_t)(16 * (gam >> 1) + 4 * (gam & 1)) * 4u;
     }
 }
 
-// Wait until at most `later` chunks of this wave's loads are outstanding.
-template <int D, int NB>
-__device__ __forceinline__ void ter3_wait(int later)
+// Half p of chunk c into s.  FULL: the chunk lies in the row; the half's
+// first word goes into the scalar base and the lane offsets are used as they
+// are.  Otherwise (the row's last, partial chunk) each word is clamped to the
+// row and addressed from the tensor's base: a clamped word can precede the
+// half's first word, and the hardware adds the 32-bit lane offset unsigned.
+template <bool FULL>
+__device__ __forceinline__ void ter_ks_load(const uint32_t *__restrict__ w, const int8_t *__restrict__ xq, int nw,
+                                            int c, int p, const TerKsOff &o, TerKsLds &s)
 {
-    static_assert(D * (NB - 1) < 64, "vmcnt field");
-    switch (later) {
-    case 0: ter2_wait<0>(); break;
-    case 1: ter2_wait<D>(); break;
-    case 2: ter2_wait<(NB > 2 ? 2 * D : 0)>(); break;
-    case 3: ter2_wait<(NB > 3 ? 3 * D : 0)>(); break;
-    default: ter2_wait<(NB > 4 ? 4 * D : 0)>(); break;
+    const int lane = threadIdx.x & 63;
+    const int w0 = 32 * c + 8 * p; // first word of the half's first run
+    const QLL_LDS_T char *xs = (const QLL_LDS_T char *)&s.x[p][0][0];
+    const QLL_LDS_T char *ws = (const QLL_LDS_T char *)&s.w[p][0][0];
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        if (FULL) {
+            ter_dma16(xq + (int64_t)w0 * 16, o.x[q], xs + 1024 * q);
+        } else {
+            const int lam = (lane & 15) ^ ((4 * q + (lane >> 4)) & 15);
+            const int rel = 16 * (lam >> 3) + (lam & 7); // word within the half's runs
+            const int word = w0 + rel < nw ? w0 + rel : nw - 1;
+            ter_dma16(xq, o.x[q] - (uint32_t)rel * 16u + (uint32_t)word * 16u, xs + 1024 * q);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        if (FULL) {
+            ter_dma16(w + w0, o.w[q], ws + 1024 * q);
+        } else {
+            const int row = 16 * q + (lane >> 2), gam = (lane & 3) ^ ((row >> 2) & 3);
+            const int rel = 16 * (gam >> 1) + 4 * (gam & 1);
+            const int word = w0 + rel + 4 <= nw ? w0 + rel : nw - 4;
+            ter_dma16(w, o.w[q] - (uint32_t)rel * 4u + (uint32_t)word * 4u, ws + 1024 * q);
+        }
     }
 }
 
-template <int WN, int NB>
-__global__ __launch_bounds__(64 * WN) void ternary_gemm3_kernel(const uint32_t *__restrict__ w, float w_scale,
-                                                                 const int8_t *__restrict__ xq,
-                                                                 const float *__restrict__ act_scale,
-                                                                 const int32_t *__restrict__ act_sum,
-                                                                 float *__restrict__ y, int64_t m, int64_t n, int nw)
+// Steps 8p .. 8p + 7 of chunk c from the LDS region into the two 32x32
+// accumulators.
+template <bool FULL>
+__device__ __forceinline__ void ter_ks_half(const TerKsLds &s, int nw, int c, int p, int r, int h, i32x16 *acc)
 {
-    static_assert(NB >= 2 && NB <= 5, "ring depth");
-    constexpr int D = 8 / WN + 4; // loads per wave and chunk
-    __shared__ Ter3Lds<WN> lds[NB];
-    const int64_t m0 = (int64_t)blockIdx.y * kTer2BM, n0 = (int64_t)blockIdx.x * (kTer2BN * WN);
-    const int lane = threadIdx.x & 63, lr = lane & 15, lh = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nch = (nw + kTerWPC - 1) / kTerWPC;
-
-    i32x4 acc[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
-    // the scales and code sums of this lane's four output rows, requested
-    // first so that the epilogue does not wait for another round trip
-    float scs[4];
-    int asums[4];
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-        const int64_t rw = m0 + 4 * lh + v < m ? m0 + 4 * lh + v : m - 1;
-        scs[v] = act_scale[rw];
-        asums[v] = act_sum[rw];
-    }
-#pragma unroll
-    for (int c = 0; c < NB; c++)
-        if (c < nch)
-            ter3_load<WN>(w, xq, m, n, nw, m0, n0, c, wave, lds[c]);
-    for (int c = 0; c < nch; c++) {
-        // chunks requested so far: the first NB, then one more per turn from c = 1
-        const int issued = (NB + (c > 0 ? c - 1 : 0)) < nch ? NB + (c > 0 ? c - 1 : 0) : nch;
-        ter3_wait<D, NB>(issued - c - 1);
-        __syncthreads();
-        if (c > 0 && c - 1 + NB < nch)
-            ter3_load<WN>(w, xq, m, n, nw, m0, n0, c - 1 + NB, wave, lds[(c - 1) % NB]);
-        const Ter3Lds<WN> &s = lds[c % NB];
-        u32x4 wv[2][2];
+    for (int g2 = 0; g2 < 2; g2++) {
+        u32x4 wv[2];
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const int wr = 32 * wave + 16 * j + lr, sw = ((16 * j + lr) >> 1) & 7;
-            wv[j][0] = s.w[wr][(2 * lh) ^ sw];
-            wv[j][1] = s.w[wr][(2 * lh + 1) ^ sw];
+            const int wr = 32 * j + r;
+            wv[j] = s.w[p][wr][(2 * h + g2) ^ ((wr >> 2) & 3)];
         }
 #pragma unroll
-        for (int st = 0; st < 8; st++) {
-            const int word = 32 * c + 8 * lh + st;
-            i32x4 a = __builtin_bit_cast(i32x4, transpose_4x4_bytes(s.x[lr][(8 * lh + st) ^ lr]));
-            if (word >= nw)
-                a = i32x4{0, 0, 0, 0};
+        for (int e = 0; e < 4; e++) {
+            const int s8 = 4 * g2 + e;
+            const i32x4 a = __builtin_bit_cast(i32x4, transpose_4x4_bytes(s.x[p][r][(8 * h + s8) ^ (r & 15)]));
 #pragma unroll
             for (int j = 0; j < 2; j++) {
-                const uint32_t cw = wv[j][st >> 2][st & 3];
+                uint32_t cw = wv[j][e];
+                if (!FULL && 32 * c + 16 * h + 8 * p + s8 >= nw)
+                    cw = 0u;
                 const i32x4 b = {(int)(cw & 0x03030303u), (int)((cw >> 2) & 0x03030303u),
                                  (int)((cw >> 4) & 0x03030303u), (int)((cw >> 6) & 0x03030303u)};
-                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[j], 0, 0, 0);
             }
         }
     }
-    // no load may still be writing this workgroup's LDS when it ends
-    ter2_wait<0>();
-    // D layout of a 16x16 tile: lane l, register v -> row 4*(l/16)+v, column l%16
+}
+
+template <bool FULL>
+__device__ __forceinline__ void ter_ks_chunk(const uint32_t *__restrict__ w, const int8_t *__restrict__ xq, int nw,
+                                             int c, int r, int h, const TerKsOff &o, TerKsLds &s, i32x16 *acc)
+{
+    constexpr int D = 12; // loads per half
+    ter_wait<0>();        // the previous chunk's fragment reads have completed
+    ter_ks_load<FULL>(w, xq, nw, c, 0, o, s);
+    ter_ks_load<FULL>(w, xq, nw, c, 1, o, s);
+    ter_wait<D>();
+    ter_ks_half<FULL>(s, nw, c, 0, r, h, acc);
+    ter_wait<0>();
+    ter_ks_half<FULL>(s, nw, c, 1, r, h, acc);
+}
+
+template <int KS>
+__global__ __launch_bounds__(64 * KS) void ternary_gemm_ks_kernel(const uint32_t *__restrict__ w, float w_scale,
+                                                                  const int8_t *__restrict__ xq,
+                                                                  const float *__restrict__ act_scale,
+                                                                  const int32_t *__restrict__ act_sum,
+                                                                  float *__restrict__ y, int64_t m, int64_t n, int nw)
+{
+    constexpr int PAD = kTerKsCols + 8; // the two lane halves of a partial-tile store land 32 banks apart
+    static_assert(kTerKsRows * PAD * 4 <= (int)sizeof(TerKsLds), "a wave's partial tile fits in its region");
+    __shared__ TerKsLds lds[KS];
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+    const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t m0 = (int64_t)blockIdx.y * kTerKsRows, n0 = (int64_t)blockIdx.x * kTerKsCols;
+    const int nch = (nw + 31) / 32;
+
+    // Epilogue: wave ks writes tile rows ks, ks + KS, ... (lane = column),
+    // so each output row's scale and code sum are wave-uniform; requested
+    // first.
+    constexpr int PER = (kTerKsRows + KS - 1) / KS;
+    float scs[PER];
+    int asums[PER];
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-        const int64_t row = m0 + 4 * lh + v;
-        if (row >= m)
-            continue;
+    for (int i = 0; i < PER; i++) {
+        const int64_t rw = m0 + ks + KS * i;
+        const int64_t rc = rw < m ? rw : m - 1;
+        scs[i] = act_scale[rc];
+        asums[i] = act_sum[rc];
+    }
+    TerKsOff o;
+    ter_ks_offsets(m, n, nw, m0, n0, o);
+
+    i32x16 acc[2] = {i32x16{}, i32x16{}};
+    for (int c = ks; c < nch; c += KS) {
+        if (32 * (c + 1) <= nw) // uniform
+            ter_ks_chunk<true>(w, xq, nw, c, r, h, o, lds[ks], acc);
+        else
+            ter_ks_chunk<false>(w, xq, nw, c, r, h, o, lds[ks], acc);
+    }
+    if (KS == 1) {
+        // D layout of a 32x32 tile: lane l, register v -> row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t col = n0 + 32 * wave + 16 * j + lr;
-            if (col < n)
-                y[row * n + col] = ternary_output(acc[j][v], asums[v], w_scale, scs[v]);
-        }
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int64_t row = m0 + 8 * (v >> 2) + 4 * h + (v & 3), col = n0 + 32 * j + r;
+                if (row < m && col < n)
+                    y[row * n + col] = ternary_output(acc[j][v], act_sum[row], w_scale, act_scale[row]);
+            }
+        return;
+    }
+    __syncthreads(); // every wave is done with its region
+    int *part = reinterpret_cast<int *>(&lds[ks]);
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int v = 0; v < 16; v++)
+            part[(8 * (v >> 2) + 4 * h + (v & 3)) * PAD + 32 * j + r] = acc[j][v];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int rr = ks + KS * i;
+        if (rr >= kTerKsRows)
+            break;
+        const int64_t row = m0 + rr, col = n0 + lane;
+        int dot = 0;
+#pragma unroll
+        for (int q = 0; q < KS; q++)
+            dot += reinterpret_cast<const int *>(&lds[q])[rr * PAD + lane];
+        if (row < m && col < n)
+            y[row * n + col] = ternary_output(dot, asums[i], w_scale, scs[i]);
     }
 }
 
@@ -692,13 +660,28 @@ hipError_t launch_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *x
                                const int32_t *act_sum, float *y, int64_t m, int64_t n, int64_t k, hipStream_t st)
 {
     const int nw = (int)(k / 16);
-    // the restructured kernel addresses both operands with 32-bit offsets
-    const bool small = m * k < ((int64_t)1 << 32) && n * (k / 4) < ((int64_t)1 << 32);
+    // the k-split kernel addresses both operands with 32-bit lane offsets
+    const bool small = m * k + 4096 < ((int64_t)1 << 32) && n * (k / 4) + 4096 < ((int64_t)1 << 32);
     if (nw % 4 == 0 && small) {
-        constexpr int WN = 2, NB = 5;
-        dim3 grid3((unsigned)((n + WN * kTer2BN - 1) / (WN * kTer2BN)), (unsigned)((m + kTer2BM - 1) / kTer2BM));
-        hipLaunchKernelGGL((ternary_gemm3_kernel<WN, NB>), grid3, dim3(64 * WN), 0, st, w, w_scale, xq, act_scale,
-                           act_sum, y, m, n, nw);
+        const int64_t tiles = ((n + kTerKsCols - 1) / kTerKsCols) * ((m + kTerKsRows - 1) / kTerKsRows);
+        const int nch = (nw + 31) / 32;
+        // about one wave per SIMD (1024), at most one chunk per wave
+        int64_t split = (kTerKsTargetWaves + tiles - 1) / tiles;
+        split = split < nch ? split : nch;
+        split = split < kTerKsMaxSplit ? split : kTerKsMaxSplit;
+        const dim3 grid((unsigned)((n + kTerKsCols - 1) / kTerKsCols), (unsigned)((m + kTerKsRows - 1) / kTerKsRows));
+#define QLL_TKS(KS)                                                                                                    \
+    hipLaunchKernelGGL((ternary_gemm_ks_kernel<KS>), grid, dim3(64 * KS), 0, st, w, w_scale, xq, act_scale, act_sum, y, \
+                       m, n, nw)
+        switch (split) {
+        case 1: QLL_TKS(1); break;
+        case 2: QLL_TKS(2); break;
+        case 3: QLL_TKS(3); break;
+        case 4: QLL_TKS(4); break;
+        case 5: QLL_TKS(5); break;
+        default: QLL_TKS(6); break;
+        }
+#undef QLL_TKS
         return hipGetLastError();
     }
     dim3 grid((unsigned)((n + TBN - 1) / TBN), (unsigned)((m + TBM - 1) / TBM));

@@ -75,7 +75,10 @@ def test_bitnet_layer_full(qll_gpu, m):
                                    (2, 33, 1088), (16, 32, 2048), (40, 100, 192), (100, 3, 4160),  # partial last chunks
                                    # m = 1, k % 64 == 0: several chunks per row, a partial chunk, and
                                    # activations beyond the pieces a thread stages from registers (k > 16384)
-                                   (1, 37, 16384), (1, 19, 65536), (1, 5, 4160), (1, 70, 6208), (1, 130, 192)])
+                                   (1, 37, 16384), (1, 19, 65536), (1, 5, 4160), (1, 70, 6208), (1, 130, 192),
+                                   # m > 1, k % 64 == 0: the GEMM's k split over 1..6 waves (by grid size
+                                   # and chunk count), several chunks per wave, ragged tiles
+                                   (1030, 2050, 1088), (7, 130, 3072), (33, 65, 6208)])
 def test_shapes(qll_gpu, m, n, k):
     rng = np.random.default_rng(m * 100 + n * 7 + k)
     codes = synth.ternary_codes(rng, n, k)
