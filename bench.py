@@ -76,7 +76,7 @@ def parse():
 # Operations of the rows beyond the hot path's core (small-m, repacked weights,
 # Q8_0 weights, transposed-B): timed the same way, but not part of a step.
 NOISY_CV = 0.08  # coefficient of variation above which a row is flagged noisy
-EXTRA_PREFIXES = ("q4r_gemm", "q8w_gemv", "q8r_gemm", "nt_", "sgemm_core", "msweep_", "f1_")
+EXTRA_PREFIXES = ("q4r_gemm", "q4p_gemv", "q8w_gemv", "q8r_gemm", "nt_", "sgemm_core", "msweep_", "f1_")
 M_SWEEP = (1, 2, 4, 8, 16, 32, 64, 129, 256, 512)  # prompt lengths straddling the tile edges
 
 
@@ -126,7 +126,7 @@ def build_ops(qll, synth, torch, np, dev, only):
 
     # ---------------------------------------------------------------- Q4_0 x Q8_0
     for s, (k, n) in enumerate(synth.SHAPES_8B):
-        need_dec = want(f"q4_gemv_{s}") or want(f"q8_quant_decode_{s}")
+        need_dec = want(f"q4_gemv_{s}") or want(f"q8_quant_decode_{s}") or want(f"q4p_gemv_{s}")
         need_pre = want(f"q4_gemm_{s}") or want(f"q8_quant_prefill_{s}") or want(f"q4r_gemm_{s}")
         if not (need_dec or need_pre):
             continue
@@ -149,6 +149,20 @@ def build_ops(qll, synth, torch, np, dev, only):
                               lambda c=copies, xqd=xqd, yd=yd, n=n, k=k: qll.qll_q4_0_q8_0_gemv(
                                   c[step_ref["i"] % len(c)], xqd, yd, n, k),
                               wbytes + (k // 32) * 34 + 4 * n, 2 * n * k, "hbm"))
+            if want(f"q4p_gemv_{s}"):
+                # the same weights in the decode-packed layout, as many rotating copies
+                pbytes = qll.qll_q4_0_decode_packed_bytes(n, k)
+                pcopies = []
+                for c0 in copies:
+                    wpk = torch.empty(pbytes, dtype=torch.uint8, device=dev)
+                    qll.qll_q4_0_decode_pack(c0, wpk, n, k)
+                    pcopies.append(wpk)
+                qll.qll_quantize_q8_0(xd, xqd, 1, k)
+                ypk = torch.empty(n, dtype=torch.float32, device=dev)
+                ops.append(Op(f"q4p_gemv_{s}", "q4_0_decode_packed", "decode",
+                              lambda c=pcopies, xqd=xqd, ypk=ypk, n=n, k=k: qll.qll_q4_0_decode_packed_q8_0_gemv(
+                                  c[step_ref["i"] % len(c)], xqd, ypk, n, k),
+                              pbytes + (k // 32) * 34 + 4 * n, 2 * n * k, "hbm"))
         if need_pre:
             m = 512
             xp = to_dev(synth.q4_prefill_x(s))
@@ -621,7 +635,8 @@ def main():
         return out
 
     per_format = {}
-    for fmt in ("q4_0", "q4_0_repacked", "q8_0", "f32", "f32_core", "f32_nt", "bf16_nt", "f16_nt", "ternary"):
+    for fmt in ("q4_0", "q4_0_repacked", "q4_0_decode_packed", "q8_0", "f32", "f32_core", "f32_nt", "bf16_nt",
+                "f16_nt", "ternary"):
         d = {kind: agg(fmt, kind) for kind in ("decode", "prefill")}
         d = {kind: v for kind, v in d.items() if v}
         if d:
@@ -647,6 +662,7 @@ def main():
         "q4_decode_us": [us(f"q4_gemv_{s}") for s in range(4)],
         "q4_prefill_us": [us(f"q4_gemm_{s}") for s in range(4)],
         "q4_prefill_repacked_us": [us(f"q4r_gemm_{s}") for s in range(4)],
+        "q4_decode_packed_us": [us(f"q4p_gemv_{s}") for s in range(4)],
         "sgemm_4096_us": us("sgemm_4096"), "sgemv_4096_us": us("sgemv_4096"),
         "ternary_m1_us": us("ternary_gemv"), "ternary_m64_us": us("ternary_gemm"),
         "m_sweep_4096x14336_us": {str(m): us(f"msweep_q4_m{m}") for m in M_SWEEP if f"msweep_q4_m{m}" in by_name},

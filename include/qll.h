@@ -206,6 +206,30 @@ int qll_q4_0_repack(const void *w, void *wp, int64_t n, int64_t k, void *stream)
 int qll_q4_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                                 size_t ws_bytes, void *stream);
 
+/* ------------------------------------------- Q4_0 packed for the decode GEMV */
+
+/* Bytes of the decode-packed form of Q4_0 weights W[n][k/32] (SIZE_MAX if the
+ * shape is invalid): n * (16 * (k/32) + 16 * ceil(k/256)) -- 18 bytes per
+ * block, as the block_q4_0 array, when k % 256 == 0. */
+size_t qll_q4_0_decode_packed_bytes(int64_t n, int64_t k);
+
+/* Load-time repack of Q4_0 weights for the decode GEMV (the packed
+ * right-hand side of [BACK] 9.7, with aligned 128-bit loads in place of the
+ * 18-byte block stride).  w: block_q4_0[n][k/32]; wp:
+ * qll_q4_0_decode_packed_bytes(n, k) bytes, written in full.  Layout, row j
+ * at j * (16 * nb + 16 * ceil(nb/8)) with nb = k/32: the nb blocks' 16 nibble
+ * bytes (their Q4_0 order) at 16 * b, then their binary16 d at 16 * nb + 2 * b,
+ * the scale plane padded with zeros to a multiple of 16 bytes.  k % 32 == 0. */
+int qll_q4_0_decode_pack(const void *w, void *wp, int64_t n, int64_t k, void *stream);
+
+/* Decode GEMV on decode-packed weights: y[n] = x.W^T, the arithmetic of
+ * qll_q4_0_q8_0_gemv per block (exact int32 block sum, f32 d_w*d_x scaling,
+ * tolerance 1e-4 * sum_b |term_b| against an f64 sum; the order of the f32
+ * sum differs, so the two are not equal bit for bit).  wp: the output of
+ * qll_q4_0_decode_pack for (n, k); xq: block_q8_0[k/32]; y: float[n];
+ * k % 32 == 0 and k <= 49152 (the activation row is staged whole in LDS). */
+int qll_q4_0_decode_packed_q8_0_gemv(const void *wp, const void *xq, float *y, int64_t n, int64_t k, void *stream);
+
 /* ------------------------------------------------ Q8_0 weights x Q8_0 activations */
 
 /* Weights quantized to Q8_0 blocks too ([BACK] 9.7: a Q8_0-quantized

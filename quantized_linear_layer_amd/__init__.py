@@ -57,6 +57,8 @@ def load(path=LIB_PATH):
         "qll_q4_0_q8_0_gemv_f32": [P, P, P, I, I, I, P, S, P],
         "qll_q4_0_q8_0_gemm_noalloc": [P, P, P, I, I, I, P],
         "qll_q4_0_repack": [P, P, I, I, P],
+        "qll_q4_0_decode_pack": [P, P, I, I, P],
+        "qll_q4_0_decode_packed_q8_0_gemv": [P, P, P, I, I, P],
         "qll_q4_0_repacked_q8_0_gemm": [P, P, P, I, I, I, P, S, P],
         "qll_q8_0_q8_0_gemv": [P, P, P, I, I, P],
         "qll_q8_0_repack": [P, P, I, I, P],
@@ -75,6 +77,8 @@ def load(path=LIB_PATH):
     L.qll_workspace_bytes.restype = ctypes.c_size_t
     L.qll_q4_0_repacked_bytes.argtypes = [I, I]
     L.qll_q4_0_repacked_bytes.restype = ctypes.c_size_t
+    L.qll_q4_0_decode_packed_bytes.argtypes = [I, I]
+    L.qll_q4_0_decode_packed_bytes.restype = ctypes.c_size_t
     L.qll_q8_0_repacked_bytes.argtypes = [I, I]
     L.qll_q8_0_repacked_bytes.restype = ctypes.c_size_t
     L.qll_status_string.argtypes = [ctypes.c_int]
@@ -175,6 +179,21 @@ def qll_q4_0_q8_0_gemv_f32(w, x, y, m, n, k, ws=None, stream=None):
     wsp, wsb = (None, 0) if ws is None else (_ptr(ws, 0, "ws"), ws.numel() * ws.element_size())
     _call("qll_q4_0_q8_0_gemv_f32", _ptr(w, n * (k // 32) * Q4_0_BLOCK_BYTES, "w"), _ptr(x, m * k * 4, "x"),
           _ptr(y, m * n * 4, "y"), m, n, k, wsp, wsb, _stream(stream))
+
+
+def qll_q4_0_decode_packed_bytes(n, k):
+    return int(load().qll_q4_0_decode_packed_bytes(int(n), int(k)))
+
+
+def qll_q4_0_decode_pack(w, wp, n, k, stream=None):
+    """Load-time repack of Q4_0 blocks into the decode GEMV's aligned groups."""
+    _call("qll_q4_0_decode_pack", _ptr(w, n * (k // 32) * Q4_0_BLOCK_BYTES, "w"),
+          _ptr(wp, qll_q4_0_decode_packed_bytes(n, k), "wp"), n, k, _stream(stream))
+
+
+def qll_q4_0_decode_packed_q8_0_gemv(wp, xq, y, n, k, stream=None):
+    _call("qll_q4_0_decode_packed_q8_0_gemv", _ptr(wp, qll_q4_0_decode_packed_bytes(n, k), "wp"),
+          _ptr(xq, (k // 32) * Q8_0_BLOCK_BYTES, "xq"), _ptr(y, n * 4, "y"), n, k, _stream(stream))
 
 
 def qll_q4_0_repacked_bytes(n, k):

@@ -301,6 +301,41 @@ int qll_q4_0_repack(const void *w, void *wp, int64_t n, int64_t k, void *stream)
                                        as_stream(stream)));
 }
 
+size_t qll_q4_0_decode_packed_bytes(int64_t n, int64_t k)
+{
+    if (!dims_ok(n, k) || k % 32 != 0)
+        return SIZE_MAX;
+    return q4_0_packed_bytes(n, k);
+}
+
+int qll_q4_0_decode_pack(const void *w, void *wp, int64_t n, int64_t k, void *stream)
+{
+    if (!w || !wp)
+        return QLL_ERR_NULL;
+    if (!dims_ok(n, k) || k % 32 != 0)
+        return QLL_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(wp))
+        return QLL_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    return launched(launch_q4_0_pack_decode(static_cast<const uint8_t *>(w), static_cast<uint8_t *>(wp), n, k,
+                                            as_stream(stream)));
+}
+
+int qll_q4_0_decode_packed_q8_0_gemv(const void *wp, const void *xq, float *y, int64_t n, int64_t k, void *stream)
+{
+    if (!wp || !xq || !y)
+        return QLL_ERR_NULL;
+    if (!dims_ok(n, k) || k % 32 != 0 || k > kMaxKQ4Gemv)
+        return QLL_ERR_SHAPE;
+    if (!aligned16(wp) || !aligned16(xq) || !aligned16(y))
+        return QLL_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    return launched(launch_q4_0_packed_gemv(static_cast<const uint8_t *>(wp), static_cast<const uint8_t *>(xq), y, n,
+                                            k, as_stream(stream)));
+}
+
 int qll_q4_0_repacked_q8_0_gemm(const void *wp, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                                 size_t ws_bytes, void *stream)
 {

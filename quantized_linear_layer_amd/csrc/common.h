@@ -124,6 +124,11 @@ hipError_t launch_gemm_nt_bf16_mfma(const float *x, const void *w, int wfmt, flo
                                     int64_t k, void *ws, hipStream_t s, bool b_kn = false);
 // Load-time repack of Q4_0 weights and the GEMM on them (6-bit matrix-core path).
 size_t q4_0_repacked_bytes(int64_t n, int64_t k);
+// Decode-packed Q4_0 weights (groups of eight blocks: nibbles, then scales).
+size_t q4_0_packed_bytes(int64_t n, int64_t k);
+hipError_t launch_q4_0_pack_decode(const uint8_t *w, uint8_t *wp, int64_t n, int64_t k, hipStream_t s);
+hipError_t launch_q4_0_packed_gemv(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int64_t k,
+                                   hipStream_t s);
 hipError_t launch_q4_0_repack(const uint8_t *w, uint8_t *wp, int64_t n, int64_t k, hipStream_t s);
 size_t q4_0_packed_gemm_workspace(int64_t m, int64_t n, int64_t k);
 hipError_t launch_q4_0_packed_gemm(const uint8_t *wp, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,

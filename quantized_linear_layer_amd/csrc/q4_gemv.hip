@@ -461,6 +461,196 @@ hipError_t launch_q4_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, 
     return launch_pair<false>(w, xq, y, n, nb, s);
 }
 
+// ------------------------------------------------------------------ decode-packed Q4_0 weights
+// A load-time layout for the decode GEMV (the packed right-hand side of the
+// Fucina reference "Backends", 9.7, rewritten once and reused by every
+// call; aligned 128-bit loads in place of the 18-byte block stride): each
+// row as two planes -- the nb blocks' 16 nibble bytes (Q4_0 order), 16 * nb
+// bytes, then their nb binary16 scales, padded to a multiple of 16 bytes
+// (8 scales) with zeros.  A row stays at 18 bytes per block when nb % 8 == 0.
+// In the GEMV, lane r of the L lanes of a row takes blocks r, r + L, ...,
+// so each load instruction of a wave reads consecutive 16-byte nibble
+// pieces (and consecutive 2-byte scales): the whole instruction is a few
+// cache lines, where a lane-private stride (an AoS unit or an interleaved
+// group per lane) spreads one instruction over tens of lines.
+__host__ __device__ inline int64_t q4p_row_bytes(int nb) { return 16 * (int64_t)nb + 16 * (int64_t)((nb + 7) / 8); }
+
+template <int U>
+struct Q4pRaw {
+    u32x4 q[U];    // nibbles of the lane's U blocks
+    uint32_t d[U]; // their binary16 scales (low half)
+};
+
+template <int L, int U>
+__device__ __forceinline__ void q4p_load(const uint8_t *__restrict__ w, int64_t row, int64_t n, int64_t row_bytes,
+                                         int nb, int bbase, int r, Q4pRaw<U> &raw)
+{
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        // blocks outside the matrix load block 0 of row 0 instead (masked in
+        // q4p_compute): unconditional loads keep the wait counts exact
+        int b = bbase + r + i * L;
+        const bool ok = row < n && b < nb;
+        const int64_t rr = ok ? row : 0;
+        b = ok ? b : 0;
+        const uint8_t *base = w + rr * row_bytes;
+        raw.q[i] = *reinterpret_cast<const u32x4 *>(base + 16 * (int64_t)b);
+        raw.d[i] = *reinterpret_cast<const uint16_t *>(base + 16 * (int64_t)nb + 2 * b);
+    }
+}
+
+template <int L, int U>
+__device__ __forceinline__ float q4p_compute(const Q4pRaw<U> &raw, int64_t row, int64_t n, int nb, int bbase, int r,
+                                             const ActLds &act)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        const int b = bbase + r + i * L;
+        if (row < n && b < nb) {
+            const uint32_t qs[4] = {raw.q[i][0], raw.q[i][1], raw.q[i][2], raw.q[i][3]};
+            acc += q4_block_dot(raw.d[i], qs, act, b);
+        }
+    }
+    return acc;
+}
+
+// The GEMV kernel's structure on the packed layout: L lanes per row, U
+// blocks per lane and work item, the next item's bytes in flight while the
+// current one is dotted.
+template <int L, int U>
+__global__ __launch_bounds__(kGemvThreads) void q4_0_packed_gemv_kernel(const uint8_t *__restrict__ w, const void *xin,
+                                                                        float *__restrict__ y, int64_t n, int nb)
+{
+    extern __shared__ u32x4 smem[];
+    constexpr int R = 64 / L, WAVES = kGemvThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / L, r = lane % L;
+    const int chunk = U * L;
+    const int chunks = (nb + chunk - 1) / chunk;
+    const int64_t row_bytes = q4p_row_bytes(nb);
+    const int64_t n_groups = (n + R - 1) / R;
+    const int64_t stride = (int64_t)gridDim.x * WAVES;
+
+    const uint8_t *xq = static_cast<const uint8_t *>(xin);
+    ActRaw araw;
+    stage_q8_load(xq, nb, araw);
+    asm volatile("" ::: "memory"); // keep these loads ahead of the weight loads
+
+    int64_t grp = (int64_t)blockIdx.x * WAVES + wave;
+    int c = 0;
+    Q4pRaw<U> cur;
+    q4p_load<L, U>(w, grp * R + g, n, row_bytes, nb, 0, r, cur);
+
+    const ActLds act = stage_q8_finish(xq, nb, araw, smem);
+
+    float acc = 0.0f;
+    while (grp < n_groups) {
+        int64_t grp2 = grp;
+        int c2 = c + 1;
+        if (c2 == chunks) {
+            c2 = 0;
+            grp2 += stride;
+        }
+        Q4pRaw<U> nxt;
+        if (grp2 < n_groups)
+            q4p_load<L, U>(w, grp2 * R + g, n, row_bytes, nb, c2 * chunk, r, nxt);
+        const int64_t row = grp * R + g;
+        acc += q4p_compute<L, U>(cur, row, n, nb, c * chunk, r, act);
+        if (c == chunks - 1) {
+#pragma unroll
+            for (int off = L / 2; off > 0; off >>= 1)
+                acc += __shfl_xor(acc, off);
+            if (row < n && r == 0)
+                y[row] = acc;
+            acc = 0.0f;
+        }
+        cur = nxt;
+        grp = grp2;
+        c = c2;
+    }
+}
+
+template <int L, int U>
+static hipError_t launch_q4p_l(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int nb, hipStream_t s)
+{
+    constexpr int R = 64 / L;
+    const int64_t groups = (n + R - 1) / R;
+    int64_t grid = (groups + kGemvThreads / 64 - 1) / (kGemvThreads / 64);
+    if (grid > 0x7fffffff)
+        grid = 0x7fffffff;
+    hipLaunchKernelGGL((q4_0_packed_gemv_kernel<L, U>), dim3((unsigned)grid), dim3(kGemvThreads),
+                       q4_gemv_lds_bytes(nb), s, w, xq, y, n, nb);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4_0_packed_gemv(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int64_t k,
+                                   hipStream_t s)
+{
+    const int nb = (int)(k / 32);
+    // the direct GEMV's lane counts, with a lane's units of two blocks as
+    // two blocks
+    if (n <= 16384) {
+        if (nb > 128)
+            return launch_q4p_l<64, 8>(w, xq, y, n, nb, s);
+        if (nb > 64)
+            return launch_q4p_l<32, 4>(w, xq, y, n, nb, s);
+        if (nb > 32)
+            return launch_q4p_l<16, 4>(w, xq, y, n, nb, s);
+        return launch_q4p_l<8, 4>(w, xq, y, n, nb, s);
+    }
+    if (nb > 256)
+        return launch_q4p_l<64, 8>(w, xq, y, n, nb, s);
+    if (nb > 128)
+        return launch_q4p_l<32, 8>(w, xq, y, n, nb, s);
+    if (nb > 64)
+        return launch_q4p_l<16, 8>(w, xq, y, n, nb, s);
+    return launch_q4p_l<8, 8>(w, xq, y, n, nb, s);
+}
+
+size_t q4_0_packed_bytes(int64_t n, int64_t k) { return (size_t)(n * q4p_row_bytes((int)(k / 32))); }
+
+// One 16-byte piece of the packed layout per thread: piece p < nb of a row
+// is block p's nibbles, piece nb + t the scales of blocks 8t .. 8t + 7.
+__global__ __launch_bounds__(256) void q4_0_pack_decode_kernel(const uint8_t *__restrict__ w, uint8_t *__restrict__ wp,
+                                                               int64_t n, int nb)
+{
+    const int per_row = nb + (nb + 7) / 8;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n * per_row)
+        return;
+    const int64_t row = i / per_row;
+    const int p = (int)(i % per_row);
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    if (p < nb) {
+        const uint8_t *src = w + (row * nb + p) * 18 + 2;
+#pragma unroll
+        for (int e = 0; e < 16; e++)
+            out[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
+    } else {
+#pragma unroll
+        for (int b = 0; b < 8; b++) {
+            const int blk = 8 * (p - nb) + b;
+            if (blk < nb) {
+                const uint8_t *src = w + (row * nb + blk) * 18;
+                out[b >> 1] |= ((uint32_t)src[0] | ((uint32_t)src[1] << 8)) << (16 * (b & 1));
+            }
+        }
+    }
+    reinterpret_cast<u32x4 *>(wp)[i] = u32x4{out[0], out[1], out[2], out[3]};
+}
+
+hipError_t launch_q4_0_pack_decode(const uint8_t *w, uint8_t *wp, int64_t n, int64_t k, hipStream_t s)
+{
+    const int nb = (int)(k / 32);
+    const int64_t pieces = n * (nb + (nb + 7) / 8);
+    const int64_t grid = (pieces + 255) / 256;
+    if (grid > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(q4_0_pack_decode_kernel, dim3((unsigned)grid), dim3(256), 0, s, w, wp, n, nb);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ Q8_0 weights
 // Decode GEMV with the weights quantized to Q8_0 blocks as well (Fucina
 // reference "Backends", 9.7: a Q8_0-quantized right-hand side against the

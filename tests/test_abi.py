@@ -111,6 +111,18 @@ def test_q4_errors(L):
     assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 2, 8, 48, NUL, 0, None) == SHAPE
     assert L.qll_q4_0_q8_0_gemv_f32(GOOD, MIS, GOOD, 2, 8, 64, NUL, 0, None) == ALIGN
     assert L.qll_q4_0_q8_0_gemv_f32(GOOD, GOOD, GOOD, 2, 8, 64, MIS, 2 ** 20, None) == ALIGN  # a workspace in use
+    # decode-packed weights: the pack and the GEMV on them
+    assert qll.qll_q4_0_decode_packed_bytes(8, 64) == 8 * (2 * 16 + 16)
+    assert qll.qll_q4_0_decode_packed_bytes(3, 4096) == 3 * 128 * 18
+    assert qll.qll_q4_0_decode_packed_bytes(2, 14336 + 32) == 2 * (449 * 16 + 57 * 16)
+    assert qll.qll_q4_0_decode_packed_bytes(8, 48) == SIZE_MAX
+    assert L.qll_q4_0_decode_pack(NUL, GOOD, 8, 64, None) == NULL
+    assert L.qll_q4_0_decode_pack(GOOD, GOOD, 8, 48, None) == SHAPE
+    assert L.qll_q4_0_decode_pack(GOOD, MIS, 8, 64, None) == ALIGN
+    assert L.qll_q4_0_decode_packed_q8_0_gemv(GOOD, NUL, GOOD, 8, 64, None) == NULL
+    assert L.qll_q4_0_decode_packed_q8_0_gemv(GOOD, GOOD, GOOD, 0, 64, None) == SHAPE
+    assert L.qll_q4_0_decode_packed_q8_0_gemv(GOOD, GOOD, GOOD, 8, 49152 + 32, None) == SHAPE
+    assert L.qll_q4_0_decode_packed_q8_0_gemv(MIS, GOOD, GOOD, 8, 64, None) == ALIGN
     # repacked weights: the repack and the GEMM on them
     assert L.qll_q4_0_repack(NUL, GOOD, 8, 64, None) == NULL
     assert L.qll_q4_0_repack(GOOD, GOOD, 8, 48, None) == SHAPE

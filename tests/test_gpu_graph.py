@@ -98,6 +98,12 @@ def _setup():
     y8 = empty(n, torch.float32)
     bufs["q8w_gemv_y"] = y8
     calls.append(lambda w8=w8, xq=xq, y8=y8, n=n, k=k: qll.qll_q8_0_q8_0_gemv(w8, xq, y8, n, k))
+    # the decode GEMV on the decode-packed Q4_0 layout
+    w4d = empty(qll.qll_q4_0_decode_packed_bytes(n, k))
+    qll.qll_q4_0_decode_pack(w4, w4d, n, k)
+    y4d = empty(n, torch.float32)
+    bufs["q4_packed_gemv_y"] = y4d
+    calls.append(lambda w4d=w4d, xq=xq, y4d=y4d, n=n, k=k: qll.qll_q4_0_decode_packed_q8_0_gemv(w4d, xq, y4d, n, k))
 
     # transposed-B: every weight type at m = 1 and m = 64, on the f32 matrix
     # core (no workspace) and on the bf16 one (a workspace); and the plain
