@@ -120,6 +120,20 @@ def test_large_n_layout(qll_gpu, m, n, k):
         assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
+# 8192 <= n < 32768 at m > 2 takes the 2-rows-per-lane-group layout: odd
+# block counts, a ragged last row group, several k-chunks
+@pytest.mark.parametrize("m", [3, 4, 8])
+@pytest.mark.parametrize("n,k", [(8193, 96), (14337, 4160), (9000, 1056)])
+def test_mid_n_layout(qll_gpu, m, n, k):
+    codes, d_bits, x = _case(m * 17 + n + k, m, n, k)
+    w = pack_q4_0(codes, d_bits)
+    y = host(q4_gemm(w, quantize_q8_0(x), m, n, k)).reshape(m, n)
+    y_ref, mag = _ref(codes, d_bits, x)
+    assert_within(y, y_ref, mag, TOL, f"small-m mid-n m={m} n={n} k={k}")
+    y2 = host(gemv_f32(w, x, m, n, k)).reshape(m, n)  # the fused entry's single launch (its own layout)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
 def _unit_scale_x(rng, m, k):
     # a +-127 in every block (d = 1 exactly), integers and exact ties elsewhere
     x = rng.integers(-126, 127, (m, k)).astype(np.float32)
