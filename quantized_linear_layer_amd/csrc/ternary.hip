@@ -304,7 +304,9 @@ hipError_t launch_ternary_gemv(const uint32_t *w, float w_scale, const int8_t *x
     return launch_ter_vec<1>(w, w_scale, xq, act_scale, act_sum, y, n, nw, st);
 }
 
-// ------------------------------------------------------------------ GEMM (m > 1)
+// ------------------------------------------------------------------ GEMM (m > 1), any k
+// The general kernel (k % 64 != 0, or operands beyond 32-bit offsets; the
+// k-split kernel further down takes the rest).
 // v_mfma_i32_16x16x64_i8: one MFMA covers 64 codes = 4 weight words.  The
 // k range is walked in chunks of kTerKC codes (32 words).  Within a chunk,
 // lane group h of an operand (lanes 16h..16h+15) takes words 8h..8h+7 in
