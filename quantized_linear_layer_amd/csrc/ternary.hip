@@ -202,7 +202,9 @@ __global__ __launch_bounds__(kTg2Threads) void ternary_gemv2_kernel(
 #pragma unroll
     for (int j = 0; j < kTg2ActRegs; j++) {
         const int i = threadIdx.x + j * kTg2Threads;
-        a[j] = xv[i < nw ? i : 0];
+        // unconditional (waits stay countable); pieces past the row reload
+        // word i % nw rather than all word 0: 3.64 against 3.83 us at 2560 -> 6912
+        a[j] = xv[i < nw ? i : i % nw];
     }
     asm volatile("" ::: "memory"); // the activation loads go out first
 
