@@ -124,16 +124,17 @@ int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64
 /* Prefill GEMM: Y[m][n] = X.W^T with the same per-block arithmetic as the
  * GEMV for every (i, j).  xq: block_q8_0[m][k/32], w: block_q4_0[n][k/32],
  * y: float[m][n].  k % 32 == 0, and k < 2^24 when m > 8 (else QLL_ERR_SHAPE:
- * the kernel addresses a 128-row panel with 32-bit offsets).  ws/ws_bytes:
- * device workspace of at least
+ * the kernels address 32 activation rows, or a 128-row panel, with 32-bit
+ * offsets).  ws/ws_bytes: device workspace of at least
  * qll_workspace_bytes(QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) bytes (nonzero for
- * m > 8): the call first writes the activations there in the matrix-core
+ * m > 32): the call first writes the activations there in the matrix-core
  * operand form (exact f16 codes, scale bits, bias terms), then split-k partial
  * sums when it splits k; contents on return are unspecified.  m == 1 runs the
- * GEMV kernel; 2 <= m <= 8 (the small-m decode band that [BACK] 9.9 gates
- * apart from the general GEMM, one row-dot per weight row in 9.9.2) runs a
- * GEMV-shaped kernel that loads every weight once for all m rows; neither
- * needs a workspace.  At m == 1 the GEMV's limit k <= 49152 applies. */
+ * GEMV kernel; 2 <= m <= 32 (the small-m band that [BACK] 9.9 gates apart
+ * from the general GEMM, one row-dot per weight row in 9.9.2) runs kernels
+ * that load every weight once for all m rows -- a GEMV-shaped one, or one
+ * that forms 16 x 16 tiles of block sums on the int8 matrix core -- and
+ * needs no workspace.  At m == 1 the GEMV's limit k <= 49152 applies. */
 int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                        size_t ws_bytes, void *stream);
 
@@ -148,7 +149,7 @@ int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64
  * call until the process ends.  The call itself allocates nothing.  Shapes
  * whose qll_workspace_bytes(QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) exceeds that
  * size return QLL_ERR_SCRATCH with nothing enqueued (every 8B-class layer at
- * m = 512 fits); m <= 8 needs no scratch.  All calls on one device share its
+ * m = 512 fits); m <= 32 needs no scratch.  All calls on one device share its
  * array and leave their contents there: two calls whose executions overlap
  * on one device (different streams, or graphs replayed concurrently) race
  * and give undefined results, so serialise them.  Other arguments and
@@ -159,18 +160,22 @@ int qll_q4_0_q8_0_gemm_noalloc(const void *w, const void *xq, float *y, int64_t 
 /* Quantize-fused decode: Y[m][n] = Q8_0(X).W^T for 1 <= m <= 8, from the f32
  * activation rows x: float[m][k] ([BACK] 9.7 quantizes the activation per
  * call), quantized to Q8_0 with exactly the arithmetic of qll_quantize_q8_0
- * and dotted as in qll_q4_0_q8_0_gemm: the result is that of
- * qll_quantize_q8_0 followed by qll_q4_0_q8_0_gemm, bit for bit, on either
- * route below.  w: block_q4_0[n][k/32], y: float[m][n], k % 32 == 0;
- * QLL_ERR_SHAPE for m outside [1, 8].
+ * and dotted with the per-block arithmetic of qll_q4_0_q8_0_gemm.
+ * w: block_q4_0[n][k/32], y: float[m][n], k % 32 == 0; QLL_ERR_SHAPE for m
+ * outside [1, 8].
  * ws is optional.  Where qll_workspace_bytes(QLL_OP_Q4_0_GEMV_F32, m, n, k)
  * is nonzero and ws (16-byte aligned, caller-owned, contents not preserved)
  * holds at least that many bytes, the rows are quantized once into ws and
- * the Q8_0 decode kernel runs on them: two launches from this one call, as
- * fast as the pair.  Otherwise (ws NULL or smaller, or no workspace needed:
- * m == 1 with a short row and a matrix that one pass of the resident
- * workgroups covers) a single launch quantizes the rows inside every
- * workgroup, which is faster only at that size. */
+ * the kernel qll_q4_0_q8_0_gemm runs for this shape runs on them: two
+ * launches from this one call, as fast as the pair, and the result is that
+ * of qll_quantize_q8_0 followed by qll_q4_0_q8_0_gemm bit for bit.
+ * Otherwise (ws NULL or smaller, or no workspace needed: m == 1 with a short
+ * row and a matrix that one pass of the resident workgroups covers) a single
+ * GEMV-shaped launch quantizes the rows inside every workgroup, which is
+ * faster only at that size: the same Q8_0 codes and block sums, the float
+ * sum over the blocks in that kernel's order (bit for bit the pair's result
+ * where qll_q4_0_q8_0_gemm also runs a GEMV-shaped kernel: m == 1, k < 256,
+ * m == 2 with n >= 8192, m <= 4 with n >= 32768). */
 int qll_q4_0_q8_0_gemv_f32(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k, void *ws,
                            size_t ws_bytes, void *stream);
 

@@ -22,11 +22,12 @@ FLAGS = ["-std=c++17", "-O3", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-# Per-source extra flags.  The two Q4_0 GEMMs: MFMA results go to VGPRs, so
-# the block sums of a row of subtiles can be in flight together (the default
-# AGPR form serialised them through one accumulator) and the fmas that apply
-# the scales read them without a v_accvgpr_read each.
-EXTRA = {"q4_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "q4_packed.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The Q4_0 matrix-core kernels: MFMA results go to
+# VGPRs, so the block sums of a row of subtiles can be in flight together
+# (the default AGPR form serialised them through one accumulator) and the
+# fmas that apply the scales read them without a v_accvgpr_read each.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"q4_gemm.hip": _VGPR_FORM, "q4_packed.hip": _VGPR_FORM, "q4_small_mfma.hip": _VGPR_FORM}
 
 
 def _compile(src):

@@ -98,11 +98,20 @@ hipError_t launch_q4_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, 
                                  hipStream_t s);
 hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                  void *ws, hipStream_t s);
-// Small-m decode (1 <= m <= kMaxMSmall): Q8_0 activations, or f32 activations
-// quantized to Q8_0 inside the launch.
+// Small-m decode: Q8_0 activations at 2 <= m <= kMaxMMfma (m <= kMaxMSmall
+// when k >= kMaxKMfma), or, in the quantize-fused entry, f32 activations
+// quantized to Q8_0 inside the launch (1 <= m <= kMaxMSmall).
 constexpr int64_t kMaxMSmall = 8;
 hipError_t launch_q4_0_q8_0_gemv_m(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                    hipStream_t s);
+// Small m on the int8 matrix core (1 <= m <= kMaxMMfma, kMinKMfma <= k <
+// kMaxKMfma: a stage is eight blocks, and 32 activation rows are addressed
+// with 32-bit offsets): Q8_0 activations, no workspace.
+constexpr int64_t kMaxMMfma = 32;
+constexpr int64_t kMinKMfma = 256, kMaxKMfma = (int64_t)1 << 24;
+hipError_t launch_q4_0_q8_0_small_m_mfma(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n,
+                                         int64_t k, hipStream_t s);
+int small_m_mfma_split(int64_t m, int64_t n, int64_t k);
 // With ws (at least q4_0_gemv_f32_workspace bytes, nonzero), the rows are
 // quantized into ws by the quantize kernel and the Q8_0 decode kernel runs
 // on them; with ws == nullptr, one launch quantizes inside each workgroup.

@@ -1154,7 +1154,22 @@ static hipError_t launch_gm(const uint8_t *w, const void *xin, float *y, int64_t
 hipError_t launch_q4_0_q8_0_gemv_m(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                    hipStream_t s)
 {
-    return launch_gm<false>(w, xq, y, m, n, k, s);
+    // the matrix-core kernel, except at m = 2 on tall matrices and m <= 4 on
+    // very tall ones, where the weight stream bounds both and this kernel's
+    // lighter staging wins (4096 -> 14336 at m = 2: 9.9 against 11.0 us;
+    // 4096 -> 128256 at m = 2 / 4: 57 / 67.5 against 65 / 71.6 us)
+    const bool gemv_style = (m == 2 && n >= 8192) || (m <= 4 && n >= 32768);
+    if (m >= 2 && k >= kMinKMfma && k < kMaxKMfma && !gemv_style)
+        return launch_q4_0_q8_0_small_m_mfma(w, xq, y, m, n, k, s);
+    // rows of fewer than eight blocks (or very long rows at m <= 8): the
+    // kernel above by groups of at most eight activation rows
+    for (int64_t a0 = 0; a0 < m; a0 += kMaxMSmall) {
+        const int64_t mm = m - a0 < kMaxMSmall ? m - a0 : kMaxMSmall;
+        const hipError_t e = launch_gm<false>(w, xq + a0 * (k / 32) * 34, y + a0 * n, mm, n, k, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 // The single launch wins only where the weights take one pass of the
@@ -1182,7 +1197,7 @@ hipError_t launch_q4_0_q8_0_gemv_f32(const uint8_t *w, const float *x, float *y,
             return e;
         if (m == 1 && k <= kMaxKQ4Gemv)
             return launch_q4_0_q8_0_gemv(w, ws, y, n, k, s);
-        return launch_gm<false>(w, ws, y, m, n, k, s);
+        return launch_q4_0_q8_0_gemv_m(w, ws, y, m, n, k, s);
     }
     // m = 1: the GEMV kernel, quantizing the row while it stages it (the
     // whole row fits in LDS up to kMaxKQ4Gemv; longer rows stage by chunks)

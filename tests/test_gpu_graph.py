@@ -49,9 +49,9 @@ def _setup():
         bufs[f"f32_{tag}_c"] = c
         calls.append(lambda a=a, b=b, c=c, m=m, n=n, k=k, ws=ws: qll.qll_sgemm(a, b, c, m, n, k, ws=ws))
 
-    # Q4_0 at small m: the GEMV-style kernel (m = 4), its quantize-fused
-    # entry (m = 3), and the 32-row GEMM with paired weight rows (even block
-    # count) and without (odd)
+    # Q4_0 at small m: the int8 matrix-core kernel (m = 4, m = 16), the
+    # GEMV-style kernel by groups of eight rows (m = 12 with three blocks per
+    # row), and the quantize-fused entry (m = 3)
     for tag, (m, n, k) in {"m4": (4, 200, 1024), "m16": (16, 300, 2048), "m12odd": (12, 140, 96)}.items():
         codes, d_bits = synth.q4_0_weights(rng, n, k)
         w = empty(n * (k // 32) * 18)

@@ -178,7 +178,7 @@ def _gemm_check(codes, d_bits, x, what):
 # with a one-row tail, weight buffer length 2 mod 4 (131 x 19 blocks)
 @pytest.mark.parametrize("m,n,k", [(2, 1, 32), (3, 7, 96), (17, 64, 512), (130, 129, 320), (128, 128, 4096),
                                    (200, 300, 64), (64, 33, 14336), (128, 256, 3232), (257, 131, 608),
-                                   # 9 <= m <= 32: 32-row tiles
+                                   # 9 <= m <= 32: the small-m kernels
                                    (9, 257, 4096), (32, 1000, 1024), (31, 128, 96), (20, 33, 14336), (12, 129, 32)])
 def test_gemm_shapes(qll_gpu, m, n, k):
     codes, d_bits, x = rand_case(m * 1000 + n + k, m, n, k)
@@ -197,7 +197,7 @@ def test_gemm_unit_scales_bit_exact(qll_gpu):
 
 
 def test_gemm_small_tile_unit_scales_bit_exact(qll_gpu):
-    # the 32-row tile path (9 <= m <= 32) on integer-valued outputs
+    # the small-m band (9 <= m <= 32) on integer-valued outputs
     rng = np.random.default_rng(18)
     m, n, k = 20, 300, 2048
     codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
@@ -210,8 +210,9 @@ def test_gemm_small_tile_unit_scales_bit_exact(qll_gpu):
 
 @pytest.mark.parametrize("s,m", [(0, 16), (1, 9), (2, 32)])
 def test_gemm_small_tile_8b_shapes_full(qll_gpu, s, m):
-    # the 32-row tile path at an 8B-class layer's full size, every output
-    # checked: the shape's weights with the first m rows of its prefill input
+    # the small-m band (9 <= m <= 32) at an 8B-class layer's full size,
+    # every output checked: the shape's weights with the first m rows of its
+    # prefill input
     codes, d_bits, _ = synth.q4_decode(s)
     x = synth.q4_prefill_x(s, m=m)
     _gemm_check(codes, d_bits, x, f"GEMM m={m} 8B shape {synth.SHAPES_8B[s]}")

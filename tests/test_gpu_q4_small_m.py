@@ -1,9 +1,13 @@
 """Parity of the small-m decode kernels against the oracle: the Q4_0 x Q8_0
 GEMM entry at 2 <= m <= 8 (weights loaded once for all rows) and the
 quantize-fused entry (f32 activations quantized to Q8_0 inside the launch)
-at 1 <= m <= 8, with and without its workspace.  Float outputs within 1e-4 * sum_b |term_b|; integer cases
-bit-exact; the fused quantization is checked bit for bit through the results
-it must reproduce."""
+at 1 <= m <= 8, with and without its workspace.  Float outputs within
+1e-4 * sum_b |term_b|; integer cases bit-exact.  The fused entry's
+in-launch quantization is checked bit for bit through the results it must
+reproduce: against the GEMM entry wherever both run the GEMV-style kernel
+(m = 1, rows of fewer than eight blocks, m = 2 on tall matrices, m <= 4 on
+very tall ones), and with
+its workspace (quantize, then the GEMM entry's kernel) always."""
 import numpy as np
 import pytest
 import torch
@@ -42,6 +46,13 @@ def _case(seed, m, n, k):
     return codes, d_bits, x
 
 
+def _gemv_style(m, n, k):
+    # shapes on which the GEMM entry runs the GEMV-style kernel, as the
+    # fused entry's single launch does (elsewhere it runs the int8
+    # matrix-core kernel, whose f32 sums are added in another order)
+    return m == 1 or k < 256 or (m == 2 and n >= 8192) or (m <= 4 and n >= 32768)
+
+
 def _ref(codes, d_bits, x):
     n, k = codes.shape
     return O.q4_0_q8_0(O.pack_q4_0(codes, d_bits), O.quantize_q8_0(x), x.shape[0], n, k)
@@ -65,12 +76,12 @@ def test_fused_f32_gemv(qll_gpu, m, n, k, route):
     y = host(gemv_f32(w, x, m, n, k, route)).reshape(m, n)
     y_ref, mag = _ref(codes, d_bits, x)
     assert_within(y, y_ref, mag, TOL, f"fused GEMV m={m} n={n} k={k}")
-    # the same dot on Q8_0 input from qll_quantize_q8_0 (the GEMV at m = 1,
-    # the small-m kernel above it): identical arithmetic after the staging,
-    # so any difference in the in-launch quantization shows up as a bit
-    # difference
-    y2 = host(q4_gemm(w, quantize_q8_0(x), m, n, k)).reshape(m, n)
-    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    # the same dot on Q8_0 input from qll_quantize_q8_0: identical arithmetic
+    # after the staging, so any difference in the in-launch quantization
+    # shows up as a bit difference
+    if route == "ws" or _gemv_style(m, n, k):
+        y2 = host(q4_gemm(w, quantize_q8_0(x), m, n, k)).reshape(m, n)
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
 @pytest.mark.parametrize("route", ["single", "ws"])
@@ -88,8 +99,9 @@ def test_fused_f32_gemv_long_rows(qll_gpu, n, k, route):
 
 
 def test_fused_workspace_short_or_absent(qll_gpu):
-    # a workspace one byte short, or none, selects the single launch: the
-    # same bits as the two-launch route
+    # a workspace one byte short, or none, selects the single launch (the
+    # same bits either way); a whole one quantizes first and runs the GEMM
+    # entry's kernel (the same bits as quantize + GEMM)
     op = qll.QLL_OP_Q4_0_GEMV_F32
     m, n, k = 3, 70, 8192
     codes, d_bits, x = _case(4242, m, n, k)
@@ -102,7 +114,11 @@ def test_fused_workspace_short_or_absent(qll_gpu):
         qll.qll_q4_0_q8_0_gemv_f32(w, dev(x), y, m, n, k, ws=ws)
         outs.append(host(y))
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
-    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+    y2 = host(q4_gemm(w, quantize_q8_0(x), m, n, k))
+    assert np.array_equal(outs[2].view(np.uint32), y2.view(np.uint32))
+    y_ref, mag = _ref(codes, d_bits, x)
+    for y in outs:
+        assert_within(y.reshape(m, n), y_ref, mag, TOL, "fused GEMV, workspace short, absent or whole")
 
 
 # n >= 32768 takes the 4-rows-per-lane-group layout: odd block counts (one
@@ -115,15 +131,17 @@ def test_large_n_layout(qll_gpu, m, n, k):
     y = host(gemv_f32(w, x, m, n, k)).reshape(m, n)
     y_ref, mag = _ref(codes, d_bits, x)
     assert_within(y, y_ref, mag, TOL, f"fused large-n m={m} n={n} k={k}")
-    if m >= 2:
-        y2 = host(q4_gemm(w, quantize_q8_0(x), m, n, k)).reshape(m, n)
+    y2 = host(q4_gemm(w, quantize_q8_0(x), m, n, k)).reshape(m, n)
+    assert_within(y2, y_ref, mag, TOL, f"GEMM large-n m={m} n={n} k={k}")
+    if _gemv_style(m, n, k):
         assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
-# 8192 <= n < 32768 at m > 2 takes the 2-rows-per-lane-group layout: odd
-# block counts, a ragged last row group, several k-chunks
+# 8192 <= n < 32768 at m > 2 takes the 2-rows-per-lane-group layout (rows of
+# fewer than eight blocks, where the GEMM entry runs the GEMV-style kernel):
+# odd block counts, a ragged last row group
 @pytest.mark.parametrize("m", [3, 4, 8])
-@pytest.mark.parametrize("n,k", [(8193, 96), (14337, 4160), (9000, 1056)])
+@pytest.mark.parametrize("n,k", [(8193, 96), (14337, 224), (9000, 160)])
 def test_mid_n_layout(qll_gpu, m, n, k):
     codes, d_bits, x = _case(m * 17 + n + k, m, n, k)
     w = pack_q4_0(codes, d_bits)
@@ -185,8 +203,9 @@ def test_fused_zero_rows(qll_gpu):
 @pytest.mark.parametrize("s", range(4))
 def test_8b_shapes_fused_m1_and_m8(qll_gpu, s):
     # full decode sizes: the fused entry at m = 1 (both routes) against the
-    # oracle on every output; at m = 8 the small-m GEMM on a sample of
-    # outputs and the fused entry's routes bit for bit against it
+    # oracle on every output; at m = 8 the small-m GEMM and the fused entry's
+    # single launch on a sample of outputs, and its workspace route
+    # (quantize, then the same kernel) bit for bit against the GEMM
     codes, d_bits, x1 = synth.q4_decode(s)
     n, k = codes.shape
     w = pack_q4_0(codes, d_bits)
@@ -197,11 +216,12 @@ def test_8b_shapes_fused_m1_and_m8(qll_gpu, s):
     assert np.array_equal(y.view(np.uint32), host(gemv_f32(w, x1, 1, n, k, "ws")).view(np.uint32))
     x8 = synth.q4_prefill_x(s)[:8]
     y8 = host(q4_gemm(w, quantize_q8_0(x8), 8, n, k)).reshape(8, n)
-    for route in ("single", "ws"):
-        yf = host(gemv_f32(w, x8, 8, n, k, route)).reshape(8, n)
-        assert np.array_equal(yf.view(np.uint32), y8.view(np.uint32)), route
+    yws = host(gemv_f32(w, x8, 8, n, k, "ws")).reshape(8, n)
+    assert np.array_equal(yws.view(np.uint32), y8.view(np.uint32))
+    ysingle = host(gemv_f32(w, x8, 8, n, k, "single")).reshape(8, n)
     rng = np.random.default_rng(300 + s)
     ii = np.concatenate([[0, 7], rng.integers(0, 8, 2000)])
     jj = np.concatenate([[0, n - 1], rng.integers(0, n, 2000)])
     y_ref, mag = O.q4_0_q8_0_sampled(wq, O.quantize_q8_0(x8), 8, n, k, ii, jj)
     assert_within(y8[ii, jj], y_ref, mag, TOL, f"small-m m=8 {synth.SHAPES_8B[s]}")
+    assert_within(ysingle[ii, jj], y_ref, mag, TOL, f"fused single launch m=8 {synth.SHAPES_8B[s]}")
