@@ -34,13 +34,7 @@
 // and d_w -- goes straight from memory to LDS (global_load_lds, which takes
 // the 2-byte aligned addresses of 18-byte weight blocks), two stages ahead.
 // Weights stay as nibbles in LDS (a quarter of the bytes of f16) and are
-// widened when the fragments are read.
-//
-// Small m (9 <= m <= 32; m <= 8 runs as a GEMV): the same kernel with 32-row
-// tiles (4 waves side by side, one 32 x 32 tile each), and, when the block
-// count is even, each weight row's two blocks of a stage loaded as the 36
-// bytes they are (nine lanes, seven rows per load) instead of one 16-byte
-// load per row, which at this compute per weight byte would bound the kernel.
+// widened when the fragments are read.  (m <= 32 runs the small-m kernels.)
 #include "common.h"
 
 namespace qll {
@@ -52,35 +46,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define QLL_LDS __attribute__((address_space(3)))
 
-constexpr int QBN = 128, QKB = 2, QNBUF = 3;
+constexpr int QBM = 128, QBN = 128, QKB = 2, QNBUF = 3;
 
-// Row-tile heights: 128 (four waves in a 2 x 2 grid of 64 x 64 tiles) or, for
-// small m, 32 (four waves side by side, one 32 x 32 tile each), which pads m
-// to 32 instead of 128.
-//
-// PW (BM = 32 and an even block count only): a stage's two weight blocks of a
-// row are 36 contiguous bytes (the pair starts at an even block), loaded as
-// nine dwords by nine consecutive lanes, seven rows per load, into a [row][9]
-// dword array; otherwise each lane loads one block's 16 code bytes (lane =
-// row) and its d_w, so one load touches 64 rows' cache lines.  With 128-row
-// tiles that costs nothing visible; with 32-row tiles, whose compute per
-// weight byte is a quarter, those requests bound the kernel.
-template <int BM, bool PW>
-struct QCfg {
-    static_assert(!PW || BM == 32, "paired weight rows go with 32-row tiles");
-    static constexpr int TI = BM == 128 ? 2 : 1;            // 32-row tiles per wave
-    static constexpr int TJ = BM == 128 ? 2 : 1;            // 32-column tiles per wave
-    static constexpr int XLoads = QKB * BM / 16 / 4;        // 1 KB activation loads per wave and stage
-    static constexpr int WLoads = PW ? 5 : 2;               // weight loads per wave and stage
-    static constexpr int Dma = XLoads + 1 + WLoads;         // + d_x or C0
-    __device__ static int wm(int wave) { return BM == 128 ? (wave >> 1) * 64 : 0; }
-    __device__ static int wn(int wave) { return BM == 128 ? (wave & 1) * 64 : wave * 32; }
-};
+// A workgroup's four waves in a 2 x 2 grid of 64 x 64 tiles: 2 x 2 MFMA tiles
+// of 32 x 32 per wave.
+constexpr int QTI = 2, QTJ = 2;
+constexpr int QXLoads = QKB * QBM / 16 / 4; // 1 KB activation loads per wave and stage
+constexpr int QDma = QXLoads + 1 + 2;       // + d_x or C0, + the weight codes and d_w
+__device__ __forceinline__ int q4gemm_wm(int wave) { return (wave >> 1) * 64; }
+__device__ __forceinline__ int q4gemm_wn(int wave) { return (wave & 1) * 64; }
 
-// Paired weight rows: 20 loads of 63 lanes (7 rows x 9 dwords) cover the 128
-// rows of a stage and 12 rows of padding (the last loads' rows past the tile
-// land there).
-constexpr int kPwLoads = 20, kPwRowsPerLoad = 7;
 constexpr int kQ4GemmThreads = 256;
 
 // Prepared activations: per (row, block) 32 halves = 4 chunks of 16 bytes.
@@ -186,31 +161,21 @@ __device__ __forceinline__ int q4gemm_slot(int kb, int row, int c)
     return c ^ (((row >> 1) ^ (row >> 3)) & 3) ^ (kb ? 3 : 0);
 }
 
-template <int BM, bool PW>
 struct Q4GemmLds {
-    u32x4 xs[QKB][BM][4];  // prepared activations, slots swizzled
+    u32x4 xs[QKB][QBM][4]; // prepared activations, slots swizzled
     u32x4 wq[QKB][QBN];    // weight code dwords 0..3 of (block, row)
-    u32x2 dx[QKB][BM];     // {binary16 bits of d_x, 0}
-    float c0[QKB][BM];
+    u32x2 dx[QKB][QBM];    // {binary16 bits of d_x, 0}
+    float c0[QKB][QBM];
     uint32_t dw[QKB][QBN]; // binary16 bits of d_w, zero-extended
 };
 
-template <int BM>
-struct Q4GemmLds<BM, true> {
-    u32x4 xs[QKB][BM][4];
-    uint32_t wp[kPwLoads * kPwRowsPerLoad * 9]; // [row][9]: the row's two blocks as stored (36 bytes)
-    u32x2 dx[QKB][BM];
-    float c0[QKB][BM];
-};
-
 // Every byte a stage needs goes straight from memory to LDS
-// (global_load_lds), QCfg<BM>::Dma wave-wide loads per wave and stage (7 for
-// BM = 128, 4 for BM = 32):
-//   * the prepared activations (16 KB, resp. 4 KB), four, resp. one, 1 KB
-//     loads per wave (lane l of a load writes LDS byte 16 l, so it fetches
-//     the chunk that belongs in that slot);
-//   * waves 0 and 1: the {d_x, 0} pairs of block kb = wave (8 BM bytes, two
-//     rows per lane); waves 2 and 3: C0 of block kb = wave - 2 (4 BM bytes);
+// (global_load_lds), QDma = 7 wave-wide loads per wave and stage:
+//   * the prepared activations (16 KB), four 1 KB loads per wave (lane l of
+//     a load writes LDS byte 16 l, so it fetches the chunk that belongs in
+//     that slot);
+//   * waves 0 and 1: the {d_x, 0} pairs of block kb = wave (1 KB, two rows
+//     per lane); waves 2 and 3: C0 of block kb = wave - 2 (512 bytes);
 //   * weight rows (wave & 1) * 64 + lane of block kb = wave >> 1: the 16
 //     code bytes (block + 2) and d_w (block + 0, a 16-bit load, which the
 //     hardware writes to LDS as a zero-extended dword).  Weight blocks are
@@ -219,16 +184,14 @@ struct Q4GemmLds<BM, true> {
 // No stage data passes through registers, so the compiler has no loads of
 // its own to wait for; the end-of-stage wait (q4gemm_sync) counts these.
 struct Q4GemmSrc {
-    uint32_t wpo[5]; // paired weight rows: byte offset of this lane's dword in each load, from (row n0, block b)
     uint32_t xo[4]; // byte offset of this lane's activation chunk for each 1 KB load, from (m0, block b)
     uint32_t so;    // byte offset of this lane's d_x pair / C0 entries, from (block b, m0)
     uint32_t wo;    // byte offset of this lane's weight block, from (row n0, block b)
 };
 
-template <int BM, bool PW>
 __device__ __forceinline__ Q4GemmSrc q4gemm_src(const Q4GemmPrep &p, int64_t n0, int64_t n, int nb)
 {
-    constexpr int XL = QCfg<BM, PW>::XLoads, RPB = BM / 16; // 1 KB regions per block
+    constexpr int XL = QXLoads, RPB = QBM / 16; // 1 KB regions per block
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     Q4GemmSrc c;
 #pragma unroll
@@ -242,32 +205,16 @@ __device__ __forceinline__ Q4GemmSrc q4gemm_src(const Q4GemmPrep &p, int64_t n0,
     const int row = (wave & 1) * 64 + lane;
     const int64_t wrow = (n0 + row < n) ? row : n - 1 - n0; // rows past n: any valid row, output dropped
     c.wo = (uint32_t)(18 * wrow * nb);
-    if (PW) {
-#pragma unroll
-        for (int j = 0; j < 5; j++) {
-            const int q = wave + 4 * j; // load q: rows 7 q .. 7 q + 6
-            const int r = q * kPwRowsPerLoad + (lane < 63 ? lane / 9 : 0);
-            const int64_t rr = (n0 + r < n) ? r : n - 1 - n0;
-            c.wpo[j] = (uint32_t)(18 * rr * nb + 4 * (lane < 63 ? lane % 9 : 0));
-        }
-    }
     return c;
 }
 
 // One wave-wide global -> LDS load: lane l reads `size` bytes at base + off
 // (base uniform, in scalar registers) and the wave writes them to LDS at
-// lds + 4 l (sizes 1 to 4, zero-extended) or lds + 16 l (size 16).  Inline
+// lds + 4 l (size 2, zero-extended) or lds + 16 l (size 16).  Inline
 // assembly keeps these loads out of the compiler's wait bookkeeping.
 __device__ __forceinline__ void q4gemm_dma16(const void *base, uint32_t off, const QLL_LDS void *lds)
 {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
-                 "s"((uint32_t)(uintptr_t)lds)
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ void q4gemm_dma4(const void *base, uint32_t off, const QLL_LDS void *lds)
-{
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
                  "s"((uint32_t)(uintptr_t)lds)
                  : "memory", "m0");
 }
@@ -295,11 +242,11 @@ struct Q4GemmBase {
 // keeps far below 4 GiB; 64-bit across the d_x and C0 arrays).  Weight
 // blocks at or past nb load block nb - 1 of the row instead: their
 // activations and d_x are zero in the prepared arrays, so they add nothing.
-template <int BM, bool PW, int WAVE>
+template <int WAVE>
 __device__ __forceinline__ void q4gemm_load_wave(const Q4GemmBase &g, const Q4GemmSrc &c, int nb, int b,
-                                                 Q4GemmLds<BM, PW> &s)
+                                                 Q4GemmLds &s)
 {
-    constexpr int XL = QCfg<BM, PW>::XLoads, RPB = BM / 16;
+    constexpr int XL = QXLoads, RPB = QBM / 16;
     const int lane = threadIdx.x & 63;
     const uint8_t *xb = g.x + (uint32_t)b * 64u;
 #pragma unroll
@@ -307,41 +254,28 @@ __device__ __forceinline__ void q4gemm_load_wave(const Q4GemmBase &g, const Q4Ge
         constexpr int r0 = WAVE * XL;
         q4gemm_dma16(xb, c.xo[j], (const QLL_LDS void *)&s.xs[(r0 + j) / RPB][((r0 + j) % RPB) * 16][0]);
     }
-    // every wave issues exactly one of these (lanes past the data masked), so
-    // the per-wave load count stays QCfg<BM, PW>::Dma
-    if (WAVE < 2) {
-        if (lane < BM / 2)
-            q4gemm_dma16(g.dx + (int64_t)(b + WAVE) * g.sblk, c.so, (const QLL_LDS void *)&s.dx[WAVE][0]);
-    } else if (lane < BM / 4) {
+    // every wave issues exactly one of these (C0: lanes past the data
+    // masked), so the per-wave load count stays QDma
+    if (WAVE < 2)
+        q4gemm_dma16(g.dx + (int64_t)(b + WAVE) * g.sblk, c.so, (const QLL_LDS void *)&s.dx[WAVE][0]);
+    else if (lane < QBM / 4)
         q4gemm_dma16(g.c0 + (int64_t)(b + WAVE - 2) * (g.sblk / 2), c.so, (const QLL_LDS void *)&s.c0[WAVE - 2][0]);
-    }
-    if constexpr (PW) {
-        // the pair (b, b + 1): b is even and so is nb, so a pair in range
-        // lies wholly inside the row; stages past the range load the last pair
-        const uint8_t *wb = g.w + 18u * (uint32_t)(b < nb ? b : nb - 2);
-#pragma unroll
-        for (int j = 0; j < 5; j++)
-            if (lane < 63) // every wave issues all five loads
-                q4gemm_dma4(wb, c.wpo[j], (const QLL_LDS void *)&s.wp[(WAVE + 4 * j) * kPwRowsPerLoad * 9]);
-    } else {
-        constexpr int kb = WAVE >> 1, rbase = (WAVE & 1) * 64;
-        const int bw = (b + kb < nb) ? b + kb : nb - 1;
-        const uint8_t *wb = g.w + 18u * (uint32_t)bw;
-        q4gemm_dma16(wb + 2, c.wo, (const QLL_LDS void *)&s.wq[kb][rbase]);
-        q4gemm_dma2(wb, c.wo, (const QLL_LDS void *)&s.dw[kb][rbase]);
-    }
+    constexpr int kb = WAVE >> 1, rbase = (WAVE & 1) * 64;
+    const int bw = (b + kb < nb) ? b + kb : nb - 1;
+    const uint8_t *wb = g.w + 18u * (uint32_t)bw;
+    q4gemm_dma16(wb + 2, c.wo, (const QLL_LDS void *)&s.wq[kb][rbase]);
+    q4gemm_dma2(wb, c.wo, (const QLL_LDS void *)&s.dw[kb][rbase]);
 }
 
 // The loads of a stage; `wave` is uniform (a scalar register).
-template <int BM, bool PW>
 __device__ __forceinline__ void q4gemm_load_stage(const Q4GemmBase &g, const Q4GemmSrc &c, int nb, int b, int wave,
-                                                  Q4GemmLds<BM, PW> &s)
+                                                  Q4GemmLds &s)
 {
     switch (wave) {
-    case 0: q4gemm_load_wave<BM, PW, 0>(g, c, nb, b, s); break;
-    case 1: q4gemm_load_wave<BM, PW, 1>(g, c, nb, b, s); break;
-    case 2: q4gemm_load_wave<BM, PW, 2>(g, c, nb, b, s); break;
-    default: q4gemm_load_wave<BM, PW, 3>(g, c, nb, b, s); break;
+    case 0: q4gemm_load_wave<0>(g, c, nb, b, s); break;
+    case 1: q4gemm_load_wave<1>(g, c, nb, b, s); break;
+    case 2: q4gemm_load_wave<2>(g, c, nb, b, s); break;
+    default: q4gemm_load_wave<3>(g, c, nb, b, s); break;
     }
 }
 
@@ -372,31 +306,20 @@ struct Q4GemmLaneOff {
     uint32_t dx, dw, c0;
 };
 
-template <int BM, bool PW>
 __device__ __forceinline__ Q4GemmLaneOff q4gemm_lane_offsets(int wm, int wn, int lane)
 {
-    using Lds = Q4GemmLds<BM, PW>;
+    using Lds = Q4GemmLds;
     const int lr = lane & 31, lh = lane >> 5;
     Q4GemmLaneOff o;
 #pragma unroll
     for (int kb = 0; kb < QKB; kb++)
 #pragma unroll
         for (int st = 0; st < 2; st++)
-            o.x[kb][st] = (uint32_t)(offsetof(Lds, xs) + (kb * BM + wm + lr) * 64 +
+            o.x[kb][st] = (uint32_t)(offsetof(Lds, xs) + (kb * QBM + wm + lr) * 64 +
                                      q4gemm_slot(kb, wm + lr, 2 * lh + st) * 16);
-    // paired weight rows: row wn + lr of the [row][9] array; the lane's eight
-    // code bytes of block 0 start 2 + 8 lh bytes in (read as the dwords from
-    // 8 lh), of block 1 at 20 + 8 lh; d_w of block 0 is the low half of dword
-    // 0, of block 1 the high half of dword 4
-    if constexpr (PW)
-        o.w = (uint32_t)(offsetof(Lds, wp) + 36 * (wn + lr) + 8 * lh);
-    else
-        o.w = (uint32_t)(offsetof(Lds, wq) + (wn + lr) * 16 + lh * 8);
+    o.w = (uint32_t)(offsetof(Lds, wq) + (wn + lr) * 16 + lh * 8);
     o.dx = (uint32_t)(offsetof(Lds, dx) + (wm + lr) * 8);
-    if constexpr (PW)
-        o.dw = (uint32_t)(offsetof(Lds, wp) + 36 * (wn + lr));
-    else
-        o.dw = (uint32_t)(offsetof(Lds, dw) + (wn + lr) * 4);
+    o.dw = (uint32_t)(offsetof(Lds, dw) + (wn + lr) * 4);
     o.c0 = (uint32_t)(offsetof(Lds, c0) + (wm + 4 * lh) * 4);
     // opaque to the compiler: it would otherwise split off the constant
     // parts again and re-add them per read (read2 pairs take 8-bit offsets)
@@ -416,7 +339,7 @@ __device__ __forceinline__ T q4gemm_lds(const QLL_LDS char *base, uint32_t off)
 }
 
 // One stage: for each of its blocks, the block sums of the wave's tile on the
-// matrix core -- 2 x 2 (BM = 128) or one (BM = 32) tiles of 32 x 32, each two K = 16 steps
+// matrix core -- 2 x 2 tiles of 32 x 32, each two K = 16 steps
 // started from C0 -- and the scale tiles, then acc += S * P.  MFMA operand
 // lanes: lane l holds row (column) l % 32 of its tile and chunk
 // 2 (l / 32) + s of the block in step s (one 8-byte read of a weight row
@@ -429,11 +352,10 @@ __device__ __forceinline__ T q4gemm_lds(const QLL_LDS char *base, uint32_t off)
 // both d_x[r] d_w[c]: S = 2 d_x d_w exactly (a product of two halves is
 // exact in f32, and so is its double).  The factor 2 leaves the kernel as an
 // exact halving of the outputs.
-template <int BM, bool PW>
 __device__ __forceinline__ void q4gemm_compute(const QLL_LDS char *base, const Q4GemmLaneOff &o, uint32_t bias,
-                                               f32x16 acc[QCfg<BM, PW>::TI][QCfg<BM, PW>::TJ])
+                                               f32x16 acc[QTI][QTJ])
 {
-    constexpr int TI = QCfg<BM, PW>::TI, TJ = QCfg<BM, PW>::TJ, NT = TI * TJ;
+    constexpr int TI = QTI, TJ = QTJ, NT = TI * TJ;
 #pragma unroll
     for (int kb = 0; kb < QKB; kb++) {
         // keeps the two blocks' reads apart (hoisted together they spill)
@@ -444,34 +366,20 @@ __device__ __forceinline__ void q4gemm_compute(const QLL_LDS char *base, const Q
         static_assert(TI == TJ, "reads interleave row and column tiles");
 #pragma unroll
         for (int i = 0; i < TI; i++) {
-            u32x2 wv;
-            uint32_t dwb;
-            if constexpr (PW) {
-                if (kb == 0) {
-                    const uint32_t d0 = q4gemm_lds<uint32_t>(base, o.w), d1 = q4gemm_lds<uint32_t>(base, o.w + 4),
-                                   d2 = q4gemm_lds<uint32_t>(base, o.w + 8);
-                    wv = u32x2{funnel(d1, d0, 16), funnel(d2, d1, 16)};
-                    dwb = q4gemm_lds<uint32_t>(base, o.dw) & 0xffffu;
-                } else {
-                    wv = u32x2{q4gemm_lds<uint32_t>(base, o.w + 20), q4gemm_lds<uint32_t>(base, o.w + 24)};
-                    dwb = q4gemm_lds<uint32_t>(base, o.dw + 16) >> 16;
-                }
-            } else {
-                wv = q4gemm_lds<u32x2>(base, o.w + kb * QBN * 16 + 512 * i);
-                dwb = q4gemm_lds<uint32_t>(base, o.dw + kb * QBN * 4 + 128 * i);
-            }
+            const u32x2 wv = q4gemm_lds<u32x2>(base, o.w + kb * QBN * 16 + 512 * i);
+            const uint32_t dwb = q4gemm_lds<uint32_t>(base, o.dw + kb * QBN * 4 + 128 * i);
 #pragma unroll
             for (int st = 0; st < 2; st++) {
                 a[i][st] = __builtin_bit_cast(f16x8, q4gemm_lds<u32x4>(base, o.x[kb][st] + 2048 * i));
                 bm[i][st] = q4gemm_wfrag(wv[st], bias);
             }
-            sa[i] = __builtin_bit_cast(f16x4, q4gemm_lds<u32x2>(base, o.dx + kb * BM * 8 + 256 * i));
+            sa[i] = __builtin_bit_cast(f16x4, q4gemm_lds<u32x2>(base, o.dx + kb * QBM * 8 + 256 * i));
             sb[i] = __builtin_bit_cast(f16x4, u32x2{dwb, 0u});
             // D layout of a 32 x 32 tile: lane l, register v -> row
             // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const f32x4 t = q4gemm_lds<f32x4>(base, o.c0 + kb * BM * 4 + 128 * i + 32 * q);
+                const f32x4 t = q4gemm_lds<f32x4>(base, o.c0 + kb * QBM * 4 + 128 * i + 32 * q);
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     c0[i][4 * q + e] = t[e];
@@ -540,23 +448,22 @@ __device__ __forceinline__ void q4gemm_sync()
     asm volatile("" ::: "memory");
 }
 
-template <int BM, bool PW>
 __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const uint8_t *__restrict__ w, Q4GemmPrep prep,
                                                                            float *__restrict__ y, int64_t m,
                                                                            int64_t n, int nb, int per_split)
 {
-    constexpr int TI = QCfg<BM, PW>::TI, TJ = QCfg<BM, PW>::TJ, DMA = QCfg<BM, PW>::Dma;
-    __shared__ Q4GemmLds<BM, PW> lds[QNBUF];
+    constexpr int TI = QTI, TJ = QTJ, DMA = QDma;
+    __shared__ Q4GemmLds lds[QNBUF];
     int64_t m_tile, n_tile;
-    q4gemm_tile(prep.mp / BM, (n + QBN - 1) / QBN, m_tile, n_tile);
-    const int64_t m0 = m_tile * BM, n0 = n_tile * QBN;
+    q4gemm_tile(prep.mp / QBM, (n + QBN - 1) / QBN, m_tile, n_tile);
+    const int64_t m0 = m_tile * QBM, n0 = n_tile * QBN;
     // split-k: blockIdx.y takes blocks [b_begin, b_begin + per_split) and
     // writes its partial tile to y + blockIdx.y * m * n (the workspace when
     // there are splits); blocks past nb have d_x = 0 in the prepared arrays
     const int b_begin = blockIdx.y * per_split;
     y += (int64_t)blockIdx.y * m * n;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = QCfg<BM, PW>::wm(wave), wn = QCfg<BM, PW>::wn(wave);
+    const int wm = q4gemm_wm(wave), wn = q4gemm_wn(wave);
 
     f32x16 acc[TI][TJ];
 #pragma unroll
@@ -565,9 +472,9 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
         for (int j = 0; j < TJ; j++)
             acc[i][j] = f32x16{};
 
-    const Q4GemmSrc src = q4gemm_src<BM, PW>(prep, n0, n, nb);
+    const Q4GemmSrc src = q4gemm_src(prep, n0, n, nb);
     const int nstages = per_split / QKB;
-    const Q4GemmLaneOff lo = q4gemm_lane_offsets<BM, PW>(wm, wn, lane);
+    const Q4GemmLaneOff lo = q4gemm_lane_offsets(wm, wn, lane);
     uint32_t bias; // 0x64006400, opaque to the compiler (see q4gemm_wfrag)
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));
 
@@ -584,14 +491,14 @@ __global__ __launch_bounds__(kQ4GemmThreads) void q4_0_q8_0_gemm_kernel(const ui
     g.w = w + 18 * n0 * (int64_t)nb;
     g.sblk = prep.mp * 8;
     const int swave = __builtin_amdgcn_readfirstlane(wave);
-    q4gemm_load_stage<BM, PW>(g, src, nb, b_begin, swave, lds[0]);
-    q4gemm_load_stage<BM, PW>(g, src, nb, b_begin + QKB, swave, lds[1]);
+    q4gemm_load_stage(g, src, nb, b_begin, swave, lds[0]);
+    q4gemm_load_stage(g, src, nb, b_begin + QKB, swave, lds[1]);
     q4gemm_sync<DMA>();
     int cur = 0; // buffer of stage st
     for (int st = 0; st < nstages; st++) {
         const int nx2 = cur == 0 ? 2 : cur - 1;
-        q4gemm_load_stage<BM, PW>(g, src, nb, b_begin + (st + 2) * QKB, swave, lds[nx2]);
-        q4gemm_compute<BM, PW>((const QLL_LDS char *)&lds[cur], lo, bias, acc);
+        q4gemm_load_stage(g, src, nb, b_begin + (st + 2) * QKB, swave, lds[nx2]);
+        q4gemm_compute((const QLL_LDS char *)&lds[cur], lo, bias, acc);
         q4gemm_sync<DMA>();
         cur = cur == 2 ? 0 : cur + 1;
     }
@@ -629,21 +536,17 @@ __global__ __launch_bounds__(256) void q4gemm_sum_splits_kernel(const float *__r
 // of 2 QKB of them.  The workspace holds the split partials (if any), then
 // the prepared activations, d_x and C0.
 struct Q4GemmPlan {
-    int bm, splits, per_split;
+    int splits, per_split;
     int64_t mp, nbp, tiles;
     size_t x_off, dx_off, c0_off, total;
 };
-
-// Row tiles of 32 for m <= kQ4SmallTileM, else 128.
-constexpr int64_t kQ4SmallTileM = 32;
 
 static Q4GemmPlan q4gemm_plan(int64_t m, int64_t n, int64_t k)
 {
     Q4GemmPlan p;
     const int64_t nb = k / 32;
-    p.bm = m <= kQ4SmallTileM ? 32 : 128;
-    p.mp = (m + p.bm - 1) / p.bm * p.bm;
-    const int64_t tiles = ((n + QBN - 1) / QBN) * (p.mp / p.bm);
+    p.mp = (m + QBM - 1) / QBM * QBM;
+    const int64_t tiles = ((n + QBN - 1) / QBN) * (p.mp / QBM);
     p.tiles = tiles;
     int64_t s = 512 / tiles;
     if (s > nb / 16)
@@ -694,15 +597,8 @@ hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, 
         return e;
     float *out = plan.splits > 1 ? reinterpret_cast<float *>(base) : y;
     const dim3 grid((unsigned)plan.tiles, (unsigned)plan.splits);
-    if (plan.bm == 32 && nb % 2 == 0)
-        hipLaunchKernelGGL((q4_0_q8_0_gemm_kernel<32, true>), grid, dim3(kQ4GemmThreads), 0, s, w, prep, out, m, n,
-                           (int)nb, plan.per_split);
-    else if (plan.bm == 32)
-        hipLaunchKernelGGL((q4_0_q8_0_gemm_kernel<32, false>), grid, dim3(kQ4GemmThreads), 0, s, w, prep, out, m, n,
-                           (int)nb, plan.per_split);
-    else
-        hipLaunchKernelGGL((q4_0_q8_0_gemm_kernel<128, false>), grid, dim3(kQ4GemmThreads), 0, s, w, prep, out, m,
-                           n, (int)nb, plan.per_split);
+    hipLaunchKernelGGL(q4_0_q8_0_gemm_kernel, grid, dim3(kQ4GemmThreads), 0, s, w, prep, out, m, n, (int)nb,
+                       plan.per_split);
     e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
         return e;

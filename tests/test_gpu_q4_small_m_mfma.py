@@ -30,7 +30,7 @@ CASES = [
     (7, 33, 512, (1, 1)),
     (16, 14336, 4096, (1, 2)),    # the 8B-class up projection
     (9, 9000, 1024, (1, 2)),
-    (3, 70001, 256, (1, 1)),      # many row tiles
+    (3, 20001, 256, (1, 1)),      # one stage
     (3, 9000, 1024, (1, 2)),
     (6, 2000, 2048, (1, 4)),
     (7, 9000, 1024, (1, 2)),
@@ -43,7 +43,7 @@ CASES = [
     (17, 20001, 2048, (2, 1)),
     (12, 129, 256, (1, 1)),       # eight blocks: one stage
     (13, 33, 2048, (1, 4)),
-    (3, 32768, 1024, (1, 2)),
+    (4, 20001, 1024, (1, 2)),
     (7, 32768, 1024, (2, 2)),
     (13, 32768, 256, (2, 1)),
     (13, 32768, 1024, (2, 2)),
@@ -86,6 +86,9 @@ def _case(seed, m, n, k):
 @pytest.mark.parametrize("m,n,k,ks", CASES)
 def test_small_m_mfma_shapes(qll_gpu, m, n, k, ks):
     assert _split(m, n, k) == ks  # the case covers the tiling and split it is listed for
+    # and reaches this kernel (the GEMM entry keeps the GEMV-style kernel at
+    # m = 2 from n = 8192 and at m <= 4 from n = 32768)
+    assert ks is None or not ((m == 2 and n >= 8192) or (m <= 4 and n >= 32768))
     codes, d_bits, x = _case(m * 1009 + n * 7 + k, m, n, k)
     y = host(q4_gemm(pack_q4_0(codes, d_bits), quantize_q8_0(x), m, n, k)).reshape(m, n)
     y_ref, mag = O.q4_0_q8_0(O.pack_q4_0(codes, d_bits), O.quantize_q8_0(x), m, n, k)
