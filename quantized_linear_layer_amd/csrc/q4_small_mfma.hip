@@ -40,7 +40,7 @@ typedef float f32x4_m __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_m __attribute__((ext_vector_type(4)));
 
 constexpr int kSmSB = 8;    // blocks per stage
-constexpr int kSmNS = 2;    // stage buffers per wave
+constexpr int kSmNS = 2;    // stage buffers per wave (1 or 2)
 constexpr int kSmGroup = 8; // block products (times tiles) formed before their sums
 
 // 16-column activation tiles for MP staged activation rows.
@@ -289,6 +289,7 @@ __global__ __launch_bounds__(64 * KS) void q4_0_small_m_mfma_kernel(const uint8_
     using L = SmLayout<T, MP>;
     constexpr int MT = sm_mt(MP), N = T * MT;
     static_assert(N * 4 * 64 * 4 <= kSmNS * L::STAGE, "a wave's partial tile fits in its stage buffers");
+    static_assert(kSmNS == 1 || kSmNS == 2, "one stage in flight at most");
     __shared__ __attribute__((aligned(16))) char stage[KS][kSmNS][L::STAGE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -310,20 +311,20 @@ __global__ __launch_bounds__(64 * KS) void q4_0_small_m_mfma_kernel(const uint8_
 #pragma unroll
         for (int i = 0; i < 4; i++)
             acc[t][i] = 0.0f;
-    // two stage buffers: stage s in buffer s % 2, the next in flight while
-    // it is computed
-    if (s0 < s1)
-        sm_load<T, MP>(wt, xq, min(s0 * kSmSB, blast), o, lds);
-    if (s0 + 1 < s1)
-        sm_load<T, MP>(wt, xq, min((s0 + 1) * kSmSB, blast), o, lds + L::STAGE);
+    // kSmNS stage buffers in a ring: stage s in buffer s % kSmNS, the
+    // kSmNS - 1 stages after it in flight while it is computed
+#pragma unroll
+    for (int j = 0; j < kSmNS; j++)
+        if (s0 + j < s1)
+            sm_load<T, MP>(wt, xq, min((s0 + j) * kSmSB, blast), o, lds + j * L::STAGE);
     for (int s2 = s0; s2 < s1; s2 += kSmNS) {
 #pragma unroll
         for (int j = 0; j < kSmNS; j++) { // buffer j: a constant offset
             const int s = s2 + j;
             if (s >= s1)
                 break;
-            if (s + 1 < s1)
-                sm_wait<L::DMA>(); // stage s has landed, stage s + 1 may not have
+            if (kSmNS > 1 && s + 1 < s1)
+                sm_wait<(kSmNS - 1) * L::DMA>(); // stage s has landed, the one after may not have
             else
                 sm_wait<0>();
             sm_stage<T, MP>(buf + j * L::STAGE, s * kSmSB - min(s * kSmSB, blast), width, acc);
