@@ -125,7 +125,7 @@ size_t qll_workspace_bytes(int op, int64_t m, int64_t n, int64_t k)
     case QLL_OP_Q4_0_Q8_0_GEMM:
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0 || (m > kMaxMSmall && k >= kMaxGemmK))
             return SIZE_MAX;
-        return m <= kMaxMMfma ? 0 : q4_0_q8_0_gemm_workspace(m, n, k);
+        return q4_small_m_path(m, n, k) ? 0 : q4_0_q8_0_gemm_workspace(m, n, k);
     case QLL_OP_TERNARY_GEMM:
         if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 16 != 0)
             return SIZE_MAX;
@@ -237,7 +237,7 @@ int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64
         return qll_q4_0_q8_0_gemv(w, xq, y, n, k, stream);
     if (!aligned16(w) || !aligned16(xq) || !aligned16(y))
         return QLL_ERR_ALIGN;
-    if (m <= kMaxMMfma && (m <= kMaxMSmall || k < kMaxKMfma)) {
+    if (q4_small_m_path(m, n, k)) {
         if (int rc = check_device())
             return rc;
         return launched(launch_q4_0_q8_0_gemv_m(static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(xq), y,
@@ -263,7 +263,7 @@ int qll_q4_0_q8_0_gemm_noalloc(const void *w, const void *xq, float *y, int64_t 
         return QLL_ERR_NULL;
     if (!dims_ok(m, k) || !dims_ok(n, k) || !dims_ok(m, n) || k % 32 != 0)
         return QLL_ERR_SHAPE;
-    if (m <= kMaxMMfma) // the decode kernels need no scratch
+    if (q4_small_m_path(m, n, k)) // the small-m kernels need no scratch
         return qll_q4_0_q8_0_gemm(w, xq, y, m, n, k, nullptr, 0, stream);
     if (k >= kMaxGemmK)
         return QLL_ERR_SHAPE;

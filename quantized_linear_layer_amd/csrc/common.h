@@ -98,9 +98,10 @@ hipError_t launch_q4_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, 
                                  hipStream_t s);
 hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                  void *ws, hipStream_t s);
-// Small-m decode: Q8_0 activations at 2 <= m <= kMaxMMfma (m <= kMaxMSmall
-// when k >= kMaxKMfma), or, in the quantize-fused entry, f32 activations
-// quantized to Q8_0 inside the launch (1 <= m <= kMaxMSmall).
+// Small-m decode: Q8_0 activations at 1 <= m <= 64 (groups of at most 32
+// rows above 32; m <= kMaxMSmall when k >= kMaxKMfma), or, in the
+// quantize-fused entry, f32 activations quantized to Q8_0 inside the launch
+// (1 <= m <= kMaxMSmall).
 constexpr int64_t kMaxMSmall = 8;
 hipError_t launch_q4_0_q8_0_gemv_m(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                    hipStream_t s);
@@ -109,6 +110,20 @@ hipError_t launch_q4_0_q8_0_gemv_m(const uint8_t *w, const uint8_t *xq, float *y
 // with 32-bit offsets): Q8_0 activations, no workspace.
 constexpr int64_t kMaxMMfma = 32;
 constexpr int64_t kMinKMfma = 256, kMaxKMfma = (int64_t)1 << 24;
+
+// Whether the Q4_0 x Q8_0 GEMM entry runs the small-m kernels (no
+// workspace) rather than the 128-row GEMM: m <= 8 at any k; otherwise
+// k < kMaxKMfma and m <= 32, or m <= 64 as groups of at most 32 activation
+// rows (each group re-reads the weights, which beats the GEMM's padding of m
+// to 128 rows up to there: 4096 -> 14336 at m = 64 33.8 against 44.0 us),
+// except on tall matrices from m = 49 (4096 -> 128256 at m = 64: 242
+// against 231 us).
+inline bool q4_small_m_path(int64_t m, int64_t n, int64_t k)
+{
+    if (m <= kMaxMSmall)
+        return true;
+    return k < kMaxKMfma && (m <= kMaxMMfma || (m <= 64 && !(n >= 32768 && m > 48)));
+}
 hipError_t launch_q4_0_q8_0_small_m_mfma(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n,
                                          int64_t k, hipStream_t s);
 int small_m_mfma_split(int64_t m, int64_t n, int64_t k);

@@ -1154,6 +1154,19 @@ static hipError_t launch_gm(const uint8_t *w, const void *xin, float *y, int64_t
 hipError_t launch_q4_0_q8_0_gemv_m(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                    hipStream_t s)
 {
+    if (m > kMaxMMfma || (m == 1 && k <= kMaxKQ4Gemv)) {
+        // groups of at most 32 activation rows (a last group of one row: the
+        // GEMV); each group's outputs are its own rows of y
+        if (m == 1)
+            return launch_q4_0_q8_0_gemv(w, xq, y, n, k, s);
+        for (int64_t a0 = 0; a0 < m; a0 += kMaxMMfma) {
+            const int64_t mm = m - a0 < kMaxMMfma ? m - a0 : kMaxMMfma;
+            const hipError_t e = launch_q4_0_q8_0_gemv_m(w, xq + a0 * (k / 32) * 34, y + a0 * n, mm, n, k, s);
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
     // the matrix-core kernel, except at m = 2 on tall matrices and m <= 4 on
     // very tall ones, where the weight stream bounds both and this kernel's
     // lighter staging wins (4096 -> 14336 at m = 2: 9.9 against 11.0 us;

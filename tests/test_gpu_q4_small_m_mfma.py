@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle as O
+import quantized_linear_layer_amd as qll
 import synth
 from gpu_util import assert_within, host, pack_q4_0, q4_gemm, quantize_q8_0
 
@@ -128,6 +129,19 @@ def test_small_m_mfma_one_hot(qll_gpu):
     dw = d_bits.view(np.float16).astype(np.float64)
     want = dw[:, pos // 32].T * (codes[:, pos].T.astype(np.float64) - 8.0) * 127.0
     assert np.array_equal(y.astype(np.float64), want)
+
+
+# 33 <= m <= 64 (48 on tall matrices): groups of at most 32 activation rows,
+# a last group of one row on the GEMV, of 2..8 rows on the small-m kernels,
+# rows of fewer than eight blocks on the GEMV-style kernel by eights
+@pytest.mark.parametrize("m,n,k", [(33, 300, 4096), (40, 1000, 1056), (64, 17, 14336), (48, 40000, 512),
+                                   (37, 129, 96), (57, 14336, 4096)])
+def test_small_m_groups(qll_gpu, m, n, k):
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) == 0  # the small-m path
+    codes, d_bits, x = _case(m * 3 + n + k, m, n, k)
+    y = host(q4_gemm(pack_q4_0(codes, d_bits), quantize_q8_0(x), m, n, k)).reshape(m, n)
+    y_ref, mag = O.q4_0_q8_0(O.pack_q4_0(codes, d_bits), O.quantize_q8_0(x), m, n, k)
+    assert_within(y, y_ref, mag, TOL, f"small-m groups m={m} n={n} k={k}")
 
 
 def test_small_m_mfma_deterministic(qll_gpu):
