@@ -211,7 +211,8 @@ def build_ops(qll, synth, torch, np, dev, only):
     # ---------------------------------------------------------------- prompt-length sweep, fused decode
     # (4096 -> 14336): m over prompt lengths that straddle the kernels' row
     # tiles (m = 1 GEMV, 2..32 the small-m kernels, which read the weights
-    # once, above it the 128-row GEMM), and the quantize-fused decode entry
+    # once, up to 64 by groups of 32 rows, above it the 128-row GEMM), and the
+    # quantize-fused decode entry
     # against the quantize + decode pair at m = 1 and m = 8 on every 8B-class
     # shape.
     for s, (k, n) in enumerate(synth.SHAPES_8B):
@@ -236,8 +237,8 @@ def build_ops(qll, synth, torch, np, dev, only):
             ops.append(Op(f"msweep_q4_m{m}", "q4_0_msweep", "sweep",
                           lambda c=copies, xqm=xqm, ym=ym, m=m, n=n, k=k, wsm=wsm: qll.qll_q4_0_q8_0_gemm(
                               c[step_ref["i"] % len(c)], xqm, ym, m, n, k, ws=wsm),
-                          wbytes + m * (k // 32) * 34 + 4 * m * n, 2 * m * n * k, "hbm" if m <= 32 else "mfma",
-                          None if m <= 32 else "f16"))
+                          wbytes + m * (k // 32) * 34 + 4 * m * n, 2 * m * n * k, "hbm" if m <= 64 else "mfma",
+                          None if m <= 64 else "f16"))
         for m in ((1, 8) if fused else ()):
             xm = xall[:m].contiguous()
             xqm = torch.empty(m * (k // 32) * 34, dtype=torch.uint8, device=dev)
