@@ -126,7 +126,6 @@ inline bool q4_small_m_path(int64_t m, int64_t n, int64_t k)
 }
 hipError_t launch_q4_0_q8_0_small_m_mfma(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n,
                                          int64_t k, hipStream_t s);
-int small_m_mfma_split(int64_t m, int64_t n, int64_t k);
 // With ws (at least q4_0_gemv_f32_workspace bytes, nonzero), the rows are
 // quantized into ws by the quantize kernel and the Q8_0 decode kernel runs
 // on them; with ws == nullptr, one launch quantizes inside each workgroup.

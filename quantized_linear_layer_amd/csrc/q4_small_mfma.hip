@@ -139,6 +139,11 @@ __device__ __forceinline__ void sm_load(const uint8_t *wt, const uint8_t *xq, in
         sm_dma16(wb, o.w[i], lds + L::W + 1024 * i);
 }
 
+// A stage's weight rows and activation rows in LDS.
+struct SmBufs {
+    const QLL_LDS_M char *w, *x;
+};
+
 template <typename V>
 __device__ __forceinline__ V sm_lds(const QLL_LDS_M char *p)
 {
@@ -184,7 +189,7 @@ __device__ __forceinline__ uint32_t sm_half_bits(const QLL_LDS_M char *p, uint32
 // row's d_w and d_x, the others zeros), every entry the exact f32 product of
 // two halves.
 template <int T, int MP, int BL>
-__device__ __forceinline__ void sm_mfma(const QLL_LDS_M char *s, uint32_t width, i32x4 (&p)[T * sm_mt(MP)],
+__device__ __forceinline__ void sm_mfma(const SmBufs &s, uint32_t width, i32x4 (&p)[T * sm_mt(MP)],
                                         f32x4_m (&sc)[T * sm_mt(MP)])
 {
     using L = SmLayout<T, MP>;
@@ -197,14 +202,14 @@ __device__ __forceinline__ void sm_mfma(const QLL_LDS_M char *s, uint32_t width,
     f16x4_m sa[T];
 #pragma unroll
     for (int u = 0; u < T; u++) {
-        const QLL_LDS_M char *wrow = s + L::W + (16 * u + r) * L::WROW + 18 * BL;
+        const QLL_LDS_M char *wrow = s.w + (16 * u + r) * L::WROW + 18 * BL;
         const uint32_t wt = sm_word<!ODD>(wrow + 2 + 4 * g) ^ 0x88888888u;
         aop[u] = (long)(((uint64_t)(wt & 0xf0f0f0f0u) << 32) | ((wt << 4) & 0xf0f0f0f0u));
         sa[u] = __builtin_bit_cast(f16x4_m, (uint64_t)sm_half_bits<ODD>(wrow, width));
     }
 #pragma unroll
     for (int t = 0; t < MT; t++) {
-        const QLL_LDS_M char *xrow = s + L::X + (16 * t + ra) * L::XROW + 34 * BL;
+        const QLL_LDS_M char *xrow = s.x + (16 * t + ra) * L::XROW + 34 * BL;
         const uint32_t x0 = sm_word<!ODD>(xrow + 2 + 4 * g), x1 = sm_word<!ODD>(xrow + 18 + 4 * g);
         const long bop = (long)(((uint64_t)x1 << 32) | x0);
         const f16x4_m sb = __builtin_bit_cast(f16x4_m, (uint64_t)sm_half_bits<ODD>(xrow, width));
@@ -227,7 +232,7 @@ __device__ __forceinline__ void sm_apply(const i32x4 (&p)[N], const f32x4_m (&sc
 }
 
 template <int T, int MP, int BL>
-__device__ __forceinline__ void sm_block(const QLL_LDS_M char *s, uint32_t width, float (&acc)[T * sm_mt(MP)][4])
+__device__ __forceinline__ void sm_block(const SmBufs &s, uint32_t width, float (&acc)[T * sm_mt(MP)][4])
 {
     i32x4 p[T * sm_mt(MP)];
     f32x4_m sc[T * sm_mt(MP)];
@@ -238,7 +243,7 @@ __device__ __forceinline__ void sm_block(const QLL_LDS_M char *s, uint32_t width
 // Blocks B0 .. B0 + G - 1: every block's products first, then their sums
 // in block order (the matrix core's latency covered by the later blocks).
 template <int T, int MP, int B0, int G>
-__device__ __forceinline__ void sm_group(const QLL_LDS_M char *s, uint32_t width, float (&acc)[T * sm_mt(MP)][4])
+__device__ __forceinline__ void sm_group(const SmBufs &s, uint32_t width, float (&acc)[T * sm_mt(MP)][4])
 {
     constexpr int N = T * sm_mt(MP);
     i32x4 p[G][N];
@@ -259,8 +264,7 @@ __device__ __forceinline__ void sm_group(const QLL_LDS_M char *s, uint32_t width
 // Blocks lo .. 7 of a stage buffer (lo > 0 only for a row's last stage,
 // which starts inside the one before).
 template <int T, int MP>
-__device__ __forceinline__ void sm_stage(const QLL_LDS_M char *s, int lo, uint32_t width,
-                                         float (&acc)[T * sm_mt(MP)][4])
+__device__ __forceinline__ void sm_stage(const SmBufs &s, int lo, uint32_t width, float (&acc)[T * sm_mt(MP)][4])
 {
     if (lo == 0) { // uniform
         constexpr int G = kSmGroup / (T * sm_mt(MP)); // 8, 4 or 2 blocks
@@ -327,7 +331,8 @@ __global__ __launch_bounds__(64 * KS) void q4_0_small_m_mfma_kernel(const uint8_
                 sm_wait<(kSmNS - 1) * L::DMA>(); // stage s has landed, the one after may not have
             else
                 sm_wait<0>();
-            sm_stage<T, MP>(buf + j * L::STAGE, s * kSmSB - min(s * kSmSB, blast), width, acc);
+            const SmBufs sb{buf + j * L::STAGE + L::W, buf + j * L::STAGE + L::X};
+            sm_stage<T, MP>(sb, s * kSmSB - min(s * kSmSB, blast), width, acc);
             if (s + kSmNS < s1) {
                 sm_wait_lds(); // this buffer's reads have completed
                 sm_load<T, MP>(wt, xq, min((s + kSmNS) * kSmSB, blast), o, lds + j * L::STAGE);
@@ -359,6 +364,119 @@ __global__ __launch_bounds__(64 * KS) void q4_0_small_m_mfma_kernel(const uint8_
     }
 }
 
+// Wait until at most n (0 .. 15) of this wave's vector-memory operations
+// are outstanding (n uniform), and all its LDS operations have completed.
+__device__ __forceinline__ void sm_wait_n(int n)
+{
+    switch (n) {
+    case 0: sm_wait<0>(); break;
+    case 1: sm_wait<1>(); break;
+    case 2: sm_wait<2>(); break;
+    case 3: sm_wait<3>(); break;
+    case 4: sm_wait<4>(); break;
+    case 5: sm_wait<5>(); break;
+    case 6: sm_wait<6>(); break;
+    case 7: sm_wait<7>(); break;
+    case 8: sm_wait<8>(); break;
+    case 9: sm_wait<9>(); break;
+    case 10: sm_wait<10>(); break;
+    case 11: sm_wait<11>(); break;
+    case 12: sm_wait<12>(); break;
+    case 13: sm_wait<13>(); break;
+    case 14: sm_wait<14>(); break;
+    default: sm_wait<15>(); break;
+    }
+}
+
+// Tall matrices: R waves, each with its own T weight tiles and the whole
+// row of blocks, share one activation stage.  Wave w loads its weight rows
+// and the activation loads i = w, w + R, ...; after its own loads have
+// landed it meets the others at a barrier (then every load of the stage has
+// landed), computes, and meets them again before the buffer it read is
+// refilled.  The activation rows are read from L2 once per R T weight tiles
+// instead of once per tile, and a wave needs only its weight rows' LDS.
+template <int T, int MP, int R>
+__global__ __launch_bounds__(64 * R) void q4_0_small_m_shared_kernel(const uint8_t *__restrict__ w,
+                                                                     const uint8_t *__restrict__ xq,
+                                                                     float *__restrict__ y, int64_t m, int64_t n,
+                                                                     int nb)
+{
+    using L = SmLayout<T, MP>;
+    constexpr int MT = sm_mt(MP), N = T * MT, WB = 1024 * L::NW, XB = 1024 * L::NX;
+    static_assert(N * 4 * 64 * 4 <= WB, "a wave's output tile fits in its weight buffer");
+    static_assert(L::NW + (L::NX + R - 1) / R <= 15, "loads per wave and stage");
+    __shared__ __attribute__((aligned(16))) char wst[2][R][WB];
+    __shared__ __attribute__((aligned(16))) char xst[2][XB];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row0 = ((int64_t)blockIdx.x * R + wave) * L::WR;
+    // a last workgroup's waves past n load row n - 1 (outputs dropped)
+    const int64_t lrow0 = row0 < n ? row0 : n - 1;
+    const uint8_t *wt = w + lrow0 * ((int64_t)nb * 18);
+    const int nst = (nb + kSmSB - 1) / kSmSB, blast = nb - kSmSB;
+    SmOff<T, MP> o;
+    sm_offsets<T, MP>(m, n, nb, lrow0, o);
+    const int nxw = (L::NX - wave + R - 1) / R; // this wave's activation loads per stage (may be 0)
+    const int dma = L::NW + nxw;
+    const uint32_t wl[2] = {(uint32_t)(uintptr_t)&wst[0][wave][0], (uint32_t)(uintptr_t)&wst[1][wave][0]};
+    const uint32_t xl[2] = {(uint32_t)(uintptr_t)&xst[0][0], (uint32_t)(uintptr_t)&xst[1][0]};
+    auto load = [&](int st, int j) {
+        const int be = min(st * kSmSB, blast);
+        const uint8_t *wb = wt + 18 * (int64_t)be, *xb = xq + 34 * (int64_t)be;
+#pragma unroll
+        for (int i = 0; i < L::NX; i++)
+            if (i % R == wave) // uniform
+                sm_dma16(xb, o.x[i], xl[j] + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < L::NW; i++)
+            sm_dma16(wb, o.w[i], wl[j] + 1024 * i);
+    };
+
+    const uint32_t width = lane < 16 ? 16u : 0u; // the scale operands live in lanes 0..15
+    float acc[N][4];
+#pragma unroll
+    for (int t = 0; t < N; t++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            acc[t][i] = 0.0f;
+    load(0, 0);
+    if (1 < nst)
+        load(1, 1);
+    for (int s2 = 0; s2 < nst; s2 += 2) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int st = s2 + j;
+            if (st >= nst)
+                break;
+            sm_wait_n(st + 1 < nst ? dma : 0); // this wave's loads of stage st have landed
+            __syncthreads();                    // and every wave's
+            const SmBufs sb{(const QLL_LDS_M char *)&wst[j][wave][0], (const QLL_LDS_M char *)&xst[j][0]};
+            sm_stage<T, MP>(sb, st * kSmSB - min(st * kSmSB, blast), width, acc);
+            if (st + 2 < nst) {
+                __syncthreads(); // every wave is done reading buffer j
+                load(st + 2, j);
+            }
+        }
+    }
+
+    // The wave's tile through its own weight buffer (its loads have all
+    // landed), as part[4 t + i][lane], then stored row-contiguously.
+    typedef float Part[N * 4][64];
+    Part &part = *reinterpret_cast<Part *>(&wst[0][wave][0]);
+#pragma unroll
+    for (int t = 0; t < N; t++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            part[4 * t + i][lane] = acc[t][i];
+    for (int oi = lane; oi < 256 * N; oi += 64) {
+        const int col = oi / L::WR, row = oi % L::WR;
+        const int u = row >> 4, t = col >> 4;
+        const int reg = 4 * (u * MT + t) + (row & 3), ln = 16 * ((row & 15) >> 2) + (col & 15);
+        if (col < m && row0 + row < n)
+            y[(int64_t)col * n + row0 + row] = part[reg][ln] * 0.0625f; // the sums were of 16 P
+    }
+}
+
 // Workgroups of one split that fit on a CU at once (the LDS bounds them).
 template <int T, int MP>
 constexpr int sm_per_cu(int ks)
@@ -380,70 +498,71 @@ static void launch_sm(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, 
 // Activation rows staged for m: 4, 8, 16 or 32.
 static int sm_rows(int64_t m) { return m <= 4 ? 4 : m <= 8 ? 8 : m <= 16 ? 16 : 32; }
 
-// 16-row weight tiles per wave: two (each activation fragment feeding two
-// block sums, so the activation rows, re-read for every weight tile, cost
-// half as much per weight byte) for tall matrices at m > 4 and for
-// 8192 <= n < 32768 at m > 16; one elsewhere, where the extra workgroups
-// matter more (measured, 4096 -> 128256 at m = 16: 96 -> 79 us; 4096 ->
-// 14336 at m = 32: 19.4 -> 17.3 us, at m = 16: 13.9 -> 14.9 us).
-int small_m_mfma_row_tiles(int64_t m, int64_t n, int64_t k)
+// 16-row weight tiles per wave, where the activation stages are the wave's
+// own: two (each activation fragment feeding two block sums, so the
+// activation rows, re-read for every weight tile, cost half as much per
+// weight byte) from n = 8192 at m > 16; one elsewhere, where the extra
+// workgroups matter more (measured, 4096 -> 14336 at m = 32: 19.4 -> 17.3
+// us, at m = 16: 13.9 -> 14.9 us).
+static int small_m_mfma_row_tiles(int64_t m, int64_t n, int64_t k)
 {
     (void)k;
-    return (n >= 32768 && m > 4) || (n >= 8192 && m > 16) ? 2 : 1;
+    return n >= 8192 && m > 16 ? 2 : 1;
 }
 
-template <int T>
-static int sm_per_cu_rt(int mp, int ks)
+static int sm_per_cu_1(int mp, int ks)
 {
-    return mp == 4 ? sm_per_cu<T, 4>(ks) : mp == 8 ? sm_per_cu<T, 8>(ks) : mp == 16 ? sm_per_cu<T, 16>(ks)
-                                                                                     : sm_per_cu<T, 32>(ks);
+    return mp == 4 ? sm_per_cu<1, 4>(ks) : mp == 8 ? sm_per_cu<1, 8>(ks) : mp == 16 ? sm_per_cu<1, 16>(ks)
+                                                                                     : sm_per_cu<1, 32>(ks);
 }
 
 // Waves per row tile: the largest split (at most 8, or 2 with two-tile
 // waves) whose workgroups all fit on the chip at once and that leaves every
 // wave at least two stages; one wave per row tile when even that is more
 // workgroups than fit.
-int small_m_mfma_split(int64_t m, int64_t n, int64_t k)
+static int small_m_mfma_split(int64_t m, int64_t n, int64_t k)
 {
     const int rt = small_m_mfma_row_tiles(m, n, k), mp = sm_rows(m);
     const int64_t tiles = (n + 16 * rt - 1) / (16 * rt), nst = (k / 32 + kSmSB - 1) / kSmSB;
-    for (int ks = rt == 2 ? 2 : 8; ks > 1; ks /= 2) { // two-tile waves go with tall matrices: few splits fit
-        const int per_cu = rt == 2 ? sm_per_cu_rt<2>(mp, ks) : sm_per_cu_rt<1>(mp, ks);
+    for (int ks = rt == 2 ? 2 : 8; ks > 1; ks /= 2) {
+        const int per_cu = rt == 2 ? sm_per_cu<2, 32>(ks) : sm_per_cu_1(mp, ks); // two tiles: m > 16
         if (nst >= 2 * ks && tiles <= 256 * per_cu)
             return ks;
     }
     return 1;
 }
 
-template <int T, int MP>
+template <int MP>
 static void launch_sm_ks(int ks, const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int nb,
                          hipStream_t s)
 {
-    if constexpr (T == 2) {
-        if (ks == 1)
-            launch_sm<T, MP, 1>(w, xq, y, m, n, nb, s);
-        else
-            launch_sm<T, MP, 2>(w, xq, y, m, n, nb, s);
-    } else {
-        switch (ks) {
-        case 1: launch_sm<T, MP, 1>(w, xq, y, m, n, nb, s); break;
-        case 2: launch_sm<T, MP, 2>(w, xq, y, m, n, nb, s); break;
-        case 4: launch_sm<T, MP, 4>(w, xq, y, m, n, nb, s); break;
-        default: launch_sm<T, MP, 8>(w, xq, y, m, n, nb, s); break;
-        }
+    switch (ks) {
+    case 1: launch_sm<1, MP, 1>(w, xq, y, m, n, nb, s); break;
+    case 2: launch_sm<1, MP, 2>(w, xq, y, m, n, nb, s); break;
+    case 4: launch_sm<1, MP, 4>(w, xq, y, m, n, nb, s); break;
+    default: launch_sm<1, MP, 8>(w, xq, y, m, n, nb, s); break;
     }
 }
 
-template <int T>
-static void launch_sm_rows(int ks, const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int nb,
-                           hipStream_t s)
+// Tall matrices (n >= 32768) at m > 4 share each activation stage among the
+// waves of a workgroup: kShR waves of kShT weight tiles (measured on
+// 4096 -> 128256 at m = 8 / 16 / 32 / 48: 78 / 80 / 126 / 194 us with
+// one-wave stages, 72 / 76 / 103 / 173 us with four waves of two tiles;
+// one tile or two waves were slower).
+constexpr int kShT = 2, kShR = 4;
+
+static bool small_m_mfma_shared(int64_t m, int64_t n, int64_t k)
 {
-    switch (sm_rows(m)) {
-    case 4: launch_sm_ks<T, (T == 2 ? 8 : 4)>(ks, w, xq, y, m, n, nb, s); break; // two-tile waves start above m = 4
-    case 8: launch_sm_ks<T, 8>(ks, w, xq, y, m, n, nb, s); break;
-    case 16: launch_sm_ks<T, 16>(ks, w, xq, y, m, n, nb, s); break;
-    default: launch_sm_ks<T, 32>(ks, w, xq, y, m, n, nb, s); break;
-    }
+    (void)k;
+    return n >= 32768 && m > 4;
+}
+
+template <int MP>
+static void launch_sh(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int nb, hipStream_t s)
+{
+    const unsigned groups = (unsigned)((n + 16 * kShT * kShR - 1) / (16 * kShT * kShR));
+    hipLaunchKernelGGL((q4_0_small_m_shared_kernel<kShT, MP, kShR>), dim3(groups), dim3(64 * kShR), 0, s, w, xq, y,
+                       m, n, nb);
 }
 
 hipError_t launch_q4_0_q8_0_small_m_mfma(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n,
@@ -453,11 +572,28 @@ hipError_t launch_q4_0_q8_0_small_m_mfma(const uint8_t *w, const uint8_t *xq, fl
         return hipErrorInvalidValue;
     if ((n + 15) / 16 > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    const int nb = (int)(k / 32), ks = small_m_mfma_split(m, n, k);
-    if (small_m_mfma_row_tiles(m, n, k) == 2)
-        launch_sm_rows<2>(ks, w, xq, y, m, n, nb, s);
-    else
-        launch_sm_rows<1>(ks, w, xq, y, m, n, nb, s);
+    const int nb = (int)(k / 32), mp = sm_rows(m);
+    if (small_m_mfma_shared(m, n, k)) { // m > 4: 8, 16 or 32 staged rows
+        if (mp == 8)
+            launch_sh<8>(w, xq, y, m, n, nb, s);
+        else if (mp == 16)
+            launch_sh<16>(w, xq, y, m, n, nb, s);
+        else
+            launch_sh<32>(w, xq, y, m, n, nb, s);
+    } else if (small_m_mfma_row_tiles(m, n, k) == 2) { // m > 16: 32 staged rows
+        if (small_m_mfma_split(m, n, k) == 1)
+            launch_sm<2, 32, 1>(w, xq, y, m, n, nb, s);
+        else
+            launch_sm<2, 32, 2>(w, xq, y, m, n, nb, s);
+    } else {
+        const int ks = small_m_mfma_split(m, n, k);
+        switch (mp) {
+        case 4: launch_sm_ks<4>(ks, w, xq, y, m, n, nb, s); break;
+        case 8: launch_sm_ks<8>(ks, w, xq, y, m, n, nb, s); break;
+        case 16: launch_sm_ks<16>(ks, w, xq, y, m, n, nb, s); break;
+        default: launch_sm_ks<32>(ks, w, xq, y, m, n, nb, s); break;
+        }
+    }
     return hipGetLastError();
 }
 

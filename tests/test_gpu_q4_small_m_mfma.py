@@ -2,7 +2,7 @@
 at 2 <= m <= 32) against the oracle.  The shapes drive every split of a row
 tile's blocks over its waves (1, 2, 4 and 8 waves; at most 4 with 32 staged
 activation rows) with each staged activation tile height (4, 8, 16 and 32
-rows), ragged last row tiles,
+rows), the workgroups that share activation stages on tall matrices, ragged last row tiles,
 ragged last stages, and rows of fewer than eight blocks (run by the
 GEMV-style kernel in groups of eight activation rows).  Float outputs within
 1e-4 * sum_b |term_b|; with unit scales every output is an integer below
@@ -18,9 +18,9 @@ from gpu_util import assert_within, host, pack_q4_0, q4_gemm, quantize_q8_0
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
 
-# (m, n, k, (16-row weight tiles per wave, waves per row tile); None: rows
-# under eight blocks, which run the GEMV-style kernel by groups of eight
-# activation rows)
+# (m, n, k, (16-row weight tiles per wave, waves per row tile), or "shared":
+# workgroups sharing activation stages; None: rows under eight blocks, which
+# run the GEMV-style kernel by groups of eight activation rows)
 CASES = [
     (2, 33, 4096, (1, 8)),        # few row tiles: the widest split; ragged last tile
     (5, 33, 4096, (1, 8)),
@@ -35,19 +35,21 @@ CASES = [
     (3, 9000, 1024, (1, 2)),
     (6, 2000, 2048, (1, 4)),
     (7, 9000, 1024, (1, 2)),
-    (8, 70001, 512, (2, 1)),
+    (8, 70001, 512, "shared"),
     (12, 129, 608, (1, 1)),       # 19 blocks: a last stage that starts inside the one before
     (12, 20001, 1056, (1, 2)),
     (32, 1000, 2048, (1, 4)),     # 32-row activation tiles
     (24, 8001, 1056, (1, 2)),     # 33 blocks
-    (20, 70000, 512, (2, 1)),
+    (20, 70000, 512, "shared"),
     (17, 20001, 2048, (2, 1)),
     (12, 129, 256, (1, 1)),       # eight blocks: one stage
     (13, 33, 2048, (1, 4)),
     (4, 20001, 1024, (1, 2)),
-    (7, 32768, 1024, (2, 2)),
-    (13, 32768, 256, (2, 1)),
-    (13, 32768, 1024, (2, 2)),
+    (7, 32768, 1024, "shared"),
+    (13, 32768, 256, "shared"),
+    (13, 32768, 1024, "shared"),
+    (9, 32808, 1056, "shared"),   # a last workgroup with waves wholly past n; 33 blocks
+    (17, 40001, 4128, "shared"),  # 129 blocks
     (29, 33, 256, (1, 1)),
     (29, 9000, 1024, (2, 2)),
     (32, 9, 32, None),            # one block
@@ -57,17 +59,21 @@ CASES = [
 
 
 def _split(m, n, k):
-    # the launcher's choices (q4_small_mfma.hip): 16-row weight tiles per
-    # wave (two from n = 32768 at m > 4 and from n = 8192 at m > 16), and
-    # waves per row tile: the largest split, at most 8 (2 with two-tile
-    # waves), whose workgroups all fit on the 256 CUs at once (160 KB of LDS
-    # each; a wave holds two stage buffers of 3 or 5 KB of weight rows and
-    # 2, 3, 5 or 9 KB for 4, 8, 16 or 32 staged activation rows) and that
-    # leaves each wave two eight-block stages; None where the row has fewer
-    # than eight blocks
+    # the launcher's choices (q4_small_mfma.hip).  From n = 32768 at m > 4:
+    # "shared", workgroups of four waves of two 16-row weight tiles sharing
+    # each activation stage.  Otherwise (16-row weight tiles per wave, waves
+    # per row tile): two tiles from n = 8192 at m > 16, else one; waves per
+    # row tile the largest split, at most 8 (2 with two-tile waves), whose
+    # workgroups all fit on the 256 CUs at once (160 KB of LDS each; a wave
+    # holds two stage buffers of 3 or 5 KB of weight rows and 2, 3, 5 or 9
+    # KB for 4, 8, 16 or 32 staged activation rows) and that leaves each
+    # wave two eight-block stages.  None where the row has fewer than eight
+    # blocks.
     if k < 256:
         return None
-    rt = 2 if (n >= 32768 and m > 4) or (n >= 8192 and m > 16) else 1
+    if n >= 32768 and m > 4:
+        return "shared"
+    rt = 2 if n >= 8192 and m > 16 else 1
     mp = 4 if m <= 4 else 8 if m <= 8 else 16 if m <= 16 else 32
     per_wave = 2 * 1024 * ({1: 3, 2: 5}[rt] + {4: 2, 8: 3, 16: 5, 32: 9}[mp])
     tiles, nst = -(-n // (16 * rt)), -(-(k // 32) // 8)
