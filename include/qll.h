@@ -127,7 +127,7 @@ int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64
  * the kernels address 32 activation rows, or a 128-row panel, with 32-bit
  * offsets).  ws/ws_bytes: device workspace of at least
  * qll_workspace_bytes(QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) bytes (nonzero for
- * the 128-row GEMM: m > 64, or m > 48 with n >= 32768): the call first
+ * the 128-row GEMM, m > 64): the call first
  * writes the activations there in the matrix-core operand form (exact f16
  * codes, scale bits, bias terms), then split-k partial sums when it splits
  * k; contents on return are unspecified.  m == 1 runs the GEMV kernel;
@@ -135,7 +135,7 @@ int qll_q4_0_q8_0_gemv(const void *w, const void *xq, float *y, int64_t n, int64
  * general GEMM, one row-dot per weight row in 9.9.2) runs kernels that load
  * every weight once for all m rows -- a GEMV-shaped one, or one that forms
  * 16 x 16 tiles of block sums on the int8 matrix core -- and 33 <= m <= 64
- * (48 with n >= 32768) runs them on groups of at most 32 activation rows;
+ * runs them on groups of at most 32 activation rows;
  * none of these needs a workspace.  At m == 1 the GEMV's limit k <= 49152
  * applies. */
 int qll_q4_0_q8_0_gemm(const void *w, const void *xq, float *y, int64_t m, int64_t n, int64_t k, void *ws,

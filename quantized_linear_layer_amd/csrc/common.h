@@ -113,16 +113,14 @@ constexpr int64_t kMinKMfma = 256, kMaxKMfma = (int64_t)1 << 24;
 
 // Whether the Q4_0 x Q8_0 GEMM entry runs the small-m kernels (no
 // workspace) rather than the 128-row GEMM: m <= 8 at any k; otherwise
-// k < kMaxKMfma and m <= 32, or m <= 64 as groups of at most 32 activation
+// k < kMaxKMfma and m <= 64, above 32 as groups of at most 32 activation
 // rows (each group re-reads the weights, which beats the GEMM's padding of m
-// to 128 rows up to there: 4096 -> 14336 at m = 64 33.8 against 44.0 us),
-// except on tall matrices from m = 49 (4096 -> 128256 at m = 64: 242
-// against 231 us).
+// to 128 rows up to there: at m = 64, 4096 -> 14336 33 against 44 us,
+// 4096 -> 128256 206 against 234 us; at m = 96 the GEMM wins).
 inline bool q4_small_m_path(int64_t m, int64_t n, int64_t k)
 {
-    if (m <= kMaxMSmall)
-        return true;
-    return k < kMaxKMfma && (m <= kMaxMMfma || (m <= 64 && !(n >= 32768 && m > 48)));
+    (void)n;
+    return m <= kMaxMSmall || (k < kMaxKMfma && m <= 64);
 }
 hipError_t launch_q4_0_q8_0_small_m_mfma(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n,
                                          int64_t k, hipStream_t s);

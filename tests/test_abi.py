@@ -64,8 +64,8 @@ def test_workspace_sizes(L):
         assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, m, 4096, 14336) == 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 8, 64, 2 ** 24) == 0         # m <= 8: no k limit
     assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 65, 4096, 14336) > 0         # the 128-row GEMM
-    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 48, 128256, 4096) == 0       # tall: groups up to 48
-    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 49, 128256, 4096) > 0
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 64, 128256, 4096) == 0
+    assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, 65, 128256, 4096) > 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_TERNARY_GEMM, 64, 6912, 2560) == 0
     assert qll.qll_workspace_bytes(qll.QLL_OP_TERNARY_GEMM, 64, 6912, 2561) == SIZE_MAX
     # the fused entry: none where its single launch is the faster route

@@ -137,7 +137,7 @@ def test_small_m_mfma_one_hot(qll_gpu):
     assert np.array_equal(y.astype(np.float64), want)
 
 
-# 33 <= m <= 64 (48 on tall matrices): groups of at most 32 activation rows,
+# 33 <= m <= 64: groups of at most 32 activation rows,
 # a last group of one row on the GEMV, of 2..8 rows on the small-m kernels,
 # rows of fewer than eight blocks on the GEMV-style kernel by eights
 @pytest.mark.parametrize("m,n,k", [(33, 300, 4096), (40, 1000, 1056), (64, 17, 14336), (48, 40000, 512),
