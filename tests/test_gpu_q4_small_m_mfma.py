@@ -141,7 +141,7 @@ def test_small_m_mfma_one_hot(qll_gpu):
 # a last group of one row on the GEMV, of 2..8 rows on the small-m kernels,
 # rows of fewer than eight blocks on the GEMV-style kernel by eights
 @pytest.mark.parametrize("m,n,k", [(33, 300, 4096), (40, 1000, 1056), (64, 17, 14336), (48, 40000, 512),
-                                   (37, 129, 96), (57, 14336, 4096)])
+                                   (37, 129, 96), (57, 14336, 4096), (64, 40000, 1056), (49, 32769, 256)])
 def test_small_m_groups(qll_gpu, m, n, k):
     assert qll.qll_workspace_bytes(qll.QLL_OP_Q4_0_Q8_0_GEMM, m, n, k) == 0  # the small-m path
     codes, d_bits, x = _case(m * 3 + n + k, m, n, k)
