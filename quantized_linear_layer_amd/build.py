@@ -27,7 +27,8 @@ FLAGS = ["-std=c++17", "-O3", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-
 # (the default AGPR form serialised them through one accumulator) and the
 # fmas that apply the scales read them without a v_accvgpr_read each.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA = {"q4_gemm.hip": _VGPR_FORM, "q4_packed.hip": _VGPR_FORM, "q4_small_mfma.hip": _VGPR_FORM}
+EXTRA = {"q4_gemm.hip": _VGPR_FORM, "q4_packed.hip": _VGPR_FORM, "q4_small_mfma.hip": _VGPR_FORM,
+         "ternary.hip": _VGPR_FORM}
 
 
 def _compile(src):

@@ -660,14 +660,217 @@ __global__ __launch_bounds__(64 * KS) void ternary_gemm_ks_kernel(const uint32_t
     }
 }
 
+// ------------------------------------------------------------------ GEMM, about one workgroup per CU, 128 <= k <= 3072
+// The k-split kernel's tile (32 activation rows x 64 weight rows) and MFMA,
+// arranged for grids that fit on the CUs at once (the BitNet layer at
+// m = 64: 216 workgroups).  There, 32-word chunks dealt to five waves leave
+// one SIMD with two waves' MFMAs and unpacking while the others have one.
+// Here eight waves, two per SIMD: the row's 128-code steps are cut into
+// four equal shares, one per SIMD, and SIMD s's share into a first part for
+// wave s and the rest for wave s + 4 (the waves of a workgroup go to the
+// SIMDs in turn), so every SIMD dots the same number of steps and always
+// has a second wave to cover one wave's dependency and LDS latencies.  A
+// wave requests its whole part in one burst into its own LDS region, its
+// 64 weight rows' words first and then the activation step by step, and
+// dots each step as soon as it has landed; no barrier until the end.
+// Layout of a region:
+//   * x[step][row][slot]: the step's 128 activation bytes of the row as
+//     eight 16-byte pieces (piece p = word p of the step), piece p in slot
+//     p ^ f(row), f(row) = (row & 7) ^ ((row >> 3) & 1): the 8 or 16 lanes
+//     that one pass of a fragment read serves fall in distinct banks.  A
+//     DMA instruction fills rows 8i .. 8i + 7 with whole 128-byte lines.
+//   * w[row][piece]: the weight row's words of the part, row-major (2 NQ
+//     pieces of 4 words), so each DMA instruction reads whole runs of
+//     2 NQ x 16 bytes.
+// Step j: lane (r, h) reads word 4h + u of activation row r (transposed to
+// the unpack order) for MFMA u = 0..3 and words 4h .. 4h + 3 of weight rows
+// r and 32 + r (one 16-byte read each).  The exact int32 partial tiles are
+// added in LDS in a fixed order at the end.
+constexpr int kTbSimds = 4, kTbWaves = 2 * kTbSimds, kTbMaxQ = 3; // 18 KB of LDS per wave at 3: 144 KB
+constexpr int64_t kTbMaxTiles = 256; // the grid fits on the 256 CUs at once
+
+template <int NQ>
+struct TbLds {
+    u32x4 x[NQ][kTerKsRows][8];
+    u32x4 w[kTerKsCols * 2 * NQ];
+};
+
+template <int NQ>
+struct TbOff {
+    uint32_t x[4];      // activation DMA i: row 8i + lane / 8 (clamped to m), its piece for slot lane % 8
+    uint32_t w[2 * NQ]; // weight DMA i: row (64i + lane) / 2NQ (clamped to n), 16-byte half of the step
+    int wq[2 * NQ];     // the step of the part that weight DMA i's piece belongs to
+};
+
+template <int NQ>
+__device__ __forceinline__ void tb_offsets(int64_t m, int64_t n, int nw, int64_t m0, int64_t n0, TbOff<NQ> &o)
+{
+    const int lane = threadIdx.x & 63;
+    // m * k and n * k / 4 are below 2^32 - 4096 (checked at launch)
+    const uint32_t xrow = (uint32_t)nw * 16u, wrow = (uint32_t)nw * 4u;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int row = 8 * i + (lane >> 3);
+        const int piece = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
+        const uint32_t gi = (uint32_t)(m0 + row < m ? m0 + row : m - 1);
+        o.x[i] = gi * xrow + 16u * (uint32_t)piece;
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * NQ; i++) {
+        const int p = 64 * i + lane, row = p / (2 * NQ), pc = p % (2 * NQ);
+        const uint32_t gj = (uint32_t)(n0 + row < n ? n0 + row : n - 1);
+        o.w[i] = gj * wrow + 16u * (uint32_t)(pc & 1);
+        o.wq[i] = pc >> 1;
+    }
+}
+
+// Step j of the region into the two 32x32 accumulators.
+template <int NQ>
+__device__ __forceinline__ void tb_step(const TbLds<NQ> &s, int j, int r, int h, i32x16 *acc)
+{
+    const int f = (r & 7) ^ ((r >> 3) & 1);
+    u32x4 wv[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++)
+        wv[jj] = s.w[(32 * jj + r) * 2 * NQ + 2 * j + h];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const i32x4 a = __builtin_bit_cast(i32x4, transpose_4x4_bytes(s.x[j][r][(4 * h + u) ^ f]));
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++) {
+            const uint32_t cw = wv[jj][u];
+            const i32x4 b = {(int)(cw & 0x03030303u), (int)((cw >> 2) & 0x03030303u),
+                             (int)((cw >> 4) & 0x03030303u), (int)((cw >> 6) & 0x03030303u)};
+            acc[jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[jj], 0, 0, 0);
+        }
+    }
+}
+
+// Wait until steps 0 .. j of a burst of NQ steps have landed (the weights
+// first, then four activation loads per step).
+template <int NQ>
+__device__ __forceinline__ void tb_wait(int j)
+{
+    static_assert(NQ <= 3, "waits below");
+    switch (4 * (NQ - 1 - j)) {
+    case 4: ter_wait<4>(); break;
+    case 8: ter_wait<8>(); break;
+    default: ter_wait<0>(); break;
+    }
+}
+
+template <int NQ>
+__global__ __launch_bounds__(64 * kTbWaves) void ternary_gemm_burst_kernel(const uint32_t *__restrict__ w,
+                                                                           float w_scale,
+                                                                           const int8_t *__restrict__ xq,
+                                                                           const float *__restrict__ act_scale,
+                                                                           const int32_t *__restrict__ act_sum,
+                                                                           float *__restrict__ y, int64_t m,
+                                                                           int64_t n, int nw)
+{
+    constexpr int PAD = kTerKsCols + 8; // the two lane halves of a partial-tile store land 32 banks apart
+    static_assert(kTerKsRows * PAD * 4 <= (int)sizeof(TbLds<NQ>), "a wave's partial tile fits in its region");
+    __shared__ TbLds<NQ> lds[kTbWaves];
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t m0 = (int64_t)blockIdx.y * kTerKsRows, n0 = (int64_t)blockIdx.x * kTerKsCols;
+    const int nq = nw >> 3;                               // 128-code steps per row (at most 2 kTbSimds NQ)
+    const int share = (nq + kTbSimds - 1) / kTbSimds;     // steps per SIMD
+    const int first = (share + 1) / 2;                    // wave s's part of SIMD s's share
+    const int sa = (wv % kTbSimds) * share;               // the share's first step
+    const int se = sa + share < nq ? sa + share : nq;     // .. and its end
+    const int qa = wv < kTbSimds ? sa : sa + first;       // this wave's part: steps qa .. qb - 1
+    const int qb0 = wv < kTbSimds ? sa + first : se;
+    const int qb = qb0 < se ? qb0 : se;
+
+    // Epilogue: wave wv writes tile rows wv, wv + 8, ...; their scales and
+    // code sums are wave-uniform and requested first.
+    constexpr int PER = kTerKsRows / kTbWaves;
+    float scs[PER];
+    int asums[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int64_t rw = m0 + wv + kTbWaves * i;
+        const int64_t rc = rw < m ? rw : m - 1;
+        scs[i] = act_scale[rc];
+        asums[i] = act_sum[rc];
+    }
+
+    i32x16 acc[2] = {i32x16{}, i32x16{}};
+    if (qa < qb) { // uniform
+        TbOff<NQ> o;
+        tb_offsets<NQ>(m, n, nw, m0, n0, o);
+        TbLds<NQ> &s = lds[wv];
+        // steps past the part (a shorter part) re-read its last step
+#pragma unroll
+        for (int i = 0; i < 2 * NQ; i++) {
+            const int qg = qa + o.wq[i] < qb ? qa + o.wq[i] : qb - 1;
+            ter_dma16(w, o.w[i] + 32u * (uint32_t)qg, (const QLL_LDS_T char *)&s.w[0] + 1024 * i);
+        }
+#pragma unroll
+        for (int j = 0; j < NQ; j++) {
+            const int qg = qa + j < qb ? qa + j : qb - 1;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                ter_dma16(xq + 128 * (int64_t)qg, o.x[i], (const QLL_LDS_T char *)&s.x[j][0][0] + 1024 * i);
+        }
+        if (qb - qa == NQ) { // uniform; no branch between the steps of a whole part
+#pragma unroll
+            for (int j = 0; j < NQ; j++) {
+                tb_wait<NQ>(j);
+                tb_step<NQ>(s, j, r, h, acc);
+            }
+        } else {
+            const int cnt = qb - qa;
+#pragma unroll
+            for (int j = 0; j < NQ; j++) {
+                tb_wait<NQ>(j);
+                if (j < cnt) // uniform
+                    tb_step<NQ>(s, j, r, h, acc);
+            }
+        }
+    }
+
+    __syncthreads(); // every wave is done with its region
+    int *part = reinterpret_cast<int *>(&lds[wv]);
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++)
+#pragma unroll
+        for (int v = 0; v < 16; v++)
+            part[(8 * (v >> 2) + 4 * h + (v & 3)) * PAD + 32 * jj + r] = acc[jj][v];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int rr = wv + kTbWaves * i;
+        const int64_t row = m0 + rr, col = n0 + lane;
+        int dot = 0;
+#pragma unroll
+        for (int q = 0; q < kTbWaves; q++)
+            dot += reinterpret_cast<const int *>(&lds[q])[rr * PAD + lane];
+        if (row < m && col < n)
+            y[row * n + col] = ternary_output(dot, asums[i], w_scale, scs[i]);
+    }
+}
+
 hipError_t launch_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *xq, const float *act_scale,
                                const int32_t *act_sum, float *y, int64_t m, int64_t n, int64_t k, hipStream_t st)
 {
     const int nw = (int)(k / 16);
     // the k-split kernel addresses both operands with 32-bit lane offsets
     const bool small = m * k + 4096 < ((int64_t)1 << 32) && n * (k / 4) + 4096 < ((int64_t)1 << 32);
+    const int64_t tiles = ((n + kTerKsCols - 1) / kTerKsCols) * ((m + kTerKsRows - 1) / kTerKsRows);
+    if (nw % 8 == 0 && nw / 8 <= 2 * kTbSimds * kTbMaxQ && small && tiles <= kTbMaxTiles) {
+        const int nq = nw / 8, share = (nq + kTbSimds - 1) / kTbSimds, first = (share + 1) / 2;
+        const dim3 grid((unsigned)((n + kTerKsCols - 1) / kTerKsCols), (unsigned)((m + kTerKsRows - 1) / kTerKsRows));
+        if (first <= 2)
+            hipLaunchKernelGGL((ternary_gemm_burst_kernel<2>), grid, dim3(64 * kTbWaves), 0, st, w, w_scale, xq,
+                               act_scale, act_sum, y, m, n, nw);
+        else
+            hipLaunchKernelGGL((ternary_gemm_burst_kernel<3>), grid, dim3(64 * kTbWaves), 0, st, w, w_scale, xq,
+                               act_scale, act_sum, y, m, n, nw);
+        return hipGetLastError();
+    }
     if (nw % 4 == 0 && small) {
-        const int64_t tiles = ((n + kTerKsCols - 1) / kTerKsCols) * ((m + kTerKsRows - 1) / kTerKsRows);
         const int nch = (nw + 31) / 32;
         // about one wave per SIMD (1024), at most one chunk per wave
         int64_t split = (kTerKsTargetWaves + tiles - 1) / tiles;

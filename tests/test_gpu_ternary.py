@@ -78,7 +78,14 @@ def test_bitnet_layer_full(qll_gpu, m):
                                    (1, 37, 16384), (1, 19, 65536), (1, 5, 4160), (1, 70, 6208), (1, 130, 192),
                                    # m > 1, k % 64 == 0: the GEMM's k split over 1..6 waves (by grid size
                                    # and chunk count), several chunks per wave, ragged tiles
-                                   (1030, 2050, 1088), (7, 130, 3072), (33, 65, 6208)])
+                                   (1030, 2050, 1088), (7, 130, 3072), (33, 65, 6208),
+                                   # k % 128 == 0, k <= 3072, at most 256 tiles: the eight-wave burst
+                                   # kernel, with waves left without steps (k = 128, 384, 1280, 2688),
+                                   # second parts shorter than the first (1280, 1920, 2560) or as long
+                                   # (3072), ragged tiles, and a grid of exactly 256 tiles; k = 6912
+                                   # beside it goes to the k-split kernel
+                                   (3, 70, 128), (40, 65, 384), (2, 64, 1280), (33, 100, 2560), (9, 200, 2688),
+                                   (20, 90, 1920), (64, 2560, 6912), (50, 8190, 256)])
 def test_shapes(qll_gpu, m, n, k):
     rng = np.random.default_rng(m * 100 + n * 7 + k)
     codes = synth.ternary_codes(rng, n, k)
