@@ -735,11 +735,24 @@ def device_record(torch, dev, copy_gbs):
 
 
 def sclk_mhz():
-    """The GPU's current shader clock as amd-smi reports it (None if unavailable)."""
+    """The GPU's current shader clock as amd-smi reports it (None if unavailable).
+
+    amd-smi is a Python script; it is run as a child of this interpreter
+    binary directly, so that no launcher (a `#!/usr/bin/env` hop) replaces
+    itself by exec in a process that may already hold the GPU.  Under a
+    profiler, whose preloaded library initialises the GPU in every child,
+    the clock is not read at all."""
     import re
+    import shutil
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
+    tool = shutil.which("amd-smi")
+    if tool is None:
+        return None
     try:
-        r = subprocess.run(["amd-smi", "metric", "-c", "-g", "0"], capture_output=True, text=True, timeout=20)
+        r = subprocess.run([sys.executable, tool, "metric", "-c", "-g", "0"], capture_output=True, text=True,
+                           timeout=20)
     except (OSError, subprocess.TimeoutExpired):
         return None
     m = re.search(r"GFX_0:.*?CLK:\s*([0-9]+)\s*MHz", r.stdout, re.S)
