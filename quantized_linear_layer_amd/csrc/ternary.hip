@@ -667,8 +667,8 @@ __global__ __launch_bounds__(64 * KS) void ternary_gemm_ks_kernel(const uint32_t
 // one SIMD with two waves' MFMAs and unpacking while the others have one.
 // Here eight waves, two per SIMD: the row's 128-code steps are cut into
 // four equal shares, one per SIMD, and SIMD s's share into a first part for
-// wave s and the rest for wave s + 4 (the waves of a workgroup go to the
-// SIMDs in turn), so every SIMD dots the same number of steps and always
+// wave s and the rest for wave s + 4 (the waves of a workgroup are placed
+// on the SIMDs in turn), so every SIMD dots the same number of steps and always
 // has a second wave to cover one wave's dependency and LDS latencies.  A
 // wave requests its whole part in one burst into its own LDS region, its
 // 64 weight rows' words first and then the activation step by step, and
@@ -680,13 +680,13 @@ __global__ __launch_bounds__(64 * KS) void ternary_gemm_ks_kernel(const uint32_t
 //     that one pass of a fragment read serves fall in distinct banks.  A
 //     DMA instruction fills rows 8i .. 8i + 7 with whole 128-byte lines.
 //   * w[row][piece]: the weight row's words of the part, row-major (2 NQ
-//     pieces of 4 words), so each DMA instruction reads whole runs of
-//     2 NQ x 16 bytes.
+//     pieces of 4 words for a part of NQ steps), so each DMA instruction
+//     reads whole runs of 2 NQ x 16 bytes.
 // Step j: lane (r, h) reads word 4h + u of activation row r (transposed to
 // the unpack order) for MFMA u = 0..3 and words 4h .. 4h + 3 of weight rows
 // r and 32 + r (one 16-byte read each).  The exact int32 partial tiles are
 // added in LDS in a fixed order at the end.
-constexpr int kTbSimds = 4, kTbWaves = 2 * kTbSimds, kTbMaxQ = 3; // 18 KB of LDS per wave at 3: 144 KB
+constexpr int kTbSimds = 4, kTbWaves = 2 * kTbSimds, kTbMaxShare = 6; // parts of <= 3 steps: 18 KB of LDS per wave
 constexpr int64_t kTbMaxTiles = 256; // the grid fits on the 256 CUs at once
 
 template <int NQ>
@@ -724,9 +724,10 @@ __device__ __forceinline__ void tb_offsets(int64_t m, int64_t n, int nw, int64_t
     }
 }
 
-// Step j of the region into the two 32x32 accumulators.
-template <int NQ>
-__device__ __forceinline__ void tb_step(const TbLds<NQ> &s, int j, int r, int h, i32x16 *acc)
+// Step j of a part of NQ steps (in a region for NR) into the two 32x32
+// accumulators.
+template <int NQ, int NR>
+__device__ __forceinline__ void tb_step(const TbLds<NR> &s, int j, int r, int h, i32x16 *acc)
 {
     const int f = (r & 7) ^ ((r >> 3) & 1);
     u32x4 wv[2];
@@ -759,7 +760,49 @@ __device__ __forceinline__ void tb_wait(int j)
     }
 }
 
-template <int NQ>
+// One wave's part, steps qa .. qb - 1 (at most NQ), into its region: the
+// burst of loads, then each step dotted as soon as it has landed.  Steps
+// past a shorter part re-read its last step (the wait counts stay static).
+template <int NQ, int NR>
+__device__ __forceinline__ void tb_part(const uint32_t *__restrict__ w, const int8_t *__restrict__ xq, int64_t m,
+                                        int64_t n, int nw, int64_t m0, int64_t n0, int qa, int qb, TbLds<NR> &s, int r,
+                                        int h, i32x16 *acc)
+{
+    static_assert(NQ <= NR, "the part fits in the region");
+    TbOff<NQ> o;
+    tb_offsets<NQ>(m, n, nw, m0, n0, o);
+#pragma unroll
+    for (int i = 0; i < 2 * NQ; i++) {
+        const int qg = qa + o.wq[i] < qb ? qa + o.wq[i] : qb - 1;
+        ter_dma16(w, o.w[i] + 32u * (uint32_t)qg, (const QLL_LDS_T char *)&s.w[0] + 1024 * i);
+    }
+#pragma unroll
+    for (int j = 0; j < NQ; j++) {
+        const int qg = qa + j < qb ? qa + j : qb - 1;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            ter_dma16(xq + 128 * (int64_t)qg, o.x[i], (const QLL_LDS_T char *)&s.x[j][0][0] + 1024 * i);
+    }
+    if (qb - qa == NQ) { // uniform; no branch between the steps of a whole part
+#pragma unroll
+        for (int j = 0; j < NQ; j++) {
+            tb_wait<NQ>(j);
+            tb_step<NQ, NR>(s, j, r, h, acc);
+        }
+    } else {
+        const int cnt = qb - qa;
+#pragma unroll
+        for (int j = 0; j < NQ; j++) {
+            tb_wait<NQ>(j);
+            if (j < cnt) // uniform
+                tb_step<NQ, NR>(s, j, r, h, acc);
+        }
+    }
+}
+
+// SHARE = steps per SIMD, ceil(k / 128 / 4): the first wave of a SIMD takes
+// NA = ceil(SHARE / 2) of them, the second the other NB.
+template <int SHARE>
 __global__ __launch_bounds__(64 * kTbWaves) void ternary_gemm_burst_kernel(const uint32_t *__restrict__ w,
                                                                            float w_scale,
                                                                            const int8_t *__restrict__ xq,
@@ -768,19 +811,18 @@ __global__ __launch_bounds__(64 * kTbWaves) void ternary_gemm_burst_kernel(const
                                                                            float *__restrict__ y, int64_t m,
                                                                            int64_t n, int nw)
 {
+    constexpr int NA = (SHARE + 1) / 2, NB = SHARE - NA, NR = NA < 2 ? 2 : NA;
     constexpr int PAD = kTerKsCols + 8; // the two lane halves of a partial-tile store land 32 banks apart
-    static_assert(kTerKsRows * PAD * 4 <= (int)sizeof(TbLds<NQ>), "a wave's partial tile fits in its region");
-    __shared__ TbLds<NQ> lds[kTbWaves];
+    static_assert(kTerKsRows * PAD * 4 <= (int)sizeof(TbLds<NR>), "a wave's partial tile fits in its region");
+    __shared__ TbLds<NR> lds[kTbWaves];
     const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t m0 = (int64_t)blockIdx.y * kTerKsRows, n0 = (int64_t)blockIdx.x * kTerKsCols;
-    const int nq = nw >> 3;                               // 128-code steps per row (at most 2 kTbSimds NQ)
-    const int share = (nq + kTbSimds - 1) / kTbSimds;     // steps per SIMD
-    const int first = (share + 1) / 2;                    // wave s's part of SIMD s's share
-    const int sa = (wv % kTbSimds) * share;               // the share's first step
-    const int se = sa + share < nq ? sa + share : nq;     // .. and its end
-    const int qa = wv < kTbSimds ? sa : sa + first;       // this wave's part: steps qa .. qb - 1
-    const int qb0 = wv < kTbSimds ? sa + first : se;
+    const int nq = nw >> 3;                           // 128-code steps per row: ceil(nq / 4) == SHARE
+    const int sa = (wv % kTbSimds) * SHARE;           // the SIMD's share: steps sa .. se - 1
+    const int se = sa + SHARE < nq ? sa + SHARE : nq;
+    const int qa = wv < kTbSimds ? sa : sa + NA;      // this wave's part: steps qa .. qb - 1
+    const int qb0 = wv < kTbSimds ? sa + NA : se;
     const int qb = qb0 < se ? qb0 : se;
 
     // Epilogue: wave wv writes tile rows wv, wv + 8, ...; their scales and
@@ -798,37 +840,10 @@ __global__ __launch_bounds__(64 * kTbWaves) void ternary_gemm_burst_kernel(const
 
     i32x16 acc[2] = {i32x16{}, i32x16{}};
     if (qa < qb) { // uniform
-        TbOff<NQ> o;
-        tb_offsets<NQ>(m, n, nw, m0, n0, o);
-        TbLds<NQ> &s = lds[wv];
-        // steps past the part (a shorter part) re-read its last step
-#pragma unroll
-        for (int i = 0; i < 2 * NQ; i++) {
-            const int qg = qa + o.wq[i] < qb ? qa + o.wq[i] : qb - 1;
-            ter_dma16(w, o.w[i] + 32u * (uint32_t)qg, (const QLL_LDS_T char *)&s.w[0] + 1024 * i);
-        }
-#pragma unroll
-        for (int j = 0; j < NQ; j++) {
-            const int qg = qa + j < qb ? qa + j : qb - 1;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                ter_dma16(xq + 128 * (int64_t)qg, o.x[i], (const QLL_LDS_T char *)&s.x[j][0][0] + 1024 * i);
-        }
-        if (qb - qa == NQ) { // uniform; no branch between the steps of a whole part
-#pragma unroll
-            for (int j = 0; j < NQ; j++) {
-                tb_wait<NQ>(j);
-                tb_step<NQ>(s, j, r, h, acc);
-            }
-        } else {
-            const int cnt = qb - qa;
-#pragma unroll
-            for (int j = 0; j < NQ; j++) {
-                tb_wait<NQ>(j);
-                if (j < cnt) // uniform
-                    tb_step<NQ>(s, j, r, h, acc);
-            }
-        }
+        if (wv < kTbSimds)
+            tb_part<NA, NR>(w, xq, m, n, nw, m0, n0, qa, qb, lds[wv], r, h, acc);
+        else if constexpr (NB > 0)
+            tb_part<NB, NR>(w, xq, m, n, nw, m0, n0, qa, qb, lds[wv], r, h, acc);
     }
 
     __syncthreads(); // every wave is done with its region
@@ -859,15 +874,21 @@ hipError_t launch_ternary_gemm(const uint32_t *w, float w_scale, const int8_t *x
     // the k-split kernel addresses both operands with 32-bit lane offsets
     const bool small = m * k + 4096 < ((int64_t)1 << 32) && n * (k / 4) + 4096 < ((int64_t)1 << 32);
     const int64_t tiles = ((n + kTerKsCols - 1) / kTerKsCols) * ((m + kTerKsRows - 1) / kTerKsRows);
-    if (nw % 8 == 0 && nw / 8 <= 2 * kTbSimds * kTbMaxQ && small && tiles <= kTbMaxTiles) {
-        const int nq = nw / 8, share = (nq + kTbSimds - 1) / kTbSimds, first = (share + 1) / 2;
+    if (nw % 8 == 0 && nw / 8 <= kTbSimds * kTbMaxShare && small && tiles <= kTbMaxTiles) {
+        const int share = (nw / 8 + kTbSimds - 1) / kTbSimds;
         const dim3 grid((unsigned)((n + kTerKsCols - 1) / kTerKsCols), (unsigned)((m + kTerKsRows - 1) / kTerKsRows));
-        if (first <= 2)
-            hipLaunchKernelGGL((ternary_gemm_burst_kernel<2>), grid, dim3(64 * kTbWaves), 0, st, w, w_scale, xq,
-                               act_scale, act_sum, y, m, n, nw);
-        else
-            hipLaunchKernelGGL((ternary_gemm_burst_kernel<3>), grid, dim3(64 * kTbWaves), 0, st, w, w_scale, xq,
-                               act_scale, act_sum, y, m, n, nw);
+#define QLL_TB(S)                                                                                                      \
+    hipLaunchKernelGGL((ternary_gemm_burst_kernel<S>), grid, dim3(64 * kTbWaves), 0, st, w, w_scale, xq, act_scale,    \
+                       act_sum, y, m, n, nw)
+        switch (share) {
+        case 1: QLL_TB(1); break;
+        case 2: QLL_TB(2); break;
+        case 3: QLL_TB(3); break;
+        case 4: QLL_TB(4); break;
+        case 5: QLL_TB(5); break;
+        default: QLL_TB(6); break;
+        }
+#undef QLL_TB
         return hipGetLastError();
     }
     if (nw % 4 == 0 && small) {
