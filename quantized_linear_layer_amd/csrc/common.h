@@ -96,6 +96,9 @@ hipError_t launch_quantize_i8_rows(const float *x, int8_t *xq, float *act_scale,
                                    int64_t k, hipStream_t s);
 hipError_t launch_q4_0_q8_0_gemv(const uint8_t *w, const uint8_t *xq, float *y, int64_t n, int64_t k,
                                  hipStream_t s);
+// y[i] = sum of parts[s * count + i] over the splits s, in split order (the
+// split-k GEMMs' second launch).
+hipError_t launch_sum_splits(const float *parts, float *y, int64_t count, int splits, hipStream_t s);
 hipError_t launch_q4_0_q8_0_gemm(const uint8_t *w, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
                                  void *ws, hipStream_t s);
 // Small-m decode: Q8_0 activations at 1 <= m <= 64 (groups of at most 32

@@ -581,19 +581,6 @@ __global__ __launch_bounds__(256) void nn_b_split_t_kernel(const float *__restri
     }
 }
 
-// y[i] = sum over s of parts[s][i], in split order.
-__global__ __launch_bounds__(256) void nb_sum_splits_kernel(const float *__restrict__ parts, float *__restrict__ y,
-                                                            int64_t count, int splits)
-{
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count)
-        return;
-    float v = parts[i];
-    for (int s = 1; s < splits; s++)
-        v += parts[s * count + i];
-    y[i] = v;
-}
-
 // b_kn: w is the plain orientation's B[k][n] (f32), transposed by the split.
 hipError_t launch_gemm_nt_bf16_mfma(const float *x, const void *w, int wfmt, float *y, int64_t m, int64_t n,
                                     int64_t k, void *ws, hipStream_t s, bool b_kn)
@@ -650,10 +637,7 @@ hipError_t launch_gemm_nt_bf16_mfma(const float *x, const void *w, int wfmt, flo
     e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
         return e;
-    const int64_t count = m * n;
-    hipLaunchKernelGGL(nb_sum_splits_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, out, y, count,
-                       plan.splits);
-    return hipGetLastError();
+    return launch_sum_splits(out, y, m * n, plan.splits, s);
 }
 
 hipError_t launch_gemv_nt(const float *x, const void *w, int wfmt, float *y, int64_t n, int64_t k, hipStream_t s)

@@ -557,18 +557,6 @@ __global__ __launch_bounds__(kPThreads) void packed_gemm_kernel(const uint8_t *_
             }
 }
 
-// y[i] = sum over s of parts[s][i], in split order.
-__global__ __launch_bounds__(256) void q4p_sum_splits_kernel(const float *__restrict__ parts, float *__restrict__ y,
-                                                             int64_t count, int splits)
-{
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count)
-        return;
-    float v = parts[i];
-    for (int s = 1; s < splits; s++)
-        v += parts[s * count + i];
-    y[i] = v;
-}
 
 // Split k when the output tiles alone leave workgroup slots empty (two
 // workgroups fit per CU); each split keeps at least 16 blocks and a multiple
@@ -642,10 +630,7 @@ static hipError_t launch_packed_gemm(const uint8_t *wp, const uint8_t *xq, float
     e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
         return e;
-    const int64_t count = m * n;
-    hipLaunchKernelGGL(q4p_sum_splits_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, out, y, count,
-                       plan.splits);
-    return hipGetLastError();
+    return launch_sum_splits(out, y, m * n, plan.splits, s);
 }
 
 hipError_t launch_q4_0_packed_gemm(const uint8_t *wp, const uint8_t *xq, float *y, int64_t m, int64_t n, int64_t k,
