@@ -1,5 +1,6 @@
 // Q4_0 x Q8_0 for a handful of activation rows (speculative or batched
-// decode, short prompts: 2 <= m <= 32) on the int8 matrix core.  For every
+// decode, short prompts: 2 <= m <= 32; the GEMM entry runs 33 <= m <= 64 as
+// groups of at most 32 rows) on the int8 matrix core.  For every
 // activation row i, weight row j and block b the arithmetic is that of
 // llama.cpp visual guide lesson 31 "CPU backend" ("How the quantized dot
 // product works"):
@@ -19,8 +20,10 @@
 // second, f16 MFMA; the vector ALU converts each sum and does one fma per
 // output and block.
 //
-// Work split.  A workgroup owns one or two 16-row weight tiles (two on tall
-// matrices, so that each activation fragment feeds two block sums).  Its KS
+// Work split (the tall-matrix form that shares activation stages between
+// waves is described at its kernel below).  A workgroup owns one or two
+// 16-row weight tiles (two on tall matrices, so that each activation
+// fragment feeds two block sums).  Its KS
 // waves take KS contiguous runs of the row's blocks, and each wave streams
 // its run -- its weight rows and every activation row, eight blocks a stage,
 // exactly as stored -- from memory into two LDS stage buffers of its own
