@@ -178,6 +178,8 @@ def _gemm_check(codes, d_bits, x, what):
 # with a one-row tail, weight buffer length 2 mod 4 (131 x 19 blocks)
 @pytest.mark.parametrize("m,n,k", [(2, 1, 32), (3, 7, 96), (17, 64, 512), (130, 129, 320), (128, 128, 4096),
                                    (200, 300, 64), (64, 33, 14336), (128, 256, 3232), (257, 131, 608),
+                                   # split k with m * n odd (the split sum's scalar path) and even
+                                   (65, 33, 14336), (129, 131, 4096), (66, 34, 8192),
                                    # 9 <= m <= 32: the small-m kernels
                                    (9, 257, 4096), (32, 1000, 1024), (31, 128, 96), (20, 33, 14336), (12, 129, 32)])
 def test_gemm_shapes(qll_gpu, m, n, k):

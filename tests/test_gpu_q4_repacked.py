@@ -83,7 +83,7 @@ def test_repack_decodes_to_codes(qll_gpu, n, k):
 # last split), m = 1 and small m (the repacked GEMM serves every m)
 @pytest.mark.parametrize("m,n,k", [(1, 7, 32), (2, 1, 32), (3, 7, 96), (8, 40, 256), (17, 64, 512), (130, 129, 320),
                                    (128, 128, 4096), (200, 300, 64), (64, 33, 14336), (128, 256, 3232),
-                                   (257, 131, 608)])
+                                   (257, 131, 608), (65, 33, 14336)])
 def test_repacked_gemm_shapes(qll_gpu, m, n, k):
     codes, d_bits, x = _case(m * 1000 + n + k, m, n, k)
     w = pack_q4_0(codes, d_bits)
