@@ -186,7 +186,10 @@ __global__ __launch_bounds__(kTg2Threads) void ternary_gemv2_kernel(
     const uint32_t *__restrict__ w, float w_scale, const int8_t *__restrict__ xq, const float *__restrict__ act_scale,
     const int32_t *__restrict__ act_sum, float *__restrict__ y, int64_t n, int nw)
 {
-    extern __shared__ u32x4 s_x[]; // [nw] transposed activation words
+    // transposed activation words, word 4u + e at [e][u]: the lanes of a row
+    // read consecutive 16-byte slots (with [4u + e] they were 64 bytes apart:
+    // 6.7 bank-conflict cycles per read; 3.11 -> 3.04 us at 2560 -> 6912)
+    extern __shared__ u32x4 s_x[];
     constexpr int R = 64 / L, WAVES = kTg2Threads / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / L, r = lane % L;
@@ -222,10 +225,10 @@ __global__ __launch_bounds__(kTg2Threads) void ternary_gemv2_kernel(
     for (int j = 0; j < kTg2ActRegs; j++) {
         const int i = threadIdx.x + j * kTg2Threads;
         if (i < nw)
-            s_x[i] = transpose_4x4_bytes(a[j]);
+            s_x[(i & 3) * nu + (i >> 2)] = transpose_4x4_bytes(a[j]);
     }
     for (int i = threadIdx.x + kTg2ActRegs * kTg2Threads; i < nw; i += kTg2Threads)
-        s_x[i] = transpose_4x4_bytes(xv[i]);
+        s_x[(i & 3) * nu + (i >> 2)] = transpose_4x4_bytes(xv[i]);
     __syncthreads();
 
     int acc[4] = {0, 0, 0, 0};
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(kTg2Threads) void ternary_gemv2_kernel(
             if (u < nu) {
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const u32x4 t = s_x[4 * u + e];
+                    const u32x4 t = s_x[e * nu + u];
                     const uint32_t word = cur[i][e];
                     acc[0] = sdot4(word & 0x03030303u, t[0], acc[0]);
                     acc[1] = sdot4((word >> 2) & 0x03030303u, t[1], acc[1]);
