@@ -53,22 +53,31 @@ __device__ __forceinline__ float nt_weight_scalar(const uint8_t *w, int64_t idx)
 template <int WFMT, int U>
 struct NtRaw {
     u32x4 w[U];
+    float4 x[U][NtW<WFMT>::V / 4];
 };
 
+// A chunk's activation pieces are requested with its weights, one chunk
+// ahead: loads retire in order, so activation loads issued inside the dot
+// would wait for the next chunk's weights (4096^2: f32 weights 15.3 -> 13.5
+// us, bf16 9.0 -> 8.3 us).
 template <int WFMT, int L, int U>
-__device__ __forceinline__ void nt_load(const uint8_t *wr, int64_t nv, int64_t c0, int r, NtRaw<WFMT, U> &raw)
+__device__ __forceinline__ void nt_load(const float *__restrict__ x, const uint8_t *wr, int64_t nv, int64_t c0, int r,
+                                        NtRaw<WFMT, U> &raw)
 {
+    constexpr int V = NtW<WFMT>::V;
 #pragma unroll
     for (int i = 0; i < U; i++) {
         int64_t v = c0 + r + (int64_t)i * L;
         v = v < nv ? v : 0; // past the row: reload vector 0 (masked in nt_dot)
+#pragma unroll
+        for (int q = 0; q < V / 4; q++)
+            raw.x[i][q] = *reinterpret_cast<const float4 *>(x + v * V + 4 * q);
         raw.w[i] = *reinterpret_cast<const u32x4 *>(wr + v * 16);
     }
 }
 
 template <int WFMT, int L, int U>
-__device__ __forceinline__ float nt_dot(const float *__restrict__ x, int64_t nv, int64_t c0, int r,
-                                        const NtRaw<WFMT, U> &raw)
+__device__ __forceinline__ float nt_dot(int64_t nv, int64_t c0, int r, const NtRaw<WFMT, U> &raw)
 {
     constexpr int V = NtW<WFMT>::V;
     float acc = 0.0f;
@@ -76,10 +85,9 @@ __device__ __forceinline__ float nt_dot(const float *__restrict__ x, int64_t nv,
     for (int i = 0; i < U; i++) {
         const int64_t v = c0 + r + (int64_t)i * L;
         if (v < nv) {
-            const float *xv = x + v * V;
 #pragma unroll
             for (int q = 0; q < V / 4; q++) {
-                const float4 xs = *reinterpret_cast<const float4 *>(xv + 4 * q);
+                const float4 xs = raw.x[i][q];
                 acc = fmaf(xs.x, nt_weight<WFMT>(raw.w[i], 4 * q + 0), acc);
                 acc = fmaf(xs.y, nt_weight<WFMT>(raw.w[i], 4 * q + 1), acc);
                 acc = fmaf(xs.z, nt_weight<WFMT>(raw.w[i], 4 * q + 2), acc);
@@ -106,11 +114,11 @@ __global__ __launch_bounds__(kGemvNtThreads) void gemv_nt_kernel(const float *__
         const int64_t nv = k / NtW<WFMT>::V;
         const int64_t step = (int64_t)L * U;
         NtRaw<WFMT, U> cur, nxt;
-        nt_load<WFMT, L, U>(wr, nv, 0, r, cur);
+        nt_load<WFMT, L, U>(x, wr, nv, 0, r, cur);
         for (int64_t c0 = 0; c0 < nv; c0 += step) {
             if (c0 + step < nv)
-                nt_load<WFMT, L, U>(wr, nv, c0 + step, r, nxt);
-            acc += nt_dot<WFMT, L, U>(x, nv, c0, r, cur);
+                nt_load<WFMT, L, U>(x, wr, nv, c0 + step, r, nxt);
+            acc += nt_dot<WFMT, L, U>(nv, c0, r, cur);
             cur = nxt;
         }
     } else {
