@@ -145,7 +145,9 @@ __device__ __forceinline__ T block_reduce_256(T v, Op op, T *scratch)
 }
 
 // One workgroup per row.  VEC = 4 when k % 4 == 0 (float4 loads, 4-byte
-// stores), else 1.
+// stores), else 1.  Rows of at most 4096 elements (VEC = 4) stay in
+// registers between the amax pass and the quantization pass, so the row is
+// read from memory once (2560 elements: 3.12 -> 2.79 us).
 template <int VEC>
 __global__ __launch_bounds__(256) void quantize_i8_rows_kernel(const float *__restrict__ x, int8_t *__restrict__ xq,
                                                                float *__restrict__ act_scale,
@@ -158,6 +160,17 @@ __global__ __launch_bounds__(256) void quantize_i8_rows_kernel(const float *__re
     int8_t *qr = xq + row * k;
     const int64_t nv = k / VEC;
     float a = 0.0f;
+    constexpr int HR = 4; // float4 pieces per thread kept in registers between the two passes
+    float4 held[HR];
+    const bool hold = VEC == 4 && nv <= 256 * HR; // uniform
+    if (hold) {
+#pragma unroll
+        for (int j = 0; j < HR; j++) {
+            const int64_t i = threadIdx.x + 256 * j;
+            held[j] = i < nv ? reinterpret_cast<const float4 *>(xr)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            a = fmaxf(a, fmaxf(fmaxf(fabsf(held[j].x), fabsf(held[j].y)), fmaxf(fabsf(held[j].z), fabsf(held[j].w))));
+        }
+    } else {
     for (int64_t i = threadIdx.x; i < nv; i += 256) {
         if (VEC == 4) {
             float4 v = reinterpret_cast<const float4 *>(xr)[i];
@@ -166,11 +179,26 @@ __global__ __launch_bounds__(256) void quantize_i8_rows_kernel(const float *__re
             a = fmaxf(a, fabsf(xr[i]));
         }
     }
+    }
     const float amax = block_reduce_256(a, [](float p, float q) { return fmaxf(p, q); }, s_f);
     float sc = (amax == 0.0f) ? 0.0f : 127.0f / amax; // IEEE division
     if (!__builtin_isfinite(sc))
         sc = 0.0f;
     int sum = 0;
+    if (hold) {
+#pragma unroll
+        for (int j = 0; j < HR; j++) {
+            const int64_t i = threadIdx.x + 256 * j;
+            if (i < nv) {
+                const float4 v = held[j];
+                int q0 = quant_i8(v.x, sc), q1 = quant_i8(v.y, sc), q2 = quant_i8(v.z, sc), q3 = quant_i8(v.w, sc);
+                sum += q0 + q1 + q2 + q3;
+                reinterpret_cast<uint32_t *>(qr)[i] =
+                    (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) | ((uint32_t)(q2 & 0xff) << 16) |
+                    ((uint32_t)(q3 & 0xff) << 24);
+            }
+        }
+    } else
     for (int64_t i = threadIdx.x; i < nv; i += 256) {
         if (VEC == 4) {
             float4 v = reinterpret_cast<const float4 *>(xr)[i];

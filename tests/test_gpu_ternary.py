@@ -19,7 +19,8 @@ def test_pack_bit_exact(qll_gpu, n, k):
     assert np.array_equal(host(w).view(np.uint32), O.pack_ternary(codes).reshape(-1))
 
 
-@pytest.mark.parametrize("m,k", [(1, 16), (3, 2560), (64, 2560), (5, 30), (2, 1027)])
+@pytest.mark.parametrize("m,k", [(1, 16), (3, 2560), (64, 2560), (5, 30), (2, 1027),
+                                 (2, 4096), (2, 4100)])  # rows held in registers up to 4096, not at 4100
 def test_quantize_i8_rows_bit_exact(qll_gpu, m, k):
     rng = np.random.default_rng(m * 13 + k)
     x = synth.normal_f32(rng, (m, k))
