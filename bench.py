@@ -504,7 +504,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by output rows across GPUs, which this build does not run).", file=sys.stderr)
+              "(the path would shard by output rows across GPUs; the library runs on one GPU).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
